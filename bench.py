@@ -1,0 +1,364 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused 4-bit MoE expert MLP on one MI355X.
+
+One step = the whole hot path on one batch of the OLMoE-1B-7B-shaped layer
+(E=64, H=2048, I=1024, top-8, T=4096, NF4, uniform router logits): route +
+permute + grouped gate_up GEMM (SiLU*up) + grouped down GEMM + gather-combine
+(forward, saving the gate/up projections) followed by the frozen-base dgrad
+(permute + down^T GEMM with the SiLU-backward epilogue + gate_up^T GEMM +
+combines). Throughput = 12*P*H*I algorithmic flops per step / wall time.
+
+Also measured in the same run:
+* per-kernel durations of the four grouped GEMMs with HIP events recorded on
+  the launch stream (library timer hook), the largest gives `roofline`;
+* the decode dequant-GEMV path on the Qwen3-30B-A3B-shaped layer (E=128,
+  H=2048, I=768, top-8, Zipf routing) at T=1 and T=8, cold cache (16 layer
+  copies rotated), as GB/s of the experts actually touched;
+* the CPU oracle (numpy float64) on a bounded sample of the same workload.
+
+Prints ONE JSON line. `--gpus N` with N > 1 exits: this build runs on one GPU.
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """HIP events through the runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+            arr[i] = ev
+        return arr
+
+    def elapsed_ms(self, start, stop):
+        assert self.hip.hipEventSynchronize(stop) == 0
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), start, stop) == 0
+        return ms.value
+
+    def destroy(self, arr):
+        for ev in arr:
+            self.hip.hipEventDestroy(ev)
+
+
+def build_layer(e4b, torch, cfg, seed, kind="nf4", copies=1):
+    from workloads import gen_weights
+
+    stacks = []
+    for which in ("gate_up", "down"):
+        w = torch.from_numpy(gen_weights(cfg, seed, which)).to("cuda")
+        stacks.append(e4b.quantize(w, kind))
+        del w
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    layers = [e4b.MoELayer(*stacks)]
+    for _ in range(copies - 1):
+        gu, dn = stacks
+        layers.append(e4b.MoELayer(
+            e4b.QuantStack(gu.packed.clone(), gu.absmax.clone(), gu.E, gu.out, gu.inn, kind),
+            e4b.QuantStack(dn.packed.clone(), dn.absmax.clone(), dn.E, dn.out, dn.inn, kind)))
+    return layers
+
+
+def train_step_fn(e4b, torch, layer, x, lg, gy, k):
+    """Raw-ABI closures for one forward (saving g|u) + dgrad with preallocated buffers."""
+    lib = e4b.load()
+    T = x.shape[0]
+    dev = x.device
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    y = torch.empty(T, layer.H, dtype=torch.bfloat16, device=dev)
+    gx = torch.empty_like(y)
+    gw = torch.empty(T, k, dtype=torch.float32, device=dev)
+    saved = torch.empty(e4b.saved_bytes(layer, T, k), dtype=torch.uint8, device=dev)
+    ws = torch.empty(e4b.workspace_bytes(layer, T, k), dtype=torch.uint8, device=dev)
+    L = layer.as_c()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    fwd_args = (ctypes.byref(L), T, k, vp(x), vp(lg), vp(idx), vp(w), vp(y), vp(saved), vp(ws),
+                ws.numel(), 1, stream)
+    bwd_args = (ctypes.byref(L), T, k, vp(idx), vp(w), vp(x), vp(saved), vp(gy), vp(gx), vp(gw),
+                vp(ws), ws.numel(), stream)
+
+    def step():
+        s1 = lib.e4b_moe_forward(*fwd_args)
+        s2 = lib.e4b_moe_dgrad(*bwd_args)
+        if s1 or s2:
+            raise RuntimeError(f"e4b status {s1} {s2}")
+
+    keep = (idx, w, y, gx, gw, saved, ws, L)
+    return step, keep
+
+
+def time_kernels(e4b, torch, ev, step, names, n):
+    """Average duration (ms) of each named kernel over n steps, events on its launch stream."""
+    lib = e4b.load()
+    out = {}
+    for name in names:
+        kid = e4b._lib.KERNELS[name]
+        start, stop = ev.create(n), ev.create(n)
+        assert lib.e4b_set_kernel_timer(kid, start, stop, n) == 0
+        for _ in range(n):
+            step()
+        torch.cuda.synchronize()
+        assert lib.e4b_set_kernel_timer(kid, None, None, 0) == 0
+        ms = [ev.elapsed_ms(start[i], stop[i]) for i in range(n)]
+        ev.destroy(start)
+        ev.destroy(stop)
+        out[name] = sum(ms) / n
+    return out
+
+
+def bench_train(args, e4b, torch, ev):
+    from workloads import get_config, gen_x, gen_grad_y, gen_logits
+    from workloads.gen import to_bf16_tensor
+
+    cfg = get_config(args.config)
+    log(f"building {cfg.name} layer E={cfg.E} H={cfg.H} I={cfg.I} k={cfg.k} T={cfg.T}")
+    layer = build_layer(e4b, torch, cfg, args.seed, args.codebook)[0]
+    x = to_bf16_tensor(gen_x(cfg, args.seed)).cuda()
+    gy = to_bf16_tensor(gen_grad_y(cfg, args.seed)).cuda()
+    lg = torch.from_numpy(gen_logits(cfg, args.seed)).cuda()
+    step, keep = train_step_fn(e4b, torch, layer, x, lg, gy, cfg.k)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    P, H, I = cfg.P, cfg.H, cfg.I
+    flops = 12.0 * P * H * I
+    tflops = flops / dt / 1e12
+    log(f"step {dt * 1e3:.3f} ms -> {tflops:.1f} TFLOP/s")
+
+    names = ["gate_up_fwd", "down_fwd", "down_dgrad", "gate_up_dgrad"]
+    kms = time_kernels(e4b, torch, ev, step, names, args.steps)
+    kflops = {"gate_up_fwd": 4.0 * P * H * I, "down_fwd": 2.0 * P * H * I,
+              "down_dgrad": 2.0 * P * H * I, "gate_up_dgrad": 4.0 * P * H * I}
+    kernels = {
+        n: {"ms": round(kms[n], 4), "tflops": round(kflops[n] / (kms[n] * 1e-3) / 1e12, 1)}
+        for n in names
+    }
+    dom = max(names, key=lambda n: kms[n])
+    achieved = kflops[dom] / (kms[dom] * 1e-3) / 1e12
+    roofline = {
+        "bound": "mfma",
+        "kernel": dom,
+        "achieved": round(achieved, 1),
+        "peak": MFMA_BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+        "traffic": None,
+    }
+    res = dict(cfg=cfg, dt=dt, tflops=tflops, kernels=kernels, roofline=roofline)
+    del keep, layer
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(args, e4b, torch, ev):
+    """Decode GEMV GB/s at T=1 and T=8 with 16 layer copies rotated (cold MALL/L2)."""
+    import numpy as np
+    from workloads import get_config, gen_x, gen_logits
+    from workloads.gen import to_bf16_tensor
+
+    copies = 16
+    cfg0 = get_config("qwen3_decode")
+    log(f"building {copies} copies of the qwen3 decode layer")
+    layers = build_layer(e4b, torch, cfg0, args.seed, "nf4", copies=copies)
+    lib = e4b.load()
+    out = {}
+    e_gu = 2 * cfg0.I * cfg0.H // 2 + 2 * cfg0.I * cfg0.H // 64 * 4  # packed + absmax per expert
+    e_dn = cfg0.H * cfg0.I // 2 + cfg0.H * cfg0.I // 64 * 4
+    for T in (1, 8):
+        cfg = get_config("qwen3_decode", T)
+        x = to_bf16_tensor(gen_x(cfg, args.seed)).cuda()
+        lg = torch.from_numpy(gen_logits(cfg, args.seed)).cuda()
+        idx = torch.empty(T, cfg.k, dtype=torch.int32, device="cuda")
+        w = torch.empty(T, cfg.k, dtype=torch.float32, device="cuda")
+        y = torch.empty(T, cfg.H, dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(e4b.workspace_bytes(layers[0], T, cfg.k), dtype=torch.uint8, device="cuda")
+        Ls = [l.as_c() for l in layers]
+        vp = lambda t: ctypes.c_void_p(t.data_ptr())
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        it = [0]
+
+        def step():
+            L = Ls[it[0] % copies]
+            it[0] += 1
+            s = lib.e4b_moe_forward(ctypes.byref(L), T, cfg.k, vp(x), vp(lg), vp(idx), vp(w), vp(y),
+                                    None, vp(ws), ws.numel(), 2, stream)
+            if s:
+                raise RuntimeError(f"e4b status {s}")
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        n = max(args.steps, 32)
+        t0 = time.perf_counter()
+        for _ in range(n):
+            step()
+        torch.cuda.synchronize()
+        call_us = (time.perf_counter() - t0) / n * 1e6
+        kms = time_kernels(e4b, torch, ev, step, ["decode_gate_up", "decode_down"], n)
+        distinct = int(np.unique(idx.cpu().numpy()).size)
+        b_gu = distinct * e_gu + T * cfg.H * 2 + T * cfg.k * cfg.I * 2
+        b_dn = distinct * e_dn + T * cfg.k * cfg.I * 2 + T * cfg.k * cfg.H * 2
+        us = (kms["decode_gate_up"] + kms["decode_down"]) * 1e3
+        gbps = (b_gu + b_dn) / (us * 1e-6) / 1e9
+        out[f"t{T}"] = {
+            "distinct_experts": distinct,
+            "bytes": b_gu + b_dn,
+            "gemv_us": round(us, 2),
+            "gbps": round(gbps, 1),
+            "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "gate_up": {"us": round(kms["decode_gate_up"] * 1e3, 2),
+                        "gbps": round(b_gu / (kms["decode_gate_up"] * 1e-3) / 1e9, 1)},
+            "down": {"us": round(kms["decode_down"] * 1e3, 2),
+                     "gbps": round(b_dn / (kms["decode_down"] * 1e-3) / 1e9, 1)},
+            "forward_call_us": round(call_us, 2),
+            "tokens_per_s": round(T / (call_us * 1e-6), 1),
+            "cache": f"cold ({copies} layer copies rotated)",
+        }
+        log(f"decode T={T}: {distinct} experts, GEMV {us:.2f} us, {gbps:.0f} GB/s")
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(args, cfg):
+    """The oracle (numpy fp64) on the first S tokens of the same workload."""
+    from concurrent.futures import ThreadPoolExecutor
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+    from workloads import gen_x, gen_grad_y, gen_logits, gen_expert_weight
+
+    S = args.cpu_tokens
+    x = gen_x(cfg, args.seed)[:S]
+    gy = gen_grad_y(cfg, args.seed)[:S]
+    idx, w = oracle.route(gen_logits(cfg, args.seed)[:S], cfg.k)
+    experts = sorted(set(int(e) for e in idx.ravel()))
+    log(f"cpu baseline: oracle weights for {len(experts)} experts")
+    stacks = {}
+
+    def prep(args_):
+        which, e = args_
+        wt = gen_expert_weight(cfg, args.seed, which, e)
+        p, a = oracle.quantize_blockwise(wt[None], args.codebook)
+        return which, e, oracle.dequantize(p, a, wt.shape[0], wt.shape[1], args.codebook)[0]
+
+    with ThreadPoolExecutor(max_workers=16) as ex:
+        for which, e, d in ex.map(prep, [(wh, e) for e in experts for wh in ("gate_up", "down")]):
+            stacks[(which, e)] = d
+    remap = {e: i for i, e in enumerate(experts)}
+    wgu = np.stack([stacks[("gate_up", e)] for e in experts])
+    wdn = np.stack([stacks[("down", e)] for e in experts])
+    del stacks
+    idx_c = np.vectorize(remap.get)(idx).astype(np.int32)
+    log(f"cpu baseline: oracle forward + dgrad on {S} tokens")
+    t0 = time.perf_counter()
+    oracle.moe_forward(x, idx_c, w, wgu, wdn)
+    oracle.moe_dgrad(x, idx_c, w, wgu, wdn, gy)
+    dt = time.perf_counter() - t0
+    flops = 12.0 * S * cfg.k * cfg.H * cfg.I
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    return {
+        "value": round(flops / dt / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {S} of {cfg.T} tokens ({S * cfg.k} routed pairs), forward + dgrad, "
+                  f"{dt:.2f} s; weight generation/quantization excluded",
+        "seconds": round(dt, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="olmoe")
+    ap.add_argument("--codebook", default="nf4")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU layout is described in DESIGN.md but not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_quantized_mixture_nf4_amd as e4b
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    e4b.load()
+    ev = HipEvents()
+    tr = bench_train(args, e4b, torch, ev)
+    dec = None if args.no_decode else bench_decode(args, e4b, torch, ev)
+    cfg = tr["cfg"]
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, cfg)
+    line = {
+        "metric": "grouped NF4 MoE fwd+dgrad TFLOP/s (% MFMA peak); decode GEMV HBM GB/s (% peak)",
+        "value": round(tr["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(tr["dt"] * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "OLMoE-1B-7B-shaped MoE layer, forward + frozen-base dgrad",
+            "E": cfg.E, "H": cfg.H, "I": cfg.I, "top_k": cfg.k, "tokens": cfg.T,
+            "routed_pairs": cfg.P, "codebook": args.codebook, "router": cfg.routing,
+            "seed": args.seed,
+        },
+        "pct_mfma_peak": round(100 * tr["tflops"] / MFMA_BF16_PEAK_TFLOPS, 2),
+        "tokens_per_s": round(cfg.T / tr["dt"], 1),
+        "roofline": tr["roofline"],
+        "kernels": tr["kernels"],
+        "decode": dec,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

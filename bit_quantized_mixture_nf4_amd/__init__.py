@@ -1,0 +1,211 @@
+"""MI355X-native fused blockwise-4-bit (NF4 / FP4) Mixture-of-Experts expert MLP.
+
+Thin Python binding over ``libe4b.so`` (C ABI in ``include/e4b.h``). PyTorch is
+used only for device memory and the current HIP stream: every computation runs
+in the library's HIP kernels. The raw entry points are available under their C
+names in :mod:`bit_quantized_mixture_nf4_amd.raw` (``e4b_quantize_nf4``,
+``e4b_dequantize_nf4``, ``e4b_moe_forward``, ``e4b_moe_dgrad``, ...); the
+functions below marshal torch tensors into them.
+
+Layout (the fused-expert storage of the experts4bit-qlora 0.1.0 sdist,
+``Experts4bit``): gate_up ``[E, 2I, H]`` (gate rows first), down
+``[E, H, I]``; packed uint8 ``[E, out*in/2]`` (even element in the high
+nibble) and fp32 absmax ``[E, out*in/64]``.
+"""
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import E4bLayer, E4bStack, E4bError, check, load  # noqa: F401
+
+CODEBOOKS = {"nf4": _lib.E4B_CB_NF4, "fp4": _lib.E4B_CB_FP4}
+PATHS = {"auto": _lib.E4B_PATH_AUTO, "grouped": _lib.E4B_PATH_GROUPED, "decode": _lib.E4B_PATH_DECODE}
+
+__all__ = [
+    "QuantStack",
+    "MoELayer",
+    "quantize",
+    "dequantize",
+    "moe_forward",
+    "moe_dgrad",
+    "workspace_bytes",
+    "saved_bytes",
+    "E4bError",
+]
+
+
+def _vp(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name, dtype, device=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+@dataclass
+class QuantStack:
+    """One quantized fused stack: packed codes + fp32 absmax of an [E, out, in] weight."""
+
+    packed: torch.Tensor  # uint8 [E, out*in/2]
+    absmax: torch.Tensor  # float32 [E, out*in/64]
+    E: int
+    out: int
+    inn: int
+    codebook: str = "nf4"
+
+    def as_c(self):
+        return E4bStack(
+            self.packed.data_ptr(), self.absmax.data_ptr(), self.E, self.out, self.inn, 64,
+            CODEBOOKS[self.codebook],
+        )
+
+    @property
+    def device(self):
+        return self.packed.device
+
+
+@dataclass
+class MoELayer:
+    """gate_up (out = 2I, in = H) and down (out = H, in = I) of one MoE layer."""
+
+    gate_up: QuantStack
+    down: QuantStack
+
+    def as_c(self):
+        return E4bLayer(self.gate_up.as_c(), self.down.as_c())
+
+    @property
+    def E(self):
+        return self.gate_up.E
+
+    @property
+    def H(self):
+        return self.gate_up.inn
+
+    @property
+    def I(self):  # noqa: E743
+        return self.down.inn
+
+    @property
+    def device(self):
+        return self.gate_up.device
+
+
+def quantize(w, codebook="nf4"):
+    """Blockwise (64) absmax 4-bit quantization of a float32 [E, out, in] device stack."""
+    if w.dim() != 3:
+        raise ValueError("w must be [E, out, in]")
+    _need(w, "w", torch.float32)
+    E, out, inn = w.shape
+    if codebook not in CODEBOOKS:
+        raise ValueError(f"codebook must be one of {sorted(CODEBOOKS)}")
+    packed = torch.empty(E, out * inn // 2, dtype=torch.uint8, device=w.device)
+    absmax = torch.empty(E, out * inn // 64, dtype=torch.float32, device=w.device)
+    code = load().e4b_quantize_nf4(
+        _vp(w), E, out, inn, 64, CODEBOOKS[codebook], _vp(packed), _vp(absmax), _stream(w)
+    )
+    check("e4b_quantize_nf4", code)
+    return QuantStack(packed, absmax, E, out, inn, codebook)
+
+
+def dequantize(stack, dtype=torch.float32):
+    """[E, out, in] device tensor of fl32(code * absmax) (or its bf16 rounding)."""
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("dtype must be float32 or bfloat16")
+    out = torch.empty(stack.E, stack.out, stack.inn, dtype=dtype, device=stack.device)
+    st = stack.as_c()
+    code = load().e4b_dequantize_nf4(
+        ctypes.byref(st), _lib.E4B_BF16 if dtype == torch.bfloat16 else _lib.E4B_F32, _vp(out),
+        _stream(out),
+    )
+    check("e4b_dequantize_nf4", code)
+    return out
+
+
+def workspace_bytes(layer, T, top_k):
+    c = layer.as_c()
+    return int(load().e4b_moe_workspace_bytes(ctypes.byref(c), T, top_k))
+
+
+def saved_bytes(layer, T, top_k):
+    c = layer.as_c()
+    return int(load().e4b_moe_saved_bytes(ctypes.byref(c), T, top_k))
+
+
+def _workspace(layer, T, top_k, ws):
+    need = workspace_bytes(layer, T, top_k)
+    if ws is None:
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=layer.device)
+    return ws
+
+
+def moe_forward(layer, x, top_k, logits=None, topk_idx=None, topk_w=None, save=False,
+                path="auto", workspace=None, out=None):
+    """Routed SwiGLU expert forward.
+
+    Either ``logits`` (float32 [T, E]: routing computed on the device) or
+    ``topk_idx`` (int32 [T, k]) and ``topk_w`` (float32 [T, k]) are given.
+    Returns ``(y bf16 [T, H], topk_idx, topk_w, saved or None)``.
+    """
+    dev = layer.device
+    _need(x, "x", torch.bfloat16, dev)
+    T = x.shape[0]
+    if logits is not None:
+        _need(logits, "logits", torch.float32, dev, (T, layer.E))
+        topk_idx = torch.empty(T, top_k, dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
+        topk_w = torch.empty(T, top_k, dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    if topk_idx is None or topk_w is None:
+        raise ValueError("give logits, or both topk_idx and topk_w")
+    _need(topk_idx, "topk_idx", torch.int32, dev, (T, top_k))
+    _need(topk_w, "topk_w", torch.float32, dev, (T, top_k))
+    y = torch.empty(T, layer.H, dtype=torch.bfloat16, device=dev) if out is None else out
+    saved = None
+    if save:
+        saved = torch.empty(max(saved_bytes(layer, T, top_k), 16) // 2, dtype=torch.bfloat16, device=dev)
+    ws = _workspace(layer, T, top_k, workspace)
+    c = layer.as_c()
+    code = load().e4b_moe_forward(
+        ctypes.byref(c), T, top_k, _vp(x), _vp(logits), _vp(topk_idx), _vp(topk_w), _vp(y),
+        _vp(saved), _vp(ws), ws.numel(), PATHS[path], _stream(x),
+    )
+    check("e4b_moe_forward", code)
+    return y, topk_idx, topk_w, saved
+
+
+def moe_dgrad(layer, topk_idx, topk_w, grad_y, x=None, saved=None, grad_w=True, workspace=None):
+    """Frozen-base input gradient. Returns ``(grad_x bf16 [T, H], grad_topk_w fp32 [T, k] or None)``."""
+    dev = layer.device
+    _need(grad_y, "grad_y", torch.bfloat16, dev)
+    T, top_k = topk_idx.shape
+    _need(topk_idx, "topk_idx", torch.int32, dev, (T, top_k))
+    _need(topk_w, "topk_w", torch.float32, dev, (T, top_k))
+    if x is not None:
+        _need(x, "x", torch.bfloat16, dev, (T, layer.H))
+    gx = torch.empty(T, layer.H, dtype=torch.bfloat16, device=dev)
+    gw = torch.empty(T, top_k, dtype=torch.float32, device=dev) if grad_w else None
+    ws = _workspace(layer, T, top_k, workspace)
+    c = layer.as_c()
+    code = load().e4b_moe_dgrad(
+        ctypes.byref(c), T, top_k, _vp(topk_idx), _vp(topk_w), _vp(x), _vp(saved), _vp(grad_y),
+        _vp(gx), _vp(gw), _vp(ws), ws.numel(), _stream(grad_y),
+    )
+    check("e4b_moe_dgrad", code)
+    return gx, gw

@@ -1,0 +1,203 @@
+// api.hip -- e4b_moe_forward / e4b_moe_dgrad: validate, then enqueue the
+// kernels of the routed expert MLP on the caller's stream (no host sync).
+//
+// Forward (experts4bit-qlora 0.1.0 sdist, Experts4bit.forward):
+//   route (optional) -> permute -> gate_up GEMM + SiLU*up -> down GEMM
+//   -> weighted gather-combine.
+// dgrad (bitsandbytes PR #1965, recompute-in-backward bullet):
+//   permute -> [gate_up GEMM again if nothing was saved] -> down GEMM on
+//   W_dn^T with the SiLU-backward epilogue -> gate_up GEMM on W_gu^T
+//   -> gather-combine of grad_x and of the routing-weight gradient.
+#include "device.h"
+#include "kernels.h"
+
+using namespace e4b;
+
+namespace e4b {
+
+hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
+                                 const int32_t *idx, const float *w, uint16_t *y, char *ws,
+                                 hipStream_t s);
+
+namespace {
+
+GemmArgs base_args(const MoePlan &p, const e4b_stack &st, char *ws) {
+  GemmArgs a{};
+  a.sorted_pair = reinterpret_cast<const int32_t *>(ws + p.off_sorted);
+  a.topk = int32_t(p.k);
+  a.Wp = st.packed;
+  a.Wa = st.absmax;
+  a.w_e_bytes = st.out * st.in / 2;
+  a.w_e_blocks = st.out * st.in / kBlock;
+  a.w_in = int32_t(st.in);
+  a.I = int32_t(p.I);
+  a.offsets = reinterpret_cast<const int32_t *>(ws + p.off_offsets);
+  a.tile_offsets = reinterpret_cast<const int32_t *>(ws + p.off_tile_offsets);
+  a.E = int32_t(p.E);
+  a.cb = p.codebook;
+  return a;
+}
+
+// gate_up projection of every routed pair: writes a = silu(g)*u (if a_out) and
+// the bf16 g|u (if gu_out).
+hipError_t run_gate_up(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
+                       uint16_t *a_out, uint16_t *gu_out, char *ws, hipStream_t s) {
+  GemmArgs a = base_args(p, L->gate_up, ws);
+  a.A = x;
+  a.lda = int32_t(p.H);
+  a.N = int32_t(p.I);
+  a.K = int32_t(p.H);
+  a.n_tiles = int32_t(p.n_tiles_gu);
+  a.grid = uint32_t(p.m_tiles_bound * p.n_tiles_gu);
+  a.C = a_out;
+  a.ldc = int32_t(p.I);
+  a.GU = gu_out;
+  return launch_grouped_gemm(GEMM_GATE_UP_FWD, a, s);
+}
+
+}  // namespace
+}  // namespace e4b
+
+#define E4B_TRY(expr)                                   \
+  do {                                                  \
+    if ((expr) != hipSuccess) return E4B_ERR_HIP;       \
+  } while (0)
+
+extern "C" e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t top_k,
+                                      const void *x_bf16, const float *router_logits,
+                                      int32_t *topk_idx, float *topk_w, void *y_bf16,
+                                      void *saved, void *ws, size_t ws_bytes, int32_t path,
+                                      hipStream_t stream) {
+  MoePlan p;
+  e4b_status st = plan_moe(L, T, top_k, &p);
+  if (st != E4B_OK) return st;
+  int use_decode = 0;
+  st = check_forward(p, x_bf16, router_logits, topk_idx, topk_w, y_bf16, saved, ws, ws_bytes,
+                     path, &use_decode);
+  if (st != E4B_OK || T == 0) return st;
+  char *w = static_cast<char *>(ws);
+  const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
+  uint16_t *y = static_cast<uint16_t *>(y_bf16);
+
+  if (router_logits)
+    E4B_TRY(launch_route(router_logits, T, int(p.E), top_k, topk_idx, topk_w, stream));
+  if (use_decode) {
+    E4B_TRY(launch_decode_forward(p, L, x, topk_idx, topk_w, y, w, stream));
+    return E4B_OK;
+  }
+  E4B_TRY(launch_permute(p, topk_idx, w, stream));
+
+  uint16_t *a_buf = reinterpret_cast<uint16_t *>(w + p.off_a);
+  uint16_t *o_buf = reinterpret_cast<uint16_t *>(w + p.off_o);
+  E4B_TRY(run_gate_up(p, L, x, a_buf, static_cast<uint16_t *>(saved), w, stream));
+
+  GemmArgs d = base_args(p, L->down, w);
+  d.A = a_buf;
+  d.lda = int32_t(p.I);
+  d.N = int32_t(p.H);
+  d.K = int32_t(p.I);
+  d.n_tiles = int32_t(p.n_tiles_h);
+  d.grid = uint32_t(p.m_tiles_bound * p.n_tiles_h);
+  d.C = o_buf;
+  d.ldc = int32_t(p.H);
+  E4B_TRY(launch_grouped_gemm(GEMM_DOWN_FWD, d, stream));
+
+  E4B_TRY(launch_combine_rows(o_buf, reinterpret_cast<const int32_t *>(w + p.off_pos), topk_w, T,
+                              top_k, int(p.H), y, stream));
+  return E4B_OK;
+}
+
+extern "C" e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t top_k,
+                                    const int32_t *topk_idx, const float *topk_w,
+                                    const void *x_bf16, const void *saved,
+                                    const void *grad_y_bf16, void *grad_x_bf16,
+                                    float *grad_topk_w, void *ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  MoePlan p;
+  e4b_status st = plan_moe(L, T, top_k, &p);
+  if (st != E4B_OK) return st;
+  st = check_dgrad(p, topk_idx, topk_w, x_bf16, saved, grad_y_bf16, grad_x_bf16, grad_topk_w, ws,
+                   ws_bytes);
+  if (st != E4B_OK || T == 0) return st;
+  char *w = static_cast<char *>(ws);
+  E4B_TRY(launch_permute(p, topk_idx, w, stream));
+
+  const uint16_t *gu = static_cast<const uint16_t *>(saved);
+  if (!gu) {
+    uint16_t *gu_ws = reinterpret_cast<uint16_t *>(w + p.off_gu);
+    E4B_TRY(run_gate_up(p, L, static_cast<const uint16_t *>(x_bf16), nullptr, gu_ws, w, stream));
+    gu = gu_ws;
+  }
+  uint16_t *dgu = reinterpret_cast<uint16_t *>(w + p.off_dgu);
+  float *partial = reinterpret_cast<float *>(w + p.off_partial);
+  uint16_t *gx = reinterpret_cast<uint16_t *>(w + p.off_gx);
+
+  GemmArgs d = base_args(p, L->down, w);
+  d.A = static_cast<const uint16_t *>(grad_y_bf16);
+  d.lda = int32_t(p.H);
+  d.N = int32_t(p.I);
+  d.K = int32_t(p.H);
+  d.n_tiles = int32_t(p.n_tiles_i);
+  d.grid = uint32_t(p.m_tiles_bound * p.n_tiles_i);
+  d.C = dgu;
+  d.ldc = int32_t(2 * p.I);
+  d.GU = const_cast<uint16_t *>(gu);
+  d.topk_w = topk_w;
+  d.partial = partial;
+  E4B_TRY(launch_grouped_gemm(GEMM_DOWN_DGRAD, d, stream));
+
+  GemmArgs u = base_args(p, L->gate_up, w);
+  u.A = dgu;
+  u.lda = int32_t(2 * p.I);
+  u.N = int32_t(p.H);
+  u.K = int32_t(2 * p.I);
+  u.n_tiles = int32_t(p.n_tiles_h);
+  u.grid = uint32_t(p.m_tiles_bound * p.n_tiles_h);
+  u.C = gx;
+  u.ldc = int32_t(p.H);
+  E4B_TRY(launch_grouped_gemm(GEMM_GATE_UP_DGRAD, u, stream));
+
+  const int32_t *pos = reinterpret_cast<const int32_t *>(w + p.off_pos);
+  E4B_TRY(launch_combine_rows(gx, pos, nullptr, T, top_k, int(p.H),
+                              static_cast<uint16_t *>(grad_x_bf16), stream));
+  if (grad_topk_w)
+    E4B_TRY(launch_combine_gradw(partial, int(p.n_tiles_i), pos, p.P, grad_topk_w, stream));
+  return E4B_OK;
+}
+
+// ---- benchmark event hooks ----
+namespace e4b {
+namespace {
+struct KernelTimer {
+  int kernel = -1;
+  hipEvent_t *start = nullptr;
+  hipEvent_t *stop = nullptr;
+  int n = 0;
+  int i = 0;
+} g_timer;
+}  // namespace
+
+void timer_before(int kernel, hipStream_t s) {
+  if (g_timer.n > 0 && kernel == g_timer.kernel)
+    (void)hipEventRecord(g_timer.start[g_timer.i % g_timer.n], s);
+}
+
+void timer_after(int kernel, hipStream_t s) {
+  if (g_timer.n > 0 && kernel == g_timer.kernel) {
+    (void)hipEventRecord(g_timer.stop[g_timer.i % g_timer.n], s);
+    ++g_timer.i;
+  }
+}
+}  // namespace e4b
+
+extern "C" e4b_status e4b_set_kernel_timer(int32_t kernel, hipEvent_t *start, hipEvent_t *stop,
+                                           int32_t n) {
+  if (kernel < 0 || kernel >= E4B_K_COUNT || n < 0) return E4B_ERR_SHAPE;
+  if (n > 0 && (!start || !stop)) return E4B_ERR_NULL;
+  e4b::g_timer.kernel = kernel;
+  e4b::g_timer.start = start;
+  e4b::g_timer.stop = stop;
+  e4b::g_timer.n = n;
+  e4b::g_timer.i = 0;
+  return E4B_OK;
+}

@@ -1,0 +1,82 @@
+// combine.hip -- deterministic gather-based combines (no float atomics).
+//
+// 0.1.0 sdist, _vendor/experts.py, Experts4bit.forward scales each expert's
+// output rows by their routing weight and index_add_s them into an fp32
+// accumulator. Here every token gathers its k pair rows through pos_of_pair
+// and sums them in fp32 in slot order j = 0..k-1, so the result is the same
+// on every run.
+#include "device.h"
+#include "kernels.h"
+
+namespace e4b {
+
+// y[t] = sum_j w[t,j] * O[pos(t,j)]   (weighted)   or   sum_j O[pos(t,j)]
+// rows of H bf16; 8 elements (16 bytes) per thread and step.
+template <bool WEIGHTED>
+__global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t *__restrict__ O,
+                                                           const int32_t *__restrict__ pos_of_pair,
+                                                           const float *__restrict__ wts, int k,
+                                                           int H, uint16_t *__restrict__ y) {
+  const int64_t t = blockIdx.x;
+  __shared__ int32_t pos[kMaxTopK];
+  __shared__ float w[kMaxTopK];
+  if (threadIdx.x < k) {
+    pos[threadIdx.x] = pos_of_pair[t * k + threadIdx.x];
+    w[threadIdx.x] = WEIGHTED ? wts[t * k + threadIdx.x] : 1.0f;
+  }
+  __syncthreads();
+  for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < k; ++j) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(O + int64_t(pos[j]) * H + h);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (WEIGHTED) {
+          acc[2 * q] += w[j] * bf16_lo(v[q]);
+          acc[2 * q + 1] += w[j] * bf16_hi(v[q]);
+        } else {
+          acc[2 * q] += bf16_lo(v[q]);
+          acc[2 * q + 1] += bf16_hi(v[q]);
+        }
+      }
+    }
+    *reinterpret_cast<u32x4 *>(y + t * H + h) =
+        u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+              pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+  }
+}
+
+// grad_w[t, j] = sum over n-tiles of partial[pos(t,j)][tile] (ascending tiles).
+__global__ __launch_bounds__(256) void combine_gradw_kernel(const float *__restrict__ partial,
+                                                            int n_tiles,
+                                                            const int32_t *__restrict__ pos_of_pair,
+                                                            int64_t P, float *__restrict__ gw) {
+  const int64_t p = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (p >= P) return;
+  const float *src = partial + int64_t(pos_of_pair[p]) * n_tiles;
+  float s = 0.0f;
+  for (int i = 0; i < n_tiles; ++i) s += src[i];
+  gw[p] = s;
+}
+
+hipError_t launch_combine_rows(const uint16_t *rows, const int32_t *pos_of_pair, const float *w,
+                               int64_t T, int k, int H, uint16_t *out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (w)
+    hipLaunchKernelGGL(combine_rows_kernel<true>, dim3(uint32_t(T)), dim3(256), 0, s, rows,
+                       pos_of_pair, w, k, H, out);
+  else
+    hipLaunchKernelGGL(combine_rows_kernel<false>, dim3(uint32_t(T)), dim3(256), 0, s, rows,
+                       pos_of_pair, w, k, H, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_gradw(const float *partial, int n_tiles, const int32_t *pos_of_pair,
+                                int64_t P, float *gw, hipStream_t s) {
+  if (P == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_gradw_kernel, dim3(uint32_t((P + 255) / 256)), dim3(256), 0, s,
+                     partial, n_tiles, pos_of_pair, P, gw);
+  return hipGetLastError();
+}
+
+}  // namespace e4b

@@ -1,0 +1,63 @@
+// kernels.h -- host-side launchers of the library's kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace e4b {
+
+enum GemmVariant {
+  GEMM_GATE_UP_FWD = 0,   // A gathered x,      B = W_gu rows,    SiLU*up epilogue
+  GEMM_DOWN_FWD = 1,      // A sorted a,        B = W_dn rows,    bf16 store
+  GEMM_DOWN_DGRAD = 2,    // A gathered grad_y, B = W_dn^T,       SiLU-backward epilogue
+  GEMM_GATE_UP_DGRAD = 3  // A sorted dGU,      B = W_gu^T,       bf16 store
+};
+
+struct GemmArgs {
+  const uint16_t *A;
+  int32_t lda;
+  const int32_t *sorted_pair;
+  int32_t topk;
+  const uint8_t *Wp;   // packed stack
+  const float *Wa;     // absmax stack
+  int64_t w_e_bytes;   // packed bytes per expert
+  int64_t w_e_blocks;  // absmax entries per expert
+  int32_t w_in;        // stored in_features
+  int32_t N;           // output columns (gate/up: number of gate-up pairs = I)
+  int32_t K;           // reduction length (multiple of 64)
+  int32_t I;           // intermediate size
+  const int32_t *offsets;
+  const int32_t *tile_offsets;
+  int32_t E;
+  int32_t n_tiles;
+  uint32_t grid;
+  int32_t cb;
+  uint16_t *C;  // STORE: C[row, col]; gate_up fwd: a[row, pair] (may be null); down dgrad: dGU
+  int32_t ldc;
+  uint16_t *GU;  // gate_up fwd: out g|u [row, 2I] (may be null); down dgrad: in g|u
+  const float *topk_w;
+  float *partial;  // down dgrad: [P, n_tiles]
+};
+
+// Benchmark event hooks (e4b_set_kernel_timer): call before / after a launch.
+void timer_before(int kernel, hipStream_t s);
+void timer_after(int kernel, hipStream_t s);
+
+hipError_t launch_route(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
+                        hipStream_t s);
+
+// Fills counts/offsets/tile_offsets/sorted_pair/pos_of_pair in the workspace.
+hipError_t launch_permute(const MoePlan &p, const int32_t *idx, char *ws, hipStream_t s);
+
+// grid must equal m_tiles_bound * n_tiles.
+hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s);
+
+hipError_t launch_combine_rows(const uint16_t *rows, const int32_t *pos_of_pair, const float *w,
+                               int64_t T, int k, int H, uint16_t *out, hipStream_t s);
+
+hipError_t launch_combine_gradw(const float *partial, int n_tiles, const int32_t *pos_of_pair,
+                                int64_t P, float *gw, hipStream_t s);
+
+}  // namespace e4b

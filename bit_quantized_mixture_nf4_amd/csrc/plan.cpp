@@ -1,0 +1,184 @@
+// plan.cpp -- host-side validation and workspace planning (no HIP calls).
+#include "plan.h"
+
+namespace e4b {
+
+namespace {
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Every element offset inside one activation-sized buffer is computed in
+// 32 bits by the kernels.
+constexpr int64_t kMaxElems32 = (int64_t(1) << 31) - 1;
+
+int bits_for(int64_t n) {
+  int b = 0;
+  while ((int64_t(1) << b) < n) ++b;
+  return b;
+}
+
+}  // namespace
+
+e4b_status check_stack(const e4b_stack *st) {
+  if (!st || !st->packed || !st->absmax) return E4B_ERR_NULL;
+  if (st->blocksize != kBlock) return E4B_ERR_BLOCKSIZE;
+  if (st->codebook != E4B_CB_NF4 && st->codebook != E4B_CB_FP4) return E4B_ERR_CODEBOOK;
+  if (st->E <= 0 || st->out <= 0 || st->in <= 0 || st->in % kBlock != 0) return E4B_ERR_SHAPE;
+  if (st->out * st->in > kMaxElems32 * 2) return E4B_ERR_SHAPE;
+  if (!aligned16(st->packed) || !aligned16(st->absmax)) return E4B_ERR_ALIGN;
+  return E4B_OK;
+}
+
+e4b_status check_quantize(const float *w, int64_t E, int64_t out, int64_t in,
+                          int32_t blocksize, int32_t codebook, const uint8_t *packed,
+                          const float *absmax) {
+  if (!w || !packed || !absmax) return E4B_ERR_NULL;
+  if (blocksize != kBlock) return E4B_ERR_BLOCKSIZE;
+  if (codebook != E4B_CB_NF4 && codebook != E4B_CB_FP4) return E4B_ERR_CODEBOOK;
+  if (E <= 0 || out <= 0 || in <= 0 || in % kBlock != 0) return E4B_ERR_SHAPE;
+  if (out * in > kMaxElems32 * 2) return E4B_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(packed) || !aligned16(absmax)) return E4B_ERR_ALIGN;
+  return E4B_OK;
+}
+
+e4b_status check_layer(const e4b_moe_layer *L, MoePlan *p) {
+  if (!L) return E4B_ERR_NULL;
+  e4b_status s = check_stack(&L->gate_up);
+  if (s != E4B_OK) return s;
+  s = check_stack(&L->down);
+  if (s != E4B_OK) return s;
+  const e4b_stack &gu = L->gate_up, &dn = L->down;
+  if (gu.codebook != dn.codebook) return E4B_ERR_CODEBOOK;
+  if (gu.E != dn.E || gu.E > kMaxE) return E4B_ERR_SHAPE;
+  if (gu.out != 2 * dn.in || gu.in != dn.out) return E4B_ERR_SHAPE;
+  p->E = gu.E;
+  p->H = gu.in;
+  p->I = dn.in;
+  p->codebook = gu.codebook;
+  return E4B_OK;
+}
+
+e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p) {
+  if (!p) return E4B_ERR_NULL;
+  *p = MoePlan{};
+  e4b_status s = check_layer(L, p);
+  if (s != E4B_OK) return s;
+  if (T < 0) return E4B_ERR_SHAPE;
+  if (top_k < 1 || top_k > kMaxTopK || top_k > p->E) return E4B_ERR_SHAPE;
+  p->T = T;
+  p->k = top_k;
+  p->P = T * top_k;
+  const int64_t P = p->P, H = p->H, I = p->I, E = p->E;
+  if (P > kMaxElems32 / 4) return E4B_ERR_SHAPE;
+  if (P * 2 * I > kMaxElems32 || P * H > kMaxElems32 || T * E > kMaxElems32) return E4B_ERR_SHAPE;
+
+  p->nchunks = (P + kPermChunk - 1) / kPermChunk;
+  const int64_t busy = P < E ? P : E;  // at most P experts have a pair
+  p->m_tiles_bound = (P + busy * (kBM - 1)) / kBM;
+  p->n_tiles_gu = (I + kBN / 2 - 1) / (kBN / 2);
+  p->n_tiles_h = (H + kBN - 1) / kBN;
+  p->n_tiles_i = (I + kBN - 1) / kBN;
+  p->nbits_e = bits_for(E);
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  const size_t n_ec = size_t(E) * size_t(p->nchunks);
+  p->off_hist = take(n_ec * 4);
+  p->off_chunk_base = take(n_ec * 4);
+  p->off_counts = take(size_t(E) * 4);
+  p->off_offsets = take(size_t(E + 1) * 4);
+  p->off_tile_offsets = take(size_t(E + 1) * 4);
+  p->off_sorted = take(size_t(P) * 4);
+  p->off_pos = take(size_t(P) * 4);
+  const size_t base = off;
+  // forward region
+  p->off_a = take(size_t(P) * I * 2);
+  p->off_o = take(size_t(P) * H * 2);
+  const size_t fwd_end = off;
+  // dgrad region (overlaps the forward region: the two calls never run at once
+  // on one workspace)
+  off = base;
+  p->off_gu = take(size_t(P) * 2 * I * 2);
+  p->off_dgu = take(size_t(P) * 2 * I * 2);
+  p->off_partial = take(size_t(P) * p->n_tiles_i * 4);
+  p->off_gx = take(size_t(P) * H * 2);
+  const size_t dgrad_end = off;
+  p->ws_bytes = fwd_end > dgrad_end ? fwd_end : dgrad_end;
+  p->saved_bytes = size_t(P) * 2 * I * 2;
+  return E4B_OK;
+}
+
+bool decode_fits(const MoePlan &p) {
+  const int64_t kmax = p.H > p.I ? p.H : p.I;
+  return p.T <= kDecodeMaxT && p.T * kmax * 2 <= kDecStageBytes && p.P <= kDecMaxPairs &&
+         (p.H / 32) * 2 <= kDecMaxChunks && (p.I / 32) <= kDecMaxChunks;
+}
+
+e4b_status check_forward(const MoePlan &p, const void *x, const float *logits,
+                         const int32_t *idx, const float *w, const void *y,
+                         const void *saved, const void *ws, size_t ws_bytes,
+                         int32_t path, int *use_decode) {
+  if (path != E4B_PATH_AUTO && path != E4B_PATH_GROUPED && path != E4B_PATH_DECODE)
+    return E4B_ERR_PATH;
+  const bool fits = decode_fits(p);
+  if (path == E4B_PATH_DECODE && (!fits || saved != nullptr)) return E4B_ERR_PATH;
+  *use_decode = path == E4B_PATH_DECODE || (path == E4B_PATH_AUTO && fits && saved == nullptr);
+  if (p.T == 0) return E4B_OK;
+  if (!x || !idx || !w || !y) return E4B_ERR_NULL;
+  if (!ws) return E4B_ERR_NULL;
+  if (ws_bytes < p.ws_bytes) return E4B_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(idx) || !aligned16(w) || !aligned16(y) || !aligned16(ws))
+    return E4B_ERR_ALIGN;
+  if (logits && !aligned16(logits)) return E4B_ERR_ALIGN;
+  if (saved && !aligned16(saved)) return E4B_ERR_ALIGN;
+  return E4B_OK;
+}
+
+e4b_status check_dgrad(const MoePlan &p, const int32_t *idx, const float *w,
+                       const void *x, const void *saved, const void *gy,
+                       const void *gx, const float *gw, const void *ws,
+                       size_t ws_bytes) {
+  if (p.T == 0) return E4B_OK;
+  if (!idx || !w || !gy || !gx) return E4B_ERR_NULL;
+  if (!saved && !x) return E4B_ERR_NULL;
+  if (!ws) return E4B_ERR_NULL;
+  if (ws_bytes < p.ws_bytes) return E4B_ERR_WORKSPACE;
+  if (!aligned16(idx) || !aligned16(w) || !aligned16(gy) || !aligned16(gx) || !aligned16(ws))
+    return E4B_ERR_ALIGN;
+  if (x && !aligned16(x)) return E4B_ERR_ALIGN;
+  if (saved && !aligned16(saved)) return E4B_ERR_ALIGN;
+  if (gw && !aligned16(gw)) return E4B_ERR_ALIGN;
+  return E4B_OK;
+}
+
+}  // namespace e4b
+
+extern "C" const char *e4b_status_string(e4b_status s) {
+  switch (s) {
+    case E4B_OK: return "ok";
+    case E4B_ERR_NULL: return "a required pointer is NULL";
+    case E4B_ERR_SHAPE: return "invalid shape (dims <= 0, in % 64 != 0, top_k out of range, E > 1024, mismatched stacks or too large)";
+    case E4B_ERR_BLOCKSIZE: return "blocksize must be 64";
+    case E4B_ERR_CODEBOOK: return "unknown codebook or gate_up/down codebooks differ";
+    case E4B_ERR_DTYPE: return "unknown output dtype";
+    case E4B_ERR_WORKSPACE: return "workspace missing or too small";
+    case E4B_ERR_ALIGN: return "device buffer not 16-byte aligned";
+    case E4B_ERR_PATH: return "invalid path (decode path needs T <= 8 and saved == NULL)";
+    case E4B_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+extern "C" size_t e4b_moe_workspace_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k) {
+  e4b::MoePlan p;
+  return e4b::plan_moe(L, T, top_k, &p) == E4B_OK ? p.ws_bytes : 0;
+}
+
+extern "C" size_t e4b_moe_saved_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k) {
+  e4b::MoePlan p;
+  return e4b::plan_moe(L, T, top_k, &p) == E4B_OK ? p.saved_bytes : 0;
+}

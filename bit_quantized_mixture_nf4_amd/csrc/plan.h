@@ -1,0 +1,73 @@
+// plan.h -- host-side argument validation and workspace planning.
+//
+// This translation unit makes no HIP call, so every status code of the C ABI
+// can be forced and checked on a machine without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/e4b.h"
+
+namespace e4b {
+
+// Tile shape shared by every grouped GEMM of the forward and dgrad.
+constexpr int kBM = 256;   // rows (routed pairs) per tile
+constexpr int kBN = 256;   // output columns per tile
+constexpr int kBK = 64;    // reduction step = one quantization block
+constexpr int kBlock = 64; // quantization block (elements along `in`)
+constexpr int kPermChunk = 1024;  // pairs per histogram / scatter chunk
+constexpr int kMaxE = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kDecodeMaxT = 8;
+constexpr int kDecMaxChunks = 1024;  // decode GEMV: 16-byte code chunks per workgroup
+constexpr int kDecMaxPairs = kDecodeMaxT * kMaxTopK;
+constexpr int kDecStageBytes = 65536;  // decode GEMV: LDS for the staged input rows
+
+struct MoePlan {
+  int64_t E, H, I, T, k, P;
+  int32_t codebook;
+  int64_t nchunks;        // permutation chunks of kPermChunk pairs
+  int64_t m_tiles_bound;  // upper bound of sum_e ceil(count_e / kBM)
+  int64_t n_tiles_gu;     // gate_up forward tiles: kBN/2 gate-up pairs per tile
+  int64_t n_tiles_h;      // tiles over H
+  int64_t n_tiles_i;      // tiles over I
+  int nbits_e;            // bits needed for an expert id
+  // workspace byte offsets
+  size_t off_hist, off_chunk_base, off_counts, off_offsets, off_tile_offsets;
+  size_t off_sorted, off_pos;
+  size_t off_a, off_o;                          // forward
+  size_t off_gu, off_dgu, off_partial, off_gx;  // dgrad
+  size_t ws_bytes;
+  size_t saved_bytes;
+};
+
+// Validates a layer descriptor; fills E, H, I, codebook.
+e4b_status check_layer(const e4b_moe_layer *L, MoePlan *p);
+
+// Validates (L, T, top_k) and computes the workspace layout.
+e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p);
+
+e4b_status check_stack(const e4b_stack *st);
+e4b_status check_quantize(const float *w, int64_t E, int64_t out, int64_t in,
+                          int32_t blocksize, int32_t codebook, const uint8_t *packed,
+                          const float *absmax);
+
+// True when (T, H, I, k) fit the decode GEMV path: T <= 8 and the bf16 input
+// rows of one expert (at most T of max(H, I) elements) fit its LDS stage.
+bool decode_fits(const MoePlan &p);
+
+e4b_status check_forward(const MoePlan &p, const void *x, const float *logits,
+                         const int32_t *idx, const float *w, const void *y,
+                         const void *saved, const void *ws, size_t ws_bytes,
+                         int32_t path, int *use_decode);
+e4b_status check_dgrad(const MoePlan &p, const int32_t *idx, const float *w,
+                       const void *x, const void *saved, const void *gy,
+                       const void *gx, const float *gw, const void *ws,
+                       size_t ws_bytes);
+
+inline bool aligned16(const void *ptr) {
+  return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0;
+}
+
+}  // namespace e4b

@@ -1,0 +1,119 @@
+// quant.hip -- blockwise absmax 4-bit quantize / dequantize of a fused stack.
+//
+// experts4bit-qlora 0.1.0 sdist, _vendor/experts.py: Experts4bit quantizes
+// each expert of an [E, out, in] stack on its own with blocksize 64 and
+// dequantizes one expert as code value times block absmax. Blocks are 64
+// consecutive row-major elements, so the flat index of an element determines
+// its block across the whole contiguous [E, out*in/64] absmax array.
+#include "device.h"
+#include "plan.h"
+
+namespace e4b {
+
+// One wavefront per 64-element block, one element per lane.
+// absmax = max |w| (exact); the code is decided with fp64 products
+// absmax * midpoint, which are exact for fp32 operands, so the decision is the
+// true nearest entry (ties: NF4 lower code, FP4 smaller magnitude). This step
+// runs once per layer, off the forward/backward path.
+__global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__ w,
+                                                       int64_t nblocks, int cb,
+                                                       uint8_t *__restrict__ packed,
+                                                       float *__restrict__ absmax) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (blk >= nblocks) return;  // whole wave exits together
+  const float v = w[blk * 64 + lane];
+  float m = fabsf(v);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  const double amax = double(m);
+  const double x = double(v);
+  int q = 0;
+  if (cb == E4B_CB_NF4) {
+    if (m == 0.0f) {
+      q = 7;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 15; ++i) {
+        const double mid = (double(codebook_value(0, i)) + double(codebook_value(0, i + 1))) * 0.5;
+        q += x > amax * mid ? 1 : 0;
+      }
+    }
+  } else {
+    const double ax = fabs(x);
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+      const double mid = (double(codebook_value(1, i)) + double(codebook_value(1, i + 1))) * 0.5;
+      q += ax > amax * mid ? 1 : 0;
+    }
+    q += signbit(v) ? 8 : 0;
+  }
+  const int q_next = __shfl_down(q, 1);
+  if ((lane & 1) == 0) packed[blk * 32 + (lane >> 1)] = uint8_t((q << 4) | q_next);
+  if (lane == 0) absmax[blk] = m;
+}
+
+// One thread per 8 consecutive elements (4 packed bytes).
+template <bool BF16>
+__global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t *__restrict__ packed,
+                                                         const float *__restrict__ absmax,
+                                                         int64_t ngroups, int cb,
+                                                         void *__restrict__ out) {
+  __shared__ float code[16];
+  if (threadIdx.x < 16) code[threadIdx.x] = codebook_value(cb, threadIdx.x);
+  __syncthreads();
+  const int64_t g = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (g >= ngroups) return;
+  const uint32_t d = packed[g];
+  const float a = absmax[g >> 3];  // 8 groups of 8 elements per 64-block
+  float v[8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    v[2 * b] = __fmul_rn(code[(d >> (8 * b + 4)) & 15u], a);
+    v[2 * b + 1] = __fmul_rn(code[(d >> (8 * b)) & 15u], a);
+  }
+  if (BF16) {
+    u32x4 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+               pack_bf16x2(v[6], v[7])};
+    reinterpret_cast<u32x4 *>(out)[g] = o;
+  } else {
+    f32x4 *o = reinterpret_cast<f32x4 *>(out) + 2 * g;
+    o[0] = f32x4{v[0], v[1], v[2], v[3]};
+    o[1] = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
+}  // namespace e4b
+
+using namespace e4b;
+
+extern "C" e4b_status e4b_quantize_nf4(const float *w, int64_t E, int64_t out, int64_t in,
+                                       int32_t blocksize, int32_t codebook, uint8_t *packed,
+                                       float *absmax, hipStream_t stream) {
+  e4b_status s = check_quantize(w, E, out, in, blocksize, codebook, packed, absmax);
+  if (s != E4B_OK) return s;
+  const int64_t nblocks = E * out * in / kBlock;
+  const int64_t grid = (nblocks + 3) / 4;
+  hipLaunchKernelGGL(quantize_kernel, dim3(uint32_t(grid)), dim3(256), 0, stream, w, nblocks,
+                     int(codebook), packed, absmax);
+  return hipGetLastError() == hipSuccess ? E4B_OK : E4B_ERR_HIP;
+}
+
+extern "C" e4b_status e4b_dequantize_nf4(const e4b_stack *st, int32_t dtype, void *w_out,
+                                         hipStream_t stream) {
+  e4b_status s = check_stack(st);
+  if (s != E4B_OK) return s;
+  if (!w_out) return E4B_ERR_NULL;
+  if (dtype != E4B_F32 && dtype != E4B_BF16) return E4B_ERR_DTYPE;
+  if (!aligned16(w_out)) return E4B_ERR_ALIGN;
+  const int64_t ngroups = st->E * st->out * st->in / 8;
+  const int64_t grid = (ngroups + 255) / 256;
+  const uint32_t *pk = reinterpret_cast<const uint32_t *>(st->packed);
+  if (dtype == E4B_BF16)
+    hipLaunchKernelGGL(dequantize_kernel<true>, dim3(uint32_t(grid)), dim3(256), 0, stream, pk,
+                       st->absmax, ngroups, int(st->codebook), w_out);
+  else
+    hipLaunchKernelGGL(dequantize_kernel<false>, dim3(uint32_t(grid)), dim3(256), 0, stream, pk,
+                       st->absmax, ngroups, int(st->codebook), w_out);
+  return hipGetLastError() == hipSuccess ? E4B_OK : E4B_ERR_HIP;
+}

@@ -1,0 +1,219 @@
+// route.hip -- top-k routing and the token-by-expert permutation.
+//
+// experts4bit-qlora 0.1.0 sdist, _vendor/experts.py, Experts4bit.forward takes
+// (top_k_index, top_k_weights) from a router outside the module and groups the
+// routed (token, slot) pairs per expert with a one-hot mask and torch.where,
+// paying a device-to-host sync for every expert. Here the grouping is a stable
+// counting sort done entirely on the device:
+//   1. histogram of expert ids per chunk of kPermChunk pairs,
+//   2. per expert, exclusive scan of its chunk counts,
+//   3. per chunk, one wavefront assigns each pair its sorted position
+//      (expert offset + chunk base + rank among equal ids, lanes in pair order).
+#include "device.h"
+#include "kernels.h"
+
+namespace e4b {
+
+// One wavefront per token. Selection compares the stored fp32 logits exactly:
+// larger value first, equal values -> lower expert id. Weights = softmax over
+// the k selected logits (fp32, summed in slot order).
+__global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ logits, int64_t T,
+                                                    int E, int k, int32_t *__restrict__ idx,
+                                                    float *__restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  constexpr int kMaxPer = kMaxE / 64;
+  float v[kMaxPer];
+  const int per = (E + 63) / 64;
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int e = i * 64 + lane;
+    v[i] = (i < per && e < E) ? logits[t * E + e] : -INFINITY;
+  }
+  uint32_t taken = 0;  // bit i: entry i of this lane already selected
+  float sel0 = 0.0f, mysel = 0.0f;
+  int myid = 0;
+  for (int j = 0; j < k; ++j) {
+    // lane-local best among untaken (lower index wins ties: ascending scan, strict >)
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      const int e = i * 64 + lane;
+      if (i < per && e < E && !(taken & (1u << i)) && (v[i] > bv || bi == 0x7fffffff)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (j == 0) sel0 = bv;
+    if (lane == j) {
+      mysel = bv;
+      myid = bi;
+    }
+  }
+  // softmax over the selected logits, lane j holds slot j
+  const float z = lane < k ? expf(mysel - sel0) : 0.0f;
+  float s = 0.0f;
+  for (int j = 0; j < k; ++j) s += __shfl(z, j);
+  if (lane < k) {
+    idx[t * k + lane] = myid;
+    wts[t * k + lane] = z / s;
+  }
+}
+
+// hist[e * nchunks + c] = number of pairs of chunk c routed to expert e.
+__global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t *__restrict__ flat_idx,
+                                                        int64_t P, int E, int64_t nchunks,
+                                                        int32_t *__restrict__ hist) {
+  __shared__ int32_t h[kMaxE];
+  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  const int64_t c = blockIdx.x;
+  const int64_t p0 = c * kPermChunk;
+  for (int i = threadIdx.x; i < kPermChunk; i += 256) {
+    const int64_t p = p0 + i;
+    if (p < P) atomicAdd(&h[flat_idx[p]], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) hist[int64_t(e) * nchunks + c] = h[e];
+}
+
+// One workgroup per expert: chunk_base[e][c] = sum_{c' < c} hist[e][c'],
+// counts[e] = total.
+__global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t *__restrict__ hist,
+                                                        int64_t nchunks,
+                                                        int32_t *__restrict__ chunk_base,
+                                                        int32_t *__restrict__ counts) {
+  __shared__ int32_t wsum[4];
+  const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int32_t *hrow = hist + int64_t(e) * nchunks;
+  int32_t *brow = chunk_base + int64_t(e) * nchunks;
+  int32_t carry = 0;
+  for (int64_t c0 = 0; c0 < nchunks; c0 += 256) {
+    const int64_t c = c0 + threadIdx.x;
+    const int32_t v = c < nchunks ? hrow[c] : 0;
+    int32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t n = __shfl_up(incl, o);
+      if (lane >= o) incl += n;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int32_t before = carry;
+    for (int i = 0; i < wv; ++i) before += wsum[i];
+    if (c < nchunks) brow[c] = before + incl - v;
+    const int32_t total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+    carry += total;
+  }
+  if (threadIdx.x == 0) counts[e] = carry;
+}
+
+// One wavefront per chunk. Writes sorted_pair / pos_of_pair; workgroup 0 also
+// writes offsets[E+1] and tile_offsets[E+1] (m-tiles of kBM rows per expert).
+__global__ __launch_bounds__(64) void perm_scatter_kernel(
+    const int32_t *__restrict__ flat_idx, int64_t P, int E, int nbits, int64_t nchunks,
+    const int32_t *__restrict__ counts, const int32_t *__restrict__ chunk_base,
+    int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pos_of_pair,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ tile_offsets) {
+  __shared__ int32_t base[kMaxE];
+  const int lane = threadIdx.x;
+  const int64_t c = blockIdx.x;
+  // exclusive scan of counts (and of m-tiles) over experts, 64 at a time
+  int32_t carry = 0, tcarry = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    const int32_t v = e < E ? counts[e] : 0;
+    const int32_t tv = (v + kBM - 1) / kBM;
+    int32_t incl = v, tincl = tv;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t n = __shfl_up(incl, o), tn = __shfl_up(tincl, o);
+      if (lane >= o) {
+        incl += n;
+        tincl += tn;
+      }
+    }
+    if (e < E) {
+      const int32_t off = carry + incl - v;
+      base[e] = off + chunk_base[int64_t(e) * nchunks + c];
+      if (c == 0) {
+        offsets[e] = off;
+        tile_offsets[e] = tcarry + tincl - tv;
+      }
+    }
+    carry += __shfl(incl, 63);
+    tcarry += __shfl(tincl, 63);
+  }
+  if (c == 0 && lane == 0) {
+    offsets[E] = carry;
+    tile_offsets[E] = tcarry;
+  }
+  __syncthreads();
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t p0 = c * kPermChunk;
+  for (int it = 0; it < kPermChunk / 64; ++it) {
+    const int64_t p = p0 + it * 64 + lane;
+    const bool valid = p < P;
+    const int e = valid ? flat_idx[p] : 0;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      match &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(match & lt);
+    const int32_t my_base = valid ? base[e] : 0;
+    __syncthreads();
+    if (valid) {
+      const int32_t pos = my_base + rank;
+      sorted_pair[pos] = int32_t(p);
+      pos_of_pair[p] = pos;
+      // the highest lane of each equal-id group advances that expert's base
+      if ((match >> lane) == 1ull) base[e] = my_base + __popcll(match);
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_route(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
+                        hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(route_kernel, dim3(uint32_t((T + 3) / 4)), dim3(256), 0, s, logits, T, E, k,
+                     idx, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const MoePlan &p, const int32_t *idx, char *ws, hipStream_t s) {
+  if (p.P == 0) return hipSuccess;
+  int32_t *hist = reinterpret_cast<int32_t *>(ws + p.off_hist);
+  int32_t *cbase = reinterpret_cast<int32_t *>(ws + p.off_chunk_base);
+  int32_t *counts = reinterpret_cast<int32_t *>(ws + p.off_counts);
+  int32_t *offsets = reinterpret_cast<int32_t *>(ws + p.off_offsets);
+  int32_t *toff = reinterpret_cast<int32_t *>(ws + p.off_tile_offsets);
+  int32_t *sorted = reinterpret_cast<int32_t *>(ws + p.off_sorted);
+  int32_t *pos = reinterpret_cast<int32_t *>(ws + p.off_pos);
+  const int E = int(p.E);
+  hipLaunchKernelGGL(perm_hist_kernel, dim3(uint32_t(p.nchunks)), dim3(256), 0, s, idx, p.P, E,
+                     p.nchunks, hist);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(uint32_t(E)), dim3(256), 0, s, hist, p.nchunks, cbase,
+                     counts);
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3(uint32_t(p.nchunks)), dim3(64), 0, s, idx, p.P, E,
+                     p.nbits_e, p.nchunks, counts, cbase, sorted, pos, offsets, toff);
+  return hipGetLastError();
+}
+
+}  // namespace e4b

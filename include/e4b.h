@@ -1,0 +1,199 @@
+/*
+ * e4b.h -- C ABI of the MI355X (gfx950) fused blockwise-4-bit Mixture-of-Experts
+ * expert MLP: quantize / dequantize a fused expert stack, the routed SwiGLU
+ * forward, and the frozen-base input gradient (dgrad).
+ *
+ * Sources (page titles; sections named per entry point below):
+ *   [sdist]  experts4bit-qlora 0.1.0 source distribution, module
+ *            experts4bit_qlora/_vendor/experts.py, class Experts4bit.
+ *   [PR]     bitsandbytes pull request #1965, "Add Experts4bit for 4-bit
+ *            quantization of fused MoE experts".
+ *   [README] experts4bit-qlora 0.4.0 README (PyPI wheel metadata).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Stacks are row-major [E, out, in] per expert ([sdist] class docstring):
+ *   gate_up is [E, 2I, H] with rows 0..I-1 the gate and rows I..2I-1 the up
+ *   projection; down is [E, H, I].
+ * - Packed codes: uint8 [E, out*in/2], two 4-bit codes per byte, the even
+ *   element of the flattened row-major [out, in] in the high nibble.
+ * - absmax: fp32 [E, out*in/64], one scale per 64 consecutive elements of a
+ *   row; in % 64 == 0 so a block never straddles a row or an expert
+ *   ([sdist] Experts4bit.__init__ block-alignment check). absmax is always
+ *   fp32 and the codebook is a library constant chosen by enum, never a
+ *   caller buffer ([PR] "Dtype-cast safety" bullet).
+ * - bf16 tensors are raw IEEE bfloat16 bit patterns (uint16).
+ * - Every pointer argument except the `const e4b_stack*`/`const
+ *   e4b_moe_layer*` descriptors (host memory, read during the call only) is
+ *   a DEVICE pointer owned by the caller; the library never allocates or
+ *   frees memory and keeps no state between calls beyond its code objects.
+ * - Device buffers must be 16-byte aligned (E4B_ERR_ALIGN otherwise).
+ * - Asynchrony: every call validates its arguments on the host, enqueues
+ *   kernels on `stream` and returns; no call synchronizes. A non-OK status is
+ *   returned synchronously and nothing is enqueued for validation errors.
+ * - Errors follow the pages' fail-loudly rule ([README] support matrix
+ *   "Unsupported" definition): a bad argument is reported, never ignored.
+ *   T == 0 is a valid no-op.
+ * - Device preconditions that are NOT checked: finite weights and logits;
+ *   0 <= topk_idx < E and distinct per token when it is an input.
+ */
+#ifndef E4B_H
+#define E4B_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  E4B_OK = 0,
+  E4B_ERR_NULL = 1,      /* a required pointer is NULL */
+  E4B_ERR_SHAPE = 2,     /* a dimension <= 0, in % 64 != 0, top_k not in [1, min(E, 32)],
+                            E > 1024, inconsistent gate_up/down shapes, or a size too large */
+  E4B_ERR_BLOCKSIZE = 3, /* blocksize != 64 */
+  E4B_ERR_CODEBOOK = 4,  /* unknown codebook, or gate_up/down codebooks differ */
+  E4B_ERR_DTYPE = 5,     /* unknown output dtype */
+  E4B_ERR_WORKSPACE = 6, /* workspace NULL or smaller than e4b_moe_workspace_bytes() */
+  E4B_ERR_ALIGN = 7,     /* a device buffer is not 16-byte aligned */
+  E4B_ERR_PATH = 8,      /* unknown path, or the decode path was asked for but does not apply (T > 8, saved != NULL, or T*max(H,I)*2 > 64 KiB) */
+  E4B_ERR_HIP = 9        /* a kernel launch failed (hipGetLastError after the launch) */
+} e4b_status;
+
+/* The 16-entry codebooks ([sdist] Experts4bit.__init__ quant_type "nf4"/"fp4"):
+ * NF4 = the NormalFloat-4 table of the QLoRA paper (arXiv:2305.14314);
+ * FP4 = e2m1 (sign bit 3, magnitudes {0,.5,1,1.5,2,3,4,6}/6). */
+typedef enum { E4B_CB_NF4 = 0, E4B_CB_FP4 = 1 } e4b_codebook;
+
+typedef enum { E4B_F32 = 0, E4B_BF16 = 1 } e4b_dtype;
+
+/* Forward path selection. AUTO = the decode dequant-GEMV path when T <= 8 and
+ * saved == NULL, else the grouped MFMA path. */
+typedef enum { E4B_PATH_AUTO = 0, E4B_PATH_GROUPED = 1, E4B_PATH_DECODE = 2 } e4b_path;
+
+/* One quantized stack (device pointers; the struct itself is host memory). */
+typedef struct {
+  const uint8_t *packed; /* [E, out*in/2] */
+  const float *absmax;   /* [E, out*in/64] */
+  int64_t E, out, in;
+  int32_t blocksize; /* must be 64 */
+  int32_t codebook;  /* e4b_codebook */
+} e4b_stack;
+
+/* A MoE layer: gate_up (out = 2I, in = H) and down (out = H, in = I), same E,
+ * same codebook ([README] "one module, one scheme"). */
+typedef struct {
+  e4b_stack gate_up;
+  e4b_stack down;
+} e4b_moe_layer;
+
+/* Blockwise absmax quantization of an fp32 [E, out, in] stack.
+ * [sdist] Experts4bit.from_float / _quantize_stack (per expert, blocksize 64,
+ * no double quantization; [PR] "Non-goals" keeps absmax a plain fp32 buffer).
+ * absmax = max |w| over each 64-block; code = nearest codebook entry to
+ * w/absmax decided exactly (ties: NF4 lower code, FP4 smaller magnitude; FP4
+ * sign bit = sign bit of w); an NF4 block of zeros stores code 7.
+ *   w      : device fp32 [E, out, in], finite (unchecked)
+ *   packed : device uint8 [E, out*in/2]   (written)
+ *   absmax : device fp32  [E, out*in/64]  (written)
+ * Errors: NULL, SHAPE (E/out/in <= 0, in % 64 != 0), BLOCKSIZE, CODEBOOK,
+ * ALIGN, HIP. */
+e4b_status e4b_quantize_nf4(const float *w, int64_t E, int64_t out, int64_t in,
+                            int32_t blocksize, int32_t codebook, uint8_t *packed,
+                            float *absmax, hipStream_t stream);
+
+/* Dequantize a whole stack: w_out[e, r, c] = fl32(code * absmax) (one fp32
+ * rounding of the exact product), or its round-to-nearest-even bf16 when
+ * dtype == E4B_BF16. [sdist] Experts4bit._dequantize_expert.
+ *   st    : host descriptor of device buffers
+ *   w_out : device [E, out, in] fp32 or bf16 (written)
+ * Errors: NULL, SHAPE, BLOCKSIZE, CODEBOOK, DTYPE, ALIGN, HIP. */
+e4b_status e4b_dequantize_nf4(const e4b_stack *st, int32_t dtype, void *w_out,
+                              hipStream_t stream);
+
+/* Routed SwiGLU expert forward. [sdist] Experts4bit.forward: for each
+ * (token t, slot j) with expert e = topk_idx[t, j],
+ *   h = W_gu[e] x_t ; g = h[:I] ; u = h[I:] ; a = silu(g) * u ;
+ *   y_t = sum_j topk_w[t, j] * (W_dn[e] a), accumulated in fp32,
+ * with W the dequantized stacks (bf16 operands, fp32 accumulation).
+ *   x_bf16        : device bf16 [T, H]
+ *   router_logits : device fp32 [T, E] or NULL. Given: topk_idx/topk_w are
+ *                   OUTPUTS = the top_k largest logits (descending, ties to the
+ *                   lower expert id) and the softmax over them. NULL: topk_idx
+ *                   and topk_w are INPUTS.
+ *   topk_idx      : device int32 [T, top_k]
+ *   topk_w        : device fp32  [T, top_k]
+ *   y_bf16        : device bf16 [T, H] (written)
+ *   saved         : device buffer of e4b_moe_saved_bytes() or NULL; when given,
+ *                   the bf16 gate and up projections of every pair are stored
+ *                   for e4b_moe_dgrad (grouped path only)
+ *   ws, ws_bytes  : device workspace, >= e4b_moe_workspace_bytes()
+ *   path          : e4b_path
+ * Errors: NULL, SHAPE, BLOCKSIZE, CODEBOOK, WORKSPACE, ALIGN, PATH, HIP. */
+e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t top_k,
+                           const void *x_bf16, const float *router_logits,
+                           int32_t *topk_idx, float *topk_w, void *y_bf16,
+                           void *saved, void *ws, size_t ws_bytes, int32_t path,
+                           hipStream_t stream);
+
+/* Frozen-base input gradient of e4b_moe_forward with routing held fixed.
+ * [PR] "What this adds", recompute-in-backward bullet: each projection's
+ * backward forms grad_output @ W from a re-dequantized W (never a saved W);
+ * frozen-base bullet: no weight gradient. Per pair (t, j), expert e:
+ *   G2 = W_dn[e]^T grad_y_t ; grad_topk_w[t, j] = G2 . a ;
+ *   grad_a = topk_w[t, j] G2 ; s = sigmoid(g) ;
+ *   dg = grad_a u s (1 + g (1 - s)) ; du = grad_a g s ;
+ *   grad_x_t = sum_j W_gu[e]^T [dg ; du].
+ *   topk_idx, topk_w : device [T, top_k] (inputs, as used by the forward)
+ *   x_bf16           : device bf16 [T, H]; required when saved == NULL
+ *                      (the gate/up projections are recomputed), ignored otherwise
+ *   saved            : the buffer filled by e4b_moe_forward, or NULL.
+ *                      Recompute and saved give bitwise-identical results.
+ *   grad_y_bf16      : device bf16 [T, H]
+ *   grad_x_bf16      : device bf16 [T, H] (written)
+ *   grad_topk_w      : device fp32 [T, top_k] (written) or NULL
+ * Errors: NULL, SHAPE, BLOCKSIZE, CODEBOOK, WORKSPACE, ALIGN, HIP. */
+e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t top_k,
+                         const int32_t *topk_idx, const float *topk_w,
+                         const void *x_bf16, const void *saved,
+                         const void *grad_y_bf16, void *grad_x_bf16,
+                         float *grad_topk_w, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* Workspace bytes that e4b_moe_forward and e4b_moe_dgrad need for (L, T,
+ * top_k) (one size serves both); 0 when the arguments are invalid. */
+size_t e4b_moe_workspace_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k);
+
+/* Bytes of the `saved` buffer: bf16 [T*top_k, 2I]; 0 when invalid. */
+size_t e4b_moe_saved_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k);
+
+/* Kernels that e4b_set_kernel_timer can bracket with events. */
+typedef enum {
+  E4B_K_GATE_UP_FWD = 0,   /* grouped gate_up GEMM + SiLU*up epilogue */
+  E4B_K_DOWN_FWD = 1,      /* grouped down GEMM */
+  E4B_K_DOWN_DGRAD = 2,    /* grouped GEMM on W_dn^T + SiLU-backward epilogue */
+  E4B_K_GATE_UP_DGRAD = 3, /* grouped GEMM on W_gu^T */
+  E4B_K_DECODE_GATE_UP = 4,/* decode dequant-GEMV, gate_up + SiLU*up */
+  E4B_K_DECODE_DOWN = 5,   /* decode dequant-GEMV, down */
+  E4B_K_COUNT = 6
+} e4b_kernel;
+
+/* Benchmark instrumentation (not part of the computation): while armed, the
+ * i-th launch of `kernel` is bracketed by hipEventRecord(start[i % n]) and
+ * hipEventRecord(stop[i % n]) on the stream it is launched on. The event
+ * arrays are caller-owned and must stay valid while armed; n == 0 disarms.
+ * Process-wide setting, not thread-safe: arm it only from a single-threaded
+ * benchmark. Errors: SHAPE (unknown kernel or n < 0), NULL (n > 0 with a
+ * NULL array). */
+e4b_status e4b_set_kernel_timer(int32_t kernel, hipEvent_t *start, hipEvent_t *stop, int32_t n);
+
+/* Static, human-readable text for a status code. */
+const char *e4b_status_string(e4b_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* E4B_H */

@@ -1,0 +1,97 @@
+"""Helpers shared by the GPU parity tests (not collected by pytest)."""
+
+import numpy as np
+import torch
+
+import oracle
+import bit_quantized_mixture_nf4_amd as e4b
+from workloads import gen_x, gen_grad_y, gen_logits, gen_weights
+
+DEV = "cuda:0"
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def tol_check(got, ref, name, rel=1e-2):
+    """max |got - ref| <= rel * max |ref| for one output tensor."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    assert np.all(np.isfinite(got)), name
+    assert err <= rel * scale, f"{name}: max err {err:.3e} > {rel} * {scale:.3e}"
+    return err, scale
+
+
+def bf16_tensor(a_f32):
+    return torch.from_numpy(np.ascontiguousarray(a_f32, np.float32)).to(torch.bfloat16).to(DEV)
+
+
+def to_np(t):
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy()
+    return t.cpu().numpy()
+
+
+class Problem:
+    """A synthetic layer + batch from the workload recipe, on the GPU and for the oracle."""
+
+    def __init__(self, cfg, seed=0, codebook="nf4", with_grad=True):
+        self.cfg, self.seed, self.codebook = cfg, seed, codebook
+        self.x = gen_x(cfg, seed)
+        self.logits = gen_logits(cfg, seed)
+        self.grad_y = gen_grad_y(cfg, seed) if with_grad else None
+        self.w_gu = gen_weights(cfg, seed, "gate_up")
+        self.w_dn = gen_weights(cfg, seed, "down")
+        gu = e4b.quantize(torch.from_numpy(self.w_gu).to(DEV), codebook)
+        dn = e4b.quantize(torch.from_numpy(self.w_dn).to(DEV), codebook)
+        self.layer = e4b.MoELayer(gu, dn)
+        self.x_d = bf16_tensor(self.x)
+        self.logits_d = torch.from_numpy(self.logits).to(DEV)
+        self.grad_y_d = bf16_tensor(self.grad_y) if with_grad else None
+        self._deq = None
+
+    def oracle_weights(self, experts=None):
+        """fp32 dequantized stacks from the oracle's own quantization."""
+        if self._deq is None:
+            cfg = self.cfg
+            pg, ag = oracle.quantize_blockwise(self.w_gu, self.codebook)
+            pd, ad = oracle.quantize_blockwise(self.w_dn, self.codebook)
+            self._deq = (
+                oracle.dequantize(pg, ag, 2 * cfg.I, cfg.H, self.codebook),
+                oracle.dequantize(pd, ad, cfg.H, cfg.I, self.codebook),
+            )
+        return self._deq
+
+
+def oracle_expert_stacks(cfg, seed, experts, kind="nf4", threads=16):
+    """Oracle-dequantized fp32 weights of only ``experts`` (regenerated per expert).
+
+    Quantization runs on row slices in parallel threads; blocks never straddle a
+    row, so quantizing row slices gives exactly the whole-stack result.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+    from workloads import gen_expert_weight
+
+    out = {"gate_up": {}, "down": {}}
+    jobs = []
+    for e in experts:
+        for which in ("gate_up", "down"):
+            w = gen_expert_weight(cfg, seed, which, e)
+            out[which][e] = np.empty_like(w)
+            rows = w.shape[0]
+            step = max(1, -(-rows // 64))
+            for r0 in range(0, rows, step):
+                jobs.append((w, out[which][e], r0, min(rows, r0 + step)))
+
+    def one(job):
+        w, dst, r0, r1 = job
+        p, a = oracle.quantize_blockwise(w[None, r0:r1], kind)
+        dst[r0:r1] = oracle.dequantize(p, a, r1 - r0, w.shape[1], kind)[0]
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(one, jobs))
+    return out

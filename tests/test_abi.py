@@ -1,0 +1,136 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/e4b.h declares, and every host-side validation error is reported
+synchronously (no device pointer is touched on these paths)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_mixture_nf4_amd as e4b
+from bit_quantized_mixture_nf4_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # a 16-byte-aligned non-null address; never dereferenced on these paths
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "e4b.h")).read()
+    return sorted(set(re.findall(r"\b(e4b_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = e4b.load()
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _stack(E=4, out=128, inn=64, packed=FAKE, absmax=FAKE, bs=64, cb=0):
+    return _lib.E4bStack(packed, absmax, E, out, inn, bs, cb)
+
+
+def _layer(E=4, H=64, I=64, **kw):
+    return _lib.E4bLayer(_stack(E, 2 * I, H, **kw), _stack(E, H, I, **kw))
+
+
+def _fwd(L, T=4, k=2, x=FAKE, logits=None, idx=FAKE, w=FAKE, y=FAKE, saved=None, ws=FAKE,
+         ws_bytes=1 << 40, path=0):
+    return e4b.load().e4b_moe_forward(ctypes.byref(L), T, k, x, logits, idx, w, y, saved, ws,
+                                      ws_bytes, path, None)
+
+
+def _dgrad(L, T=4, k=2, idx=FAKE, w=FAKE, x=FAKE, saved=None, gy=FAKE, gx=FAKE, gw=FAKE,
+           ws=FAKE, ws_bytes=1 << 40):
+    return e4b.load().e4b_moe_dgrad(ctypes.byref(L), T, k, idx, w, x, saved, gy, gx, gw, ws,
+                                    ws_bytes, None)
+
+
+def test_quantize_validation():
+    q = e4b.load().e4b_quantize_nf4
+    assert q(None, 1, 64, 64, 64, 0, FAKE, FAKE, None) == _lib.E4B_ERR_NULL
+    assert q(FAKE, 1, 64, 64, 64, 0, None, FAKE, None) == _lib.E4B_ERR_NULL
+    assert q(FAKE, 1, 64, 96, 64, 0, FAKE, FAKE, None) == _lib.E4B_ERR_SHAPE
+    assert q(FAKE, 0, 64, 64, 64, 0, FAKE, FAKE, None) == _lib.E4B_ERR_SHAPE
+    assert q(FAKE, 1, 64, 64, 128, 0, FAKE, FAKE, None) == _lib.E4B_ERR_BLOCKSIZE
+    assert q(FAKE, 1, 64, 64, 64, 2, FAKE, FAKE, None) == _lib.E4B_ERR_CODEBOOK
+    assert q(FAKE + 4, 1, 64, 64, 64, 0, FAKE, FAKE, None) == _lib.E4B_ERR_ALIGN
+
+
+def test_dequantize_validation():
+    d = e4b.load().e4b_dequantize_nf4
+    st = _stack()
+    assert d(ctypes.byref(st), 0, None, None) == _lib.E4B_ERR_NULL
+    assert d(ctypes.byref(st), 7, FAKE, None) == _lib.E4B_ERR_DTYPE
+    assert d(ctypes.byref(st), 0, FAKE + 8, None) == _lib.E4B_ERR_ALIGN
+    assert d(ctypes.byref(_stack(bs=32)), 0, FAKE, None) == _lib.E4B_ERR_BLOCKSIZE
+    assert d(ctypes.byref(_stack(cb=5)), 0, FAKE, None) == _lib.E4B_ERR_CODEBOOK
+    assert d(ctypes.byref(_stack(inn=100)), 0, FAKE, None) == _lib.E4B_ERR_SHAPE
+    assert d(ctypes.byref(_stack(packed=None)), 0, FAKE, None) == _lib.E4B_ERR_NULL
+    assert d(None, 0, FAKE, None) == _lib.E4B_ERR_NULL
+
+
+def test_layer_validation():
+    L = _layer()
+    bad_cb = _lib.E4bLayer(_stack(4, 128, 64, cb=0), _stack(4, 64, 64, cb=1))
+    assert _fwd(bad_cb) == _lib.E4B_ERR_CODEBOOK
+    bad_shape = _lib.E4bLayer(_stack(4, 130, 64), _stack(4, 64, 64))
+    assert _fwd(bad_shape) == _lib.E4B_ERR_SHAPE
+    bad_e = _lib.E4bLayer(_stack(4, 128, 64), _stack(5, 64, 64))
+    assert _fwd(bad_e) == _lib.E4B_ERR_SHAPE
+    big_e = _layer(E=2048)
+    assert _fwd(big_e) == _lib.E4B_ERR_SHAPE
+    assert _fwd(L, k=0) == _lib.E4B_ERR_SHAPE
+    assert _fwd(L, k=5) == _lib.E4B_ERR_SHAPE  # top_k > E
+    assert _fwd(L, T=-1) == _lib.E4B_ERR_SHAPE
+    assert e4b.load().e4b_moe_forward(None, 4, 2, FAKE, None, FAKE, FAKE, FAKE, None, FAKE,
+                                      1 << 40, 0, None) == _lib.E4B_ERR_NULL
+
+
+def test_forward_and_dgrad_argument_errors():
+    L = _layer()
+    need = e4b.load().e4b_moe_workspace_bytes(ctypes.byref(L), 4, 2)
+    assert need > 0
+    assert _fwd(L, x=None) == _lib.E4B_ERR_NULL
+    assert _fwd(L, y=None) == _lib.E4B_ERR_NULL
+    assert _fwd(L, ws=None) == _lib.E4B_ERR_NULL
+    assert _fwd(L, ws_bytes=need - 1) == _lib.E4B_ERR_WORKSPACE
+    assert _fwd(L, x=FAKE + 2) == _lib.E4B_ERR_ALIGN
+    assert _fwd(L, logits=FAKE + 4) == _lib.E4B_ERR_ALIGN
+    assert _fwd(L, path=3) == _lib.E4B_ERR_PATH
+    assert _fwd(L, T=9, path=2) == _lib.E4B_ERR_PATH  # decode path needs T <= 8
+    assert _fwd(L, T=4, path=2, saved=FAKE) == _lib.E4B_ERR_PATH
+    big = _layer(E=4, H=8192, I=64)
+    assert _fwd(big, T=8, path=2) == _lib.E4B_ERR_PATH  # staging would exceed 64 KiB
+    assert _dgrad(L, gy=None) == _lib.E4B_ERR_NULL
+    assert _dgrad(L, x=None, saved=None) == _lib.E4B_ERR_NULL
+    assert _dgrad(L, ws_bytes=need - 1) == _lib.E4B_ERR_WORKSPACE
+    assert _dgrad(L, gw=FAKE + 4) == _lib.E4B_ERR_ALIGN
+
+
+def test_zero_tokens_is_a_noop():
+    L = _layer()
+    assert _fwd(L, T=0, x=None, idx=None, w=None, y=None, ws=None, ws_bytes=0) == _lib.E4B_OK
+    assert _dgrad(L, T=0, idx=None, w=None, x=None, gy=None, gx=None, gw=None, ws=None,
+                  ws_bytes=0) == _lib.E4B_OK
+
+
+@pytest.mark.parametrize("E,H,I,k,T", [(8, 256, 128, 2, 64), (64, 2048, 1024, 8, 4096),
+                                       (128, 2048, 768, 8, 16384), (8, 4096, 14336, 2, 8192)])
+def test_workspace_and_saved_sizes(E, H, I, k, T):
+    L = _layer(E=E, H=H, I=I)
+    lib = e4b.load()
+    P = T * k
+    saved = lib.e4b_moe_saved_bytes(ctypes.byref(L), T, k)
+    assert saved == P * 2 * I * 2
+    ws = lib.e4b_moe_workspace_bytes(ctypes.byref(L), T, k)
+    # at least the dgrad intermediates: g|u, dGU, grad_x rows
+    assert ws >= P * (2 * I * 2 * 2 + H * 2)
+    assert lib.e4b_moe_workspace_bytes(ctypes.byref(L), T, E + 1) == 0
+
+
+def test_status_strings():
+    for code in range(10):
+        assert len(_lib.status_string(code)) > 0

@@ -1,0 +1,102 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times, on outputs the oracle computes token by token.
+
+For each workload a few seeded tokens are drawn; the oracle regenerates and
+quantizes only the experts those tokens route to and computes their rows of
+y, grad_x and grad_topk_w (the bar: 1e-2 * max|oracle| per tensor). Routing
+ids are compared for every token. Properties that hold at any size
+(recompute == saved, bitwise run-to-run) are checked on the whole output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import bit_quantized_mixture_nf4_amd as e4b
+from workloads import get_config, gen_x, gen_grad_y, gen_logits, gen_weights
+from gpu_util import DEV, announce, tol_check, to_np, bf16_tensor, oracle_expert_stacks
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(cfg, seed, kind):
+    stacks = []
+    for which in ("gate_up", "down"):
+        w = gen_weights(cfg, seed, which)
+        wd = torch.from_numpy(w).to(DEV)
+        del w
+        stacks.append(e4b.quantize(wd, kind))
+        del wd
+    torch.cuda.empty_cache()
+    return e4b.MoELayer(*stacks)
+
+
+def _sampled_oracle(cfg, seed, kind, x, gy, idx_ref, w_ref, tokens):
+    experts = sorted(set(int(e) for e in idx_ref[tokens].ravel()))
+    announce(f"oracle weights for {len(experts)} experts")
+    st = oracle_expert_stacks(cfg, seed, experts, kind)
+    remap = {e: i for i, e in enumerate(experts)}
+    wgu = np.stack([st["gate_up"][e] for e in experts])
+    wdn = np.stack([st["down"][e] for e in experts])
+    idx_c = np.vectorize(remap.get)(idx_ref[tokens]).astype(np.int32)
+    y = oracle.moe_forward(x[tokens], idx_c, w_ref[tokens], wgu, wdn)
+    gxw = oracle.moe_dgrad(x[tokens], idx_c, w_ref[tokens], wgu, wdn, gy[tokens]) if gy is not None else None
+    return y, gxw
+
+
+@pytest.mark.parametrize("name,kind,ntok", [("olmoe", "nf4", 6), ("qwen3_prefill", "nf4", 6),
+                                            ("mixtral", "fp4", 1), ("mixtral", "nf4", 1)])
+def test_full_size_forward_dgrad_sampled(name, kind, ntok):
+    cfg = get_config(name)
+    seed = 0
+    announce(f"{name} {kind} full size E{cfg.E} H{cfg.H} I{cfg.I} k{cfg.k} T{cfg.T}")
+    layer = _layer(cfg, seed, kind)
+    x = gen_x(cfg, seed)
+    gy = gen_grad_y(cfg, seed)
+    lg = gen_logits(cfg, seed)
+    x_d, gy_d = bf16_tensor(x), bf16_tensor(gy)
+    ws = torch.empty(e4b.workspace_bytes(layer, cfg.T, cfg.k), dtype=torch.uint8, device=DEV)
+    y, idx, w, saved = e4b.moe_forward(layer, x_d, cfg.k, logits=torch.from_numpy(lg).to(DEV),
+                                       save=True, workspace=ws)
+    y = y.clone()
+    gx, gw = e4b.moe_dgrad(layer, idx, w, gy_d, saved=saved, workspace=ws)
+    gx, gw = gx.clone(), gw.clone()
+    gx2, gw2 = e4b.moe_dgrad(layer, idx, w, gy_d, x=x_d, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(gx.view(torch.int16), gx2.view(torch.int16))
+    assert torch.equal(gw.view(torch.int32), gw2.view(torch.int32))
+    y2, _, _, _ = e4b.moe_forward(layer, x_d, cfg.k, topk_idx=idx, topk_w=w, workspace=ws)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+    idx_ref, w_ref = oracle.route(lg, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.max(np.abs(w.cpu().numpy() - w_ref)) <= 1e-6
+    rng = np.random.default_rng(123)
+    tokens = np.sort(rng.choice(cfg.T, size=ntok, replace=False))
+    y_ref, (gx_ref, gw_ref) = _sampled_oracle(cfg, seed, kind, x, gy, idx_ref, w_ref, tokens)
+    t_d = torch.from_numpy(tokens).to(DEV)
+    tol_check(to_np(y[t_d]), y_ref, f"{name} y")
+    tol_check(to_np(gx[t_d]), gx_ref, f"{name} grad_x")
+    tol_check(to_np(gw[t_d]), gw_ref, f"{name} grad_topk_w")
+    del layer, ws, saved
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_decode_full_size(T):
+    cfg = get_config("qwen3_decode", T)
+    seed = 0
+    announce(f"qwen3 decode full size T={T}")
+    layer = _layer(cfg, seed, "nf4")
+    x = gen_x(cfg, seed)
+    lg = gen_logits(cfg, seed)
+    y, idx, w, _ = e4b.moe_forward(layer, bf16_tensor(x), cfg.k, logits=torch.from_numpy(lg).to(DEV),
+                                   path="decode")
+    idx_ref, w_ref = oracle.route(lg, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    tokens = np.arange(T)
+    y_ref, _ = _sampled_oracle(cfg, seed, "nf4", x, None, idx_ref, w_ref, tokens)
+    tol_check(to_np(y), y_ref, f"decode T={T} y")
+    yg, _, _, _ = e4b.moe_forward(layer, bf16_tensor(x), cfg.k, topk_idx=idx, topk_w=w, path="grouped")
+    tol_check(to_np(yg), y_ref, f"grouped T={T} y")
