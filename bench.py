@@ -313,6 +313,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 5 times (the reference "
+                         "kernel for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -325,6 +328,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+        return
     e4b.load()
     ev = HipEvents()
     tr = bench_train(args, e4b, torch, ev)

@@ -22,7 +22,7 @@
 //                 this tile's share of d y / d routing weight.
 //
 // Tile: kBM x kBN x kBK = 256 x 256 x 64 (one quantization block per K-step),
-// 256 threads = 4 waves in 2 x 2, each wave 128 x 128 = 4 x 4 MFMA 32x32x16
+// 512 threads = 8 waves in 4 x 2, each wave 64 x 128 = 2 x 4 MFMA 32x32x16
 // tiles. A and the dequantized B are staged in double-buffered LDS; B is
 // dequantized once per workgroup (codebook in LDS, fp32 multiply by the block
 // absmax, round-to-nearest-even bf16), i.e. exactly the bf16 view that
@@ -38,11 +38,15 @@ enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_DSWIGLU = 2 };
 
 
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // 8 waves: 2 per SIMD
 constexpr int kLds = kBK + 8;  // padded row (bf16 elements): 144 bytes, conflict-free b128 access
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
+// Waves are laid out 4 (M) x 2 (N); wave w -> (wm = w / 2, wn = w % 2), so the
+// waves holding the first 128 rows sit on all four SIMDs and a tile whose
+// rows end early frees whole SIMDs. Each wave owns 64 x 128 outputs
+// (2 x 4 MFMA 32x32x16 tiles, 128 fp32 accumulators per lane).
 template <int AMODE, int BMODE, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kLds];
@@ -71,80 +75,64 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 
   if (tid < 16) sCode[tid] = codebook_value(g.cb, tid);
 
-  // ---- A source rows: thread handles column chunk (tid & 7), rows (tid >> 3) + 32 i ----
+  // ---- A rows: column chunk (tid & 7) of rows (tid >> 3) + 64 i. Rows past
+  // the segment read the last valid row: their outputs are never stored. ----
   const int a_cc = tid & 7;
-  uint32_t a_off[8];
+  uint32_t a_off[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    uint32_t off = 0xFFFFFFFFu;
-    if (r < valid_rows) {
-      const int srow = seg + row0 + r;
-      const int src = AMODE == A_GATHER ? g.sorted_pair[srow] / g.topk : srow;
-      off = uint32_t(src) * uint32_t(g.lda) + uint32_t(a_cc * 8);
-    }
-    a_off[i] = off;
+  for (int i = 0; i < 4; ++i) {
+    const int r = min((tid >> 3) + 64 * i, valid_rows - 1);
+    const int srow = seg + row0 + r;
+    const int src = AMODE == A_GATHER ? g.sorted_pair[srow] / g.topk : srow;
+    a_off[i] = uint32_t(src) * uint32_t(g.lda) + uint32_t(a_cc * 8);
   }
 
-  // ---- B source ----
+  // ---- B source; columns past N read a valid weight row/column instead
+  // (their outputs are never stored) ----
   const uint8_t *wp = g.Wp + int64_t(e) * g.w_e_bytes;
   const float *wa = g.Wa + int64_t(e) * g.w_e_blocks;
   const int row_bytes = g.w_in >> 1, row_blocks = g.w_in >> 6;
-  // B_NT: this thread owns tile column tid (one weight row)
+  // B_NT: thread owns half (32 elements) of one tile column = one weight row
+  const int b_c = tid >> 1, b_half = tid & 1;
   int b_row = 0;
-  bool b_valid = false;
   if (BMODE == B_NT) {
     if (EPI == EPI_SWIGLU) {
-      const int c = tid;
-      const int cw = c >> 7, j = (c & 127) >> 5, ll = c & 31;
+      const int cw = b_c >> 7, j = (b_c & 127) >> 5, ll = b_c & 31;
       const int pair = nt * (kBN / 2) + cw * 64 + (j & 1) * 32 + ll;
-      b_valid = pair < g.I;
-      b_row = pair + (j >= 2 ? g.I : 0);
+      b_row = pair < g.I ? pair + (j >= 2 ? g.I : 0) : 0;
     } else {
-      b_row = nt * kBN + tid;
-      b_valid = b_row < g.N;
+      b_row = nt * kBN + b_c;
+      b_row = b_row < g.N ? b_row : 0;
     }
   }
-  // B_NN: this thread owns an 8 (k) x 8 (n) patch: n group cg, k group kg
-  const int b_cg = tid >> 3, b_kg = tid & 7;
-  const int b_n = nt * kBN + b_cg * 8;
-  if (BMODE == B_NN) b_valid = b_n < g.N;
+  const uint8_t *b_src_nt = wp + int64_t(b_row) * row_bytes + b_half * 16;
+  const float *b_am_nt = wa + int64_t(b_row) * row_blocks;
+  // B_NN: thread owns a 4 (k) x 8 (n) patch: n group cg (32), k group kg (16)
+  const int b_cg = tid >> 4, b_kg = tid & 15;
+  int b_n = nt * kBN + b_cg * 8;
+  b_n = b_n < g.N ? b_n : 0;
+  const uint8_t *b_src_nn = wp + int64_t(b_kg * 4) * row_bytes + (b_n >> 1);
+  const float *b_am_nn = wa + int64_t(b_kg * 4) * row_blocks + (b_n >> 6);
 
-  u32x4 ra[8];
-  u32x4 rb[2];
-  uint32_t rbn[8];
-  float ram[8];
+  u32x4 ra[4];
+  u32x4 rb;
+  float ram;
+  uint32_t rbn[4];
+  float ramn[4];
 
   auto load = [&](int ks) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (a_off[i] != 0xFFFFFFFFu)
-        ra[i] = *reinterpret_cast<const u32x4 *>(g.A + a_off[i] + uint32_t(ks * kBK));
-      else
-        ra[i] = u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < 4; ++i)
+      ra[i] = *reinterpret_cast<const u32x4 *>(g.A + a_off[i] + uint32_t(ks * kBK));
     if (BMODE == B_NT) {
-      if (b_valid) {
-        const u32x4 *src =
-            reinterpret_cast<const u32x4 *>(wp + int64_t(b_row) * row_bytes + ks * (kBK / 2));
-        rb[0] = src[0];
-        rb[1] = src[1];
-        ram[0] = wa[int64_t(b_row) * row_blocks + ks];
-      } else {
-        rb[0] = rb[1] = u32x4{0, 0, 0, 0};
-        ram[0] = 0.0f;
-      }
+      rb = *reinterpret_cast<const u32x4 *>(b_src_nt + ks * (kBK / 2));
+      ram = b_am_nt[ks];
     } else {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int64_t k = int64_t(ks) * kBK + b_kg * 8 + r;
-        if (b_valid) {
-          rbn[r] = *reinterpret_cast<const uint32_t *>(wp + k * row_bytes + (b_n >> 1));
-          ram[r] = wa[k * row_blocks + (b_n >> 6)];
-        } else {
-          rbn[r] = 0;
-          ram[r] = 0.0f;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int64_t k = int64_t(ks) * kBK + r;
+        rbn[r] = *reinterpret_cast<const uint32_t *>(b_src_nn + k * row_bytes);
+        ramn[r] = b_am_nn[k * row_blocks];
       }
     }
   };
@@ -152,56 +140,51 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   auto store = [&](int buf) {
     uint16_t *a_dst = sA[buf];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      *reinterpret_cast<u32x4 *>(a_dst + r * kLds + a_cc * 8) = ra[i];
-    }
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4 *>(a_dst + ((tid >> 3) + 64 * i) * kLds + a_cc * 8) = ra[i];
     uint16_t *b_dst = sB[buf];
     if (BMODE == B_NT) {
-      const float am = ram[0];
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const uint32_t w = rb[d >> 2][d & 3];
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t w = rb[d];
         float v[8];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          v[2 * b] = __fmul_rn(sCode[(w >> (8 * b + 4)) & 15u], am);
-          v[2 * b + 1] = __fmul_rn(sCode[(w >> (8 * b)) & 15u], am);
+          v[2 * b] = __fmul_rn(sCode[(w >> (8 * b + 4)) & 15u], ram);
+          v[2 * b + 1] = __fmul_rn(sCode[(w >> (8 * b)) & 15u], ram);
         }
-        *reinterpret_cast<u32x4 *>(b_dst + tid * kLds + d * 8) =
+        *reinterpret_cast<u32x4 *>(b_dst + b_c * kLds + b_half * 32 + d * 8) =
             u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                   pack_bf16x2(v[6], v[7])};
       }
     } else {
-      float v[8][8];  // [k row r][n col c]
+      float v[4][8];  // [k row r][n col c]
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
+      for (int r = 0; r < 4; ++r) {
         const uint32_t w = rbn[r];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          v[r][2 * b] = __fmul_rn(sCode[(w >> (8 * b + 4)) & 15u], ram[r]);
-          v[r][2 * b + 1] = __fmul_rn(sCode[(w >> (8 * b)) & 15u], ram[r]);
+          v[r][2 * b] = __fmul_rn(sCode[(w >> (8 * b + 4)) & 15u], ramn[r]);
+          v[r][2 * b + 1] = __fmul_rn(sCode[(w >> (8 * b)) & 15u], ramn[r]);
         }
       }
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        *reinterpret_cast<u32x4 *>(b_dst + (b_cg * 8 + c) * kLds + b_kg * 8) =
-            u32x4{pack_bf16x2(v[0][c], v[1][c]), pack_bf16x2(v[2][c], v[3][c]),
-                  pack_bf16x2(v[4][c], v[5][c]), pack_bf16x2(v[6][c], v[7][c])};
-      }
+      for (int c = 0; c < 8; ++c)
+        *reinterpret_cast<u32x2 *>(b_dst + (b_cg * 8 + c) * kLds + b_kg * 4) =
+            u32x2{pack_bf16x2(v[0][c], v[1][c]), pack_bf16x2(v[2][c], v[3][c])};
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // number of 32-row MFMA tiles of this wave that hold valid rows
-  const int mi_valid = max(0, min(4, (valid_rows - wm * 128 + 31) >> 5));
+  // a wave whose 64 rows all lie past the segment skips its MFMAs
+  const bool wave_active = wm * 64 < valid_rows;
 
   const int nK = g.K / kBK;
   __syncthreads();  // sCode visible
@@ -212,24 +195,23 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 
   for (int ks = 0; ks < nK; ++ks) {
     const int cur = ks & 1;
-    const uint16_t *a_src = sA[cur] + (wm * 128 + (lane & 31)) * kLds + (lane >> 5) * 8;
-    const uint16_t *b_src = sB[cur] + (wn * 128 + (lane & 31)) * kLds + (lane >> 5) * 8;
+    if (wave_active) {
+      const uint16_t *a_src = sA[cur] + (wm * 64 + (lane & 31)) * kLds + (lane >> 5) * 8;
+      const uint16_t *b_src = sB[cur] + (wn * 128 + (lane & 31)) * kLds + (lane >> 5) * 8;
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8 af[4], bfr[4];
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        bf16x8 af[2], bfr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8 *>(a_src + i * 32 * kLds + kk * 16);
+        for (int i = 0; i < 2; ++i)
+          af[i] = *reinterpret_cast<const bf16x8 *>(a_src + i * 32 * kLds + kk * 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8 *>(b_src + j * 32 * kLds + kk * 16);
+        for (int j = 0; j < 4; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8 *>(b_src + j * 32 * kLds + kk * 16);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i < mi_valid) {
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
       }
     }
     if (ks + 1 < nK) store(cur ^ 1);
@@ -238,12 +220,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   }
 
   // ---- epilogue ----
-  // acc[i][j][r]: row = wm*128 + i*32 + 8*(r/4) + 4*(lane/32) + r%4,
+  // acc[i][j][r]: row = wm*64 + i*32 + 8*(r/4) + 4*(lane/32) + r%4,
   //               col = wn*128 + j*32 + lane%32
-  const int lrow_base = wm * 128 + 4 * (lane >> 5);
+  const int lrow_base = wm * 64 + 4 * (lane >> 5);
   if (EPI == EPI_STORE) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = lrow_base + i * 32 + 8 * (r >> 2) + (r & 3);
@@ -259,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
     }
   } else if (EPI == EPI_SWIGLU) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = lrow_base + i * 32 + 8 * (r >> 2) + (r & 3);
@@ -284,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   } else {  // EPI_DSWIGLU
     float *red = reinterpret_cast<float *>(sA[0]);  // [2][kBM] partial row sums
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = lrow_base + i * 32 + 8 * (r >> 2) + (r & 3);
@@ -313,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
         // sum over the 32 columns held by this half-wave (fixed butterfly order)
 #pragma unroll
         for (int o = 1; o < 32; o <<= 1) part += __shfl_xor(part, o);
-        if ((lane & 31) == 0) red[wn * kBM + i * 32 + 8 * (r >> 2) + (r & 3) + 4 * (lane >> 5) + wm * 128] = part;
+        if ((lane & 31) == 0) red[wn * kBM + row] = part;
       }
     }
     __syncthreads();
