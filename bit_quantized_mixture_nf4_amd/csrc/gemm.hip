@@ -193,110 +193,147 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   if (nK > 1) load(1);
   __syncthreads();
 
-  for (int ks = 0; ks < nK; ++ks) {
-    const int cur = ks & 1;
-    if (wave_active) {
-      const uint16_t *a_src = sA[cur] + (wm * 64 + (lane & 31)) * kLds + (lane >> 5) * 8;
-      const uint16_t *b_src = sB[cur] + (wn * 128 + (lane & 31)) * kLds + (lane >> 5) * 8;
+  // The two waves sharing a SIMD (w and w + 4) run the two halves of a K-step
+  // in opposite order, so one issues MFMAs while the other dequantizes and
+  // stores the next stage. Within one barrier interval both orders are safe:
+  // the compute reads buffer `cur` (filled before the previous barrier) and
+  // the stores fill buffer `cur ^ 1` (last read before the previous barrier).
+  auto compute = [&](int cur) {
+    if (!wave_active) return;
+    const uint16_t *a_src = sA[cur] + (wm * 64 + (lane & 31)) * kLds + (lane >> 5) * 8;
+    const uint16_t *b_src = sB[cur] + (wn * 128 + (lane & 31)) * kLds + (lane >> 5) * 8;
 #pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        bf16x8 af[2], bfr[4];
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      bf16x8 af[2], bfr[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          af[i] = *reinterpret_cast<const bf16x8 *>(a_src + i * 32 * kLds + kk * 16);
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const bf16x8 *>(a_src + i * 32 * kLds + kk * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8 *>(b_src + j * 32 * kLds + kk * 16);
+      // weights are the MFMA A-operand: acc[i][j] holds D[tile col][tile row]
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8 *>(b_src + j * 32 * kLds + kk * 16);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_s_setprio(0);
     }
-    if (ks + 1 < nK) store(cur ^ 1);
-    if (ks + 2 < nK) load(ks + 2);
+  };
+  const bool store_first = wave >= 4;
+  for (int ks = 0; ks < nK; ++ks) {
+    const int cur = ks & 1;
+    if (store_first) {
+      if (ks + 1 < nK) store(cur ^ 1);
+      if (ks + 2 < nK) load(ks + 2);
+      compute(cur);
+    } else {
+      compute(cur);
+      if (ks + 1 < nK) store(cur ^ 1);
+      if (ks + 2 < nK) load(ks + 2);
+    }
     __syncthreads();
   }
 
   // ---- epilogue ----
-  // acc[i][j][r]: row = wm*64 + i*32 + 8*(r/4) + 4*(lane/32) + r%4,
-  //               col = wn*128 + j*32 + lane%32
-  const int lrow_base = wm * 64 + 4 * (lane >> 5);
+  // acc[i][j][4q + t]: tile row  = wm*64 + i*32 + lane%32,
+  //                    tile col  = wn*128 + j*32 + 8q + 4*(lane/32) + t   (t = 0..3)
+  // so each lane holds runs of 4 consecutive columns of one row.
+  const int lrow = wm * 64 + (lane & 31);
+  const int lcol = wn * 128 + 4 * (lane >> 5);
   if (EPI == EPI_STORE) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      const int row = lrow + i * 32;
+      if (row < valid_rows) {
+        uint16_t *crow = g.C + int64_t(seg + row0 + row) * g.ldc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = lrow_base + i * 32 + 8 * (r >> 2) + (r & 3);
-        if (row < valid_rows) {
-          const int64_t grow = seg + row0 + row;
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = nt * kBN + wn * 128 + j * 32 + (lane & 31);
-            if (col < g.N) g.C[grow * g.ldc + col] = f32_to_bf16(acc[i][j][r]);
+          for (int q = 0; q < 4; ++q) {
+            const int col = nt * kBN + lcol + j * 32 + 8 * q;
+            const f32x16 &a = acc[i][j];
+            if (col < g.N)
+              *reinterpret_cast<u32x2 *>(crow + col) =
+                  u32x2{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
           }
-        }
       }
     }
   } else if (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      const int row = lrow + i * 32;
+      if (row < valid_rows) {
+        const int64_t grow = seg + row0 + row;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = lrow_base + i * 32 + 8 * (r >> 2) + (r & 3);
-        if (row < valid_rows) {
-          const int64_t grow = seg + row0 + row;
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int pair = nt * (kBN / 2) + wn * 64 + jj * 32 + (lane & 31);
+          for (int q = 0; q < 4; ++q) {
+            const int pair = nt * (kBN / 2) + wn * 64 + jj * 32 + 8 * q + 4 * (lane >> 5);
             if (pair < g.I) {
-              const float gv = acc[i][jj][r], uv = acc[i][jj + 2][r];
-              const float a = gv * sigmoidf_(gv) * uv;
-              if (g.C) g.C[grow * g.ldc + pair] = f32_to_bf16(a);
+              float gv[4], uv[4], av[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                gv[t] = acc[i][jj][4 * q + t];
+                uv[t] = acc[i][jj + 2][4 * q + t];
+                av[t] = gv[t] * sigmoidf_(gv[t]) * uv[t];
+              }
+              if (g.C)
+                *reinterpret_cast<u32x2 *>(g.C + grow * g.ldc + pair) =
+                    u32x2{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
               if (g.GU) {
-                g.GU[grow * (2 * g.I) + pair] = f32_to_bf16(gv);
-                g.GU[grow * (2 * g.I) + g.I + pair] = f32_to_bf16(uv);
+                *reinterpret_cast<u32x2 *>(g.GU + grow * (2 * g.I) + pair) =
+                    u32x2{pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
+                *reinterpret_cast<u32x2 *>(g.GU + grow * (2 * g.I) + g.I + pair) =
+                    u32x2{pack_bf16x2(uv[0], uv[1]), pack_bf16x2(uv[2], uv[3])};
               }
             }
           }
-        }
       }
     }
   } else {  // EPI_DSWIGLU
     float *red = reinterpret_cast<float *>(sA[0]);  // [2][kBM] partial row sums
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      const int row = lrow + i * 32;
+      float part = 0.0f;
+      if (row < valid_rows) {
+        const int64_t grow = seg + row0 + row;
+        const float wr = g.topk_w[g.sorted_pair[grow]];
+        const uint16_t *gurow = g.GU + grow * (2 * g.I);
+        uint16_t *crow = g.C + grow * g.ldc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = lrow_base + i * 32 + 8 * (r >> 2) + (r & 3);
-        float part = 0.0f;
-        if (row < valid_rows) {
-          const int64_t grow = seg + row0 + row;
-          const float wr = g.topk_w[g.sorted_pair[grow]];
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = nt * kBN + wn * 128 + j * 32 + (lane & 31);
+          for (int q = 0; q < 4; ++q) {
+            const int n = nt * kBN + lcol + j * 32 + 8 * q;
             if (n < g.N) {
-              const float gv = bf16_to_f32(g.GU[grow * (2 * g.I) + n]);
-              const float uv = bf16_to_f32(g.GU[grow * (2 * g.I) + g.I + n]);
-              const float s = sigmoidf_(gv);
-              const float silu = gv * s;
-              const float G2 = acc[i][j][r];
-              part += G2 * (silu * uv);
-              const float ga = wr * G2;
-              const float dg = ga * uv * s * (1.0f + gv * (1.0f - s));
-              const float du = ga * silu;
-              g.C[grow * g.ldc + n] = f32_to_bf16(dg);
-              g.C[grow * g.ldc + g.I + n] = f32_to_bf16(du);
+              const u32x2 gg = *reinterpret_cast<const u32x2 *>(gurow + n);
+              const u32x2 uu = *reinterpret_cast<const u32x2 *>(gurow + g.I + n);
+              const float gv[4] = {bf16_lo(gg[0]), bf16_hi(gg[0]), bf16_lo(gg[1]), bf16_hi(gg[1])};
+              const float uv[4] = {bf16_lo(uu[0]), bf16_hi(uu[0]), bf16_lo(uu[1]), bf16_hi(uu[1])};
+              float dg[4], du[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                const float s = sigmoidf_(gv[t]);
+                const float silu = gv[t] * s;
+                const float G2 = acc[i][j][4 * q + t];
+                part += G2 * (silu * uv[t]);
+                const float ga = wr * G2;
+                dg[t] = ga * uv[t] * s * (1.0f + gv[t] * (1.0f - s));
+                du[t] = ga * silu;
+              }
+              *reinterpret_cast<u32x2 *>(crow + n) =
+                  u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+              *reinterpret_cast<u32x2 *>(crow + g.I + n) =
+                  u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
             }
           }
-        }
-        // sum over the 32 columns held by this half-wave (fixed butterfly order)
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) part += __shfl_xor(part, o);
-        if ((lane & 31) == 0) red[wn * kBM + row] = part;
       }
+      // the two half-waves hold the two column halves of the same rows
+      part += __shfl_xor(part, 32);
+      if (lane < 32) red[wn * kBM + row] = part;
     }
     __syncthreads();
     if (tid < valid_rows) {
