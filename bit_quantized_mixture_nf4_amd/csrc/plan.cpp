@@ -113,9 +113,11 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
 }
 
 bool decode_fits(const MoePlan &p) {
+  // a row slice of 64 (T <= 2) or 32 (T <= 8) elements per lane, at most 64
+  // lanes per row
   const int64_t kmax = p.H > p.I ? p.H : p.I;
-  return p.T <= kDecodeMaxT && p.T * kmax * 2 <= kDecStageBytes && p.P <= kDecMaxPairs &&
-         (p.H / 32) * 2 <= kDecMaxChunks && (p.I / 32) <= kDecMaxChunks;
+  const int64_t epl = p.T <= 2 ? 64 : 32;
+  return p.T <= kDecodeMaxT && p.P <= kDecMaxPairs && kmax <= 64 * epl;
 }
 
 e4b_status check_forward(const MoePlan &p, const void *x, const float *logits,
@@ -167,7 +169,7 @@ extern "C" const char *e4b_status_string(e4b_status s) {
     case E4B_ERR_DTYPE: return "unknown output dtype";
     case E4B_ERR_WORKSPACE: return "workspace missing or too small";
     case E4B_ERR_ALIGN: return "device buffer not 16-byte aligned";
-    case E4B_ERR_PATH: return "invalid path (decode path needs T <= 8 and saved == NULL)";
+    case E4B_ERR_PATH: return "invalid path (decode path needs T <= 8, saved == NULL and max(H, I) <= 4096 (T <= 2) or 2048)";
     case E4B_ERR_HIP: return "HIP kernel launch failed";
   }
   return "unknown status";

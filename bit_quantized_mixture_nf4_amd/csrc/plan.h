@@ -20,9 +20,7 @@ constexpr int kPermChunk = 1024;  // pairs per histogram / scatter chunk
 constexpr int kMaxE = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kDecodeMaxT = 8;
-constexpr int kDecMaxChunks = 1024;  // decode GEMV: 16-byte code chunks per workgroup
 constexpr int kDecMaxPairs = kDecodeMaxT * kMaxTopK;
-constexpr int kDecStageBytes = 65536;  // decode GEMV: LDS for the staged input rows
 
 struct MoePlan {
   int64_t E, H, I, T, k, P;
@@ -53,8 +51,8 @@ e4b_status check_quantize(const float *w, int64_t E, int64_t out, int64_t in,
                           int32_t blocksize, int32_t codebook, const uint8_t *packed,
                           const float *absmax);
 
-// True when (T, H, I, k) fit the decode GEMV path: T <= 8 and the bf16 input
-// rows of one expert (at most T of max(H, I) elements) fit its LDS stage.
+// True when (T, H, I, k) fit the decode GEMV path: T <= 8 and a weight row
+// spans at most 64 lanes of 64 (T <= 2) or 32 (T <= 8) elements.
 bool decode_fits(const MoePlan &p);
 
 e4b_status check_forward(const MoePlan &p, const void *x, const float *logits,
