@@ -11,15 +11,19 @@
 //            expert; a = silu(g) * u is written as bf16;
 //   down     one workgroup per (distinct expert, block of rows of H);
 //   combine  the shared deterministic gather-combine.
-// No MFMA: each code byte is expanded through a 256-entry LDS table into two
-// bf16 codebook values and contracted with bf16 activations by
-// v_dot2c_f32_bf16 in fp32; the block absmax scales each lane's partial sum.
+// The projections of the (at most 8) tokens of one expert form a skinny GEMM:
+// it runs on the 16x16x32 bf16 MFMA with the tokens as the 16-row A operand
+// (rows past the expert's token count are computed and dropped), so the cost
+// per weight byte does not grow with the number of tokens. Each code byte is
+// expanded through a 256-entry LDS table into two bf16 codebook values; the
+// block absmax scales the fp32 partial of each 64-element block.
 #include "device.h"
 #include "kernels.h"
 
 namespace e4b {
 
-constexpr int kDecThreads = 256;
+constexpr int kDecWaves = 8;  // waves of a decode workgroup: one K eighth each
+constexpr int kDecThreads = 64 * kDecWaves;
 
 // Workspace layout of the decode path (inside the permutation region).
 struct DecodeWs {
@@ -29,11 +33,6 @@ struct DecodeWs {
   int32_t *sorted;      // [P] pair id at sorted position
   int32_t *pos;         // [P] sorted position of pair id
 };
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                         __builtin_bit_cast(bf16x2, b), c, false);
-}
 
 __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restrict__ idx, int P,
                                                           DecodeWs w) {
@@ -71,150 +70,196 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restr
   }
 }
 
-// One wavefront streams weight rows of one expert past a fixed slice of the
-// reduction dimension: lane l owns elements [kl*EPL, kl*EPL + EPL) of every
-// row (kl = l % LPR, LPR lanes per row, 64/LPR rows per pass) and keeps the
-// matching slice of the input vector of each of the expert's NP tokens in
-// registers (loaded once, reused for all its rows). Loads of kBatch passes are
-// issued before any of them is used. Each code byte is expanded through a
-// 256-entry LDS table into two bf16 codebook values and contracted with the
-// inputs by v_dot2c_f32_bf16; the lane's block absmax scales its partial sum
-// once; the LPR partials of a row are summed with shuffles. GATE_UP processes
-// gate row u and up row I + u in the same lanes and writes a = silu(g) * up;
-// otherwise row u's dot product is written.
-constexpr int kBatch = 4;
+// Skinny-GEMM form of the projection of one expert's np <= 8 tokens, on the
+// 16x16x32 bf16 MFMA: the tokens' inputs are the A operand (16 rows, rows past
+// np repeat the last token and are not stored), 16 weight rows of the expert
+// are the B operand, the reduction runs over in_features.
+//
+// A workgroup owns a chunk of consecutive tiles of 16 output units of one
+// expert: the chunk length is chosen on the device from the number of
+// distinct experts, so that about wg_target workgroups have work (the grid
+// holds one workgroup per (expert slot, tile) and the surplus exits at once); its eight waves split the K blocks in eighths, so each wave holds
+// its eighth of the token inputs in registers for all tiles. Per tile and
+// 64-element absmax block, lane (g = l / 16, m = l % 16) loads the 8 code bytes
+// [8g, 8g + 8) of weight row m, expands each byte into two bf16 codebook
+// values through an LDS table (replicated kTblCopies times so that the lanes
+// of a half-wave read distinct banks), and two MFMAs contract the block; the
+// block's absmax (weight row m is the lane's output column) scales the fp32
+// partial before it joins the accumulator. Weight bytes and absmax of the
+// next tile are in flight while a tile is contracted. Per tile
+// the eight K partials meet in a double-buffered LDS slot and are summed in a
+// fixed order (one barrier per tile). GATE_UP runs the gate and up tiles of
+// the same units in the same lanes and writes a = silu(g) * up.
+constexpr int kTblCopies = 32;
 
-template <bool GATE_UP, int NP, int EPL>
-__device__ __forceinline__ void decode_rows(const uint32_t *tbl, const uint8_t *wp,
-                                            const float *wa, int K_in, int n_units, int I,
-                                            const uint16_t *vin, int k_route, const DecodeWs &w,
-                                            int s0, uint16_t *out, int ldo, int u_first,
-                                            int units_per_wave, int lane) {
-  constexpr int WPL = EPL / 2;   // bf16-pair words per lane
-  constexpr int NV = EPL / 32;   // 16-byte weight loads per row slice
-  constexpr int NR = GATE_UP ? 2 : 1;
-  const int cpr = K_in / EPL;    // lanes holding data per row
-  int LPR = 1;
-  while (LPR < cpr) LPR <<= 1;
-  const int rpp = 64 / LPR;
-  const int ru = lane / LPR, kl = lane % LPR;
-  const bool kvalid = kl < cpr;
-  const int kbase = kvalid ? kl * EPL : 0;
-  const int row_bytes = K_in >> 1, row_blocks = K_in >> 6;
-  wp += kbase >> 1;
-  wa += kbase >> 6;
-
-  // Lanes past the end of a row (kl >= cpr) read the row's first slice (always
-  // in bounds) and zero their input slice, so they contribute exact zeros.
-  uint32_t xr[NP][WPL];
-#pragma unroll
-  for (int q = 0; q < NP; ++q) {
-    const int64_t row = GATE_UP ? int64_t(w.sorted[s0 + q] / k_route) : int64_t(s0 + q);
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(vin + row * K_in + kbase);
-#pragma unroll
-    for (int c = 0; c < WPL / 4; ++c) {
-      const u32x4 v = src[c];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) xr[q][4 * c + t] = kvalid ? v[t] : 0u;
-    }
-  }
-
-  for (int p0 = 0; p0 < units_per_wave; p0 += kBatch * rpp) {
-    u32x4 wv[kBatch][NR][NV];
-    float am[kBatch][NR];
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int u = u_first + p0 + b * rpp + ru;
-      const int uc = u < n_units ? u : 0;
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int64_t row = r == 0 ? uc : I + uc;
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(wp + row * row_bytes);
-#pragma unroll
-        for (int c = 0; c < NV; ++c) wv[b][r][c] = src[c];
-        am[b][r] = wa[row * row_blocks];
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      float acc[NR][NP];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-#pragma unroll
-        for (int q = 0; q < NP; ++q) acc[r][q] = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NV; ++c)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const uint32_t word = wv[b][r][c][t];
-#pragma unroll
-            for (int y = 0; y < 4; ++y) {
-              const uint32_t codes = tbl[(word >> (8 * y)) & 255u];
-#pragma unroll
-              for (int q = 0; q < NP; ++q)
-                acc[r][q] = dot2_bf16(codes, xr[q][16 * c + 4 * t + y], acc[r][q]);
-            }
-          }
-#pragma unroll
-        for (int q = 0; q < NP; ++q) {
-          float v = acc[r][q] * am[b][r];
-#pragma unroll
-          for (int o = 32; o >= 1; o >>= 1)
-            if (o < LPR) v += __shfl_xor(v, o);
-          acc[r][q] = v;
-        }
-      }
-      const int u = u_first + p0 + b * rpp + ru;
-      if (u < n_units && kl == 0) {
-#pragma unroll
-        for (int q = 0; q < NP; ++q) {
-          const float g = acc[0][q];
-          const float v = GATE_UP ? g / (1.0f + __expf(-g)) * acc[NR - 1][q] : g;
-          out[int64_t(s0 + q) * ldo + u] = f32_to_bf16(v);
-        }
-      }
-    }
-  }
-}
-
-template <bool GATE_UP, int MAXNP, int EPL>
-__global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(
+// AM_VEC: every wave owns 0 or MAXB blocks and MAXB divides the blocks per row,
+// so a wave's absmax run is one aligned vector load.
+template <bool GATE_UP, int MAXB, bool AM_VEC>
+__global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
     const uint8_t *__restrict__ Wp, const float *__restrict__ Wa, int64_t w_e_bytes,
     int64_t w_e_blocks, int K_in, int n_units, int I, const uint16_t *__restrict__ vin,
-    int k_route, DecodeWs w, int cb, uint16_t *__restrict__ out, int ldo, int units_per_wave) {
-  __shared__ uint32_t tbl[256];
-  const int d = blockIdx.y;
-  if (d >= w.n_distinct[0]) return;
+    int k_route, DecodeWs w, int cb, uint16_t *__restrict__ out, int ldo, int wg_target) {
+  constexpr int NR = GATE_UP ? 2 : 1;
+  __shared__ uint32_t tbl[256 * kTblCopies];
+  __shared__ f32x4 s_red[2][NR][kDecWaves][64];
+  const int n_tiles = n_units >> 4;
+  const int n_dist = w.n_distinct[0];
+  const int tiles_per_wg = min(n_tiles, max(1, (n_dist * n_tiles + wg_target - 1) / wg_target));
+  const int chunks = (n_tiles + tiles_per_wg - 1) / tiles_per_wg;
+  const int d = blockIdx.x / chunks;
+  if (d >= n_dist) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // code byte -> (bf16 code of the high nibble | bf16 code of the low nibble << 16)
-  tbl[tid] = pack_bf16x2(codebook_value(cb, tid >> 4), codebook_value(cb, tid & 15));
-  __syncthreads();
+  const int g = lane >> 4, m = lane & 15;
+  // entry (byte, copy) at byte * kTblCopies + copy: high nibble's code in the
+  // low half, low nibble's code in the high half (element order in memory)
+  // (thread tid fills entries tid + 512 k: low nibble tid / 32, high nibble k)
+  static_assert(kDecThreads == 16 * kTblCopies, "table fill layout");
+  {
+    const float lo = codebook_value(cb, tid / kTblCopies);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) tbl[tid + kDecThreads * k] = pack_bf16x2(codebook_value(cb, k), lo);
+  }
+  const uint32_t *tl = tbl + (lane & (kTblCopies - 1));
+
   const int e = w.dexp[d];
   const int s0 = w.dseg[d];
-  const int np = w.dseg[d + 1] - s0;  // <= T when tokens' experts are distinct
+  const int np = w.dseg[d + 1] - s0;
+  const int nblk = K_in >> 6;
+  const int tile0 = (blockIdx.x - d * chunks) * tiles_per_wg;
+  const int nt = min(tiles_per_wg, n_tiles - tile0);
   const uint8_t *wp = Wp + int64_t(e) * w_e_bytes;
   const float *wa = Wa + int64_t(e) * w_e_blocks;
-  const int u_first = (blockIdx.x * (kDecThreads / 64) + wave) * units_per_wave;
-#define E4B_DEC_CASE(N)                                                                      \
-  case N:                                                                                    \
-    if constexpr (N <= MAXNP)                                                                \
-      decode_rows<GATE_UP, N, EPL>(tbl, wp, wa, K_in, n_units, I, vin, k_route, w, s0, out, \
-                                   ldo, u_first, units_per_wave, lane);                      \
-    break;
-  switch (np < MAXNP ? np : MAXNP) {
-    E4B_DEC_CASE(1)
-    E4B_DEC_CASE(2)
-    E4B_DEC_CASE(3)
-    E4B_DEC_CASE(4)
-    E4B_DEC_CASE(5)
-    E4B_DEC_CASE(6)
-    E4B_DEC_CASE(7)
-    E4B_DEC_CASE(8)
-    default:
-      break;
+
+  // this wave's K blocks [b0, b0 + nb); loads of blocks past nb read a valid
+  // block of the row instead (their products are never formed), so every load
+  // is unconditional and the wait counts stay exact
+  const int bpw = (nblk + kDecWaves - 1) / kDecWaves;
+  const int b0 = wave * bpw;
+  const int nb = max(0, min(bpw, nblk - b0));
+  const int row_bytes = K_in >> 1;
+  int bcl[MAXB];
+#pragma unroll
+  for (int b = 0; b < MAXB; ++b) bcl[b] = min(b0 + b, nblk - 1);
+
+  // the tokens' inputs for this wave's blocks (registers, all tiles)
+  const int q = min(m, np - 1);
+  const int64_t xrow = GATE_UP ? int64_t(w.sorted[s0 + q] / k_route) : int64_t(s0 + q);
+  const uint16_t *xp = vin + xrow * K_in + 16 * g;
+  u32x4 xr[MAXB][2];
+#pragma unroll
+  for (int b = 0; b < MAXB; ++b) {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(xp + bcl[b] * 64);
+    xr[b][0] = src[0];
+    xr[b][1] = src[1];
   }
-#undef E4B_DEC_CASE
+
+  struct Stage {
+    u32x2 wv[NR][MAXB];
+    float am[NR][MAXB];
+  };
+  auto load_tile = [&](int t, Stage &st) {
+    const int u = (tile0 + t) * 16 + m;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int64_t row = u + r * I;
+      const uint8_t *src = wp + row * row_bytes + 8 * g;
+      const float *ap = wa + row * nblk;
+#pragma unroll
+      for (int b = 0; b < MAXB; ++b)
+        st.wv[r][b] = *reinterpret_cast<const u32x2 *>(src + bcl[b] * 32);
+      if constexpr (AM_VEC) {
+        const float *av = ap + min(b0, nblk - MAXB);
+        if constexpr (MAXB == 2) {
+          const f32x2 v = *reinterpret_cast<const f32x2 *>(av);
+          st.am[r][0] = v[0];
+          st.am[r][1] = v[1];
+        } else {
+#pragma unroll
+          for (int c = 0; c < MAXB / 4; ++c) {
+            const f32x4 v = reinterpret_cast<const f32x4 *>(av)[c];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st.am[r][4 * c + i] = v[i];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < MAXB; ++b) st.am[r][b] = ap[bcl[b]];
+      }
+    }
+  };
+  Stage st0, st1;
+  load_tile(0, st0);
+  if (nt == 1) {
+    __syncthreads();
+  } else {
+    load_tile(1, st1);
+    __syncthreads();
+  }
+
+  auto contract = [&](const Stage &st, int slot) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int b = 0; b < MAXB; ++b) {
+        if (b < nb) {
+          u32x4 c0, c1;
+#pragma unroll
+          for (int y = 0; y < 4; ++y) {
+            c0[y] = tl[((st.wv[r][b][0] >> (8 * y)) & 255u) * kTblCopies];
+            c1[y] = tl[((st.wv[r][b][1] >> (8 * y)) & 255u) * kTblCopies];
+          }
+          f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, xr[b][0]), __builtin_bit_cast(bf16x8, c0),
+              f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xr[b][1]),
+                                                         __builtin_bit_cast(bf16x8, c1), part,
+                                                         0, 0, 0);
+          const float am = st.am[r][b];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j] += part[j] * am;
+        }
+      }
+      s_red[slot][r][wave][lane] = acc;
+    }
+  };
+  // sum the K parts of tile t: thread (token row qq, unit mm)
+  auto reduce_store = [&](int t, int slot) {
+    if (tid < 16 * np) {
+      const int qq = tid >> 4, mm = tid & 15;
+      const int src_lane = 16 * (qq >> 2) + mm, comp = qq & 3;
+      float v[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float sum = s_red[slot][r][0][src_lane][comp];
+#pragma unroll
+        for (int k = 1; k < kDecWaves; ++k) sum += s_red[slot][r][k][src_lane][comp];
+        v[r] = sum;
+      }
+      const float val = GATE_UP ? v[0] / (1.0f + __expf(-v[0])) * v[NR - 1] : v[0];
+      out[int64_t(s0 + qq) * ldo + (tile0 + t) * 16 + mm] = f32_to_bf16(val);
+    }
+  };
+  if (nt == 1) {
+    contract(st0, 0);
+    __syncthreads();
+    reduce_store(0, 0);
+    return;
+  }
+  // two tiles in flight; prefetch ids past the last tile are clamped to it
+  // (a redundant load keeps the wait counts of every iteration identical)
+  for (int t = 0; t < nt; t += 2) {
+    contract(st0, 0);
+    load_tile(min(t + 2, nt - 1), st0);
+    __syncthreads();
+    reduce_store(t, 0);
+    if (t + 1 < nt) contract(st1, 1);
+    load_tile(min(t + 3, nt - 1), st1);
+    __syncthreads();
+    if (t + 1 < nt) reduce_store(t + 1, 1);
+  }
 }
+
 
 hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
                                  const int32_t *idx, const float *wts, uint16_t *y, char *ws,
@@ -235,40 +280,44 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
   const int ymax = int(p.P < p.E ? p.P : p.E);
   const int H = int(p.H), I = int(p.I);
   const e4b_stack &gu = L->gate_up, &dn = L->down;
-  auto lanes_per_row = [](int K_in, int epl) {
-    int l = 1;
-    while (l < K_in / epl) l <<= 1;
-    return l;
+  // two workgroups of the decode kernel fit one CU (LDS); aim at one wave of them
+  const int wg_target = 512;
+  auto launch = [&](bool gate_up, int K_in, int n_units, const e4b_stack &st,
+                    const uint16_t *vin, uint16_t *dst, int ldo, int kernel_id) {
+    const int nblk = K_in / kBlock;
+    const int bpw = (nblk + kDecWaves - 1) / kDecWaves;
+    const int tiles = n_units / 16;
+    const dim3 grid(uint32_t(tiles * ymax));
+    const int64_t eb = st.out * st.in / 2, ea = st.out * st.in / kBlock;
+    timer_before(kernel_id, s);
+#define E4B_DEC_LAUNCH(GU, MB, AV)                                                            \
+  hipLaunchKernelGGL((decode_mfma_kernel<GU, MB, AV>), grid, dim3(kDecThreads), 0, s,          \
+                     st.packed, st.absmax, eb, ea, K_in, n_units, I, vin, int(p.k), w,         \
+                     p.codebook, dst, ldo, wg_target)
+#define E4B_DEC_LAUNCH_MB(GU)                                                                 \
+  do {                                                                                        \
+    const int mb = bpw <= 2 ? 2 : (bpw <= 4 ? 4 : 8);                                         \
+    const bool av = bpw == mb && nblk % mb == 0;                                              \
+    if (mb == 2) {                                                                            \
+      if (av) E4B_DEC_LAUNCH(GU, 2, true); else E4B_DEC_LAUNCH(GU, 2, false);                 \
+    } else if (mb == 4) {                                                                     \
+      if (av) E4B_DEC_LAUNCH(GU, 4, true); else E4B_DEC_LAUNCH(GU, 4, false);                 \
+    } else {                                                                                  \
+      if (av) E4B_DEC_LAUNCH(GU, 8, true); else E4B_DEC_LAUNCH(GU, 8, false);                 \
+    }                                                                                         \
+  } while (0)
+    if (gate_up)
+      E4B_DEC_LAUNCH_MB(true);
+    else
+      E4B_DEC_LAUNCH_MB(false);
+#undef E4B_DEC_LAUNCH_MB
+#undef E4B_DEC_LAUNCH
+    timer_after(kernel_id, s);
   };
-  // row units per wave: kBatch passes for one token, up to 4 batches when the
-  // per-wave input slices of several tokens must be amortized over more rows
-  const int batches = p.T <= 1 ? 1 : (p.T <= 2 ? 2 : 4);
-  auto launch_pair = [&](auto gu_kernel, auto dn_kernel, int epl) {
-    // gate_up: I gate/up row pairs over K_in = H
-    const int upw_g = batches * kBatch * (64 / lanes_per_row(H, epl));
-    const int wg_g = (I + 4 * upw_g - 1) / (4 * upw_g);
-    timer_before(E4B_K_DECODE_GATE_UP, s);
-    hipLaunchKernelGGL(gu_kernel, dim3(uint32_t(wg_g), uint32_t(ymax)), dim3(kDecThreads), 0, s,
-                       gu.packed, gu.absmax, gu.out * gu.in / 2, gu.out * gu.in / kBlock, H, I, I,
-                       x, int(p.k), w, p.codebook, a_buf, I, upw_g);
-    timer_after(E4B_K_DECODE_GATE_UP, s);
-    // down: H rows over K_in = I
-    const int upw_d = batches * kBatch * (64 / lanes_per_row(I, epl));
-    const int wg_d = (H + 4 * upw_d - 1) / (4 * upw_d);
-    timer_before(E4B_K_DECODE_DOWN, s);
-    hipLaunchKernelGGL(dn_kernel, dim3(uint32_t(wg_d), uint32_t(ymax)), dim3(kDecThreads), 0, s,
-                       dn.packed, dn.absmax, dn.out * dn.in / 2, dn.out * dn.in / kBlock, I, H, I,
-                       a_buf, int(p.k), w, p.codebook, o_buf, H, upw_d);
-    timer_after(E4B_K_DECODE_DOWN, s);
-  };
-  if (p.T <= 1)
-    launch_pair(decode_gemv_kernel<true, 1, 64>, decode_gemv_kernel<false, 1, 64>, 64);
-  else if (p.T <= 2)
-    launch_pair(decode_gemv_kernel<true, 2, 64>, decode_gemv_kernel<false, 2, 64>, 64);
-  else if (p.T <= 4)
-    launch_pair(decode_gemv_kernel<true, 4, 32>, decode_gemv_kernel<false, 4, 32>, 32);
-  else
-    launch_pair(decode_gemv_kernel<true, 8, 32>, decode_gemv_kernel<false, 8, 32>, 32);
+  // gate_up: I units (gate row u, up row I + u) over K_in = H
+  launch(true, H, I, gu, x, a_buf, I, E4B_K_DECODE_GATE_UP);
+  // down: H rows over K_in = I
+  launch(false, I, H, dn, a_buf, o_buf, H, E4B_K_DECODE_DOWN);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_combine_rows(o_buf, w.pos, wts, p.T, int(p.k), H, y, s);

@@ -113,11 +113,8 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
 }
 
 bool decode_fits(const MoePlan &p) {
-  // a row slice of 64 (T <= 2) or 32 (T <= 8) elements per lane, at most 64
-  // lanes per row
   const int64_t kmax = p.H > p.I ? p.H : p.I;
-  const int64_t epl = p.T <= 2 ? 64 : 32;
-  return p.T <= kDecodeMaxT && p.P <= kDecMaxPairs && kmax <= 64 * epl;
+  return p.T <= kDecodeMaxT && p.P <= kDecMaxPairs && kmax <= kDecodeMaxK;
 }
 
 e4b_status check_forward(const MoePlan &p, const void *x, const float *logits,

@@ -21,6 +21,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kDecodeMaxT = 8;
 constexpr int kDecMaxPairs = kDecodeMaxT * kMaxTopK;
+constexpr int kDecodeMaxK = 4096;  // max(H, I) on the decode path
 
 struct MoePlan {
   int64_t E, H, I, T, k, P;

@@ -58,7 +58,7 @@ typedef enum {
   E4B_ERR_DTYPE = 5,     /* unknown output dtype */
   E4B_ERR_WORKSPACE = 6, /* workspace NULL or smaller than e4b_moe_workspace_bytes() */
   E4B_ERR_ALIGN = 7,     /* a device buffer is not 16-byte aligned */
-  E4B_ERR_PATH = 8,      /* unknown path, or the decode path was asked for but does not apply (T > 8, saved != NULL, or max(H, I) above 4096 for T <= 2, 2048 for T <= 8) */
+  E4B_ERR_PATH = 8,      /* unknown path, or the decode path was asked for but does not apply (T > 8, saved != NULL, or max(H, I) above 4096) */
   E4B_ERR_HIP = 9        /* a kernel launch failed (hipGetLastError after the launch) */
 } e4b_status;
 
