@@ -11,12 +11,10 @@
 //            expert; a = silu(g) * u is written as bf16;
 //   down     one workgroup per (distinct expert, block of rows of H);
 //   combine  the shared deterministic gather-combine.
-// The projections of the (at most 8) tokens of one expert form a skinny GEMM:
-// it runs on the 16x16x32 bf16 MFMA with the tokens as the 16-row A operand
-// (rows past the expert's token count are computed and dropped), so the cost
-// per weight byte does not grow with the number of tokens. Each code byte is
-// expanded through a 256-entry LDS table into two bf16 codebook values; the
-// block absmax scales the fp32 partial of each 64-element block.
+// No MFMA: the decode projections are bandwidth-bound GEMVs on the vector
+// ALU. Each code byte is expanded through an LDS table into two bf16 codebook
+// values and contracted with bf16 inputs by v_dot2_f32_bf16 in fp32; the block
+// absmax scales each lane's partial sum.
 #include "device.h"
 #include "kernels.h"
 
@@ -25,20 +23,45 @@ namespace e4b {
 constexpr int kDecWaves = 8;  // waves of a decode workgroup: one K eighth each
 constexpr int kDecThreads = 64 * kDecWaves;
 
-// Workspace layout of the decode path (inside the permutation region).
+// Workspace layout of the decode path (inside the permutation region, plus a
+// work map after the forward buffers).
 struct DecodeWs {
   int32_t *n_distinct;  // [1]
   int32_t *dexp;        // [kDecMaxPairs] expert id of distinct expert d (ascending)
   int32_t *dseg;        // [kDecMaxPairs + 1] sorted-pair offsets of distinct expert d
   int32_t *sorted;      // [P] pair id at sorted position
   int32_t *pos;         // [P] sorted position of pair id
+  int32_t *map_count;   // [2] workgroups with work: gate_up, down
+  int32_t *map_gu;      // [min(E, P) * I / 16] work item of gate_up workgroup b
+  int32_t *map_dn;      // [min(E, P) * H / 16] work item of down workgroup b
 };
 
+// work item: distinct expert d, first tile, tile count
+__host__ __device__ constexpr int32_t dec_item(int d, int tile0, int nt) {
+  return d | (tile0 << 8) | (nt << 17);
+}
+
+// Tiles per workgroup for an expert with np tokens: about wg_target
+// workgroups if every expert had one token, fewer tiles per workgroup for
+// experts with more tokens (their bytes cost more ALU work).
+__device__ __forceinline__ int dec_tiles_per_wg(int n_dist, int n_tiles, int np, int wg_target) {
+  const int base = (n_dist * n_tiles + wg_target - 1) / wg_target;
+  const int npb = np <= 1 ? 1 : (np <= 2 ? 2 : (np <= 4 ? 4 : 8));
+  return min(n_tiles, max(1, 2 * base / (1 + npb)));
+}
+
+// One workgroup: groups the P <= 256 routed pairs by expert (stable), lists
+// the distinct experts in ascending order and writes the work maps of the
+// two GEMV launches (chunks of tiles of 16 units per distinct expert).
 __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restrict__ idx, int P,
-                                                          DecodeWs w) {
+                                                          int tiles_gu, int tiles_dn,
+                                                          int wg_target, DecodeWs w) {
   __shared__ int32_t s_e[kDecMaxPairs];
   __shared__ int32_t s_sorted[kDecMaxPairs];
   __shared__ int32_t s_first[kDecMaxPairs];
+  __shared__ int32_t s_dseg[kDecMaxPairs + 1];
+  __shared__ int32_t s_scan[2][2][kDecMaxPairs];
+  __shared__ int32_t s_n;
   const int p = threadIdx.x;
   if (p < P) s_e[p] = idx[p];
   __syncthreads();
@@ -61,205 +84,278 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restr
     for (int q = 0; q < p; ++q) d += s_first[q];
     w.dexp[d] = s_e[s_sorted[p]];
     w.dseg[d] = p;
+    s_dseg[d] = p;
   }
   if (p == 0) {
     int n = 0;
     for (int q = 0; q < P; ++q) n += s_first[q];
     w.n_distinct[0] = n;
     w.dseg[n] = P;
+    s_dseg[n] = P;
+    s_n = n;
+  }
+  __syncthreads();
+  // chunks per distinct expert, then an inclusive scan over experts
+  const int n = s_n;
+  int tpw[2] = {1, 1};
+  const int tiles[2] = {tiles_gu, tiles_dn};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int c = 0;
+    if (p < n) {
+      tpw[j] = dec_tiles_per_wg(n, tiles[j], s_dseg[p + 1] - s_dseg[p], wg_target);
+      c = (tiles[j] + tpw[j] - 1) / tpw[j];
+    }
+    s_scan[j][0][p] = c;
+  }
+  __syncthreads();
+  int src = 0;
+  for (int off = 1; off < kDecMaxPairs; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int v = s_scan[j][src][p];
+      s_scan[j][src ^ 1][p] = p >= off ? v + s_scan[j][src][p - off] : v;
+    }
+    src ^= 1;
+    __syncthreads();
+  }
+  int32_t *maps[2] = {w.map_gu, w.map_dn};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (p < n) {
+      const int end = s_scan[j][src][p];
+      const int first = p > 0 ? s_scan[j][src][p - 1] : 0;
+      for (int b = first; b < end; ++b) {
+        const int tile0 = (b - first) * tpw[j];
+        maps[j][b] = dec_item(p, tile0, min(tpw[j], tiles[j] - tile0));
+      }
+    }
+    if (p == 0) w.map_count[j] = n > 0 ? s_scan[j][src][n - 1] : 0;
   }
 }
 
-// Skinny-GEMM form of the projection of one expert's np <= 8 tokens, on the
-// 16x16x32 bf16 MFMA: the tokens' inputs are the A operand (16 rows, rows past
-// np repeat the last token and are not stored), 16 weight rows of the expert
-// are the B operand, the reduction runs over in_features.
+// Dequant-GEMV of the (at most 8) tokens of one expert against a block of its
+// weight rows, on the vector ALU (no MFMA): every packed byte is read once and
+// used for all the expert's tokens.
 //
 // A workgroup owns a chunk of consecutive tiles of 16 output units of one
-// expert: the chunk length is chosen on the device from the number of
-// distinct experts, so that about wg_target workgroups have work (the grid
-// holds one workgroup per (expert slot, tile) and the surplus exits at once); its eight waves split the K blocks in eighths, so each wave holds
-// its eighth of the token inputs in registers for all tiles. Per tile and
-// 64-element absmax block, lane (g = l / 16, m = l % 16) loads the 8 code bytes
-// [8g, 8g + 8) of weight row m, expands each byte into two bf16 codebook
-// values through an LDS table (replicated kTblCopies times so that the lanes
-// of a half-wave read distinct banks), and two MFMAs contract the block; the
-// block's absmax (weight row m is the lane's output column) scales the fp32
-// partial before it joins the accumulator. Weight bytes and absmax of the
-// next tile are in flight while a tile is contracted. Per tile
-// the eight K partials meet in a double-buffered LDS slot and are summed in a
-// fixed order (one barrier per tile). GATE_UP runs the gate and up tiles of
-// the same units in the same lanes and writes a = silu(g) * up.
+// expert, read from the work map of the prep kernel (the grid holds one
+// workgroup per (expert slot, tile); the surplus exits at once).
+// The eight waves split the K blocks in eighths. Inside a wave, 16 lanes share
+// a weight row (lane kl holds bytes [kl * BPL, kl * BPL + BPL) of the wave's
+// K part, inside one absmax block) and a pass covers 4 rows, so a load
+// instruction reads 4 runs of 16 * BPL contiguous bytes. Each lane keeps its
+// K slice of every token's input in registers for all tiles. A code byte is
+// expanded through an LDS table (replicated kTblCopies times, lanes of a
+// half-wave hit distinct banks) into two bf16 codebook values, contracted
+// with the inputs by v_dot2_f32_bf16 in fp32; the lane's partial is scaled by
+// its block absmax and the 16 lanes of a row are summed with DPP row
+// permutes. Per tile the eight K parts meet in a double-buffered LDS slot and
+// are summed in a fixed order (one barrier per tile). GATE_UP runs gate row u
+// and up row I + u in the same lanes and writes a = silu(g) * up.
 constexpr int kTblCopies = 32;
+constexpr int kDecPass = 4;  // passes of 4 rows per tile of 16 units
 
-// AM_VEC: every wave owns 0 or MAXB blocks and MAXB divides the blocks per row,
-// so a wave's absmax run is one aligned vector load.
-template <bool GATE_UP, int MAXB, bool AM_VEC>
-__global__ __launch_bounds__(kDecThreads) void decode_mfma_kernel(
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the same bits.
+__device__ __forceinline__ float row16_sum(float v) {
+  v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x141>(v);  // row_half_mirror
+  v = dpp_add<0x140>(v);  // row_mirror
+  return v;
+}
+
+template <int BPL>
+struct DecLoad;
+template <>
+struct DecLoad<4> {
+  typedef uint32_t T;
+  static __device__ __forceinline__ uint32_t word(const T &v, int i) { return v; }
+};
+template <>
+struct DecLoad<8> {
+  typedef u32x2 T;
+  static __device__ __forceinline__ uint32_t word(const T &v, int i) { return v[i]; }
+};
+template <>
+struct DecLoad<16> {
+  typedef u32x4 T;
+  static __device__ __forceinline__ uint32_t word(const T &v, int i) { return v[i]; }
+};
+
+struct DecCtx {
+  const uint8_t *wp;   // this expert's packed rows, at the lane's byte offset
+  const float *wa;     // this expert's absmax, at the lane's block
+  int row_bytes, nblk, I, tile0, nt, s0, np, kl, rq, wave, tid;
+  bool kvalid;
+};
+
+template <bool GATE_UP, int NP, int BPL>
+__device__ __forceinline__ void decode_tiles(const DecCtx &c, const uint32_t *tl,
+                                             const uint16_t *__restrict__ xin, int64_t (&xrow)[NP],
+                                             int K_in, float (*s_red)[GATE_UP ? 2 : 1][kDecWaves][16][8],
+                                             uint16_t *__restrict__ out, int ldo, int xoff) {
+  constexpr int NR = GATE_UP ? 2 : 1;
+  constexpr int WPL = BPL / 4;  // packed words per lane
+  typedef typename DecLoad<BPL>::T LT;
+  // the tokens' inputs: 2 * BPL elements each, zero past the wave's K part
+  uint32_t xr[NP][BPL];
+#pragma unroll
+  for (int q = 0; q < NP; ++q) {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(xin + xrow[q] * K_in + xoff);
+#pragma unroll
+    for (int i = 0; i < BPL / 4; ++i) {
+      const u32x4 v = src[i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xr[q][4 * i + j] = c.kvalid ? v[j] : 0u;
+    }
+  }
+  LT wv[kDecPass][NR];
+  float am[kDecPass][NR];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int ps = 0; ps < kDecPass; ++ps) {
+      const int u = (c.tile0 + t) * 16 + 4 * ps + c.rq;
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const int64_t row = u + r * c.I;
+        wv[ps][r] = *reinterpret_cast<const LT *>(c.wp + row * c.row_bytes);
+        am[ps][r] = c.wa[row * c.nblk];
+      }
+    }
+  };
+  load_tile(0);
+  __syncthreads();  // lookup table ready
+  for (int t = 0; t < c.nt; ++t) {
+    const int slot = t & 1;
+    // the next tile's loads are issued once this tile's bytes are expanded;
+    // past the last tile the last one is reloaded (uniform wait counts)
+    const int tn = min(t + 1, c.nt - 1);
+#pragma unroll
+    for (int ps = 0; ps < kDecPass; ++ps) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        uint32_t codes[BPL];
+#pragma unroll
+        for (int i = 0; i < WPL; ++i) {
+          const uint32_t word = DecLoad<BPL>::word(wv[ps][r], i);
+#pragma unroll
+          for (int y = 0; y < 4; ++y) codes[4 * i + y] = tl[((word >> (8 * y)) & 255u) * kTblCopies];
+        }
+        const float a = am[ps][r];
+        {
+          const int u = (c.tile0 + tn) * 16 + 4 * ps + c.rq;
+          const int64_t row = u + r * c.I;
+          wv[ps][r] = *reinterpret_cast<const LT *>(c.wp + row * c.row_bytes);
+          am[ps][r] = c.wa[row * c.nblk];
+        }
+        float acc[NP];
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+          float sacc = 0.0f;
+#pragma unroll
+          for (int i = 0; i < BPL; ++i) sacc = dot2_bf16(codes[i], xr[q][i], sacc);
+          acc[q] = row16_sum(sacc * a);
+        }
+        float v = acc[0];
+#pragma unroll
+        for (int q = 1; q < NP; ++q) v = c.kl == q ? acc[q] : v;
+        if (c.kl < NP) s_red[slot][r][c.wave][4 * ps + c.rq][c.kl] = v;
+      }
+    }
+    __syncthreads();
+    // sum the K parts of tile t: thread (token qq, unit mm)
+    if (c.tid < 16 * c.np) {
+      const int qq = c.tid >> 4, mm = c.tid & 15;
+      float v[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float sum = s_red[slot][r][0][mm][qq];
+#pragma unroll
+        for (int k = 1; k < kDecWaves; ++k) sum += s_red[slot][r][k][mm][qq];
+        v[r] = sum;
+      }
+      const float val = GATE_UP ? v[0] / (1.0f + __expf(-v[0])) * v[NR - 1] : v[0];
+      out[int64_t(c.s0 + qq) * ldo + (c.tile0 + t) * 16 + mm] = f32_to_bf16(val);
+    }
+  }
+}
+
+template <bool GATE_UP, int BPL>
+__global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(
     const uint8_t *__restrict__ Wp, const float *__restrict__ Wa, int64_t w_e_bytes,
     int64_t w_e_blocks, int K_in, int n_units, int I, const uint16_t *__restrict__ vin,
-    int k_route, DecodeWs w, int cb, uint16_t *__restrict__ out, int ldo, int wg_target) {
+    int k_route, DecodeWs w, int cb, uint16_t *__restrict__ out, int ldo) {
   constexpr int NR = GATE_UP ? 2 : 1;
   __shared__ uint32_t tbl[256 * kTblCopies];
-  __shared__ f32x4 s_red[2][NR][kDecWaves][64];
-  const int n_tiles = n_units >> 4;
-  const int n_dist = w.n_distinct[0];
-  const int tiles_per_wg = min(n_tiles, max(1, (n_dist * n_tiles + wg_target - 1) / wg_target));
-  const int chunks = (n_tiles + tiles_per_wg - 1) / tiles_per_wg;
-  const int d = blockIdx.x / chunks;
-  if (d >= n_dist) return;
+  __shared__ float s_red[2][NR][kDecWaves][16][8];
+  const int count = w.map_count[GATE_UP ? 0 : 1];
+  const int item = (GATE_UP ? w.map_gu : w.map_dn)[blockIdx.x];
+  if (int(blockIdx.x) >= count) return;
+  const int d = item & 255;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, m = lane & 15;
   // entry (byte, copy) at byte * kTblCopies + copy: high nibble's code in the
-  // low half, low nibble's code in the high half (element order in memory)
-  // (thread tid fills entries tid + 512 k: low nibble tid / 32, high nibble k)
+  // low half, low nibble's code in the high half (element order in memory);
+  // thread tid fills entries tid + 512 k (low nibble tid / 32, high nibble k)
   static_assert(kDecThreads == 16 * kTblCopies, "table fill layout");
   {
     const float lo = codebook_value(cb, tid / kTblCopies);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) tbl[tid + kDecThreads * k] = pack_bf16x2(codebook_value(cb, k), lo);
+    for (int k = 0; k < 16; ++k)
+      tbl[tid + kDecThreads * k] = pack_bf16x2(codebook_value(cb, k), lo);
   }
   const uint32_t *tl = tbl + (lane & (kTblCopies - 1));
 
+  DecCtx c;
+  c.tid = tid;
+  c.wave = wave;
+  c.kl = lane & 15;
+  c.rq = lane >> 4;
   const int e = w.dexp[d];
-  const int s0 = w.dseg[d];
-  const int np = w.dseg[d + 1] - s0;
-  const int nblk = K_in >> 6;
-  const int tile0 = (blockIdx.x - d * chunks) * tiles_per_wg;
-  const int nt = min(tiles_per_wg, n_tiles - tile0);
-  const uint8_t *wp = Wp + int64_t(e) * w_e_bytes;
-  const float *wa = Wa + int64_t(e) * w_e_blocks;
-
-  // this wave's K blocks [b0, b0 + nb); loads of blocks past nb read a valid
-  // block of the row instead (their products are never formed), so every load
-  // is unconditional and the wait counts stay exact
-  const int bpw = (nblk + kDecWaves - 1) / kDecWaves;
+  c.s0 = w.dseg[d];
+  c.np = w.dseg[d + 1] - c.s0;
+  c.nblk = K_in >> 6;
+  c.I = I;
+  c.tile0 = (item >> 8) & 511;
+  c.nt = item >> 17;
+  c.row_bytes = K_in >> 1;
+  // this wave's K blocks [b0, b0 + nb); lanes past them (kvalid false) read
+  // the row's first bytes and carry zero inputs
+  const int bpw = (c.nblk + kDecWaves - 1) / kDecWaves;
   const int b0 = wave * bpw;
-  const int nb = max(0, min(bpw, nblk - b0));
-  const int row_bytes = K_in >> 1;
-  int bcl[MAXB];
-#pragma unroll
-  for (int b = 0; b < MAXB; ++b) bcl[b] = min(b0 + b, nblk - 1);
+  const int nb = max(0, min(bpw, c.nblk - b0));
+  c.kvalid = c.kl * BPL < nb * 32;
+  const int kbyte = c.kvalid ? b0 * 32 + c.kl * BPL : 0;
+  c.wp = Wp + int64_t(e) * w_e_bytes + kbyte;
+  c.wa = Wa + int64_t(e) * w_e_blocks + (kbyte >> 5);
+  const int xoff = 2 * kbyte;  // element offset of the lane's input slice
 
-  // the tokens' inputs for this wave's blocks (registers, all tiles)
-  const int q = min(m, np - 1);
-  const int64_t xrow = GATE_UP ? int64_t(w.sorted[s0 + q] / k_route) : int64_t(s0 + q);
-  const uint16_t *xp = vin + xrow * K_in + 16 * g;
-  u32x4 xr[MAXB][2];
-#pragma unroll
-  for (int b = 0; b < MAXB; ++b) {
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(xp + bcl[b] * 64);
-    xr[b][0] = src[0];
-    xr[b][1] = src[1];
+#define E4B_DEC_NP(N)                                                                        \
+  {                                                                                          \
+    int64_t xrow[N];                                                                         \
+    for (int q = 0; q < N; ++q) {                                                            \
+      const int qc = min(q, c.np - 1);                                                       \
+      xrow[q] = GATE_UP ? int64_t(w.sorted[c.s0 + qc] / k_route) : int64_t(c.s0 + qc);       \
+    }                                                                                        \
+    decode_tiles<GATE_UP, N, BPL>(c, tl, vin, xrow, K_in, s_red, out, ldo, xoff);            \
   }
-
-  struct Stage {
-    u32x2 wv[NR][MAXB];
-    float am[NR][MAXB];
-  };
-  auto load_tile = [&](int t, Stage &st) {
-    const int u = (tile0 + t) * 16 + m;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int64_t row = u + r * I;
-      const uint8_t *src = wp + row * row_bytes + 8 * g;
-      const float *ap = wa + row * nblk;
-#pragma unroll
-      for (int b = 0; b < MAXB; ++b)
-        st.wv[r][b] = *reinterpret_cast<const u32x2 *>(src + bcl[b] * 32);
-      if constexpr (AM_VEC) {
-        const float *av = ap + min(b0, nblk - MAXB);
-        if constexpr (MAXB == 2) {
-          const f32x2 v = *reinterpret_cast<const f32x2 *>(av);
-          st.am[r][0] = v[0];
-          st.am[r][1] = v[1];
-        } else {
-#pragma unroll
-          for (int c = 0; c < MAXB / 4; ++c) {
-            const f32x4 v = reinterpret_cast<const f32x4 *>(av)[c];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st.am[r][4 * c + i] = v[i];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int b = 0; b < MAXB; ++b) st.am[r][b] = ap[bcl[b]];
-      }
-    }
-  };
-  Stage st0, st1;
-  load_tile(0, st0);
-  if (nt == 1) {
-    __syncthreads();
-  } else {
-    load_tile(1, st1);
-    __syncthreads();
-  }
-
-  auto contract = [&](const Stage &st, int slot) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int b = 0; b < MAXB; ++b) {
-        if (b < nb) {
-          u32x4 c0, c1;
-#pragma unroll
-          for (int y = 0; y < 4; ++y) {
-            c0[y] = tl[((st.wv[r][b][0] >> (8 * y)) & 255u) * kTblCopies];
-            c1[y] = tl[((st.wv[r][b][1] >> (8 * y)) & 255u) * kTblCopies];
-          }
-          f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, xr[b][0]), __builtin_bit_cast(bf16x8, c0),
-              f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xr[b][1]),
-                                                         __builtin_bit_cast(bf16x8, c1), part,
-                                                         0, 0, 0);
-          const float am = st.am[r][b];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j] += part[j] * am;
-        }
-      }
-      s_red[slot][r][wave][lane] = acc;
-    }
-  };
-  // sum the K parts of tile t: thread (token row qq, unit mm)
-  auto reduce_store = [&](int t, int slot) {
-    if (tid < 16 * np) {
-      const int qq = tid >> 4, mm = tid & 15;
-      const int src_lane = 16 * (qq >> 2) + mm, comp = qq & 3;
-      float v[NR];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        float sum = s_red[slot][r][0][src_lane][comp];
-#pragma unroll
-        for (int k = 1; k < kDecWaves; ++k) sum += s_red[slot][r][k][src_lane][comp];
-        v[r] = sum;
-      }
-      const float val = GATE_UP ? v[0] / (1.0f + __expf(-v[0])) * v[NR - 1] : v[0];
-      out[int64_t(s0 + qq) * ldo + (tile0 + t) * 16 + mm] = f32_to_bf16(val);
-    }
-  };
-  if (nt == 1) {
-    contract(st0, 0);
-    __syncthreads();
-    reduce_store(0, 0);
-    return;
-  }
-  // two tiles in flight; prefetch ids past the last tile are clamped to it
-  // (a redundant load keeps the wait counts of every iteration identical)
-  for (int t = 0; t < nt; t += 2) {
-    contract(st0, 0);
-    load_tile(min(t + 2, nt - 1), st0);
-    __syncthreads();
-    reduce_store(t, 0);
-    if (t + 1 < nt) contract(st1, 1);
-    load_tile(min(t + 3, nt - 1), st1);
-    __syncthreads();
-    if (t + 1 < nt) reduce_store(t + 1, 1);
-  }
+  if (c.np <= 1) E4B_DEC_NP(1)
+  else if (c.np <= 2) E4B_DEC_NP(2)
+  else if (c.np <= 4) E4B_DEC_NP(4)
+  else E4B_DEC_NP(8)
+#undef E4B_DEC_NP
 }
-
 
 hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
                                  const int32_t *idx, const float *wts, uint16_t *y, char *ws,
@@ -275,13 +371,17 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
   uint16_t *a_buf = reinterpret_cast<uint16_t *>(ws + p.off_a);
   uint16_t *o_buf = reinterpret_cast<uint16_t *>(ws + p.off_o);
   const int P = int(p.P);
-  hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(256), 0, s, idx, P, w);
+  w.map_count = reinterpret_cast<int32_t *>(ws + p.off_dmap);
+  w.map_gu = w.map_count + 4;
+  w.map_dn = w.map_gu + (p.P < p.E ? p.P : p.E) * (p.I / 16);
+  // two workgroups of the decode kernel fit one CU; aim at one wave of them
+  const int wg_target = 512;
+  hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(256), 0, s, idx, P, int(p.I / 16),
+                     int(p.H / 16), wg_target, w);
 
   const int ymax = int(p.P < p.E ? p.P : p.E);
   const int H = int(p.H), I = int(p.I);
   const e4b_stack &gu = L->gate_up, &dn = L->down;
-  // two workgroups of the decode kernel fit one CU (LDS); aim at one wave of them
-  const int wg_target = 512;
   auto launch = [&](bool gate_up, int K_in, int n_units, const e4b_stack &st,
                     const uint16_t *vin, uint16_t *dst, int ldo, int kernel_id) {
     const int nblk = K_in / kBlock;
@@ -290,27 +390,20 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
     const dim3 grid(uint32_t(tiles * ymax));
     const int64_t eb = st.out * st.in / 2, ea = st.out * st.in / kBlock;
     timer_before(kernel_id, s);
-#define E4B_DEC_LAUNCH(GU, MB, AV)                                                            \
-  hipLaunchKernelGGL((decode_mfma_kernel<GU, MB, AV>), grid, dim3(kDecThreads), 0, s,          \
-                     st.packed, st.absmax, eb, ea, K_in, n_units, I, vin, int(p.k), w,         \
-                     p.codebook, dst, ldo, wg_target)
-#define E4B_DEC_LAUNCH_MB(GU)                                                                 \
-  do {                                                                                        \
-    const int mb = bpw <= 2 ? 2 : (bpw <= 4 ? 4 : 8);                                         \
-    const bool av = bpw == mb && nblk % mb == 0;                                              \
-    if (mb == 2) {                                                                            \
-      if (av) E4B_DEC_LAUNCH(GU, 2, true); else E4B_DEC_LAUNCH(GU, 2, false);                 \
-    } else if (mb == 4) {                                                                     \
-      if (av) E4B_DEC_LAUNCH(GU, 4, true); else E4B_DEC_LAUNCH(GU, 4, false);                 \
-    } else {                                                                                  \
-      if (av) E4B_DEC_LAUNCH(GU, 8, true); else E4B_DEC_LAUNCH(GU, 8, false);                 \
-    }                                                                                         \
-  } while (0)
-    if (gate_up)
-      E4B_DEC_LAUNCH_MB(true);
-    else
-      E4B_DEC_LAUNCH_MB(false);
-#undef E4B_DEC_LAUNCH_MB
+#define E4B_DEC_LAUNCH(GU, B)                                                                 \
+  hipLaunchKernelGGL((decode_gemv_kernel<GU, B>), grid, dim3(kDecThreads), 0, s, st.packed,     \
+                     st.absmax, eb, ea, K_in, n_units, I, vin, int(p.k), w, p.codebook, dst,    \
+                     ldo)
+    // bytes per lane: 16 lanes cover the wave's bpw blocks (32 bytes each)
+    if (gate_up) {
+      if (bpw <= 2) E4B_DEC_LAUNCH(true, 4);
+      else if (bpw <= 4) E4B_DEC_LAUNCH(true, 8);
+      else E4B_DEC_LAUNCH(true, 16);
+    } else {
+      if (bpw <= 2) E4B_DEC_LAUNCH(false, 4);
+      else if (bpw <= 4) E4B_DEC_LAUNCH(false, 8);
+      else E4B_DEC_LAUNCH(false, 16);
+    }
 #undef E4B_DEC_LAUNCH
     timer_after(kernel_id, s);
   };
