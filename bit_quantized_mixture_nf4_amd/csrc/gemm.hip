@@ -21,11 +21,13 @@
 //   EPI_DSWIGLU : dgrad of act(gate) * up scaled by the routing weight, plus
 //                 this tile's share of d y / d routing weight.
 //
-// Tile: kBM x kBN x kBK = 256 x 256 x 64 (one quantization block per K-step),
-// 512 threads = 8 waves in 4 x 2, each wave 64 x 128 = 2 x 4 MFMA 32x32x16
-// tiles. A and the dequantized B are staged in double-buffered LDS; B is
-// dequantized once per workgroup (codebook in LDS, fp32 multiply by the block
-// absmax, round-to-nearest-even bf16), i.e. exactly the bf16 view that
+// Tile: kBM x kBN x kBK = 256 x 128 x 64 (one quantization block per K-step),
+// 256 threads = 4 waves stacked along M, each wave 64 x 128 = 2 x 4 MFMA
+// 32x32x16 tiles. A and the dequantized B are staged in one LDS stage; two
+// workgroups share a CU (registers: 2 waves per SIMD), so one contracts while
+// the other refills its stage or runs its epilogue. B is dequantized once per
+// workgroup (codebook in LDS, fp32 multiply by the block absmax,
+// round-to-nearest-even bf16), i.e. exactly the bf16 view that
 // e4b_dequantize_nf4 returns.
 #include "device.h"
 #include "kernels.h"
@@ -38,7 +40,11 @@ enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_DSWIGLU = 2 };
 
 
 
-constexpr int kThreads = 512;  // 8 waves: 2 per SIMD
+constexpr int kThreads = 256 * kGemmWavesN;  // 4 x kGemmWavesN waves
+// one LDS stage when two workgroups share a CU (they hide each other's
+// staging and epilogues), two when one workgroup owns the CU
+constexpr int kStages = kGemmWavesN == 1 ? 1 : 2;
+constexpr int kAPass = kBM * 8 / kThreads;  // A rows per thread per K-step
 constexpr int kLds = kBK + 8;  // padded row (bf16 elements): 144 bytes, conflict-free b128 access
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
@@ -48,15 +54,15 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __ex
 // rows end early frees whole SIMDs. Each wave owns 64 x 128 outputs
 // (2 x 4 MFMA 32x32x16 tiles, 128 fp32 accumulators per lane).
 template <int AMODE, int BMODE, int EPI>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kLds];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kLds];
+__global__ __launch_bounds__(kThreads, kStages == 1 ? 2 : 1) void grouped_gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kStages][kBM * kLds];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kStages][kBN * kLds];
   __shared__ float sCode[16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kGemmWavesN, wn = wave % kGemmWavesN;
 
   // ---- tile -> (expert, m-tile, n-tile) ----
   const uint32_t L = xcd_remap(blockIdx.x, g.grid);
@@ -75,13 +81,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 
   if (tid < 16) sCode[tid] = codebook_value(g.cb, tid);
 
-  // ---- A rows: column chunk (tid & 7) of rows (tid >> 3) + 64 i. Rows past
-  // the segment read the last valid row: their outputs are never stored. ----
+  // ---- A rows: column chunk (tid & 7) of rows (tid >> 3) + (kThreads / 8) i.
+  // Rows past the segment read the last valid row: their outputs are never
+  // stored. ----
   const int a_cc = tid & 7;
-  uint32_t a_off[4];
+  uint32_t a_off[kAPass];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = min((tid >> 3) + 64 * i, valid_rows - 1);
+  for (int i = 0; i < kAPass; ++i) {
+    const int r = min((tid >> 3) + (kThreads / 8) * i, valid_rows - 1);
     const int srow = seg + row0 + r;
     const int src = AMODE == A_GATHER ? g.sorted_pair[srow] / g.topk : srow;
     a_off[i] = uint32_t(src) * uint32_t(g.lda) + uint32_t(a_cc * 8);
@@ -107,14 +114,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   }
   const uint8_t *b_src_nt = wp + int64_t(b_row) * row_bytes + b_half * 16;
   const float *b_am_nt = wa + int64_t(b_row) * row_blocks;
-  // B_NN: thread owns a 4 (k) x 8 (n) patch: n group cg (32), k group kg (16)
+  // B_NN: thread owns a 4 (k) x 8 (n) patch: n group cg, k group kg (16)
   const int b_cg = tid >> 4, b_kg = tid & 15;
   int b_n = nt * kBN + b_cg * 8;
   b_n = b_n < g.N ? b_n : 0;
   const uint8_t *b_src_nn = wp + int64_t(b_kg * 4) * row_bytes + (b_n >> 1);
   const float *b_am_nn = wa + int64_t(b_kg * 4) * row_blocks + (b_n >> 6);
 
-  u32x4 ra[4];
+  u32x4 ra[kAPass];
   u32x4 rb;
   float ram;
   uint32_t rbn[4];
@@ -122,7 +129,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
 
   auto load = [&](int ks) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kAPass; ++i)
       ra[i] = *reinterpret_cast<const u32x4 *>(g.A + a_off[i] + uint32_t(ks * kBK));
     if (BMODE == B_NT) {
       rb = *reinterpret_cast<const u32x4 *>(b_src_nt + ks * (kBK / 2));
@@ -140,19 +147,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
   auto store = [&](int buf) {
     uint16_t *a_dst = sA[buf];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4 *>(a_dst + ((tid >> 3) + 64 * i) * kLds + a_cc * 8) = ra[i];
+    for (int i = 0; i < kAPass; ++i)
+      *reinterpret_cast<u32x4 *>(a_dst + ((tid >> 3) + (kThreads / 8) * i) * kLds + a_cc * 8) =
+          ra[i];
     uint16_t *b_dst = sB[buf];
     if (BMODE == B_NT) {
+      // all 32 codebook reads are issued before the first product
+      float c[32];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t w = rb[d];
-        float v[8];
+      for (int d = 0; d < 4; ++d)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          v[2 * b] = __fmul_rn(sCode[(w >> (8 * b + 4)) & 15u], ram);
-          v[2 * b + 1] = __fmul_rn(sCode[(w >> (8 * b)) & 15u], ram);
+          c[8 * d + 2 * b] = sCode[(rb[d] >> (8 * b + 4)) & 15u];
+          c[8 * d + 2 * b + 1] = sCode[(rb[d] >> (8 * b)) & 15u];
         }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = __fmul_rn(c[8 * d + e], ram);
         *reinterpret_cast<u32x4 *>(b_dst + b_c * kLds + b_half * 32 + d * 8) =
             u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                   pack_bf16x2(v[6], v[7])};
@@ -221,19 +234,33 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       __builtin_amdgcn_s_setprio(0);
     }
   };
-  const bool store_first = wave >= 4;
-  for (int ks = 0; ks < nK; ++ks) {
-    const int cur = ks & 1;
-    if (store_first) {
-      if (ks + 1 < nK) store(cur ^ 1);
-      if (ks + 2 < nK) load(ks + 2);
-      compute(cur);
-    } else {
-      compute(cur);
-      if (ks + 1 < nK) store(cur ^ 1);
-      if (ks + 2 < nK) load(ks + 2);
+  if constexpr (kStages == 1) {
+    // one stage: contract it, then refill it from the registers loaded one
+    // K-step earlier and start the loads of the step after
+    for (int ks = 0; ks < nK; ++ks) {
+      compute(0);
+      __syncthreads();
+      if (ks + 1 < nK) {
+        store(0);
+        if (ks + 2 < nK) load(ks + 2);
+      }
+      __syncthreads();
     }
-    __syncthreads();
+  } else {
+    const bool store_first = wave >= 4;
+    for (int ks = 0; ks < nK; ++ks) {
+      const int cur = ks & 1;
+      if (store_first) {
+        if (ks + 1 < nK) store(cur ^ 1);
+        if (ks + 2 < nK) load(ks + 2);
+        compute(cur);
+      } else {
+        compute(cur);
+        if (ks + 1 < nK) store(cur ^ 1);
+        if (ks + 2 < nK) load(ks + 2);
+      }
+      __syncthreads();
+    }
   }
 
   // ---- epilogue ----
@@ -293,52 +320,75 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmArgs g) {
       }
     }
   } else {  // EPI_DSWIGLU
-    float *red = reinterpret_cast<float *>(sA[0]);  // [2][kBM] partial row sums
+    float *red = reinterpret_cast<float *>(sA[0]);  // [kGemmWavesN][kBM] partial row sums
+    // The saved g|u of the lane's 2 x 4 x 4 column runs are fetched in eight
+    // batches (row half i, column group j), one batch ahead of its use, with
+    // rows and columns clamped into range (out-of-range results are not
+    // stored), so the loads of a batch overlap the arithmetic of the previous.
+    int64_t grow[2];
+    float wr[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) grow[i] = seg + row0 + min(lrow + i * 32, valid_rows - 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wr[i] = g.topk_w[g.sorted_pair[grow[i]]];
+    u32x2 gg[2][4], uu[2][4];
+    auto fetch = [&](int b, int slot) {
+      const int i = b >> 2, j = b & 3;
+      const uint16_t *gurow = g.GU + grow[i] * (2 * g.I);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = min(nt * kBN + lcol + j * 32 + 8 * q, g.N - 4);
+        gg[slot][q] = *reinterpret_cast<const u32x2 *>(gurow + n);
+        uu[slot][q] = *reinterpret_cast<const u32x2 *>(gurow + g.I + n);
+      }
+    };
+    float part[2] = {0.0f, 0.0f};
+    fetch(0, 0);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      if (b + 1 < 8) fetch(b + 1, (b + 1) & 1);
+      const int i = b >> 2, j = b & 3, slot = b & 1;
+      const bool row_ok = lrow + i * 32 < valid_rows;
+      uint16_t *crow = g.C + grow[i] * g.ldc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nt * kBN + lcol + j * 32 + 8 * q;
+        const u32x2 gq = gg[slot][q], uq = uu[slot][q];
+        const float gv[4] = {bf16_lo(gq[0]), bf16_hi(gq[0]), bf16_lo(gq[1]), bf16_hi(gq[1])};
+        const float uv[4] = {bf16_lo(uq[0]), bf16_hi(uq[0]), bf16_lo(uq[1]), bf16_hi(uq[1])};
+        float dg[4], du[4], pq = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float s = sigmoidf_(gv[t]);
+          const float silu = gv[t] * s;
+          const float G2 = acc[i][j][4 * q + t];
+          pq += G2 * (silu * uv[t]);
+          const float ga = wr[i] * G2;
+          dg[t] = ga * uv[t] * s * (1.0f + gv[t] * (1.0f - s));
+          du[t] = ga * silu;
+        }
+        if (row_ok && n < g.N) {
+          part[i] += pq;
+          *reinterpret_cast<u32x2 *>(crow + n) =
+              u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+          *reinterpret_cast<u32x2 *>(crow + g.I + n) =
+              u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int row = lrow + i * 32;
-      float part = 0.0f;
-      if (row < valid_rows) {
-        const int64_t grow = seg + row0 + row;
-        const float wr = g.topk_w[g.sorted_pair[grow]];
-        const uint16_t *gurow = g.GU + grow * (2 * g.I);
-        uint16_t *crow = g.C + grow * g.ldc;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int n = nt * kBN + lcol + j * 32 + 8 * q;
-            if (n < g.N) {
-              const u32x2 gg = *reinterpret_cast<const u32x2 *>(gurow + n);
-              const u32x2 uu = *reinterpret_cast<const u32x2 *>(gurow + g.I + n);
-              const float gv[4] = {bf16_lo(gg[0]), bf16_hi(gg[0]), bf16_lo(gg[1]), bf16_hi(gg[1])};
-              const float uv[4] = {bf16_lo(uu[0]), bf16_hi(uu[0]), bf16_lo(uu[1]), bf16_hi(uu[1])};
-              float dg[4], du[4];
-#pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                const float s = sigmoidf_(gv[t]);
-                const float silu = gv[t] * s;
-                const float G2 = acc[i][j][4 * q + t];
-                part += G2 * (silu * uv[t]);
-                const float ga = wr * G2;
-                dg[t] = ga * uv[t] * s * (1.0f + gv[t] * (1.0f - s));
-                du[t] = ga * silu;
-              }
-              *reinterpret_cast<u32x2 *>(crow + n) =
-                  u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-              *reinterpret_cast<u32x2 *>(crow + g.I + n) =
-                  u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
-            }
-          }
-      }
       // the two half-waves hold the two column halves of the same rows
-      part += __shfl_xor(part, 32);
-      if (lane < 32) red[wn * kBM + row] = part;
+      const float pr = part[i] + __shfl_xor(part[i], 32);
+      if (lane < 32) red[wn * kBM + lrow + i * 32] = pr;
     }
     __syncthreads();
-    if (tid < valid_rows) {
-      const int64_t grow = seg + row0 + tid;
-      g.partial[grow * g.n_tiles + nt] = red[tid] + red[kBM + tid];
+    for (int r = tid; r < valid_rows; r += kThreads) {
+      const int64_t grow = seg + row0 + r;
+      float sum = red[r];
+#pragma unroll
+      for (int c = 1; c < kGemmWavesN; ++c) sum += red[c * kBM + r];
+      g.partial[grow * g.n_tiles + nt] = sum;
     }
   }
 }

@@ -12,8 +12,9 @@
 namespace e4b {
 
 // Tile shape shared by every grouped GEMM of the forward and dgrad.
+constexpr int kGemmWavesN = 1;  // waves of a GEMM workgroup along N (4 along M)
 constexpr int kBM = 256;   // rows (routed pairs) per tile
-constexpr int kBN = 256;   // output columns per tile
+constexpr int kBN = 128 * kGemmWavesN;  // output columns per tile
 constexpr int kBK = 64;    // reduction step = one quantization block
 constexpr int kBlock = 64; // quantization block (elements along `in`)
 constexpr int kPermChunk = 1024;  // pairs per histogram / scatter chunk
