@@ -50,87 +50,97 @@ __device__ __forceinline__ int dec_tiles_per_wg(int n_dist, int n_tiles, int np,
   return min(n_tiles, max(1, 2 * base / (1 + npb)));
 }
 
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
 // One workgroup: groups the P <= 256 routed pairs by expert (stable), lists
 // the distinct experts in ascending order and writes the work maps of the
 // two GEMV launches (chunks of tiles of 16 units per distinct expert).
+// Ranks come from comparisons of unique (expert, pair) keys, segment starts
+// and the chunk offsets from wave ballots and scans.
 __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restrict__ idx, int P,
                                                           int tiles_gu, int tiles_dn,
                                                           int wg_target, DecodeWs w) {
-  __shared__ int32_t s_e[kDecMaxPairs];
-  __shared__ int32_t s_sorted[kDecMaxPairs];
-  __shared__ int32_t s_first[kDecMaxPairs];
+  static_assert(kDecMaxPairs == 256, "one thread per routed pair");
+  __shared__ __attribute__((aligned(16))) int32_t s_key[kDecMaxPairs];
+  __shared__ int32_t s_sorted_e[kDecMaxPairs];
   __shared__ int32_t s_dseg[kDecMaxPairs + 1];
-  __shared__ int32_t s_scan[2][2][kDecMaxPairs];
-  __shared__ int32_t s_n;
-  const int p = threadIdx.x;
-  if (p < P) s_e[p] = idx[p];
+  __shared__ int32_t s_wsum[3][4];
+  const int p = threadIdx.x, lane = p & 63, wv = p >> 6;
+  // unique sort key: expert, then pair id (stable)
+  const int key = p < P ? idx[p] * kDecMaxPairs + p : 0x7FFFFFFF;
+  s_key[p] = key;
   __syncthreads();
   int pos = 0;
+  const int4 *k4 = reinterpret_cast<const int4 *>(s_key);
+#pragma unroll 4
+  for (int q = 0; q < (P + 3) / 4; ++q) {
+    const int4 v = k4[q];
+    pos += (v.x < key) + (v.y < key) + (v.z < key) + (v.w < key);
+  }
   if (p < P) {
-    const int e = s_e[p];
-    for (int q = 0; q < P; ++q) {
-      const int eq = s_e[q];
-      pos += (eq < e || (eq == e && q < p)) ? 1 : 0;
-    }
-    s_sorted[pos] = p;
+    s_sorted_e[pos] = key / kDecMaxPairs;
     w.sorted[pos] = p;
     w.pos[p] = pos;
   }
   __syncthreads();
-  if (p < P) s_first[p] = (p == 0 || s_e[s_sorted[p - 1]] != s_e[s_sorted[p]]) ? 1 : 0;
+  // distinct experts: position p starts a segment
+  const bool first = p < P && (p == 0 || s_sorted_e[p - 1] != s_sorted_e[p]);
+  const uint64_t fm = __ballot(first);
+  int d = __popcll(fm & ((1ull << lane) - 1));
+  if (lane == 0) s_wsum[0][wv] = __popcll(fm);
   __syncthreads();
-  if (p < P && s_first[p]) {
-    int d = 0;
-    for (int q = 0; q < p; ++q) d += s_first[q];
-    w.dexp[d] = s_e[s_sorted[p]];
+  for (int v = 0; v < wv; ++v) d += s_wsum[0][v];
+  const int n = s_wsum[0][0] + s_wsum[0][1] + s_wsum[0][2] + s_wsum[0][3];
+  if (first) {
+    w.dexp[d] = s_sorted_e[p];
     w.dseg[d] = p;
     s_dseg[d] = p;
   }
   if (p == 0) {
-    int n = 0;
-    for (int q = 0; q < P; ++q) n += s_first[q];
     w.n_distinct[0] = n;
     w.dseg[n] = P;
     s_dseg[n] = P;
-    s_n = n;
   }
   __syncthreads();
-  // chunks per distinct expert, then an inclusive scan over experts
-  const int n = s_n;
-  int tpw[2] = {1, 1};
+  // chunks of tiles per distinct expert (thread = distinct expert), then an
+  // inclusive scan over the experts; each expert writes its work items
   const int tiles[2] = {tiles_gu, tiles_dn};
+  int tpw[2], incl[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
+    tpw[j] = 1;
     int c = 0;
     if (p < n) {
       tpw[j] = dec_tiles_per_wg(n, tiles[j], s_dseg[p + 1] - s_dseg[p], wg_target);
       c = (tiles[j] + tpw[j] - 1) / tpw[j];
     }
-    s_scan[j][0][p] = c;
+    incl[j] = wave_inclusive_scan(c, lane);
+    if (lane == 63) s_wsum[1 + j][wv] = incl[j];
   }
   __syncthreads();
-  int src = 0;
-  for (int off = 1; off < kDecMaxPairs; off <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int v = s_scan[j][src][p];
-      s_scan[j][src ^ 1][p] = p >= off ? v + s_scan[j][src][p - off] : v;
-    }
-    src ^= 1;
-    __syncthreads();
-  }
   int32_t *maps[2] = {w.map_gu, w.map_dn};
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
+    int base = 0;
+    for (int v = 0; v < wv; ++v) base += s_wsum[1 + j][v];
+    const int end = base + incl[j];
     if (p < n) {
-      const int end = s_scan[j][src][p];
-      const int first = p > 0 ? s_scan[j][src][p - 1] : 0;
-      for (int b = first; b < end; ++b) {
-        const int tile0 = (b - first) * tpw[j];
+      const int c = (tiles[j] + tpw[j] - 1) / tpw[j];
+      const int first_b = end - c;
+      for (int b = first_b; b < end; ++b) {
+        const int tile0 = (b - first_b) * tpw[j];
         maps[j][b] = dec_item(p, tile0, min(tpw[j], tiles[j] - tile0));
       }
     }
-    if (p == 0) w.map_count[j] = n > 0 ? s_scan[j][src][n - 1] : 0;
+    if (p == 0)
+      w.map_count[j] = s_wsum[1 + j][0] + s_wsum[1 + j][1] + s_wsum[1 + j][2] + s_wsum[1 + j][3];
   }
 }
 
