@@ -33,6 +33,7 @@ GemmArgs base_args(const MoePlan &p, const e4b_stack &st, char *ws) {
   a.I = int32_t(p.I);
   a.offsets = reinterpret_cast<const int32_t *>(ws + p.off_offsets);
   a.tile_offsets = reinterpret_cast<const int32_t *>(ws + p.off_tile_offsets);
+  a.tile_map = reinterpret_cast<const int4 *>(ws + p.off_tile_map);
   a.E = int32_t(p.E);
   a.cb = p.codebook;
   return a;

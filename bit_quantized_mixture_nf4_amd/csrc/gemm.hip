@@ -68,16 +68,10 @@ __global__ __launch_bounds__(kThreads, kStages == 1 ? 2 : 1) void grouped_gemm_k
   const uint32_t L = xcd_remap(blockIdx.x, g.grid);
   const int mt = int(L / uint32_t(g.n_tiles));
   const int nt = int(L % uint32_t(g.n_tiles));
-  if (mt >= g.tile_offsets[g.E]) return;
-  int lo = 0, hi = g.E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (g.tile_offsets[mid] <= mt) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int seg = g.offsets[e];
-  const int row0 = (mt - g.tile_offsets[e]) * kBM;
-  const int valid_rows = min(kBM, g.offsets[e + 1] - seg - row0);
+  const int n_mt = g.tile_offsets[g.E];
+  const int4 tm = g.tile_map[min(mt, int(g.grid / uint32_t(g.n_tiles)) - 1)];
+  if (mt >= n_mt) return;
+  const int e = tm.x, seg = tm.y, row0 = tm.z, valid_rows = tm.w;
 
   if (tid < 16) sCode[tid] = codebook_value(g.cb, tid);
 

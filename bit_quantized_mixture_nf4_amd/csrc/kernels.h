@@ -30,6 +30,7 @@ struct GemmArgs {
   int32_t I;           // intermediate size
   const int32_t *offsets;
   const int32_t *tile_offsets;
+  const int4 *tile_map;  // per m-tile: expert, segment start, first row, rows
   int32_t E;
   int32_t n_tiles;
   uint32_t grid;
@@ -48,7 +49,7 @@ void timer_after(int kernel, hipStream_t s);
 hipError_t launch_route(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
                         hipStream_t s);
 
-// Fills counts/offsets/tile_offsets/sorted_pair/pos_of_pair in the workspace.
+// Fills counts/offsets/tile_offsets/tile_map/sorted_pair/pos_of_pair in the workspace.
 hipError_t launch_permute(const MoePlan &p, const int32_t *idx, char *ws, hipStream_t s);
 
 // grid must equal m_tiles_bound * n_tiles.

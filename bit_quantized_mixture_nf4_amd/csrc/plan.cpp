@@ -94,6 +94,7 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   p->off_tile_offsets = take(size_t(E + 1) * 4);
   p->off_sorted = take(size_t(P) * 4);
   p->off_pos = take(size_t(P) * 4);
+  p->off_tile_map = take(size_t(p->m_tiles_bound) * 16);
   const size_t base = off;
   // forward region
   p->off_a = take(size_t(P) * I * 2);

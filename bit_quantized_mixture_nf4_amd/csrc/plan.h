@@ -36,6 +36,7 @@ struct MoePlan {
   // workspace byte offsets
   size_t off_hist, off_chunk_base, off_counts, off_offsets, off_tile_offsets;
   size_t off_sorted, off_pos;
+  size_t off_tile_map;  // int4 per m-tile: expert, segment start, first row, rows
   size_t off_a, off_o;                          // forward
   size_t off_dmap;                              // forward, decode path: work maps
   size_t off_gu, off_dgu, off_partial, off_gx;  // dgrad

@@ -123,12 +123,15 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t *__restric
 }
 
 // One wavefront per chunk. Writes sorted_pair / pos_of_pair; workgroup 0 also
-// writes offsets[E+1] and tile_offsets[E+1] (m-tiles of kBM rows per expert).
+// writes offsets[E+1], tile_offsets[E+1] (m-tiles of kBM rows per expert) and
+// the tile map (expert, segment start, first row, rows) of every m-tile, so a
+// GEMM workgroup finds its tile with one load.
 __global__ __launch_bounds__(64) void perm_scatter_kernel(
     const int32_t *__restrict__ flat_idx, int64_t P, int E, int nbits, int64_t nchunks,
     const int32_t *__restrict__ counts, const int32_t *__restrict__ chunk_base,
     int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pos_of_pair,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ tile_offsets) {
+    int32_t *__restrict__ offsets, int32_t *__restrict__ tile_offsets,
+    int4 *__restrict__ tile_map) {
   __shared__ int32_t base[kMaxE];
   const int lane = threadIdx.x;
   const int64_t c = blockIdx.x;
@@ -152,7 +155,10 @@ __global__ __launch_bounds__(64) void perm_scatter_kernel(
       base[e] = off + chunk_base[int64_t(e) * nchunks + c];
       if (c == 0) {
         offsets[e] = off;
-        tile_offsets[e] = tcarry + tincl - tv;
+        const int32_t t0 = tcarry + tincl - tv;
+        tile_offsets[e] = t0;
+        for (int t = 0; t < tv; ++t)
+          tile_map[t0 + t] = int4{e, off, t * kBM, min(kBM, v - t * kBM)};
       }
     }
     carry += __shfl(incl, 63);
@@ -206,13 +212,14 @@ hipError_t launch_permute(const MoePlan &p, const int32_t *idx, char *ws, hipStr
   int32_t *toff = reinterpret_cast<int32_t *>(ws + p.off_tile_offsets);
   int32_t *sorted = reinterpret_cast<int32_t *>(ws + p.off_sorted);
   int32_t *pos = reinterpret_cast<int32_t *>(ws + p.off_pos);
+  int4 *tmap = reinterpret_cast<int4 *>(ws + p.off_tile_map);
   const int E = int(p.E);
   hipLaunchKernelGGL(perm_hist_kernel, dim3(uint32_t(p.nchunks)), dim3(256), 0, s, idx, p.P, E,
                      p.nchunks, hist);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(uint32_t(E)), dim3(256), 0, s, hist, p.nchunks, cbase,
                      counts);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(uint32_t(p.nchunks)), dim3(64), 0, s, idx, p.P, E,
-                     p.nbits_e, p.nchunks, counts, cbase, sorted, pos, offsets, toff);
+                     p.nbits_e, p.nchunks, counts, cbase, sorted, pos, offsets, toff, tmap);
   return hipGetLastError();
 }
 
