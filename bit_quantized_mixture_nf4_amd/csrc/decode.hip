@@ -41,13 +41,18 @@ __host__ __device__ constexpr int32_t dec_item(int d, int tile0, int nt) {
   return d | (tile0 << 8) | (nt << 17);
 }
 
-// Tiles per workgroup for an expert with np tokens: about wg_target
-// workgroups if every expert had one token, fewer tiles per workgroup for
-// experts with more tokens (their bytes cost more ALU work).
-__device__ __forceinline__ int dec_tiles_per_wg(int n_dist, int n_tiles, int np, int wg_target) {
-  const int base = (n_dist * n_tiles + wg_target - 1) / wg_target;
+// Relative cost of a tile of an expert with np tokens, in eighths of the cost
+// of a one-token tile (measured: the ALU work per byte grows with the token
+// bucket; faster for gate_up, whose rows are longer).
+__device__ __forceinline__ int dec_tile_cost8(int np, bool gate_up) {
   const int npb = np <= 1 ? 1 : (np <= 2 ? 2 : (np <= 4 ? 4 : 8));
-  return min(n_tiles, max(1, 2 * base / (1 + npb)));
+  return gate_up ? 8 + 2 * (npb - 1) : 8 + 4 * (npb - 1) / 3;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
@@ -66,12 +71,13 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 // and the chunk offsets from wave ballots and scans.
 __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restrict__ idx, int P,
                                                           int tiles_gu, int tiles_dn,
-                                                          int wg_target, DecodeWs w) {
+                                                          int target_gu, int target_dn,
+                                                          DecodeWs w) {
   static_assert(kDecMaxPairs == 256, "one thread per routed pair");
   __shared__ __attribute__((aligned(16))) int32_t s_key[kDecMaxPairs];
   __shared__ int32_t s_sorted_e[kDecMaxPairs];
   __shared__ int32_t s_dseg[kDecMaxPairs + 1];
-  __shared__ int32_t s_wsum[3][4];
+  __shared__ int32_t s_wsum[5][4];
   const int p = threadIdx.x, lane = p & 63, wv = p >> 6;
   // unique sort key: expert, then pair id (stable)
   const int key = p < P ? idx[p] * kDecMaxPairs + p : 0x7FFFFFFF;
@@ -109,16 +115,33 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restr
     s_dseg[n] = P;
   }
   __syncthreads();
-  // chunks of tiles per distinct expert (thread = distinct expert), then an
-  // inclusive scan over the experts; each expert writes its work items
+  // Tiles per workgroup (thread = distinct expert): the total cost of all
+  // tiles is split into about target workgroups of equal cost (target = the
+  // workgroups the GEMV kernel keeps resident), then an inclusive scan over
+  // the experts gives each expert's work items.
   const int tiles[2] = {tiles_gu, tiles_dn};
+  const int target[2] = {target_gu, target_dn};
+  const int np_d = p < n ? s_dseg[p + 1] - s_dseg[p] : 0;
+  int c8[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    c8[j] = dec_tile_cost8(np_d, j == 0);
+    const int tot = wave_sum(p < n ? tiles[j] * c8[j] : 0);
+    if (lane == 0) s_wsum[3 + j][wv] = tot;
+  }
+  __syncthreads();
   int tpw[2], incl[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
+    const int total = s_wsum[3 + j][0] + s_wsum[3 + j][1] + s_wsum[3 + j][2] + s_wsum[3 + j][3];
     tpw[j] = 1;
     int c = 0;
     if (p < n) {
-      tpw[j] = dec_tiles_per_wg(n, tiles[j], s_dseg[p + 1] - s_dseg[p], wg_target);
+      // chunks in proportion to the expert's share of the cost, rounded down,
+      // so that the workgroups never exceed the resident set (one more would
+      // start a second round and double the kernel's span)
+      const int want = max(1, min(tiles[j], int(int64_t(tiles[j]) * c8[j] * target[j] / total)));
+      tpw[j] = (tiles[j] + want - 1) / want;
       c = (tiles[j] + tpw[j] - 1) / tpw[j];
     }
     incl[j] = wave_inclusive_scan(c, lane);
@@ -367,6 +390,34 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(
 #undef E4B_DEC_NP
 }
 
+// Workgroups of one decode GEMV variant resident on the current device at
+// once (occupancy x compute units), cached per device; 0 if the query fails.
+static int dec_resident_workgroups(bool gate_up, int bpl) {
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev][2][3];  // 0: not yet queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  const int vi = bpl == 4 ? 0 : (bpl == 8 ? 1 : 2);
+  int &slot = cache[dev][gate_up ? 1 : 0][vi];
+  if (slot > 0) return slot;
+  const void *fn = nullptr;
+  if (gate_up)
+    fn = vi == 0 ? reinterpret_cast<const void *>(&decode_gemv_kernel<true, 4>)
+         : vi == 1 ? reinterpret_cast<const void *>(&decode_gemv_kernel<true, 8>)
+                   : reinterpret_cast<const void *>(&decode_gemv_kernel<true, 16>);
+  else
+    fn = vi == 0 ? reinterpret_cast<const void *>(&decode_gemv_kernel<false, 4>)
+         : vi == 1 ? reinterpret_cast<const void *>(&decode_gemv_kernel<false, 8>)
+                   : reinterpret_cast<const void *>(&decode_gemv_kernel<false, 16>);
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kDecThreads, 0) != hipSuccess)
+    return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  slot = per_cu * cus;
+  return slot;
+}
+
 hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
                                  const int32_t *idx, const float *wts, uint16_t *y, char *ws,
                                  hipStream_t s) {
@@ -384,18 +435,25 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
   w.map_count = reinterpret_cast<int32_t *>(ws + p.off_dmap);
   w.map_gu = w.map_count + 4;
   w.map_dn = w.map_gu + (p.P < p.E ? p.P : p.E) * (p.I / 16);
-  // two workgroups of the decode kernel fit one CU; aim at one wave of them
-  const int wg_target = 512;
-  hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(256), 0, s, idx, P, int(p.I / 16),
-                     int(p.H / 16), wg_target, w);
-
   const int ymax = int(p.P < p.E ? p.P : p.E);
   const int H = int(p.H), I = int(p.I);
   const e4b_stack &gu = L->gate_up, &dn = L->down;
+  // bytes per lane: 16 lanes cover the wave's bpw blocks (32 bytes each)
+  auto bpl_of = [](int K_in) {
+    const int bpw = (K_in / kBlock + kDecWaves - 1) / kDecWaves;
+    return bpw <= 2 ? 4 : (bpw <= 4 ? 8 : 16);
+  };
+  const int bpl_gu = bpl_of(H), bpl_dn = bpl_of(I);
+  // the workgroups each GEMV kernel keeps resident on the device
+  const int target_gu = dec_resident_workgroups(true, bpl_gu);
+  const int target_dn = dec_resident_workgroups(false, bpl_dn);
+  if (target_gu <= 0 || target_dn <= 0) return hipErrorInvalidDeviceFunction;
+  hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(256), 0, s, idx, P, I / 16, H / 16,
+                     target_gu, target_dn, w);
+
   auto launch = [&](bool gate_up, int K_in, int n_units, const e4b_stack &st,
                     const uint16_t *vin, uint16_t *dst, int ldo, int kernel_id) {
-    const int nblk = K_in / kBlock;
-    const int bpw = (nblk + kDecWaves - 1) / kDecWaves;
+    const int bpl = bpl_of(K_in);
     const int tiles = n_units / 16;
     const dim3 grid(uint32_t(tiles * ymax));
     const int64_t eb = st.out * st.in / 2, ea = st.out * st.in / kBlock;
@@ -404,14 +462,13 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
   hipLaunchKernelGGL((decode_gemv_kernel<GU, B>), grid, dim3(kDecThreads), 0, s, st.packed,     \
                      st.absmax, eb, ea, K_in, n_units, I, vin, int(p.k), w, p.codebook, dst,    \
                      ldo)
-    // bytes per lane: 16 lanes cover the wave's bpw blocks (32 bytes each)
     if (gate_up) {
-      if (bpw <= 2) E4B_DEC_LAUNCH(true, 4);
-      else if (bpw <= 4) E4B_DEC_LAUNCH(true, 8);
+      if (bpl == 4) E4B_DEC_LAUNCH(true, 4);
+      else if (bpl == 8) E4B_DEC_LAUNCH(true, 8);
       else E4B_DEC_LAUNCH(true, 16);
     } else {
-      if (bpw <= 2) E4B_DEC_LAUNCH(false, 4);
-      else if (bpw <= 4) E4B_DEC_LAUNCH(false, 8);
+      if (bpl == 4) E4B_DEC_LAUNCH(false, 4);
+      else if (bpl == 8) E4B_DEC_LAUNCH(false, 8);
       else E4B_DEC_LAUNCH(false, 16);
     }
 #undef E4B_DEC_LAUNCH
