@@ -5,7 +5,7 @@
 //   route (optional) -> permute -> gate_up GEMM + SiLU*up -> down GEMM
 //   -> weighted gather-combine.
 // dgrad (bitsandbytes PR #1965, recompute-in-backward bullet):
-//   permute -> [gate_up GEMM again if nothing was saved] -> down GEMM on
+//   [permute + gate_up GEMM again if nothing was saved] -> down GEMM on
 //   W_dn^T with the SiLU-backward epilogue -> gate_up GEMM on W_gu^T
 //   -> gather-combine of grad_x and of the routing-weight gradient.
 #include "device.h"
@@ -21,9 +21,9 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
 
 namespace {
 
-GemmArgs base_args(const MoePlan &p, const e4b_stack &st, char *ws) {
+GemmArgs base_args(const MoePlan &p, const e4b_stack &st, const PermView &v) {
   GemmArgs a{};
-  a.sorted_pair = reinterpret_cast<const int32_t *>(ws + p.off_sorted);
+  a.sorted_pair = v.sorted;
   a.topk = int32_t(p.k);
   a.Wp = st.packed;
   a.Wa = st.absmax;
@@ -31,9 +31,9 @@ GemmArgs base_args(const MoePlan &p, const e4b_stack &st, char *ws) {
   a.w_e_blocks = st.out * st.in / kBlock;
   a.w_in = int32_t(st.in);
   a.I = int32_t(p.I);
-  a.offsets = reinterpret_cast<const int32_t *>(ws + p.off_offsets);
-  a.tile_offsets = reinterpret_cast<const int32_t *>(ws + p.off_tile_offsets);
-  a.tile_map = reinterpret_cast<const int4 *>(ws + p.off_tile_map);
+  a.offsets = v.offsets;
+  a.tile_offsets = v.tile_offsets;
+  a.tile_map = v.tile_map;
   a.E = int32_t(p.E);
   a.cb = p.codebook;
   return a;
@@ -42,8 +42,8 @@ GemmArgs base_args(const MoePlan &p, const e4b_stack &st, char *ws) {
 // gate_up projection of every routed pair: writes a = silu(g)*u (if a_out) and
 // the bf16 g|u (if gu_out).
 hipError_t run_gate_up(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
-                       uint16_t *a_out, uint16_t *gu_out, char *ws, hipStream_t s) {
-  GemmArgs a = base_args(p, L->gate_up, ws);
+                       uint16_t *a_out, uint16_t *gu_out, const PermView &v, hipStream_t s) {
+  GemmArgs a = base_args(p, L->gate_up, v);
   a.A = x;
   a.lda = int32_t(p.H);
   a.N = int32_t(p.I);
@@ -86,13 +86,15 @@ extern "C" e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t
     E4B_TRY(launch_decode_forward(p, L, x, topk_idx, topk_w, y, w, stream));
     return E4B_OK;
   }
-  E4B_TRY(launch_permute(p, topk_idx, w, stream));
+  // with a saved buffer the permutation is written there for the dgrad
+  const PermView v = saved ? perm_in_saved(p, static_cast<char *>(saved)) : perm_in_workspace(p, w);
+  E4B_TRY(launch_permute(p, topk_idx, w, v, stream));
 
   uint16_t *a_buf = reinterpret_cast<uint16_t *>(w + p.off_a);
   uint16_t *o_buf = reinterpret_cast<uint16_t *>(w + p.off_o);
-  E4B_TRY(run_gate_up(p, L, x, a_buf, static_cast<uint16_t *>(saved), w, stream));
+  E4B_TRY(run_gate_up(p, L, x, a_buf, static_cast<uint16_t *>(saved), v, stream));
 
-  GemmArgs d = base_args(p, L->down, w);
+  GemmArgs d = base_args(p, L->down, v);
   d.A = a_buf;
   d.lda = int32_t(p.I);
   d.N = int32_t(p.H);
@@ -103,8 +105,7 @@ extern "C" e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t
   d.ldc = int32_t(p.H);
   E4B_TRY(launch_grouped_gemm(GEMM_DOWN_FWD, d, stream));
 
-  E4B_TRY(launch_combine_rows(o_buf, reinterpret_cast<const int32_t *>(w + p.off_pos), topk_w, T,
-                              top_k, int(p.H), y, stream));
+  E4B_TRY(launch_combine_rows(o_buf, v.pos, topk_w, T, top_k, int(p.H), y, stream));
   return E4B_OK;
 }
 
@@ -121,19 +122,24 @@ extern "C" e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t t
                    ws_bytes);
   if (st != E4B_OK || T == 0) return st;
   char *w = static_cast<char *>(ws);
-  E4B_TRY(launch_permute(p, topk_idx, w, stream));
-
+  // the saved buffer holds the forward's permutation; without it the
+  // permutation and the gate_up projection are recomputed
   const uint16_t *gu = static_cast<const uint16_t *>(saved);
-  if (!gu) {
+  PermView v;
+  if (saved) {
+    v = perm_in_saved(p, static_cast<char *>(const_cast<void *>(saved)));
+  } else {
+    v = perm_in_workspace(p, w);
+    E4B_TRY(launch_permute(p, topk_idx, w, v, stream));
     uint16_t *gu_ws = reinterpret_cast<uint16_t *>(w + p.off_gu);
-    E4B_TRY(run_gate_up(p, L, static_cast<const uint16_t *>(x_bf16), nullptr, gu_ws, w, stream));
+    E4B_TRY(run_gate_up(p, L, static_cast<const uint16_t *>(x_bf16), nullptr, gu_ws, v, stream));
     gu = gu_ws;
   }
   uint16_t *dgu = reinterpret_cast<uint16_t *>(w + p.off_dgu);
   float *partial = reinterpret_cast<float *>(w + p.off_partial);
   uint16_t *gx = reinterpret_cast<uint16_t *>(w + p.off_gx);
 
-  GemmArgs d = base_args(p, L->down, w);
+  GemmArgs d = base_args(p, L->down, v);
   d.A = static_cast<const uint16_t *>(grad_y_bf16);
   d.lda = int32_t(p.H);
   d.N = int32_t(p.I);
@@ -147,7 +153,7 @@ extern "C" e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t t
   d.partial = partial;
   E4B_TRY(launch_grouped_gemm(GEMM_DOWN_DGRAD, d, stream));
 
-  GemmArgs u = base_args(p, L->gate_up, w);
+  GemmArgs u = base_args(p, L->gate_up, v);
   u.A = dgu;
   u.lda = int32_t(2 * p.I);
   u.N = int32_t(p.H);
@@ -158,7 +164,7 @@ extern "C" e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t t
   u.ldc = int32_t(p.H);
   E4B_TRY(launch_grouped_gemm(GEMM_GATE_UP_DGRAD, u, stream));
 
-  const int32_t *pos = reinterpret_cast<const int32_t *>(w + p.off_pos);
+  const int32_t *pos = v.pos;
   E4B_TRY(launch_combine_rows(gx, pos, nullptr, T, top_k, int(p.H),
                               static_cast<uint16_t *>(grad_x_bf16), stream));
   if (grad_topk_w)

@@ -49,8 +49,21 @@ void timer_after(int kernel, hipStream_t s);
 hipError_t launch_route(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
                         hipStream_t s);
 
-// Fills counts/offsets/tile_offsets/tile_map/sorted_pair/pos_of_pair in the workspace.
-hipError_t launch_permute(const MoePlan &p, const int32_t *idx, char *ws, hipStream_t s);
+// Where the routing permutation lives: in the workspace, or in the saved
+// buffer when the forward keeps it for the dgrad.
+struct PermView {
+  int32_t *offsets;       // [E + 1] first sorted position of each expert
+  int32_t *tile_offsets;  // [E + 1] first m-tile of each expert
+  int4 *tile_map;         // [m_tiles_bound] expert, segment start, first row, rows
+  int32_t *sorted;        // [P] pair id at sorted position
+  int32_t *pos;           // [P] sorted position of pair id
+};
+PermView perm_in_workspace(const MoePlan &p, char *ws);
+PermView perm_in_saved(const MoePlan &p, char *saved);
+
+// Fills the permutation (histogram scratch and counts in the workspace).
+hipError_t launch_permute(const MoePlan &p, const int32_t *idx, char *ws, const PermView &v,
+                          hipStream_t s);
 
 // grid must equal m_tiles_bound * n_tiles.
 hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s);

@@ -110,7 +110,12 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   p->off_gx = take(size_t(P) * H * 2);
   const size_t dgrad_end = off;
   p->ws_bytes = fwd_end > dgrad_end ? fwd_end : dgrad_end;
-  p->saved_bytes = size_t(P) * 2 * I * 2;
+  p->sv_tile_map = size_t(P) * 2 * I * 2;  // a multiple of 256: I % 64 == 0
+  p->sv_tile_offsets = p->sv_tile_map + size_t(p->m_tiles_bound) * 16;
+  p->sv_offsets = p->sv_tile_offsets + size_t(E + 1) * 4;
+  p->sv_sorted = p->sv_offsets + size_t(E + 1) * 4;
+  p->sv_pos = p->sv_sorted + size_t(P) * 4;
+  p->saved_bytes = p->sv_pos + size_t(P) * 4;
   return E4B_OK;
 }
 
@@ -168,7 +173,7 @@ extern "C" const char *e4b_status_string(e4b_status s) {
     case E4B_ERR_DTYPE: return "unknown output dtype";
     case E4B_ERR_WORKSPACE: return "workspace missing or too small";
     case E4B_ERR_ALIGN: return "device buffer not 16-byte aligned";
-    case E4B_ERR_PATH: return "invalid path (decode path needs T <= 8, saved == NULL and max(H, I) <= 4096 (T <= 2) or 2048)";
+    case E4B_ERR_PATH: return "invalid path (decode path needs T <= 8, saved == NULL and max(H, I) <= 4096)";
     case E4B_ERR_HIP: return "HIP kernel launch failed";
   }
   return "unknown status";

@@ -41,6 +41,9 @@ struct MoePlan {
   size_t off_dmap;                              // forward, decode path: work maps
   size_t off_gu, off_dgu, off_partial, off_gx;  // dgrad
   size_t ws_bytes;
+  // saved buffer (dense): bf16 g|u [P, 2I], then the forward's permutation
+  // (tile map, tile offsets, offsets, sorted pairs, pair positions)
+  size_t sv_tile_map, sv_tile_offsets, sv_offsets, sv_sorted, sv_pos;
   size_t saved_bytes;
 };
 

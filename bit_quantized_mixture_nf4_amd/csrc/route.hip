@@ -131,7 +131,7 @@ __global__ __launch_bounds__(64) void perm_scatter_kernel(
     const int32_t *__restrict__ counts, const int32_t *__restrict__ chunk_base,
     int32_t *__restrict__ sorted_pair, int32_t *__restrict__ pos_of_pair,
     int32_t *__restrict__ offsets, int32_t *__restrict__ tile_offsets,
-    int4 *__restrict__ tile_map) {
+    int4 *__restrict__ tile_map, int64_t m_tiles_bound) {
   __shared__ int32_t base[kMaxE];
   const int lane = threadIdx.x;
   const int64_t c = blockIdx.x;
@@ -168,6 +168,9 @@ __global__ __launch_bounds__(64) void perm_scatter_kernel(
     offsets[E] = carry;
     tile_offsets[E] = tcarry;
   }
+  // unused tile map entries are zeroed (no stale bytes in a saved buffer)
+  if (c == 0)
+    for (int64_t t = tcarry + lane; t < m_tiles_bound; t += 64) tile_map[t] = int4{0, 0, 0, 0};
   __syncthreads();
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int64_t p0 = c * kPermChunk;
@@ -203,23 +206,40 @@ hipError_t launch_route(const float *logits, int64_t T, int E, int k, int32_t *i
   return hipGetLastError();
 }
 
-hipError_t launch_permute(const MoePlan &p, const int32_t *idx, char *ws, hipStream_t s) {
+PermView perm_in_workspace(const MoePlan &p, char *ws) {
+  PermView v;
+  v.offsets = reinterpret_cast<int32_t *>(ws + p.off_offsets);
+  v.tile_offsets = reinterpret_cast<int32_t *>(ws + p.off_tile_offsets);
+  v.tile_map = reinterpret_cast<int4 *>(ws + p.off_tile_map);
+  v.sorted = reinterpret_cast<int32_t *>(ws + p.off_sorted);
+  v.pos = reinterpret_cast<int32_t *>(ws + p.off_pos);
+  return v;
+}
+
+PermView perm_in_saved(const MoePlan &p, char *saved) {
+  PermView v;
+  v.offsets = reinterpret_cast<int32_t *>(saved + p.sv_offsets);
+  v.tile_offsets = reinterpret_cast<int32_t *>(saved + p.sv_tile_offsets);
+  v.tile_map = reinterpret_cast<int4 *>(saved + p.sv_tile_map);
+  v.sorted = reinterpret_cast<int32_t *>(saved + p.sv_sorted);
+  v.pos = reinterpret_cast<int32_t *>(saved + p.sv_pos);
+  return v;
+}
+
+hipError_t launch_permute(const MoePlan &p, const int32_t *idx, char *ws, const PermView &v,
+                          hipStream_t s) {
   if (p.P == 0) return hipSuccess;
   int32_t *hist = reinterpret_cast<int32_t *>(ws + p.off_hist);
   int32_t *cbase = reinterpret_cast<int32_t *>(ws + p.off_chunk_base);
   int32_t *counts = reinterpret_cast<int32_t *>(ws + p.off_counts);
-  int32_t *offsets = reinterpret_cast<int32_t *>(ws + p.off_offsets);
-  int32_t *toff = reinterpret_cast<int32_t *>(ws + p.off_tile_offsets);
-  int32_t *sorted = reinterpret_cast<int32_t *>(ws + p.off_sorted);
-  int32_t *pos = reinterpret_cast<int32_t *>(ws + p.off_pos);
-  int4 *tmap = reinterpret_cast<int4 *>(ws + p.off_tile_map);
   const int E = int(p.E);
   hipLaunchKernelGGL(perm_hist_kernel, dim3(uint32_t(p.nchunks)), dim3(256), 0, s, idx, p.P, E,
                      p.nchunks, hist);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(uint32_t(E)), dim3(256), 0, s, hist, p.nchunks, cbase,
                      counts);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3(uint32_t(p.nchunks)), dim3(64), 0, s, idx, p.P, E,
-                     p.nbits_e, p.nchunks, counts, cbase, sorted, pos, offsets, toff, tmap);
+                     p.nbits_e, p.nchunks, counts, cbase, v.sorted, v.pos, v.offsets,
+                     v.tile_offsets, v.tile_map, p.m_tiles_bound);
   return hipGetLastError();
 }
 

@@ -127,8 +127,9 @@ e4b_status e4b_dequantize_nf4(const e4b_stack *st, int32_t dtype, void *w_out,
  *   topk_w        : device fp32  [T, top_k]
  *   y_bf16        : device bf16 [T, H] (written)
  *   saved         : device buffer of e4b_moe_saved_bytes() or NULL; when given,
- *                   the bf16 gate and up projections of every pair are stored
- *                   for e4b_moe_dgrad (grouped path only)
+ *                   the bf16 gate and up projections of every pair and the
+ *                   routing permutation are stored for e4b_moe_dgrad
+ *                   (grouped path only)
  *   ws, ws_bytes  : device workspace, >= e4b_moe_workspace_bytes()
  *   path          : e4b_path
  * Errors: NULL, SHAPE, BLOCKSIZE, CODEBOOK, WORKSPACE, ALIGN, PATH, HIP. */
@@ -149,8 +150,10 @@ e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t top_k,
  *   topk_idx, topk_w : device [T, top_k] (inputs, as used by the forward)
  *   x_bf16           : device bf16 [T, H]; required when saved == NULL
  *                      (the gate/up projections are recomputed), ignored otherwise
- *   saved            : the buffer filled by e4b_moe_forward, or NULL.
- *                      Recompute and saved give bitwise-identical results.
+ *   saved            : the buffer filled by e4b_moe_forward, or NULL. Its
+ *                      permutation replaces topk_idx (which must be the
+ *                      forward's). Recompute and saved give bitwise-identical
+ *                      results.
  *   grad_y_bf16      : device bf16 [T, H]
  *   grad_x_bf16      : device bf16 [T, H] (written)
  *   grad_topk_w      : device fp32 [T, top_k] (written) or NULL
@@ -166,7 +169,8 @@ e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t top_k,
  * top_k) (one size serves both); 0 when the arguments are invalid. */
 size_t e4b_moe_workspace_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k);
 
-/* Bytes of the `saved` buffer: bf16 [T*top_k, 2I]; 0 when invalid. */
+/* Bytes of the `saved` buffer: bf16 [T*top_k, 2I] followed by the routing
+ * permutation (int32 arrays over experts, m-tiles and pairs); 0 when invalid. */
 size_t e4b_moe_saved_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k);
 
 /* Kernels that e4b_set_kernel_timer can bracket with events. */
