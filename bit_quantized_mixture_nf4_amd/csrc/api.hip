@@ -158,8 +158,8 @@ extern "C" e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t t
   u.lda = int32_t(2 * p.I);
   u.N = int32_t(p.H);
   u.K = int32_t(2 * p.I);
-  u.n_tiles = int32_t(p.n_tiles_h);
-  u.grid = uint32_t(p.m_tiles_bound * p.n_tiles_h);
+  u.n_tiles = int32_t(p.n_tiles_h_gud);
+  u.grid = uint32_t(p.m_tiles_bound * p.n_tiles_h_gud);
   u.C = gx;
   u.ldc = int32_t(p.H);
   E4B_TRY(launch_grouped_gemm(GEMM_GATE_UP_DGRAD, u, stream));

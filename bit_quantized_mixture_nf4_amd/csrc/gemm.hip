@@ -21,13 +21,13 @@
 //   EPI_DSWIGLU : dgrad of act(gate) * up scaled by the routing weight, plus
 //                 this tile's share of d y / d routing weight.
 //
-// Tile: kBM x kBN x kBK = 256 x 128 x 64 (one quantization block per K-step),
-// 256 threads = 4 waves stacked along M, each wave 64 x 128 = 2 x 4 MFMA
-// 32x32x16 tiles. A and the dequantized B are staged in one LDS stage; two
-// workgroups share a CU (registers: 2 waves per SIMD), so one contracts while
-// the other refills its stage or runs its epilogue. B is dequantized once per
-// workgroup (codebook in LDS, fp32 multiply by the block absmax,
-// round-to-nearest-even bf16), i.e. exactly the bf16 view that
+// Tile: 256 (pairs) x 128 * WN (columns) x 64 (one quantization block per
+// K-step); 4 x WN waves, each 64 x 128 = 2 x 4 MFMA 32x32x16 tiles. WN = 2
+// (gate_up forward and both down GEMMs): 512 threads, one workgroup per CU,
+// double-buffered LDS. WN = 1 (gate_up dgrad): 256 threads, one LDS stage,
+// two workgroups per CU. A and the dequantized B are staged in LDS; B is
+// dequantized once per workgroup (codebook in LDS, fp32 multiply by the block
+// absmax, round-to-nearest-even bf16), i.e. exactly the bf16 view that
 // e4b_dequantize_nf4 returns.
 #include "device.h"
 #include "kernels.h"
@@ -40,11 +40,6 @@ enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_DSWIGLU = 2 };
 
 
 
-constexpr int kThreads = 256 * kGemmWavesN;  // 4 x kGemmWavesN waves
-// one LDS stage when two workgroups share a CU (they hide each other's
-// staging and epilogues), two when one workgroup owns the CU
-constexpr int kStages = kGemmWavesN == 1 ? 1 : 2;
-constexpr int kAPass = kBM * 8 / kThreads;  // A rows per thread per K-step
 constexpr int kLds = kBK + 8;  // padded row (bf16 elements): 144 bytes, conflict-free b128 access
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
@@ -53,8 +48,17 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __ex
 // waves holding the first 128 rows sit on all four SIMDs and a tile whose
 // rows end early frees whole SIMDs. Each wave owns 64 x 128 outputs
 // (2 x 4 MFMA 32x32x16 tiles, 128 fp32 accumulators per lane).
-template <int AMODE, int BMODE, int EPI>
-__global__ __launch_bounds__(kThreads, kStages == 1 ? 2 : 1) void grouped_gemm_kernel(GemmArgs g) {
+// WN waves along N (4 along M): the tile has 128 * WN columns. WN = 2: 512
+// threads, two LDS stages (one workgroup per CU; the two waves of a SIMD run
+// the halves of a K-step in opposite order). WN = 1: 256 threads, one LDS
+// stage, two workgroups per CU hide each other's staging and epilogues.
+template <int AMODE, int BMODE, int EPI, int WN>
+__global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel(GemmArgs g) {
+  constexpr int kGemmWavesN = WN;
+  constexpr int kThreads = 256 * WN;
+  constexpr int kBN = 128 * WN;
+  constexpr int kStages = WN == 1 ? 1 : 2;
+  constexpr int kAPass = kBM * 8 / kThreads;  // A rows per thread per K-step
   __shared__ __attribute__((aligned(16))) uint16_t sA[kStages][kBM * kLds];
   __shared__ __attribute__((aligned(16))) uint16_t sB[kStages][kBN * kLds];
   __shared__ float sCode[16];
@@ -389,20 +393,24 @@ __global__ __launch_bounds__(kThreads, kStages == 1 ? 2 : 1) void grouped_gemm_k
 
 hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s) {
   if (a.grid == 0) return hipSuccess;
-  const dim3 grid(a.grid), block(kThreads);
+  const dim3 grid(a.grid);
   timer_before(int(v), s);
   switch (v) {
     case GEMM_GATE_UP_FWD:
-      hipLaunchKernelGGL((grouped_gemm_kernel<A_GATHER, B_NT, EPI_SWIGLU>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((grouped_gemm_kernel<A_GATHER, B_NT, EPI_SWIGLU, kBNWide / 128>), grid,
+                         dim3(2 * kBNWide), 0, s, a);
       break;
     case GEMM_DOWN_FWD:
-      hipLaunchKernelGGL((grouped_gemm_kernel<A_DIRECT, B_NT, EPI_STORE>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((grouped_gemm_kernel<A_DIRECT, B_NT, EPI_STORE, kBNWide / 128>), grid,
+                         dim3(2 * kBNWide), 0, s, a);
       break;
     case GEMM_DOWN_DGRAD:
-      hipLaunchKernelGGL((grouped_gemm_kernel<A_GATHER, B_NN, EPI_DSWIGLU>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((grouped_gemm_kernel<A_GATHER, B_NN, EPI_DSWIGLU, kBNWide / 128>), grid,
+                         dim3(2 * kBNWide), 0, s, a);
       break;
     case GEMM_GATE_UP_DGRAD:
-      hipLaunchKernelGGL((grouped_gemm_kernel<A_DIRECT, B_NN, EPI_STORE>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((grouped_gemm_kernel<A_DIRECT, B_NN, EPI_STORE, kBNNarrow / 128>), grid,
+                         dim3(2 * kBNNarrow), 0, s, a);
       break;
   }
   const hipError_t err = hipGetLastError();

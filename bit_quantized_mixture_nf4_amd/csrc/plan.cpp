@@ -75,9 +75,10 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   p->nchunks = (P + kPermChunk - 1) / kPermChunk;
   const int64_t busy = P < E ? P : E;  // at most P experts have a pair
   p->m_tiles_bound = (P + busy * (kBM - 1)) / kBM;
-  p->n_tiles_gu = (I + kBN / 2 - 1) / (kBN / 2);
-  p->n_tiles_h = (H + kBN - 1) / kBN;
-  p->n_tiles_i = (I + kBN - 1) / kBN;
+  p->n_tiles_gu = (I + kBNWide / 2 - 1) / (kBNWide / 2);
+  p->n_tiles_h = (H + kBNWide - 1) / kBNWide;
+  p->n_tiles_i = (I + kBNWide - 1) / kBNWide;
+  p->n_tiles_h_gud = (H + kBNNarrow - 1) / kBNNarrow;
   p->nbits_e = bits_for(E);
 
   size_t off = 0;

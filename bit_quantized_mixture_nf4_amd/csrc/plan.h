@@ -12,9 +12,12 @@
 namespace e4b {
 
 // Tile shape shared by every grouped GEMM of the forward and dgrad.
-constexpr int kGemmWavesN = 1;  // waves of a GEMM workgroup along N (4 along M)
 constexpr int kBM = 256;   // rows (routed pairs) per tile
-constexpr int kBN = 128 * kGemmWavesN;  // output columns per tile
+// output columns per tile: 256 (8 waves, one workgroup per CU) for the gate_up
+// forward and both down GEMMs, 128 (4 waves, two workgroups per CU) for the
+// gate_up dgrad, each the faster shape for that GEMM
+constexpr int kBNWide = 256;
+constexpr int kBNNarrow = 128;
 constexpr int kBK = 64;    // reduction step = one quantization block
 constexpr int kBlock = 64; // quantization block (elements along `in`)
 constexpr int kPermChunk = 1024;  // pairs per histogram / scatter chunk
@@ -29,9 +32,10 @@ struct MoePlan {
   int32_t codebook;
   int64_t nchunks;        // permutation chunks of kPermChunk pairs
   int64_t m_tiles_bound;  // upper bound of sum_e ceil(count_e / kBM)
-  int64_t n_tiles_gu;     // gate_up forward tiles: kBN/2 gate-up pairs per tile
-  int64_t n_tiles_h;      // tiles over H
-  int64_t n_tiles_i;      // tiles over I
+  int64_t n_tiles_gu;     // gate_up forward tiles: kBNWide/2 gate-up pairs per tile
+  int64_t n_tiles_h;      // down forward tiles over H (kBNWide)
+  int64_t n_tiles_i;      // down dgrad tiles over I (kBNWide)
+  int64_t n_tiles_h_gud;  // gate_up dgrad tiles over H (kBNNarrow)
   int nbits_e;            // bits needed for an expert id
   // workspace byte offsets
   size_t off_hist, off_chunk_base, off_counts, off_offsets, off_tile_offsets;
