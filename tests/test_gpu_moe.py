@@ -213,3 +213,60 @@ def test_single_expert_top1_is_dense_swiglu():
     u = x @ wgu[0, cfg.I :].T.astype(np.float64)
     ref = (g / (1 + np.exp(-g)) * u) @ wdn[0].T.astype(np.float64)
     tol_check(to_np(y), ref, "dense y")
+
+
+def _decode_case(cfg, idx, seed=1, kind="nf4", path="decode"):
+    """One forward path vs the oracle with given routing ids (weights drawn here)."""
+    T, k = idx.shape
+    # ids are a precondition the kernels do not check: in range, distinct per token
+    assert idx.min() >= 0 and idx.max() < cfg.E and all(len(set(r)) == k for r in idx.tolist())
+    pb = Problem(cfg, seed=seed, codebook=kind, with_grad=False)
+    w = np.random.default_rng(seed).random((T, k)).astype(np.float32) + 0.1
+    idx_d = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).to(DEV)
+    w_d = torch.from_numpy(w).to(DEV)
+    y, _, _, _ = e4b.moe_forward(pb.layer, pb.x_d, k, topk_idx=idx_d, topk_w=w_d, path=path)
+    tol_check(to_np(y), _oracle_fwd(pb, idx, w.astype(np.float64)), f"y {path} {cfg.name}")
+
+
+@pytest.mark.parametrize("kind", ["nf4", "fp4"])
+def test_decode_all_tokens_share_experts(kind):
+    """Every token on the same k experts: the 8-token bucket of the GEMV."""
+    cfg = MoEConfig("share", E=16, H=512, I=256, k=4, T=8, routing="normal")
+    announce(f"decode share {kind} E16 H512 I256 k4 T8")
+    idx = np.tile(np.array([[3, 9, 0, 14]], np.int32), (8, 1))
+    _decode_case(cfg, idx, kind=kind)
+
+
+def test_decode_mixed_token_counts():
+    """Experts with 1, 2, 3, 5 and 8 tokens in one call (every bucket of the GEMV)."""
+    cfg = MoEConfig("mixed", E=32, H=1024, I=512, k=4, T=8, routing="normal")
+    announce("decode mixed counts E32 H1024 I512 k4 T8")
+    idx = np.zeros((8, 4), np.int32)
+    for t in range(8):
+        # expert 0: 8 tokens; 2: 5; 4: 3; 15-17: 2 each; the rest 1
+        idx[t] = [0, 2 if t < 5 else 20 + t, 4 if t < 3 else 12 + t, 10 + t]
+    _decode_case(cfg, idx)
+
+
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_longest_and_shortest_rows(path):
+    """in_features 4096 (the decode limit: 16 bytes per lane) and 64 (one block)."""
+    cfg = MoEConfig("long", E=4, H=4096, I=64, k=2, T=5, routing="normal")
+    announce(f"{path} long rows E4 H4096 I64 k2 T5")
+    idx = np.array([[0, 1], [1, 2], [3, 0], [2, 3], [0, 2]], np.int32)
+    _decode_case(cfg, idx, path=path)
+
+
+def test_grouped_topk_equals_E():
+    """Every token routed to every expert (top_k = E)."""
+    cfg = MoEConfig("allE", E=4, H=256, I=128, k=4, T=96, routing="normal")
+    announce("grouped top_k = E E4 H256 I128 T96")
+    pb = Problem(cfg, seed=4)
+    y, idx, w, saved = e4b.moe_forward(pb.layer, pb.x_d, cfg.k, logits=pb.logits_d, save=True)
+    idx_ref, w_ref = oracle.route(pb.logits, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    tol_check(to_np(y), _oracle_fwd(pb, idx_ref, w_ref), "y top_k=E")
+    gx, gw = e4b.moe_dgrad(pb.layer, idx, w, pb.grad_y_d, saved=saved)
+    gx_ref, gw_ref = _oracle_dgrad(pb, idx_ref, w_ref)
+    tol_check(to_np(gx), gx_ref, "grad_x top_k=E")
+    tol_check(to_np(gw), gw_ref, "grad_w top_k=E")
