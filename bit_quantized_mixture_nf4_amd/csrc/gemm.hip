@@ -42,7 +42,8 @@ enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_DSWIGLU = 2 };
 
 constexpr int kLds = kBK + 8;  // padded row (bf16 elements): 144 bytes, conflict-free b128 access
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// hardware reciprocal (about 1 ulp): the result is rounded to bf16 anyway
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Waves are laid out 4 (M) x 2 (N); wave w -> (wm = w / 2, wn = w % 2), so the
 // waves holding the first 128 rows sit on all four SIMDs and a tile whose
@@ -59,9 +60,10 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   constexpr int kBN = 128 * WN;
   constexpr int kStages = WN == 1 ? 1 : 2;
   constexpr int kAPass = kBM * 8 / kThreads;  // A rows per thread per K-step
+  // the codebook first: its LDS address fits a ds_read's immediate offset
+  __shared__ __attribute__((aligned(64))) float sCode[16];
   __shared__ __attribute__((aligned(16))) uint16_t sA[kStages][kBM * kLds];
   __shared__ __attribute__((aligned(16))) uint16_t sB[kStages][kBN * kLds];
-  __shared__ float sCode[16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -150,15 +152,23 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
           ra[i];
     uint16_t *b_dst = sB[buf];
     if (BMODE == B_NT) {
-      // all 32 codebook reads are issued before the first product
+      // all 32 codebook reads are issued before the first product; each
+      // byte of hi4 / lo4 is the byte offset (4 * nibble) of a table entry
       float c[32];
+      const char *tbl = reinterpret_cast<const char *>(sCode);
 #pragma unroll
-      for (int d = 0; d < 4; ++d)
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t hi4 = (rb[d] >> 2) & 0x3C3C3C3Cu, lo4 = (rb[d] << 2) & 0x3C3C3C3Cu;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          c[8 * d + 2 * b] = sCode[(rb[d] >> (8 * b + 4)) & 15u];
-          c[8 * d + 2 * b + 1] = sCode[(rb[d] >> (8 * b)) & 15u];
+          // v_perm: byte b of the source into byte 0, zeros above
+          const uint32_t sel = 0x0C0C0C00u | uint32_t(b);
+          c[8 * d + 2 * b] =
+              *reinterpret_cast<const float *>(tbl + __builtin_amdgcn_perm(0u, hi4, sel));
+          c[8 * d + 2 * b + 1] =
+              *reinterpret_cast<const float *>(tbl + __builtin_amdgcn_perm(0u, lo4, sel));
         }
+      }
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         float v[8];
@@ -173,10 +183,15 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint32_t w = rbn[r];
+        const uint32_t hi4 = (w >> 2) & 0x3C3C3C3Cu, lo4 = (w << 2) & 0x3C3C3C3Cu;
+        const char *tbl = reinterpret_cast<const char *>(sCode);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          v[r][2 * b] = __fmul_rn(sCode[(w >> (8 * b + 4)) & 15u], ramn[r]);
-          v[r][2 * b + 1] = __fmul_rn(sCode[(w >> (8 * b)) & 15u], ramn[r]);
+          const uint32_t sel = 0x0C0C0C00u | uint32_t(b);
+          v[r][2 * b] = __fmul_rn(
+              *reinterpret_cast<const float *>(tbl + __builtin_amdgcn_perm(0u, hi4, sel)), ramn[r]);
+          v[r][2 * b + 1] = __fmul_rn(
+              *reinterpret_cast<const float *>(tbl + __builtin_amdgcn_perm(0u, lo4, sel)), ramn[r]);
         }
       }
 #pragma unroll
@@ -213,22 +228,34 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
     if (!wave_active) return;
     const uint16_t *a_src = sA[cur] + (wm * 64 + (lane & 31)) * kLds + (lane >> 5) * 8;
     const uint16_t *b_src = sB[cur] + (wn * 128 + (lane & 31)) * kLds + (lane >> 5) * 8;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8 af[2], bfr[4];
+    // fragments of k-slice kk + 1 are read while the MFMAs of kk run (the
+    // one-workgroup-per-CU tiles; the narrow tile has no registers to spare)
+    constexpr bool kPrefetch = WN == 2;
+    bf16x8 af[2][2], bfr[2][4];
+    auto frag = [&](int kk, int slot) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const bf16x8 *>(a_src + i * 32 * kLds + kk * 16);
+        af[slot][i] = *reinterpret_cast<const bf16x8 *>(a_src + i * 32 * kLds + kk * 16);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8 *>(b_src + j * 32 * kLds + kk * 16);
+        bfr[slot][j] = *reinterpret_cast<const bf16x8 *>(b_src + j * 32 * kLds + kk * 16);
+    };
+    if (kPrefetch) frag(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int slot = kPrefetch ? kk & 1 : 0;
+      if (!kPrefetch)
+        frag(kk, 0);
+      else if (kk + 1 < kBK / 16)
+        frag(kk + 1, (kk + 1) & 1);
       // weights are the MFMA A-operand: acc[i][j] holds D[tile col][tile row]
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[slot][j], af[slot][i],
+                                                              acc[i][j], 0, 0, 0);
       __builtin_amdgcn_s_setprio(0);
     }
   };
