@@ -5,7 +5,7 @@
 // syncs, and single-row projections read the packed 4-bit weight directly
 // instead of materializing a dequantized expert. Here, for T <= 8:
 //   prep     one workgroup groups the <= 8*k routed pairs by expert (stable)
-//            and lists the distinct experts in ascending order;
+//            and writes one self-contained work item per GEMV workgroup;
 //   gate_up  one workgroup per (distinct expert, block of gate/up row pairs):
 //            every packed byte is read once for all tokens routed to that
 //            expert; a = silu(g) * u is written as bf16;
@@ -26,19 +26,20 @@ constexpr int kDecThreads = 64 * kDecWaves;
 // Workspace layout of the decode path (inside the permutation region, plus a
 // work map after the forward buffers).
 struct DecodeWs {
-  int32_t *n_distinct;  // [1]
-  int32_t *dexp;        // [kDecMaxPairs] expert id of distinct expert d (ascending)
-  int32_t *dseg;        // [kDecMaxPairs + 1] sorted-pair offsets of distinct expert d
   int32_t *sorted;      // [P] pair id at sorted position
   int32_t *pos;         // [P] sorted position of pair id
   int32_t *map_count;   // [2] workgroups with work: gate_up, down
-  int32_t *map_gu;      // [min(E, P) * I / 16] work item of gate_up workgroup b
-  int32_t *map_dn;      // [min(E, P) * H / 16] work item of down workgroup b
+  int4 *map_gu;         // [min(E, P) * I / 16] work item of gate_up workgroup b
+  int4 *map_dn;         // [min(E, P) * H / 16] work item of down workgroup b
+                        // (sized for tiles of 16 units; tiles are kDecTile)
 };
 
-// work item: distinct expert d, first tile, tile count
-__host__ __device__ constexpr int32_t dec_item(int d, int tile0, int nt) {
-  return d | (tile0 << 8) | (nt << 17);
+// A work item is everything a GEMV workgroup needs before its loads:
+//   x: expert | token count << 16     y: first tile | tile count << 16
+//   z: first sorted position          w: token of sorted position z + q in
+//                                        bits [4q, 4q + 4) (q < 8; T <= 8)
+__host__ __device__ inline int4 dec_item(int e, int np, int tile0, int nt, int s0, int toks) {
+  return int4{e | (np << 16), tile0 | (nt << 16), s0, toks};
 }
 
 // Relative cost of a tile of an expert with np tokens, in eighths of the cost
@@ -66,16 +67,17 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 
 // One workgroup: groups the P <= 256 routed pairs by expert (stable), lists
 // the distinct experts in ascending order and writes the work maps of the
-// two GEMV launches (chunks of tiles of 16 units per distinct expert).
+// two GEMV launches (chunks of tiles of kDecTile units per distinct expert).
 // Ranks come from comparisons of unique (expert, pair) keys, segment starts
 // and the chunk offsets from wave ballots and scans.
 __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restrict__ idx, int P,
-                                                          int tiles_gu, int tiles_dn,
+                                                          int k_route, int tiles_gu, int tiles_dn,
                                                           int target_gu, int target_dn,
                                                           DecodeWs w) {
   static_assert(kDecMaxPairs == 256, "one thread per routed pair");
   __shared__ __attribute__((aligned(16))) int32_t s_key[kDecMaxPairs];
   __shared__ int32_t s_sorted_e[kDecMaxPairs];
+  __shared__ int32_t s_sorted_p[kDecMaxPairs];
   __shared__ int32_t s_dseg[kDecMaxPairs + 1];
   __shared__ int32_t s_wsum[5][4];
   const int p = threadIdx.x, lane = p & 63, wv = p >> 6;
@@ -92,6 +94,7 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restr
   }
   if (p < P) {
     s_sorted_e[pos] = key / kDecMaxPairs;
+    s_sorted_p[pos] = p;
     w.sorted[pos] = p;
     w.pos[p] = pos;
   }
@@ -104,16 +107,8 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restr
   __syncthreads();
   for (int v = 0; v < wv; ++v) d += s_wsum[0][v];
   const int n = s_wsum[0][0] + s_wsum[0][1] + s_wsum[0][2] + s_wsum[0][3];
-  if (first) {
-    w.dexp[d] = s_sorted_e[p];
-    w.dseg[d] = p;
-    s_dseg[d] = p;
-  }
-  if (p == 0) {
-    w.n_distinct[0] = n;
-    w.dseg[n] = P;
-    s_dseg[n] = P;
-  }
+  if (first) s_dseg[d] = p;
+  if (p == 0) s_dseg[n] = P;
   __syncthreads();
   // Tiles per workgroup (thread = distinct expert): the total cost of all
   // tiles is split into about target workgroups of equal cost (target = the
@@ -148,7 +143,15 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restr
     if (lane == 63) s_wsum[1 + j][wv] = incl[j];
   }
   __syncthreads();
-  int32_t *maps[2] = {w.map_gu, w.map_dn};
+  // this expert's id, segment and tokens (np <= 8: one token per expert
+  // slot, T <= 8)
+  int e_d = 0, s0 = 0, toks = 0;
+  if (p < n) {
+    s0 = s_dseg[p];
+    e_d = s_sorted_e[s0];
+    for (int q = 0; q < min(np_d, 8); ++q) toks |= (s_sorted_p[s0 + q] / k_route) << (4 * q);
+  }
+  int4 *maps[2] = {w.map_gu, w.map_dn};
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     int base = 0;
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restr
       const int first_b = end - c;
       for (int b = first_b; b < end; ++b) {
         const int tile0 = (b - first_b) * tpw[j];
-        maps[j][b] = dec_item(p, tile0, min(tpw[j], tiles[j] - tile0));
+        maps[j][b] = dec_item(e_d, np_d, tile0, min(tpw[j], tiles[j] - tile0), s0, toks);
       }
     }
     if (p == 0)
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restr
 // weight rows, on the vector ALU (no MFMA): every packed byte is read once and
 // used for all the expert's tokens.
 //
-// A workgroup owns a chunk of consecutive tiles of 16 output units of one
+// A workgroup owns a chunk of consecutive tiles of kDecTile output units of one
 // expert, read from the work map of the prep kernel (the grid holds one
 // workgroup per (expert slot, tile); the surplus exits at once).
 // The eight waves split the K blocks in eighths. Inside a wave, 16 lanes share
@@ -187,7 +190,8 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restr
 // are summed in a fixed order (one barrier per tile). GATE_UP runs gate row u
 // and up row I + u in the same lanes and writes a = silu(g) * up.
 constexpr int kTblCopies = 32;
-constexpr int kDecPass = 4;  // passes of 4 rows per tile of 16 units
+constexpr int kDecPass = 4;             // passes of 4 rows per tile
+constexpr int kDecTile = 4 * kDecPass;  // output units per tile
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
@@ -231,13 +235,14 @@ struct DecCtx {
   const uint8_t *wp;   // this expert's packed rows, at the lane's byte offset
   const float *wa;     // this expert's absmax, at the lane's block
   int row_bytes, nblk, I, tile0, nt, s0, np, kl, rq, wave, tid;
-  bool kvalid;
+  int n_active;        // waves with K blocks (the others only meet the barriers)
+  bool kvalid, active; // lane holds K bytes; this wave has K blocks
 };
 
 template <bool GATE_UP, int NP, int BPL>
 __device__ __forceinline__ void decode_tiles(const DecCtx &c, const uint32_t *tl,
                                              const uint16_t *__restrict__ xin, int64_t (&xrow)[NP],
-                                             int K_in, float (*s_red)[GATE_UP ? 2 : 1][kDecWaves][16][8],
+                                             int K_in, float (*s_red)[GATE_UP ? 2 : 1][kDecWaves][kDecTile][8],
                                              uint16_t *__restrict__ out, int ldo, int xoff) {
   constexpr int NR = GATE_UP ? 2 : 1;
   constexpr int WPL = BPL / 4;  // packed words per lane
@@ -256,10 +261,11 @@ __device__ __forceinline__ void decode_tiles(const DecCtx &c, const uint32_t *tl
   }
   LT wv[kDecPass][NR];
   float am[kDecPass][NR];
+  const bool active = c.active;
   auto load_tile = [&](int t) {
 #pragma unroll
     for (int ps = 0; ps < kDecPass; ++ps) {
-      const int u = (c.tile0 + t) * 16 + 4 * ps + c.rq;
+      const int u = (c.tile0 + t) * kDecTile + 4 * ps + c.rq;
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         const int64_t row = u + r * c.I;
@@ -268,13 +274,15 @@ __device__ __forceinline__ void decode_tiles(const DecCtx &c, const uint32_t *tl
       }
     }
   };
-  load_tile(0);
+  if (active) load_tile(0);
   __syncthreads();  // lookup table ready
   for (int t = 0; t < c.nt; ++t) {
     const int slot = t & 1;
     // the next tile's loads are issued once this tile's bytes are expanded;
     // past the last tile the last one is reloaded (uniform wait counts)
     const int tn = min(t + 1, c.nt - 1);
+    // waves without K blocks (small K) skip the work and only meet the barrier
+    if (active) {
 #pragma unroll
     for (int ps = 0; ps < kDecPass; ++ps) {
 #pragma unroll
@@ -288,7 +296,7 @@ __device__ __forceinline__ void decode_tiles(const DecCtx &c, const uint32_t *tl
         }
         const float a = am[ps][r];
         {
-          const int u = (c.tile0 + tn) * 16 + 4 * ps + c.rq;
+          const int u = (c.tile0 + tn) * kDecTile + 4 * ps + c.rq;
           const int64_t row = u + r * c.I;
           wv[ps][r] = *reinterpret_cast<const LT *>(c.wp + row * c.row_bytes);
           am[ps][r] = c.wa[row * c.nblk];
@@ -307,20 +315,20 @@ __device__ __forceinline__ void decode_tiles(const DecCtx &c, const uint32_t *tl
         if (c.kl < NP) s_red[slot][r][c.wave][4 * ps + c.rq][c.kl] = v;
       }
     }
+    }
     __syncthreads();
     // sum the K parts of tile t: thread (token qq, unit mm)
-    if (c.tid < 16 * c.np) {
-      const int qq = c.tid >> 4, mm = c.tid & 15;
+    if (c.tid < kDecTile * c.np) {
+      const int qq = c.tid / kDecTile, mm = c.tid % kDecTile;
       float v[NR];
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         float sum = s_red[slot][r][0][mm][qq];
-#pragma unroll
-        for (int k = 1; k < kDecWaves; ++k) sum += s_red[slot][r][k][mm][qq];
+        for (int k = 1; k < c.n_active; ++k) sum += s_red[slot][r][k][mm][qq];
         v[r] = sum;
       }
       const float val = GATE_UP ? v[0] / (1.0f + __expf(-v[0])) * v[NR - 1] : v[0];
-      out[int64_t(c.s0 + qq) * ldo + (c.tile0 + t) * 16 + mm] = f32_to_bf16(val);
+      out[int64_t(c.s0 + qq) * ldo + (c.tile0 + t) * kDecTile + mm] = f32_to_bf16(val);
     }
   }
 }
@@ -332,11 +340,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(
     int k_route, DecodeWs w, int cb, uint16_t *__restrict__ out, int ldo) {
   constexpr int NR = GATE_UP ? 2 : 1;
   __shared__ uint32_t tbl[256 * kTblCopies];
-  __shared__ float s_red[2][NR][kDecWaves][16][8];
+  __shared__ float s_red[2][NR][kDecWaves][kDecTile][8];
+  static_assert(kDecTile * 8 <= kDecThreads, "one reducing thread per (token, unit)");
   const int count = w.map_count[GATE_UP ? 0 : 1];
-  const int item = (GATE_UP ? w.map_gu : w.map_dn)[blockIdx.x];
+  const int4 item = (GATE_UP ? w.map_gu : w.map_dn)[blockIdx.x];
   if (int(blockIdx.x) >= count) return;
-  const int d = item & 255;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // entry (byte, copy) at byte * kTblCopies + copy: high nibble's code in the
   // low half, low nibble's code in the high half (element order in memory);
@@ -355,19 +363,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(
   c.wave = wave;
   c.kl = lane & 15;
   c.rq = lane >> 4;
-  const int e = w.dexp[d];
-  c.s0 = w.dseg[d];
-  c.np = w.dseg[d + 1] - c.s0;
+  const int e = item.x & 0xFFFF;
+  c.np = min(item.x >> 16, 8);  // <= T <= 8 when the ids are distinct per token
+  c.tile0 = item.y & 0xFFFF;
+  c.nt = item.y >> 16;
+  c.s0 = item.z;
   c.nblk = K_in >> 6;
   c.I = I;
-  c.tile0 = (item >> 8) & 511;
-  c.nt = item >> 17;
   c.row_bytes = K_in >> 1;
   // this wave's K blocks [b0, b0 + nb); lanes past them (kvalid false) read
   // the row's first bytes and carry zero inputs
   const int bpw = (c.nblk + kDecWaves - 1) / kDecWaves;
   const int b0 = wave * bpw;
   const int nb = max(0, min(bpw, c.nblk - b0));
+  c.n_active = (c.nblk + bpw - 1) / bpw;
+  c.active = nb > 0;
   c.kvalid = c.kl * BPL < nb * 32;
   const int kbyte = c.kvalid ? b0 * 32 + c.kl * BPL : 0;
   c.wp = Wp + int64_t(e) * w_e_bytes + kbyte;
@@ -379,7 +389,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(
     int64_t xrow[N];                                                                         \
     for (int q = 0; q < N; ++q) {                                                            \
       const int qc = min(q, c.np - 1);                                                       \
-      xrow[q] = GATE_UP ? int64_t(w.sorted[c.s0 + qc] / k_route) : int64_t(c.s0 + qc);       \
+      xrow[q] = GATE_UP ? int64_t((item.w >> (4 * qc)) & 15) : int64_t(c.s0 + qc);         \
     }                                                                                        \
     decode_tiles<GATE_UP, N, BPL>(c, tl, vin, xrow, K_in, s_red, out, ldo, xoff);            \
   }
@@ -422,18 +432,14 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
                                  const int32_t *idx, const float *wts, uint16_t *y, char *ws,
                                  hipStream_t s) {
   DecodeWs w;
-  // the decode path reuses slots of the permutation region:
-  // dexp <= min(E, P) entries, dseg <= min(E, P) + 1 entries
-  w.n_distinct = reinterpret_cast<int32_t *>(ws + p.off_tile_offsets);
-  w.dexp = reinterpret_cast<int32_t *>(ws + p.off_counts);
-  w.dseg = reinterpret_cast<int32_t *>(ws + p.off_offsets);
+  // the decode path reuses the sorted / pos slots of the permutation region
   w.sorted = reinterpret_cast<int32_t *>(ws + p.off_sorted);
   w.pos = reinterpret_cast<int32_t *>(ws + p.off_pos);
   uint16_t *a_buf = reinterpret_cast<uint16_t *>(ws + p.off_a);
   uint16_t *o_buf = reinterpret_cast<uint16_t *>(ws + p.off_o);
   const int P = int(p.P);
   w.map_count = reinterpret_cast<int32_t *>(ws + p.off_dmap);
-  w.map_gu = w.map_count + 4;
+  w.map_gu = reinterpret_cast<int4 *>(w.map_count + 4);
   w.map_dn = w.map_gu + (p.P < p.E ? p.P : p.E) * (p.I / 16);
   const int ymax = int(p.P < p.E ? p.P : p.E);
   const int H = int(p.H), I = int(p.I);
@@ -448,13 +454,13 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
   const int target_gu = dec_resident_workgroups(true, bpl_gu);
   const int target_dn = dec_resident_workgroups(false, bpl_dn);
   if (target_gu <= 0 || target_dn <= 0) return hipErrorInvalidDeviceFunction;
-  hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(256), 0, s, idx, P, I / 16, H / 16,
-                     target_gu, target_dn, w);
+  hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(256), 0, s, idx, P, int(p.k),
+                     I / kDecTile, H / kDecTile, target_gu, target_dn, w);
 
   auto launch = [&](bool gate_up, int K_in, int n_units, const e4b_stack &st,
                     const uint16_t *vin, uint16_t *dst, int ldo, int kernel_id) {
     const int bpl = bpl_of(K_in);
-    const int tiles = n_units / 16;
+    const int tiles = n_units / kDecTile;
     const dim3 grid(uint32_t(tiles * ymax));
     const int64_t eb = st.out * st.in / 2, ea = st.out * st.in / kBlock;
     timer_before(kernel_id, s);

@@ -100,7 +100,7 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   // forward region
   p->off_a = take(size_t(P) * I * 2);
   p->off_o = take(size_t(P) * H * 2);
-  p->off_dmap = T <= kDecodeMaxT ? take(16 + size_t(busy) * size_t(H / 16 + I / 16) * 4) : 0;
+  p->off_dmap = T <= kDecodeMaxT ? take(16 + size_t(busy) * size_t(H / 16 + I / 16) * 16) : 0;
   const size_t fwd_end = off;
   // dgrad region (overlaps the forward region: the two calls never run at once
   // on one workspace)
