@@ -15,6 +15,8 @@ What it computes (float64 unless a step fixes another precision):
   SwiGLU expert forward, and the frozen-base input gradient (dgrad).
 * ``fidelity``   -- relative reconstruction / forward error used for the
   storage-fidelity ordering.
+* ``lora``       -- per-expert LoRA adapters over the frozen base: forward,
+  dgrad and the adapter weight gradients.
 
 Sources: the experts4bit-qlora / bitsandbytes pages on fused 4-bit expert
 storage (the 0.1.0 sdist's ``_vendor/experts.py`` module ``Experts4bit``; the
@@ -25,8 +27,9 @@ the passage it follows.
 Pin status (see tests/test_oracle_*.py):
 
 * codebooks, quantize, dequantize, bf16 rounding, route, permute, forward,
-  dgrad, fidelity ordering: pinned by published tables, closed forms,
-  brute force, finite differences and library cross-checks.
+  dgrad, fidelity ordering, LoRA forward / backward: pinned by published
+  tables, closed forms (merged weights W + s B A), brute force, finite
+  differences and library cross-checks.
 * absolute fidelity magnitudes quoted on the pages (forward relative error
   about 0.17 nf4 / 0.22 fp4 / 0.003 bf16) use an undefined metric and
   bitsandbytes' own tables: parity unpinned. Only the ordering is checked.
@@ -42,3 +45,4 @@ from .quant import (  # noqa: F401
 )
 from .moe import route, permute, moe_forward, moe_dgrad, silu  # noqa: F401
 from .fidelity import rel_fro, reconstruction_errors  # noqa: F401
+from .lora import lora_forward, lora_backward  # noqa: F401

@@ -14,6 +14,7 @@ Distributions (the workloads' recipe):
 * activations x and output gradients grad_y: N(0, 1) drawn in fp32, rounded
   to bf16 (nearest even, via torch's conversion);
 * expert weights: fp32 N(0, 0.02^2);
+* per-expert LoRA adapters (fp32): N(0, 0.02^2), A [E, r, in], B [E, out, r];
 * router logits (fp32): ``normal`` N(0, 1); ``uniform`` i.i.d. U[0, 1);
   ``zipf`` ``-s*ln(e+1) + Gumbel(0, 1)`` so that Gumbel top-k draws k
   distinct experts with P(e) proportional to (e+1)^-s (expert 0 hottest).
@@ -26,5 +27,6 @@ from .gen import (  # noqa: F401
     gen_logits,
     gen_weights,
     gen_expert_weight,
+    gen_lora,
     to_bf16_tensor,
 )

@@ -7,6 +7,7 @@ import numpy as np
 
 # tensor ids of the independent streams
 _X, _W_GU, _W_DN, _LOGITS, _GRAD_Y = 1, 2, 3, 4, 5
+_A_GU, _B_GU, _A_DN, _B_DN = 6, 7, 8, 9
 
 
 def _rng(seed, tid, sub=None):
@@ -83,3 +84,16 @@ def gen_weights(cfg, seed, which, experts=None, threads=None):
     with ThreadPoolExecutor(max_workers=n) as ex:
         list(ex.map(fill, range(len(experts))))
     return out
+
+
+def gen_lora(cfg, seed, r):
+    """Synthetic per-expert LoRA adapters (fp32, N(0, weight_std^2)), as
+    ``(A_gu [E, r, H], B_gu [E, 2I, r], A_dn [E, r, I], B_dn [E, H, r])``."""
+    shapes = ((_A_GU, (cfg.E, r, cfg.H)), (_B_GU, (cfg.E, 2 * cfg.I, r)),
+              (_A_DN, (cfg.E, r, cfg.I)), (_B_DN, (cfg.E, cfg.H, r)))
+    out = []
+    for tid, shape in shapes:
+        m = _rng(seed, tid, r).standard_normal(shape, dtype=np.float32)
+        m *= np.float32(cfg.weight_std)
+        out.append(m)
+    return tuple(out)
