@@ -19,7 +19,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import E4bLayer, E4bStack, E4bError, check, load  # noqa: F401
+from ._lib import E4bLayer, E4bLora, E4bStack, E4bError, check, load  # noqa: F401
 
 CODEBOOKS = {"nf4": _lib.E4B_CB_NF4, "fp4": _lib.E4B_CB_FP4}
 PATHS = {"auto": _lib.E4B_PATH_AUTO, "grouped": _lib.E4B_PATH_GROUPED, "decode": _lib.E4B_PATH_DECODE}
@@ -31,6 +31,10 @@ __all__ = [
     "dequantize",
     "moe_forward",
     "moe_dgrad",
+    "Lora",
+    "moe_lora_forward",
+    "moe_lora_backward",
+    "lora_workspace_bytes",
     "workspace_bytes",
     "saved_bytes",
     "E4bError",
@@ -209,3 +213,100 @@ def moe_dgrad(layer, topk_idx, topk_w, grad_y, x=None, saved=None, grad_w=True, 
     )
     check("e4b_moe_dgrad", code)
     return gx, gw
+
+
+@dataclass
+class Lora:
+    """Per-expert LoRA adapters (fp32 device tensors): A_gu [E, r, H],
+    B_gu [E, 2I, r], A_dn [E, r, I], B_dn [E, H, r]; scale alpha / r."""
+
+    A_gu: torch.Tensor
+    B_gu: torch.Tensor
+    A_dn: torch.Tensor
+    B_dn: torch.Tensor
+    alpha: float
+
+    @property
+    def r(self):
+        return self.A_gu.shape[1]
+
+    def check(self, layer):
+        E, H, I, r = layer.E, layer.H, layer.I, self.r
+        for name, t, shape in (("A_gu", self.A_gu, (E, r, H)), ("B_gu", self.B_gu, (E, 2 * I, r)),
+                               ("A_dn", self.A_dn, (E, r, I)), ("B_dn", self.B_dn, (E, H, r))):
+            _need(t, name, torch.float32, layer.device, shape)
+
+    def as_c(self):
+        return E4bLora(self.A_gu.data_ptr(), self.B_gu.data_ptr(), self.A_dn.data_ptr(),
+                       self.B_dn.data_ptr(), self.r, float(self.alpha))
+
+
+def lora_workspace_bytes(layer, T, top_k):
+    c = layer.as_c()
+    return int(load().e4b_moe_lora_workspace_bytes(ctypes.byref(c), T, top_k))
+
+
+def _lora_workspace(layer, T, top_k, ws):
+    if ws is None:
+        return torch.empty(max(lora_workspace_bytes(layer, T, top_k), 256), dtype=torch.uint8,
+                           device=layer.device)
+    return ws
+
+
+def moe_lora_forward(layer, lora, x, top_k, logits=None, topk_idx=None, topk_w=None, save=False,
+                     workspace=None):
+    """Forward with per-expert LoRA adapters (grouped path).
+
+    Returns ``(y bf16 [T, H], topk_idx, topk_w, saved or None)``.
+    """
+    dev = layer.device
+    lora.check(layer)
+    _need(x, "x", torch.bfloat16, dev)
+    T = x.shape[0]
+    if logits is not None:
+        _need(logits, "logits", torch.float32, dev, (T, layer.E))
+        topk_idx = torch.empty(T, top_k, dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
+        topk_w = torch.empty(T, top_k, dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    if topk_idx is None or topk_w is None:
+        raise ValueError("give logits, or both topk_idx and topk_w")
+    _need(topk_idx, "topk_idx", torch.int32, dev, (T, top_k))
+    _need(topk_w, "topk_w", torch.float32, dev, (T, top_k))
+    y = torch.empty(T, layer.H, dtype=torch.bfloat16, device=dev)
+    saved = None
+    if save:
+        saved = torch.empty(max(saved_bytes(layer, T, top_k), 16) // 2, dtype=torch.bfloat16, device=dev)
+    ws = _lora_workspace(layer, T, top_k, workspace)
+    c, lc = layer.as_c(), lora.as_c()
+    code = load().e4b_moe_lora_forward(
+        ctypes.byref(c), ctypes.byref(lc), T, top_k, _vp(x), _vp(logits), _vp(topk_idx),
+        _vp(topk_w), _vp(y), _vp(saved), _vp(ws), ws.numel(), _stream(x),
+    )
+    check("e4b_moe_lora_forward", code)
+    return y, topk_idx, topk_w, saved
+
+
+def moe_lora_backward(layer, lora, topk_idx, topk_w, x, grad_y, saved=None, grad_w=True,
+                      workspace=None):
+    """Input gradient, routing-weight gradient and adapter gradients.
+
+    Returns ``(grad_x bf16 [T, H], grad_topk_w fp32 or None, (dA_gu, dB_gu, dA_dn, dB_dn))``.
+    """
+    dev = layer.device
+    lora.check(layer)
+    _need(grad_y, "grad_y", torch.bfloat16, dev)
+    T, top_k = topk_idx.shape
+    _need(topk_idx, "topk_idx", torch.int32, dev, (T, top_k))
+    _need(topk_w, "topk_w", torch.float32, dev, (T, top_k))
+    _need(x, "x", torch.bfloat16, dev, (T, layer.H))
+    gx = torch.empty(T, layer.H, dtype=torch.bfloat16, device=dev)
+    gw = torch.empty(T, top_k, dtype=torch.float32, device=dev) if grad_w else None
+    grads = tuple(torch.empty_like(t) for t in (lora.A_gu, lora.B_gu, lora.A_dn, lora.B_dn))
+    ws = _lora_workspace(layer, T, top_k, workspace)
+    c, lc = layer.as_c(), lora.as_c()
+    code = load().e4b_moe_lora_backward(
+        ctypes.byref(c), ctypes.byref(lc), T, top_k, _vp(topk_idx), _vp(topk_w), _vp(x),
+        _vp(saved), _vp(grad_y), _vp(gx), _vp(gw), *(_vp(g) for g in grads), _vp(ws), ws.numel(),
+        _stream(grad_y),
+    )
+    check("e4b_moe_lora_backward", code)
+    return gx, gw, grads

@@ -34,6 +34,9 @@ EXPORTS = (
     "e4b_moe_dgrad",
     "e4b_moe_workspace_bytes",
     "e4b_moe_saved_bytes",
+    "e4b_moe_lora_forward",
+    "e4b_moe_lora_backward",
+    "e4b_moe_lora_workspace_bytes",
     "e4b_status_string",
     "e4b_set_kernel_timer",
 )
@@ -65,6 +68,17 @@ class E4bLayer(ctypes.Structure):
     _fields_ = [("gate_up", E4bStack), ("down", E4bStack)]
 
 
+class E4bLora(ctypes.Structure):
+    _fields_ = [
+        ("A_gu", ctypes.c_void_p),
+        ("B_gu", ctypes.c_void_p),
+        ("A_dn", ctypes.c_void_p),
+        ("B_dn", ctypes.c_void_p),
+        ("r", ctypes.c_int32),
+        ("alpha", ctypes.c_float),
+    ]
+
+
 _lib = None
 
 
@@ -79,7 +93,7 @@ def load():
         )
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
-    st, lay = ctypes.POINTER(E4bStack), ctypes.POINTER(E4bLayer)
+    st, lay, lo = ctypes.POINTER(E4bStack), ctypes.POINTER(E4bLayer), ctypes.POINTER(E4bLora)
     sigs = {
         "e4b_quantize_nf4": (i32, [vp, i64, i64, i64, i32, i32, vp, vp, vp]),
         "e4b_dequantize_nf4": (i32, [st, i32, vp, vp]),
@@ -87,6 +101,10 @@ def load():
         "e4b_moe_dgrad": (i32, [lay, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "e4b_moe_workspace_bytes": (sz, [lay, i64, i32]),
         "e4b_moe_saved_bytes": (sz, [lay, i64, i32]),
+        "e4b_moe_lora_forward": (i32, [lay, lo, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "e4b_moe_lora_backward": (
+            i32, [lay, lo, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "e4b_moe_lora_workspace_bytes": (sz, [lay, i64, i32]),
         "e4b_status_string": (ctypes.c_char_p, [i32]),
         "e4b_set_kernel_timer": (i32, [i32, vp, vp, i32]),
     }

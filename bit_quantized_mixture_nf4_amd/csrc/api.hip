@@ -172,6 +172,211 @@ extern "C" e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t t
   return E4B_OK;
 }
 
+// ---- LoRA over the frozen base ----
+namespace e4b {
+namespace {
+
+struct LoraWs {
+  float *xa, *aa, *gb, *hb;
+  uint16_t *pk_bgu, *pk_bdn, *pk_agu, *pk_adn;
+};
+
+LoraWs lora_ws(const MoePlan &p, char *w) {
+  LoraWs l;
+  l.xa = reinterpret_cast<float *>(w + p.off_l_xa);
+  l.aa = reinterpret_cast<float *>(w + p.off_l_aa);
+  l.gb = reinterpret_cast<float *>(w + p.off_l_gb);
+  l.hb = reinterpret_cast<float *>(w + p.off_l_hb);
+  l.pk_bgu = reinterpret_cast<uint16_t *>(w + p.off_pk_bgu);
+  l.pk_bdn = reinterpret_cast<uint16_t *>(w + p.off_pk_bdn);
+  l.pk_agu = reinterpret_cast<uint16_t *>(w + p.off_pk_agu);
+  l.pk_adn = reinterpret_cast<uint16_t *>(w + p.off_pk_adn);
+  return l;
+}
+
+float lora_scale(const e4b_lora *lo) { return lo->alpha / float(lo->r); }
+
+// x A_gu^T per pair, then the gate_up GEMM with the s B_gu slice.
+hipError_t lora_gate_up(const MoePlan &p, const e4b_moe_layer *L, const e4b_lora *lo,
+                        const uint16_t *x, const int32_t *idx, uint16_t *a_out, uint16_t *gu_out,
+                        const PermView &v, const LoraWs &l, hipStream_t s) {
+  hipError_t err = launch_lora_project(LS_X_GATHER, x, p.H, int(p.H), int(p.I), v.sorted, idx,
+                                       int(p.k), p.P, lo->A_gu, false, lo->r, l.xa, s);
+  if (err != hipSuccess) return err;
+  GemmArgs a = base_args(p, L->gate_up, v);
+  a.A = x;
+  a.lda = int32_t(p.H);
+  a.N = int32_t(p.I);
+  a.K = int32_t(p.H);
+  a.n_tiles = int32_t(p.n_tiles_gu);
+  a.grid = uint32_t(p.m_tiles_bound * p.n_tiles_gu);
+  a.C = a_out;
+  a.ldc = int32_t(p.I);
+  a.GU = gu_out;
+  a.lora_p = l.xa;
+  a.lora_w = l.pk_bgu;
+  a.lora_rows = int32_t(2 * p.I);
+  return launch_grouped_gemm(GEMM_GATE_UP_FWD, a, s);
+}
+
+}  // namespace
+}  // namespace e4b
+
+extern "C" e4b_status e4b_moe_lora_forward(const e4b_moe_layer *L, const e4b_lora *lora,
+                                           int64_t T, int32_t top_k, const void *x_bf16,
+                                           const float *router_logits, int32_t *topk_idx,
+                                           float *topk_w, void *y_bf16, void *saved, void *ws,
+                                           size_t ws_bytes, hipStream_t stream) {
+  MoePlan p;
+  e4b_status st = plan_moe(L, T, top_k, &p);
+  if (st != E4B_OK) return st;
+  st = check_lora(lora);
+  if (st != E4B_OK) return st;
+  int use_decode = 0;
+  st = check_forward(p, x_bf16, router_logits, topk_idx, topk_w, y_bf16, saved, ws, ws_bytes,
+                     E4B_PATH_GROUPED, &use_decode);
+  if (st != E4B_OK || T == 0) return st;
+  if (ws_bytes < p.lora_ws_bytes) return E4B_ERR_WORKSPACE;
+  char *w = static_cast<char *>(ws);
+  const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
+  const LoraWs l = lora_ws(p, w);
+  const float sc = lora_scale(lora);
+
+  if (router_logits)
+    E4B_TRY(launch_route(router_logits, T, int(p.E), top_k, topk_idx, topk_w, stream));
+  const PermView v = saved ? perm_in_saved(p, static_cast<char *>(saved)) : perm_in_workspace(p, w);
+  E4B_TRY(launch_permute(p, topk_idx, w, v, stream));
+  E4B_TRY(launch_lora_pack(lora->B_gu, p.E, int(2 * p.I), lora->r, sc, false, l.pk_bgu, stream));
+  E4B_TRY(launch_lora_pack(lora->B_dn, p.E, int(p.H), lora->r, sc, false, l.pk_bdn, stream));
+
+  uint16_t *a_buf = reinterpret_cast<uint16_t *>(w + p.off_a);
+  uint16_t *o_buf = reinterpret_cast<uint16_t *>(w + p.off_o);
+  E4B_TRY(lora_gate_up(p, L, lora, x, topk_idx, a_buf, static_cast<uint16_t *>(saved), v, l,
+                       stream));
+  E4B_TRY(launch_lora_project(LS_ROWS, a_buf, p.I, int(p.I), int(p.I), v.sorted, topk_idx,
+                              int(p.k), p.P, lora->A_dn, false, lora->r, l.aa, stream));
+  GemmArgs d = base_args(p, L->down, v);
+  d.A = a_buf;
+  d.lda = int32_t(p.I);
+  d.N = int32_t(p.H);
+  d.K = int32_t(p.I);
+  d.n_tiles = int32_t(p.n_tiles_h);
+  d.grid = uint32_t(p.m_tiles_bound * p.n_tiles_h);
+  d.C = o_buf;
+  d.ldc = int32_t(p.H);
+  d.lora_p = l.aa;
+  d.lora_w = l.pk_bdn;
+  d.lora_rows = int32_t(p.H);
+  E4B_TRY(launch_grouped_gemm(GEMM_DOWN_FWD, d, stream));
+  E4B_TRY(launch_combine_rows(o_buf, v.pos, topk_w, T, top_k, int(p.H),
+                              static_cast<uint16_t *>(y_bf16), stream));
+  return E4B_OK;
+}
+
+extern "C" e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lora *lora,
+                                            int64_t T, int32_t top_k, const int32_t *topk_idx,
+                                            const float *topk_w, const void *x_bf16,
+                                            const void *saved, const void *grad_y_bf16,
+                                            void *grad_x_bf16, float *grad_topk_w, float *dA_gu,
+                                            float *dB_gu, float *dA_dn, float *dB_dn, void *ws,
+                                            size_t ws_bytes, hipStream_t stream) {
+  MoePlan p;
+  e4b_status st = plan_moe(L, T, top_k, &p);
+  if (st != E4B_OK) return st;
+  st = check_lora(lora);
+  if (st != E4B_OK) return st;
+  st = check_dgrad(p, topk_idx, topk_w, x_bf16, saved, grad_y_bf16, grad_x_bf16, grad_topk_w, ws,
+                   ws_bytes);
+  if (st != E4B_OK || T == 0) return st;
+  if (!dA_gu || !dB_gu || !dA_dn || !dB_dn || !x_bf16) return E4B_ERR_NULL;
+  if (!aligned16(dA_gu) || !aligned16(dB_gu) || !aligned16(dA_dn) || !aligned16(dB_dn))
+    return E4B_ERR_ALIGN;
+  if (ws_bytes < p.lora_ws_bytes) return E4B_ERR_WORKSPACE;
+  char *w = static_cast<char *>(ws);
+  const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
+  const uint16_t *gy = static_cast<const uint16_t *>(grad_y_bf16);
+  const LoraWs l = lora_ws(p, w);
+  const float sc = lora_scale(lora);
+  const int r = lora->r;
+
+  const uint16_t *gu = static_cast<const uint16_t *>(saved);
+  PermView v;
+  if (saved) {
+    v = perm_in_saved(p, static_cast<char *>(const_cast<void *>(saved)));
+    // x A_gu^T for dB_gu (the forward's copy may have been overwritten)
+    E4B_TRY(launch_lora_project(LS_X_GATHER, x, p.H, int(p.H), int(p.I), v.sorted, topk_idx,
+                                int(p.k), p.P, lora->A_gu, false, r, l.xa, stream));
+  } else {
+    v = perm_in_workspace(p, w);
+    E4B_TRY(launch_permute(p, topk_idx, w, v, stream));
+    E4B_TRY(launch_lora_pack(lora->B_gu, p.E, int(2 * p.I), r, sc, false, l.pk_bgu, stream));
+    uint16_t *gu_ws = reinterpret_cast<uint16_t *>(w + p.off_gu);
+    E4B_TRY(lora_gate_up(p, L, lora, x, topk_idx, nullptr, gu_ws, v, l, stream));
+    gu = gu_ws;
+  }
+  E4B_TRY(launch_lora_pack(lora->A_dn, p.E, int(p.I), r, sc, true, l.pk_adn, stream));
+  E4B_TRY(launch_lora_pack(lora->A_gu, p.E, int(p.H), r, sc, true, l.pk_agu, stream));
+  uint16_t *dgu = reinterpret_cast<uint16_t *>(w + p.off_dgu);
+  float *partial = reinterpret_cast<float *>(w + p.off_partial);
+  uint16_t *gx = reinterpret_cast<uint16_t *>(w + p.off_gx);
+
+  // grad_y B_dn per pair, then the down dgrad GEMM with the s A_dn^T slice
+  E4B_TRY(launch_lora_project(LS_X_GATHER, gy, p.H, int(p.H), int(p.I), v.sorted, topk_idx,
+                              int(p.k), p.P, lora->B_dn, true, r, l.gb, stream));
+  GemmArgs d = base_args(p, L->down, v);
+  d.A = gy;
+  d.lda = int32_t(p.H);
+  d.N = int32_t(p.I);
+  d.K = int32_t(p.H);
+  d.n_tiles = int32_t(p.n_tiles_i);
+  d.grid = uint32_t(p.m_tiles_bound * p.n_tiles_i);
+  d.C = dgu;
+  d.ldc = int32_t(2 * p.I);
+  d.GU = const_cast<uint16_t *>(gu);
+  d.topk_w = topk_w;
+  d.partial = partial;
+  d.lora_p = l.gb;
+  d.lora_w = l.pk_adn;
+  d.lora_rows = int32_t(p.I);
+  E4B_TRY(launch_grouped_gemm(GEMM_DOWN_DGRAD, d, stream));
+
+  // dGU B_gu per pair, then the gate_up dgrad GEMM with the s A_gu^T slice
+  E4B_TRY(launch_lora_project(LS_ROWS, dgu, 2 * p.I, int(2 * p.I), int(p.I), v.sorted, topk_idx,
+                              int(p.k), p.P, lora->B_gu, true, r, l.hb, stream));
+  GemmArgs u = base_args(p, L->gate_up, v);
+  u.A = dgu;
+  u.lda = int32_t(2 * p.I);
+  u.N = int32_t(p.H);
+  u.K = int32_t(2 * p.I);
+  u.n_tiles = int32_t(p.n_tiles_h_gud);
+  u.grid = uint32_t(p.m_tiles_bound * p.n_tiles_h_gud);
+  u.C = gx;
+  u.ldc = int32_t(p.H);
+  u.lora_p = l.hb;
+  u.lora_w = l.pk_agu;
+  u.lora_rows = int32_t(p.H);
+  E4B_TRY(launch_grouped_gemm(GEMM_GATE_UP_DGRAD, u, stream));
+
+  E4B_TRY(launch_combine_rows(gx, v.pos, nullptr, T, top_k, int(p.H),
+                              static_cast<uint16_t *>(grad_x_bf16), stream));
+  if (grad_topk_w)
+    E4B_TRY(launch_combine_gradw(partial, int(p.n_tiles_i), v.pos, p.P, grad_topk_w, stream));
+
+  // adapter gradients: a A_dn^T from the saved / recomputed g|u, then the
+  // four per-expert outer-product sums
+  E4B_TRY(launch_lora_project(LS_GU_ACT, gu, 2 * p.I, int(p.I), int(p.I), v.sorted, topk_idx,
+                              int(p.k), p.P, lora->A_dn, false, r, l.aa, stream));
+  E4B_TRY(launch_lora_wgrad(LS_ROWS, dgu, 2 * p.I, int(2 * p.I), int(p.I), v.sorted, v.offsets,
+                            int(p.k), topk_w, p.E, l.xa, false, r, sc, false, dB_gu, stream));
+  E4B_TRY(launch_lora_wgrad(LS_X_GATHER, x, p.H, int(p.H), int(p.I), v.sorted, v.offsets, int(p.k),
+                            topk_w, p.E, l.hb, false, r, sc, true, dA_gu, stream));
+  E4B_TRY(launch_lora_wgrad(LS_WX_GATHER, gy, p.H, int(p.H), int(p.I), v.sorted, v.offsets,
+                            int(p.k), topk_w, p.E, l.aa, false, r, sc, false, dB_dn, stream));
+  E4B_TRY(launch_lora_wgrad(LS_GU_ACT, gu, 2 * p.I, int(p.I), int(p.I), v.sorted, v.offsets,
+                            int(p.k), topk_w, p.E, l.gb, true, r, sc, true, dA_dn, stream));
+  return E4B_OK;
+}
+
 // ---- benchmark event hooks ----
 namespace e4b {
 namespace {

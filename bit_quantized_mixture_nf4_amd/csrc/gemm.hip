@@ -288,6 +288,43 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
     }
   }
 
+  // ---- LoRA: one more 16-deep slice, pair side = the per-pair projection
+  // (fp32 [P, 16], rounded to bf16 here), weight side = the bf16 pack of the
+  // scaled adapter [E, rows, 16] at the weight row of each tile column ----
+  if (g.lora_p != nullptr && wave_active) {
+    const int kh = lane >> 5;
+    bf16x8 pf[2], wf[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = min(wm * 64 + i * 32 + (lane & 31), valid_rows - 1);
+      const float4 *src =
+          reinterpret_cast<const float4 *>(g.lora_p + int64_t(seg + row0 + r) * kLoraK + 8 * kh);
+      const float4 v0 = src[0], v1 = src[1];
+      const u32x4 q{pack_bf16x2(v0.x, v0.y), pack_bf16x2(v0.z, v0.w), pack_bf16x2(v1.x, v1.y),
+                    pack_bf16x2(v1.z, v1.w)};
+      pf[i] = __builtin_bit_cast(bf16x8, q);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = wn * 128 + j * 32 + (lane & 31);
+      int row;
+      if (BMODE == B_NT && EPI == EPI_SWIGLU) {
+        const int pair = nt * (kBN / 2) + wn * 64 + (j & 1) * 32 + (lane & 31);
+        row = pair < g.I ? pair + (j >= 2 ? g.I : 0) : 0;
+      } else {
+        row = nt * kBN + c;
+        row = row < g.N ? row : 0;
+      }
+      wf[j] = *reinterpret_cast<const bf16x8 *>(g.lora_w + (int64_t(e) * g.lora_rows + row) * kLoraK +
+                                                8 * kh);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], pf[i], acc[i][j], 0, 0, 0);
+  }
+
   // ---- epilogue ----
   // acc[i][j][4q + t]: tile row  = wm*64 + i*32 + lane%32,
   //                    tile col  = wn*128 + j*32 + 8q + 4*(lane/32) + t   (t = 0..3)

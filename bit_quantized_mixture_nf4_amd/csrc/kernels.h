@@ -40,6 +40,12 @@ struct GemmArgs {
   uint16_t *GU;  // gate_up fwd: out g|u [row, 2I] (may be null); down dgrad: in g|u
   const float *topk_w;
   float *partial;  // down dgrad: [P, n_tiles]
+  // LoRA slice (null: none): per-pair projection fp32 [P, kLoraK] in sorted
+  // order, and the bf16 pack of the scaled adapter [E, lora_rows, kLoraK]
+  // indexed by the weight row of each output column
+  const float *lora_p;
+  const uint16_t *lora_w;
+  int32_t lora_rows;
 };
 
 // Benchmark event hooks (e4b_set_kernel_timer): call before / after a launch.
@@ -70,6 +76,33 @@ hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s);
 
 hipError_t launch_combine_rows(const uint16_t *rows, const int32_t *pos_of_pair, const float *w,
                                int64_t T, int k, int H, uint16_t *out, hipStream_t s);
+
+// ---- LoRA (lora.hip) ----
+// out[e, n, :] = bf16(s * M[e, n, j]) for j < r, 0 up to kLoraK, where
+// M = B [E, N, r] (trans = false) or M[e, n, j] = A[e, j, n] for A [E, r, N].
+hipError_t launch_lora_pack(const float *M, int64_t E, int N, int r, float s, bool trans,
+                            uint16_t *out, hipStream_t st);
+
+// Source rows of a per-pair projection / of an adapter gradient.
+enum LoraSrc {
+  LS_X_GATHER = 0,  // src[token(sorted pair)]           (x or grad_y, [T, ld])
+  LS_ROWS = 1,      // src[sorted position]               (a or dGU, [P, ld])
+  LS_GU_ACT = 2,    // silu(g) * u from g|u [P, 2I] rows  (the activation a)
+  LS_WX_GATHER = 3  // topk_w[pair] * src[token(pair)]    (the weighted grad_y)
+};
+// out[s, j] = sum_k src(s)[k] M(e(s), k, j) (j < r, zero up to kLoraK), fp32
+// [P, kLoraK]; M = A [E, r, K] (m_is_b = false) or B [E, K, r] (true).
+hipError_t launch_lora_project(int src_mode, const uint16_t *src, int64_t ld, int K, int I,
+                               const int32_t *sorted, const int32_t *flat_idx, int topk,
+                               int64_t P, const float *M, bool m_is_b, int r, float *out,
+                               hipStream_t st);
+// Adapter gradient of expert e: G[n, j] = s * sum over e's sorted pairs of
+// U(pair)[n] * V(pair)[j] (* topk_w[pair] when v_weighted), written as
+// [E, N, r] (a B-shaped gradient) or [E, r, N] (A-shaped, out_trans).
+hipError_t launch_lora_wgrad(int u_mode, const uint16_t *src, int64_t ld, int N, int I,
+                             const int32_t *sorted, const int32_t *offsets, int topk,
+                             const float *topk_w, int64_t E, const float *V, bool v_weighted,
+                             int r, float s, bool out_trans, float *out, hipStream_t st);
 
 hipError_t launch_combine_gradw(const float *partial, int n_tiles, const int32_t *pos_of_pair,
                                 int64_t P, float *gw, hipStream_t s);

@@ -111,6 +111,16 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   p->off_gx = take(size_t(P) * H * 2);
   const size_t dgrad_end = off;
   p->ws_bytes = fwd_end > dgrad_end ? fwd_end : dgrad_end;
+  off = p->ws_bytes;
+  p->off_l_xa = take(size_t(P) * kLoraK * 4);
+  p->off_l_aa = take(size_t(P) * kLoraK * 4);
+  p->off_l_gb = take(size_t(P) * kLoraK * 4);
+  p->off_l_hb = take(size_t(P) * kLoraK * 4);
+  p->off_pk_bgu = take(size_t(E) * 2 * I * kLoraK * 2);
+  p->off_pk_bdn = take(size_t(E) * H * kLoraK * 2);
+  p->off_pk_agu = take(size_t(E) * H * kLoraK * 2);
+  p->off_pk_adn = take(size_t(E) * I * kLoraK * 2);
+  p->lora_ws_bytes = off;
   p->sv_tile_map = size_t(P) * 2 * I * 2;  // a multiple of 256: I % 64 == 0
   p->sv_tile_offsets = p->sv_tile_map + size_t(p->m_tiles_bound) * 16;
   p->sv_offsets = p->sv_tile_offsets + size_t(E + 1) * 4;
@@ -142,6 +152,15 @@ e4b_status check_forward(const MoePlan &p, const void *x, const float *logits,
     return E4B_ERR_ALIGN;
   if (logits && !aligned16(logits)) return E4B_ERR_ALIGN;
   if (saved && !aligned16(saved)) return E4B_ERR_ALIGN;
+  return E4B_OK;
+}
+
+e4b_status check_lora(const e4b_lora *lora) {
+  if (!lora || !lora->A_gu || !lora->B_gu || !lora->A_dn || !lora->B_dn) return E4B_ERR_NULL;
+  if (lora->r < 1 || lora->r > kLoraK) return E4B_ERR_SHAPE;
+  if (!aligned16(lora->A_gu) || !aligned16(lora->B_gu) || !aligned16(lora->A_dn) ||
+      !aligned16(lora->B_dn))
+    return E4B_ERR_ALIGN;
   return E4B_OK;
 }
 
@@ -183,6 +202,11 @@ extern "C" const char *e4b_status_string(e4b_status s) {
 extern "C" size_t e4b_moe_workspace_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k) {
   e4b::MoePlan p;
   return e4b::plan_moe(L, T, top_k, &p) == E4B_OK ? p.ws_bytes : 0;
+}
+
+extern "C" size_t e4b_moe_lora_workspace_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k) {
+  e4b::MoePlan p;
+  return e4b::plan_moe(L, T, top_k, &p) == E4B_OK ? p.lora_ws_bytes : 0;
 }
 
 extern "C" size_t e4b_moe_saved_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k) {

@@ -26,6 +26,7 @@ constexpr int kMaxTopK = 32;
 constexpr int kDecodeMaxT = 8;
 constexpr int kDecMaxPairs = kDecodeMaxT * kMaxTopK;
 constexpr int kDecodeMaxK = 4096;  // max(H, I) on the decode path
+constexpr int kLoraK = 16;         // LoRA rank slot: one 16-deep MFMA slice (r <= 16)
 
 struct MoePlan {
   int64_t E, H, I, T, k, P;
@@ -45,6 +46,12 @@ struct MoePlan {
   size_t off_dmap;                              // forward, decode path: work maps
   size_t off_gu, off_dgu, off_partial, off_gx;  // dgrad
   size_t ws_bytes;
+  // LoRA calls: after the base workspace, fp32 [P, kLoraK] per-pair
+  // projections (x A_gu^T, a A_dn^T, grad_y B_dn, dGU B_gu) and bf16
+  // [E, rows, kLoraK] operand packs (s B_gu, s B_dn, s A_gu^T, s A_dn^T)
+  size_t off_l_xa, off_l_aa, off_l_gb, off_l_hb;
+  size_t off_pk_bgu, off_pk_bdn, off_pk_agu, off_pk_adn;
+  size_t lora_ws_bytes;
   // saved buffer (dense): bf16 g|u [P, 2I], then the forward's permutation
   // (tile map, tile offsets, offsets, sorted pairs, pair positions)
   size_t sv_tile_map, sv_tile_offsets, sv_offsets, sv_sorted, sv_pos;
@@ -70,6 +77,9 @@ e4b_status check_forward(const MoePlan &p, const void *x, const float *logits,
                          const int32_t *idx, const float *w, const void *y,
                          const void *saved, const void *ws, size_t ws_bytes,
                          int32_t path, int *use_decode);
+// Validates a LoRA descriptor against the plan (pointers, alignment, 1 <= r <= kLoraK).
+e4b_status check_lora(const e4b_lora *lora);
+
 e4b_status check_dgrad(const MoePlan &p, const int32_t *idx, const float *w,
                        const void *x, const void *saved, const void *gy,
                        const void *gx, const float *gw, const void *ws,

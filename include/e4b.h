@@ -173,6 +173,55 @@ size_t e4b_moe_workspace_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k)
  * permutation (int32 arrays over experts, m-tiles and pairs); 0 when invalid. */
 size_t e4b_moe_saved_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k);
 
+/* Per-expert LoRA adapters over the frozen base (fp32 device buffers).
+ * [README] Quickstart: ExpertsLoRA(base, r=8, alpha=16) attaches trainable
+ * per-expert LoRA to a frozen 4-bit stack; only the adapters train. The
+ * adapter module is not printed on the pages; the usual LoRA form is used on
+ * both projections of every expert e, with scale s = alpha / r:
+ *   h = W_gu[e] x + s B_gu[e] (A_gu[e] x),  o = W_dn[e] a + s B_dn[e] (A_dn[e] a).
+ *   A_gu : [E, r, H]    B_gu : [E, 2I, r]  (rows follow the gate | up rows)
+ *   A_dn : [E, r, I]    B_dn : [E, H, r]
+ * 1 <= r <= 16. The low-rank term enters each grouped GEMM as one extra
+ * 16-deep MFMA slice (bf16 operands, fp32 accumulation). */
+typedef struct {
+  const float *A_gu, *B_gu, *A_dn, *B_dn;
+  int32_t r;
+  float alpha;
+} e4b_lora;
+
+/* Forward of e4b_moe_forward with LoRA adapters; always the grouped path
+ * (saved, when given, is filled exactly as by e4b_moe_forward).
+ * ws must hold e4b_moe_lora_workspace_bytes(). Errors as e4b_moe_forward,
+ * plus NULL / SHAPE for the adapter descriptor (r outside [1, 16]). */
+e4b_status e4b_moe_lora_forward(const e4b_moe_layer *L, const e4b_lora *lora, int64_t T,
+                                int32_t top_k, const void *x_bf16, const float *router_logits,
+                                int32_t *topk_idx, float *topk_w, void *y_bf16, void *saved,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward of e4b_moe_lora_forward with routing held fixed: the input
+ * gradient and grad_topk_w as e4b_moe_dgrad (the base stays frozen) plus the
+ * adapter gradients of sum(grad_y * y), per pair (t, j), G_o = topk_w grad_y_t:
+ *   grad_a = W_dn^T G_o + s A_dn^T (B_dn^T G_o)
+ *   dB_dn += s G_o (A_dn a)^T         dA_dn += s (B_dn^T G_o) a^T
+ *   grad_h = [dg ; du] from grad_a     grad_x_t += W_gu^T grad_h + s A_gu^T (B_gu^T grad_h)
+ *   dB_gu += s grad_h (A_gu x_t)^T     dA_gu += s (B_gu^T grad_h) x_t^T
+ *   x_bf16   : device bf16 [T, H], required (the adapter gradients use it)
+ *   saved    : as e4b_moe_dgrad (NULL recomputes the gate/up projections)
+ *   dA_gu, dB_gu, dA_dn, dB_dn : device fp32, adapter shapes (written, not
+ *              accumulated); each sum runs over an expert's pairs in sorted
+ *              order, so results are deterministic
+ * Errors as e4b_moe_dgrad, plus NULL / SHAPE for the adapters. */
+e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lora *lora, int64_t T,
+                                 int32_t top_k, const int32_t *topk_idx, const float *topk_w,
+                                 const void *x_bf16, const void *saved, const void *grad_y_bf16,
+                                 void *grad_x_bf16, float *grad_topk_w, float *dA_gu,
+                                 float *dB_gu, float *dA_dn, float *dB_dn, void *ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes of the two LoRA calls (the base workspace plus the
+ * adapters' per-pair projections and bf16 operand packs); 0 when invalid. */
+size_t e4b_moe_lora_workspace_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k);
+
 /* Kernels that e4b_set_kernel_timer can bracket with events. */
 typedef enum {
   E4B_K_GATE_UP_FWD = 0,   /* grouped gate_up GEMM + SiLU*up epilogue */

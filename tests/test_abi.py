@@ -138,3 +138,34 @@ def test_workspace_and_saved_sizes(E, H, I, k, T):
 def test_status_strings():
     for code in range(10):
         assert len(_lib.status_string(code)) > 0
+
+
+def _lora(r=8, a=FAKE):
+    return _lib.E4bLora(a, FAKE, FAKE, FAKE, r, 16.0)
+
+
+def test_lora_argument_errors():
+    L = _layer()
+    lib = e4b.load()
+    need = lib.e4b_moe_lora_workspace_bytes(ctypes.byref(L), 4, 2)
+    assert need > lib.e4b_moe_workspace_bytes(ctypes.byref(L), 4, 2)
+
+    def fwd(lo, ws_bytes=1 << 40, T=4, x=FAKE):
+        return lib.e4b_moe_lora_forward(ctypes.byref(L), lo, T, 2, x, None, FAKE, FAKE, FAKE,
+                                        None, FAKE, ws_bytes, None)
+
+    def bwd(lo, ws_bytes=1 << 40, T=4, x=FAKE, dA=FAKE):
+        return lib.e4b_moe_lora_backward(ctypes.byref(L), lo, T, 2, FAKE, FAKE, x, None, FAKE,
+                                         FAKE, FAKE, dA, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+
+    for call in (fwd, bwd):
+        assert call(None) == _lib.E4B_ERR_NULL
+        assert call(ctypes.byref(_lora(a=None))) == _lib.E4B_ERR_NULL
+        assert call(ctypes.byref(_lora(r=0))) == _lib.E4B_ERR_SHAPE
+        assert call(ctypes.byref(_lora(r=17))) == _lib.E4B_ERR_SHAPE
+        assert call(ctypes.byref(_lora(a=FAKE + 4))) == _lib.E4B_ERR_ALIGN
+        assert call(ctypes.byref(_lora()), ws_bytes=need - 1) == _lib.E4B_ERR_WORKSPACE
+        assert call(ctypes.byref(_lora()), T=0, x=None) == _lib.E4B_OK
+    assert bwd(ctypes.byref(_lora()), x=None) == _lib.E4B_ERR_NULL
+    assert bwd(ctypes.byref(_lora()), dA=None) == _lib.E4B_ERR_NULL
+    assert bwd(ctypes.byref(_lora()), dA=FAKE + 4) == _lib.E4B_ERR_ALIGN
