@@ -178,7 +178,8 @@ namespace {
 
 struct LoraWs {
   float *xa, *aa, *gb, *hb;
-  uint16_t *pk_bgu, *pk_bdn, *pk_agu, *pk_adn;
+  uint16_t *pk_bgu, *pk_bdn, *pk_agu, *pk_adn;  // GEMM slices: scaled, by output column
+  uint16_t *pj_agu, *pj_adn, *pj_bdn, *pj_bgu;  // projections: j-major
 };
 
 LoraWs lora_ws(const MoePlan &p, char *w) {
@@ -191,17 +192,21 @@ LoraWs lora_ws(const MoePlan &p, char *w) {
   l.pk_bdn = reinterpret_cast<uint16_t *>(w + p.off_pk_bdn);
   l.pk_agu = reinterpret_cast<uint16_t *>(w + p.off_pk_agu);
   l.pk_adn = reinterpret_cast<uint16_t *>(w + p.off_pk_adn);
+  l.pj_agu = reinterpret_cast<uint16_t *>(w + p.off_pj_agu);
+  l.pj_adn = reinterpret_cast<uint16_t *>(w + p.off_pj_adn);
+  l.pj_bdn = reinterpret_cast<uint16_t *>(w + p.off_pj_bdn);
+  l.pj_bgu = reinterpret_cast<uint16_t *>(w + p.off_pj_bgu);
   return l;
 }
 
 float lora_scale(const e4b_lora *lo) { return lo->alpha / float(lo->r); }
 
 // x A_gu^T per pair, then the gate_up GEMM with the s B_gu slice.
-hipError_t lora_gate_up(const MoePlan &p, const e4b_moe_layer *L, const e4b_lora *lo,
-                        const uint16_t *x, const int32_t *idx, uint16_t *a_out, uint16_t *gu_out,
-                        const PermView &v, const LoraWs &l, hipStream_t s) {
-  hipError_t err = launch_lora_project(LS_X_GATHER, x, p.H, int(p.H), int(p.I), v.sorted, idx,
-                                       int(p.k), p.P, lo->A_gu, false, lo->r, l.xa, s);
+hipError_t lora_gate_up(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
+                        uint16_t *a_out, uint16_t *gu_out, const PermView &v, const LoraWs &l,
+                        hipStream_t s) {
+  hipError_t err = launch_lora_project_mfma(LS_X_GATHER, x, p.H, int(p.H), int(p.I), v.sorted,
+                                            int(p.k), v, int(p.E), p.m_tiles_bound, l.pj_agu, l.xa, s);
   if (err != hipSuccess) return err;
   GemmArgs a = base_args(p, L->gate_up, v);
   a.A = x;
@@ -248,13 +253,14 @@ extern "C" e4b_status e4b_moe_lora_forward(const e4b_moe_layer *L, const e4b_lor
   E4B_TRY(launch_permute(p, topk_idx, w, v, stream));
   E4B_TRY(launch_lora_pack(lora->B_gu, p.E, int(2 * p.I), lora->r, sc, false, l.pk_bgu, stream));
   E4B_TRY(launch_lora_pack(lora->B_dn, p.E, int(p.H), lora->r, sc, false, l.pk_bdn, stream));
+  E4B_TRY(launch_lora_pack_jk(lora->A_gu, p.E, int(p.H), lora->r, false, l.pj_agu, stream));
+  E4B_TRY(launch_lora_pack_jk(lora->A_dn, p.E, int(p.I), lora->r, false, l.pj_adn, stream));
 
   uint16_t *a_buf = reinterpret_cast<uint16_t *>(w + p.off_a);
   uint16_t *o_buf = reinterpret_cast<uint16_t *>(w + p.off_o);
-  E4B_TRY(lora_gate_up(p, L, lora, x, topk_idx, a_buf, static_cast<uint16_t *>(saved), v, l,
-                       stream));
-  E4B_TRY(launch_lora_project(LS_ROWS, a_buf, p.I, int(p.I), int(p.I), v.sorted, topk_idx,
-                              int(p.k), p.P, lora->A_dn, false, lora->r, l.aa, stream));
+  E4B_TRY(lora_gate_up(p, L, x, a_buf, static_cast<uint16_t *>(saved), v, l, stream));
+  E4B_TRY(launch_lora_project_mfma(LS_ROWS, a_buf, p.I, int(p.I), int(p.I), v.sorted, int(p.k), v,
+                                   int(p.E), p.m_tiles_bound, l.pj_adn, l.aa, stream));
   GemmArgs d = base_args(p, L->down, v);
   d.A = a_buf;
   d.lda = int32_t(p.I);
@@ -300,18 +306,22 @@ extern "C" e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lo
   const int r = lora->r;
 
   const uint16_t *gu = static_cast<const uint16_t *>(saved);
+  E4B_TRY(launch_lora_pack_jk(lora->A_gu, p.E, int(p.H), r, false, l.pj_agu, stream));
+  E4B_TRY(launch_lora_pack_jk(lora->A_dn, p.E, int(p.I), r, false, l.pj_adn, stream));
+  E4B_TRY(launch_lora_pack_jk(lora->B_dn, p.E, int(p.H), r, true, l.pj_bdn, stream));
+  E4B_TRY(launch_lora_pack_jk(lora->B_gu, p.E, int(2 * p.I), r, true, l.pj_bgu, stream));
   PermView v;
   if (saved) {
     v = perm_in_saved(p, static_cast<char *>(const_cast<void *>(saved)));
     // x A_gu^T for dB_gu (the forward's copy may have been overwritten)
-    E4B_TRY(launch_lora_project(LS_X_GATHER, x, p.H, int(p.H), int(p.I), v.sorted, topk_idx,
-                                int(p.k), p.P, lora->A_gu, false, r, l.xa, stream));
+    E4B_TRY(launch_lora_project_mfma(LS_X_GATHER, x, p.H, int(p.H), int(p.I), v.sorted, int(p.k),
+                                     v, int(p.E), p.m_tiles_bound, l.pj_agu, l.xa, stream));
   } else {
     v = perm_in_workspace(p, w);
     E4B_TRY(launch_permute(p, topk_idx, w, v, stream));
     E4B_TRY(launch_lora_pack(lora->B_gu, p.E, int(2 * p.I), r, sc, false, l.pk_bgu, stream));
     uint16_t *gu_ws = reinterpret_cast<uint16_t *>(w + p.off_gu);
-    E4B_TRY(lora_gate_up(p, L, lora, x, topk_idx, nullptr, gu_ws, v, l, stream));
+    E4B_TRY(lora_gate_up(p, L, x, nullptr, gu_ws, v, l, stream));
     gu = gu_ws;
   }
   E4B_TRY(launch_lora_pack(lora->A_dn, p.E, int(p.I), r, sc, true, l.pk_adn, stream));
@@ -321,8 +331,8 @@ extern "C" e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lo
   uint16_t *gx = reinterpret_cast<uint16_t *>(w + p.off_gx);
 
   // grad_y B_dn per pair, then the down dgrad GEMM with the s A_dn^T slice
-  E4B_TRY(launch_lora_project(LS_X_GATHER, gy, p.H, int(p.H), int(p.I), v.sorted, topk_idx,
-                              int(p.k), p.P, lora->B_dn, true, r, l.gb, stream));
+  E4B_TRY(launch_lora_project_mfma(LS_X_GATHER, gy, p.H, int(p.H), int(p.I), v.sorted, int(p.k),
+                                   v, int(p.E), p.m_tiles_bound, l.pj_bdn, l.gb, stream));
   GemmArgs d = base_args(p, L->down, v);
   d.A = gy;
   d.lda = int32_t(p.H);
@@ -341,8 +351,8 @@ extern "C" e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lo
   E4B_TRY(launch_grouped_gemm(GEMM_DOWN_DGRAD, d, stream));
 
   // dGU B_gu per pair, then the gate_up dgrad GEMM with the s A_gu^T slice
-  E4B_TRY(launch_lora_project(LS_ROWS, dgu, 2 * p.I, int(2 * p.I), int(p.I), v.sorted, topk_idx,
-                              int(p.k), p.P, lora->B_gu, true, r, l.hb, stream));
+  E4B_TRY(launch_lora_project_mfma(LS_ROWS, dgu, 2 * p.I, int(2 * p.I), int(p.I), v.sorted,
+                                   int(p.k), v, int(p.E), p.m_tiles_bound, l.pj_bgu, l.hb, stream));
   GemmArgs u = base_args(p, L->gate_up, v);
   u.A = dgu;
   u.lda = int32_t(2 * p.I);
@@ -364,8 +374,8 @@ extern "C" e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lo
 
   // adapter gradients: a A_dn^T from the saved / recomputed g|u, then the
   // four per-expert outer-product sums
-  E4B_TRY(launch_lora_project(LS_GU_ACT, gu, 2 * p.I, int(p.I), int(p.I), v.sorted, topk_idx,
-                              int(p.k), p.P, lora->A_dn, false, r, l.aa, stream));
+  E4B_TRY(launch_lora_project_mfma(LS_GU_ACT, gu, 2 * p.I, int(p.I), int(p.I), v.sorted, int(p.k),
+                                   v, int(p.E), p.m_tiles_bound, l.pj_adn, l.aa, stream));
   E4B_TRY(launch_lora_wgrad(LS_ROWS, dgu, 2 * p.I, int(2 * p.I), int(p.I), v.sorted, v.offsets,
                             int(p.k), topk_w, p.E, l.xa, false, r, sc, false, dB_gu, stream));
   E4B_TRY(launch_lora_wgrad(LS_X_GATHER, x, p.H, int(p.H), int(p.I), v.sorted, v.offsets, int(p.k),

@@ -90,12 +90,17 @@ enum LoraSrc {
   LS_GU_ACT = 2,    // silu(g) * u from g|u [P, 2I] rows  (the activation a)
   LS_WX_GATHER = 3  // topk_w[pair] * src[token(pair)]    (the weighted grad_y)
 };
+// j-major bf16 pack [E, kLoraK, K] of an adapter for the MFMA projection.
+hipError_t launch_lora_pack_jk(const float *M, int64_t E, int K, int r, bool m_is_b,
+                               uint16_t *out, hipStream_t st);
 // out[s, j] = sum_k src(s)[k] M(e(s), k, j) (j < r, zero up to kLoraK), fp32
-// [P, kLoraK]; M = A [E, r, K] (m_is_b = false) or B [E, K, r] (true).
-hipError_t launch_lora_project(int src_mode, const uint16_t *src, int64_t ld, int K, int I,
-                               const int32_t *sorted, const int32_t *flat_idx, int topk,
-                               int64_t P, const float *M, bool m_is_b, int r, float *out,
-                               hipStream_t st);
+// [P, kLoraK], on MFMA over the m-tiles of the permutation (rows of a tile
+// share one expert); Mj is the j-major pack of the adapter (M = A [E, r, K]
+// or B [E, K, r] packed by launch_lora_pack_jk).
+hipError_t launch_lora_project_mfma(int src_mode, const uint16_t *src, int64_t ld, int K, int I,
+                                    const int32_t *sorted, int topk, const PermView &v, int E,
+                                    int64_t m_tiles_bound, const uint16_t *Mj, float *out,
+                                    hipStream_t st);
 // Adapter gradient of expert e: G[n, j] = s * sum over e's sorted pairs of
 // U(pair)[n] * V(pair)[j] (* topk_w[pair] when v_weighted), written as
 // [E, N, r] (a B-shaped gradient) or [E, r, N] (A-shaped, out_trans).

@@ -6,8 +6,8 @@
 //   h = W_gu x + s B_gu (A_gu x),   o = W_dn a + s B_dn (A_dn a),   s = alpha / r.
 // Here the low-rank products are split into
 //   * a per-pair projection onto the rank space (x A_gu^T, a A_dn^T and, in
-//     the backward, grad_y B_dn and dGU B_gu): one wavefront per routed pair,
-//     fp32, written as [P, 16] in sorted-pair order;
+//     the backward, grad_y B_dn and dGU B_gu) on MFMA over the m-tiles of
+//     the permutation, fp32, written as [P, 16] in sorted-pair order;
 //   * one extra 16-deep MFMA slice inside the grouped GEMM that already
 //     produces the projection (gemm.hip), against a bf16 pack of the scaled
 //     adapter laid out by output column;
@@ -46,76 +46,84 @@ __global__ __launch_bounds__(256) void lora_pack_kernel(const float *__restrict_
 
 __device__ __forceinline__ float silu_f(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
-// Eight consecutive source values of row `row` at column k0 (bf16 -> fp32).
+// j-major bf16 pack of an adapter for the projections: out[e, j, k] =
+// bf16(M(e, k, j)) for j < r, zero for r <= j < kLoraK, with M(e, k, j) =
+// A[e, j, k] (A [E, r, K]) or B[e, k, j] (B [E, K, r]). One thread per
+// (e, j, run of 8 k).
+template <bool MB>
+__global__ __launch_bounds__(256) void lora_pack_jk_kernel(const float *__restrict__ M, int64_t E,
+                                                           int K, int r, uint16_t *__restrict__ out) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per_e = int64_t(kLoraK) * (K / 8);
+  if (i >= E * per_e) return;
+  const int64_t e = i / per_e;
+  const int j = int((i % per_e) / (K / 8));
+  const int k0 = int(i % (K / 8)) * 8;
+  float v[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    float m = 0.0f;
+    if (j < r) m = MB ? M[(e * K + k0 + q) * r + j] : M[(e * r + j) * K + k0 + q];
+    v[q] = m;
+  }
+  *reinterpret_cast<u32x4 *>(out + (e * kLoraK + j) * K + k0) =
+      u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+            pack_bf16x2(v[6], v[7])};
+}
+
+// Per-pair projection as MFMA: one workgroup per m-tile (256 sorted rows of
+// one expert), each wave 64 rows as four 16-row groups, K in steps of 32 with
+// v_mfma_f32_16x16x32_bf16 (A = the source rows in bf16, B = the j-major
+// adapter pack [E, 16, K]); out[s, j] fp32 for the tile's valid rows.
 template <int SRC>
-__device__ __forceinline__ void lora_src8(const uint16_t *row, int k0, int I, float (&v)[8]) {
-  if (SRC == LS_GU_ACT) {
-    const u32x4 gq = *reinterpret_cast<const u32x4 *>(row + k0);
-    const u32x4 uq = *reinterpret_cast<const u32x4 *>(row + I + k0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[2 * q] = silu_f(bf16_lo(gq[q])) * bf16_lo(uq[q]);
-      v[2 * q + 1] = silu_f(bf16_hi(gq[q])) * bf16_hi(uq[q]);
-    }
-  } else {
-    const u32x4 q4 = *reinterpret_cast<const u32x4 *>(row + k0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      v[2 * q] = bf16_lo(q4[q]);
-      v[2 * q + 1] = bf16_hi(q4[q]);
-    }
-  }
-}
-
-__device__ __forceinline__ float wave_allsum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// One wavefront per sorted pair s; the 64 lanes split K in runs of 8.
-template <int SRC, bool MB>
-__global__ __launch_bounds__(256) void lora_project_kernel(
+__global__ __launch_bounds__(256) void lora_project_mfma_kernel(
     const uint16_t *__restrict__ src, int64_t ld, int K, int I, const int32_t *__restrict__ sorted,
-    const int32_t *__restrict__ flat_idx, int topk, int64_t P, const float *__restrict__ M, int r,
-    float *__restrict__ out) {
-  const int64_t s = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (s >= P) return;
-  const int p = sorted[s];
-  const int e = flat_idx[p];
-  const uint16_t *row = SRC == LS_X_GATHER ? src + int64_t(p / topk) * ld : src + s * ld;
-  float acc[kLoraK];
+    int topk, const int4 *__restrict__ tile_map, const int32_t *__restrict__ tile_offsets, int E,
+    const uint16_t *__restrict__ Mj, float *__restrict__ out) {
+  const int mt = blockIdx.x;
+  if (mt >= tile_offsets[E]) return;
+  const int4 tm = tile_map[mt];
+  const int e = tm.x, seg = tm.y, row0 = tm.z, valid = tm.w;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave * 64 >= valid) return;  // no barriers in this kernel
+  const int r16 = lane & 15, kb = (lane >> 4) * 8;
+  const uint16_t *rowp[4];
 #pragma unroll
-  for (int j = 0; j < kLoraK; ++j) acc[j] = 0.0f;
-  for (int k0 = lane * 8; k0 < K; k0 += 512) {
-    float xv[8];
-    lora_src8<SRC>(row, k0, I, xv);
+  for (int gi = 0; gi < 4; ++gi) {
+    const int srow = seg + row0 + min(wave * 64 + gi * 16 + r16, valid - 1);
+    rowp[gi] = (SRC == LS_X_GATHER ? src + int64_t(sorted[srow] / topk) * ld : src + srow * ld) + kb;
+  }
+  const uint16_t *mp = Mj + (int64_t(e) * kLoraK + r16) * K + kb;
+  f32x4 acc[4];
 #pragma unroll
-    for (int j = 0; j < kLoraK; ++j) {
-      if (j < r) {
-        float a = acc[j];
-        if (MB) {
-          const float *m = M + (int64_t(e) * K + k0) * r + j;
+  for (int gi = 0; gi < 4; ++gi) acc[gi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    const bf16x8 mb = *reinterpret_cast<const bf16x8 *>(mp + k0);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) a += xv[q] * m[q * r];
-        } else {
-          const float4 *m = reinterpret_cast<const float4 *>(M + (int64_t(e) * r + j) * K + k0);
-          const float4 m0 = m[0], m1 = m[1];
-          a += xv[0] * m0.x + xv[1] * m0.y + xv[2] * m0.z + xv[3] * m0.w;
-          a += xv[4] * m1.x + xv[5] * m1.y + xv[6] * m1.z + xv[7] * m1.w;
-        }
-        acc[j] = a;
+    for (int gi = 0; gi < 4; ++gi) {
+      u32x4 q;
+      if (SRC == LS_GU_ACT) {
+        const u32x4 gq = *reinterpret_cast<const u32x4 *>(rowp[gi] + k0);
+        const u32x4 uq = *reinterpret_cast<const u32x4 *>(rowp[gi] + I + k0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          q[t] = pack_bf16x2(silu_f(bf16_lo(gq[t])) * bf16_lo(uq[t]),
+                             silu_f(bf16_hi(gq[t])) * bf16_hi(uq[t]));
+      } else {
+        q = *reinterpret_cast<const u32x4 *>(rowp[gi] + k0);
       }
+      acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, q), mb, acc[gi],
+                                                        0, 0, 0);
     }
   }
-  float mine = 0.0f;
+  // D[row 4 * (lane / 16) + t][col lane % 16]
 #pragma unroll
-  for (int j = 0; j < kLoraK; ++j) {
-    const float t = j < r ? wave_allsum(acc[j]) : 0.0f;
-    mine = lane == j ? t : mine;
-  }
-  if (lane < kLoraK) out[s * kLoraK + lane] = mine;
+  for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int rr = wave * 64 + gi * 16 + 4 * (lane >> 4) + t;
+      if (rr < valid) out[int64_t(seg + row0 + rr) * kLoraK + r16] = acc[gi][t];
+    }
 }
 
 // Adapter gradient: grid (column blocks of 512, expert). Thread owns two
@@ -202,7 +210,7 @@ hipError_t launch_lora_pack(const float *M, int64_t E, int N, int r, float s, bo
                             uint16_t *out, hipStream_t st) {
   const int64_t EN = E * N;
   if (EN == 0) return hipSuccess;
-  const dim3 grid(uint32_t((EN + 255) / 256));
+  const dim3 grid{uint32_t((EN + 255) / 256)};
   if (trans)
     hipLaunchKernelGGL(lora_pack_kernel<true>, grid, dim3(256), 0, st, M, EN, N, r, s, out);
   else
@@ -210,25 +218,32 @@ hipError_t launch_lora_pack(const float *M, int64_t E, int N, int r, float s, bo
   return hipGetLastError();
 }
 
-hipError_t launch_lora_project(int src_mode, const uint16_t *src, int64_t ld, int K, int I,
-                               const int32_t *sorted, const int32_t *flat_idx, int topk,
-                               int64_t P, const float *M, bool m_is_b, int r, float *out,
-                               hipStream_t st) {
-  if (P == 0) return hipSuccess;
-  const dim3 grid(uint32_t((P + 3) / 4));
-#define E4B_LP(SM, MB)                                                                       \
-  hipLaunchKernelGGL((lora_project_kernel<SM, MB>), grid, dim3(256), 0, st, src, ld, K, I,  \
-                     sorted, flat_idx, topk, P, M, r, out)
-  if (src_mode == LS_X_GATHER) {
-    if (m_is_b) E4B_LP(LS_X_GATHER, true); else E4B_LP(LS_X_GATHER, false);
-  } else if (src_mode == LS_ROWS) {
-    if (m_is_b) E4B_LP(LS_ROWS, true); else E4B_LP(LS_ROWS, false);
-  } else if (src_mode == LS_GU_ACT) {
-    if (m_is_b) E4B_LP(LS_GU_ACT, true); else E4B_LP(LS_GU_ACT, false);
-  } else {
-    return hipErrorInvalidValue;
-  }
-#undef E4B_LP
+hipError_t launch_lora_pack_jk(const float *M, int64_t E, int K, int r, bool m_is_b,
+                               uint16_t *out, hipStream_t st) {
+  const int64_t n = E * kLoraK * (K / 8);
+  if (n == 0) return hipSuccess;
+  const dim3 grid{uint32_t((n + 255) / 256)};
+  if (m_is_b)
+    hipLaunchKernelGGL(lora_pack_jk_kernel<true>, grid, dim3(256), 0, st, M, E, K, r, out);
+  else
+    hipLaunchKernelGGL(lora_pack_jk_kernel<false>, grid, dim3(256), 0, st, M, E, K, r, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_project_mfma(int src_mode, const uint16_t *src, int64_t ld, int K, int I,
+                                    const int32_t *sorted, int topk, const PermView &v, int E,
+                                    int64_t m_tiles_bound, const uint16_t *Mj, float *out,
+                                    hipStream_t st) {
+  if (m_tiles_bound == 0) return hipSuccess;
+  const dim3 grid{uint32_t(m_tiles_bound)};
+#define E4B_LPM(SM)                                                                          \
+  hipLaunchKernelGGL((lora_project_mfma_kernel<SM>), grid, dim3(256), 0, st, src, ld, K, I,  \
+                     sorted, topk, v.tile_map, v.tile_offsets, E, Mj, out)
+  if (src_mode == LS_X_GATHER) E4B_LPM(LS_X_GATHER);
+  else if (src_mode == LS_ROWS) E4B_LPM(LS_ROWS);
+  else if (src_mode == LS_GU_ACT) E4B_LPM(LS_GU_ACT);
+  else return hipErrorInvalidValue;
+#undef E4B_LPM
   return hipGetLastError();
 }
 
@@ -237,7 +252,7 @@ hipError_t launch_lora_wgrad(int u_mode, const uint16_t *src, int64_t ld, int N,
                              const float *topk_w, int64_t E, const float *V, bool v_weighted,
                              int r, float s, bool out_trans, float *out, hipStream_t st) {
   if (E == 0 || N == 0) return hipSuccess;
-  const dim3 grid(uint32_t((N / 2 + 255) / 256), uint32_t(E));
+  const dim3 grid{uint32_t((N / 2 + 255) / 256), uint32_t(E)};
 #define E4B_LW(UM)                                                                             \
   hipLaunchKernelGGL((lora_wgrad_kernel<UM>), grid, dim3(256), 0, st, src, ld, N, I, sorted,   \
                      offsets, topk, topk_w, V, v_weighted, r, s, out_trans, out)

@@ -120,6 +120,10 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   p->off_pk_bdn = take(size_t(E) * H * kLoraK * 2);
   p->off_pk_agu = take(size_t(E) * H * kLoraK * 2);
   p->off_pk_adn = take(size_t(E) * I * kLoraK * 2);
+  p->off_pj_agu = take(size_t(E) * kLoraK * H * 2);
+  p->off_pj_adn = take(size_t(E) * kLoraK * I * 2);
+  p->off_pj_bdn = take(size_t(E) * kLoraK * H * 2);
+  p->off_pj_bgu = take(size_t(E) * kLoraK * 2 * I * 2);
   p->lora_ws_bytes = off;
   p->sv_tile_map = size_t(P) * 2 * I * 2;  // a multiple of 256: I % 64 == 0
   p->sv_tile_offsets = p->sv_tile_map + size_t(p->m_tiles_bound) * 16;

@@ -51,6 +51,8 @@ struct MoePlan {
   // [E, rows, kLoraK] operand packs (s B_gu, s B_dn, s A_gu^T, s A_dn^T)
   size_t off_l_xa, off_l_aa, off_l_gb, off_l_hb;
   size_t off_pk_bgu, off_pk_bdn, off_pk_agu, off_pk_adn;
+  // j-major bf16 [E, kLoraK, K] packs for the projections: A_gu, A_dn, B_dn^T, B_gu^T
+  size_t off_pj_agu, off_pj_adn, off_pj_bdn, off_pj_bgu;
   size_t lora_ws_bytes;
   // saved buffer (dense): bf16 g|u [P, 2I], then the forward's permutation
   // (tile map, tile offsets, offsets, sorted pairs, pair positions)
