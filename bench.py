@@ -14,9 +14,11 @@ Also measured in the same run:
 * the decode dequant-GEMV path on the Qwen3-30B-A3B-shaped layer (E=128,
   H=2048, I=768, top-8, Zipf routing) at T=1 and T=8, cold cache (16 layer
   copies rotated), as GB/s of the experts actually touched;
+* the same training step with per-expert LoRA adapters (r=8, alpha=16) over
+  the frozen base (`lora`);
 * the CPU oracle (numpy float64) on a bounded sample of the same workload.
 
-Prints ONE JSON line. `--gpus N` with N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line. `--gpus N` with N > 1 exits: the library runs on one GPU.
 """
 
 import argparse
@@ -114,6 +116,66 @@ def train_step_fn(e4b, torch, layer, x, lg, gy, k):
 
     keep = (idx, w, y, gx, gw, saved, ws, L)
     return step, keep
+
+
+def lora_step_fn(e4b, torch, layer, lora, x, lg, gy, k):
+    """Raw-ABI closures for one LoRA forward (saving g|u) + backward with preallocated buffers."""
+    lib = e4b.load()
+    T = x.shape[0]
+    dev = x.device
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    y = torch.empty(T, layer.H, dtype=torch.bfloat16, device=dev)
+    gx = torch.empty_like(y)
+    gw = torch.empty(T, k, dtype=torch.float32, device=dev)
+    grads = [torch.empty_like(t) for t in (lora.A_gu, lora.B_gu, lora.A_dn, lora.B_dn)]
+    saved = torch.empty(e4b.saved_bytes(layer, T, k), dtype=torch.uint8, device=dev)
+    ws = torch.empty(e4b.lora_workspace_bytes(layer, T, k), dtype=torch.uint8, device=dev)
+    L, LC = layer.as_c(), lora.as_c()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    fwd_args = (ctypes.byref(L), ctypes.byref(LC), T, k, vp(x), vp(lg), vp(idx), vp(w), vp(y),
+                vp(saved), vp(ws), ws.numel(), stream)
+    bwd_args = (ctypes.byref(L), ctypes.byref(LC), T, k, vp(idx), vp(w), vp(x), vp(saved), vp(gy),
+                vp(gx), vp(gw), *(vp(g) for g in grads), vp(ws), ws.numel(), stream)
+
+    def step():
+        s1 = lib.e4b_moe_lora_forward(*fwd_args)
+        s2 = lib.e4b_moe_lora_backward(*bwd_args)
+        if s1 or s2:
+            raise RuntimeError(f"e4b status {s1} {s2}")
+
+    keep = (idx, w, y, gx, gw, grads, saved, ws, L, LC)
+    return step, keep
+
+
+def bench_lora(args, e4b, torch, cfg, layer, x, lg, gy, base_dt):
+    """The same training step with per-expert LoRA adapters (r, alpha as on the pages)."""
+    from workloads import gen_lora
+
+    r, alpha = 8, 16.0
+    lora = e4b.Lora(*(torch.from_numpy(m).cuda() for m in gen_lora(cfg, args.seed, r)), alpha=alpha)
+    step, keep = lora_step_fn(e4b, torch, layer, lora, x, lg, gy, cfg.k)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    P, H, I = cfg.P, cfg.H, cfg.I
+    # base GEMM flops plus the low-rank products (forward, dgrad slices, projections, adapter grads)
+    lora_flops = 2.0 * P * r * (H + 2 * I + I + H) * 3
+    log(f"lora r={r}: step {dt * 1e3:.3f} ms ({dt / base_dt:.3f} x the frozen-base step)")
+    del keep
+    return {
+        "r": r, "alpha": alpha,
+        "ms_per_step": round(dt * 1e3, 4),
+        "tflops_base_flops": round(12.0 * P * H * I / dt / 1e12, 1),
+        "lora_flops_per_step": lora_flops,
+        "vs_frozen_base_step": round(dt / base_dt, 4),
+    }
 
 
 def time_kernels(e4b, torch, ev, step, names, n):
@@ -218,6 +280,7 @@ def bench_train(args, e4b, torch, ev):
         "traffic": measured_traffic(dom, "olmoe"),
     }
     res = dict(cfg=cfg, dt=dt, tflops=tflops, kernels=kernels, roofline=roofline)
+    res["lora"] = None if args.no_lora else bench_lora(args, e4b, torch, cfg, layer, x, lg, gy, dt)
     del keep, layer
     torch.cuda.empty_cache()
     return res
@@ -358,13 +421,14 @@ def main():
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-lora", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU layout is described in DESIGN.md but not built.", file=sys.stderr)
+              "no multi-GPU path is built.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -413,6 +477,7 @@ def main():
         "roofline": tr["roofline"],
         "kernels": tr["kernels"],
         "decode": dec,
+        "lora": tr["lora"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -12,7 +12,8 @@
 //     produces the projection (gemm.hip), against a bf16 pack of the scaled
 //     adapter laid out by output column;
 //   * the adapter gradients: per expert, a fixed-order sum over its pairs of
-//     outer products (no atomics; deterministic).
+//     outer products, on MFMA with the pairs as the reduction (no atomics;
+//     deterministic).
 #include "device.h"
 #include "kernels.h"
 
@@ -126,11 +127,16 @@ __global__ __launch_bounds__(256) void lora_project_mfma_kernel(
     }
 }
 
-// Adapter gradient: grid (column blocks of 512, expert). Thread owns two
-// columns n, n + 1; the expert's pairs are visited in sorted order in
-// batches of kWgBatch (their rank vectors staged in LDS, their source values
-// loaded together), so every sum has one fixed order.
-constexpr int kWgBatch = 32;
+// Adapter gradient on MFMA: G[n, j] = s * sum over expert e's sorted pairs p
+// of U(p)[n] V(p)[j]. Grid (column blocks of 64, expert); the four waves own
+// 16 columns each. The pairs are taken in chunks of 32 in sorted order: the
+// chunk's U rows (64 columns, bf16) and rank vectors (bf16) are written to
+// LDS transposed, so that one v_mfma_f32_16x16x32_bf16 per wave (A = U^T
+// [16 n x 32 p], B = V [32 p x 16 j]) consumes the chunk; the next chunk's
+// loads are in flight meanwhile. Every sum runs in one fixed order.
+constexpr int kWgCols = 64;
+constexpr int kWgChunk = 32;
+constexpr int kWgPad = kWgChunk + 8;  // LDS row of one column / rank: 32 pairs + pad (bf16)
 
 template <int U>
 __global__ __launch_bounds__(256) void lora_wgrad_kernel(
@@ -138,72 +144,81 @@ __global__ __launch_bounds__(256) void lora_wgrad_kernel(
     const int32_t *__restrict__ offsets, int topk, const float *__restrict__ topk_w,
     const float *__restrict__ V, bool v_weighted, int r, float sc, bool out_trans,
     float *__restrict__ out) {
-  __shared__ float sv[kWgBatch][kLoraK];
+  __shared__ __attribute__((aligned(16))) uint16_t su[kWgCols][kWgPad];  // U^T
+  __shared__ __attribute__((aligned(16))) uint16_t sv[kLoraK][kWgPad];   // V^T
   const int e = blockIdx.y;
-  const int n = (blockIdx.x * 256 + threadIdx.x) * 2;
+  const int n_base = blockIdx.x * kWgCols;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int s0 = offsets[e], s1 = offsets[e + 1];
-  const int nc = min(n, N - 2);  // clamped column pair (N is even); stores are guarded
-  float acc[2][kLoraK];
+  // staging roles: U: pair q = tid / 8 of the chunk, columns 8 * (tid % 8) ..;
+  // V: threads < 128, pair tid / 4, ranks 4 * (tid % 4) ..
+  const int uq = tid >> 3, un = (tid & 7) * 8;
+  const int ncol = min(n_base + un, N - 8);  // clamped (N % 8 == 0); results past N are not stored
+  const int vq = tid >> 2, vj = (tid & 3) * 4;
+  u32x4 ureg;
+  float vreg[4];
+  auto load = [&](int c0) {
+    const int s = min(c0 + uq, s1 - 1);
+    const bool live = c0 + uq < s1;
+    const int p = sorted[s];
+    const uint16_t *row = (U == LS_X_GATHER || U == LS_WX_GATHER) ? src + int64_t(p / topk) * ld
+                                                                  : src + int64_t(s) * ld;
+    u32x4 q = *reinterpret_cast<const u32x4 *>(row + ncol);
+    if (U == LS_GU_ACT) {
+      const u32x4 uu = *reinterpret_cast<const u32x4 *>(row + I + ncol);
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+      for (int t = 0; t < 4; ++t)
+        q[t] = pack_bf16x2(silu_f(bf16_lo(q[t])) * bf16_lo(uu[t]),
+                           silu_f(bf16_hi(q[t])) * bf16_hi(uu[t]));
+    } else if (U == LS_WX_GATHER) {
+      const float wp = topk_w[p];
 #pragma unroll
-    for (int j = 0; j < kLoraK; ++j) acc[c][j] = 0.0f;
-  for (int b = s0; b < s1; b += kWgBatch) {
-    const int nb = min(kWgBatch, s1 - b);
-    __syncthreads();  // previous batch's rank vectors consumed
-    for (int t = threadIdx.x; t < kWgBatch * kLoraK; t += 256) {
-      const int q = t / kLoraK, j = t % kLoraK;
-      float v = 0.0f;
-      if (q < nb) {
-        const int s = b + q;
-        v = V[int64_t(s) * kLoraK + j];
-        if (v_weighted) v *= topk_w[sorted[s]];
-      }
-      sv[q][j] = v;
+      for (int t = 0; t < 4; ++t) q[t] = pack_bf16x2(wp * bf16_lo(q[t]), wp * bf16_hi(q[t]));
+    }
+    ureg = live ? q : u32x4{0u, 0u, 0u, 0u};
+    if (tid < kWgChunk * 4) {
+      const int sv_ = min(c0 + vq, s1 - 1);
+      const bool vlive = c0 + vq < s1;
+      const float4 v4 = *reinterpret_cast<const float4 *>(V + int64_t(sv_) * kLoraK + vj);
+      const float w = v_weighted ? topk_w[sorted[sv_]] : 1.0f;
+      vreg[0] = vlive ? w * v4.x : 0.0f;
+      vreg[1] = vlive ? w * v4.y : 0.0f;
+      vreg[2] = vlive ? w * v4.z : 0.0f;
+      vreg[3] = vlive ? w * v4.w : 0.0f;
+    }
+  };
+  f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (s0 < s1) load(s0);
+  for (int c0 = s0; c0 < s1; c0 += kWgChunk) {
+    // stage the loaded chunk transposed
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      su[un + 2 * t][uq] = uint16_t(ureg[t] & 0xFFFFu);
+      su[un + 2 * t + 1][uq] = uint16_t(ureg[t] >> 16);
+    }
+    if (tid < kWgChunk * 4) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sv[vj + t][vq] = uint16_t(pack_bf16x2(vreg[t], 0.0f) & 0xFFFFu);
     }
     __syncthreads();
-    float u[kWgBatch][2];
-#pragma unroll
-    for (int q = 0; q < kWgBatch; ++q) {
-      const int s = b + min(q, nb - 1);
-      const int p = sorted[s];
-      const uint16_t *row = (U == LS_X_GATHER || U == LS_WX_GATHER) ? src + int64_t(p / topk) * ld
-                                                                    : src + int64_t(s) * ld;
-      const uint32_t w2 = *reinterpret_cast<const uint32_t *>(row + nc);
-      float u0 = bf16_lo(w2), u1 = bf16_hi(w2);
-      if (U == LS_GU_ACT) {
-        const uint32_t up = *reinterpret_cast<const uint32_t *>(row + I + nc);
-        u0 = silu_f(u0) * bf16_lo(up);
-        u1 = silu_f(u1) * bf16_hi(up);
-      }
-      if (U == LS_WX_GATHER) {
-        const float wp = topk_w[p];
-        u0 *= wp;
-        u1 *= wp;
-      }
-      const bool live = q < nb;
-      u[q][0] = live ? u0 : 0.0f;
-      u[q][1] = live ? u1 : 0.0f;
-    }
-#pragma unroll
-    for (int q = 0; q < kWgBatch; ++q)
-#pragma unroll
-      for (int j = 0; j < kLoraK; ++j) {
-        const float v = sv[q][j];
-        acc[0][j] += u[q][0] * v;
-        acc[1][j] += u[q][1] * v;
-      }
+    if (c0 + kWgChunk < s1) load(c0 + kWgChunk);
+    // A = U^T rows (columns n), B = V^T rows (ranks j): 8 consecutive pairs per lane
+    const bf16x8 af = *reinterpret_cast<const bf16x8 *>(&su[wave * 16 + (lane & 15)][8 * (lane >> 4)]);
+    const bf16x8 bf = *reinterpret_cast<const bf16x8 *>(&sv[lane & 15][8 * (lane >> 4)]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc, 0, 0, 0);
+    __syncthreads();
   }
-  if (n >= N) return;
+  // D[n = 4 * (lane / 16) + t][j = lane % 16] of the wave's 16 columns
+  const int j = lane & 15;
+  if (j >= r) return;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int j = 0; j < kLoraK; ++j)
-      if (j < r) {
-        const int64_t o = out_trans ? (int64_t(e) * r + j) * N + n + c
-                                    : (int64_t(e) * N + n + c) * r + j;
-        out[o] = sc * acc[c][j];
-      }
+  for (int t = 0; t < 4; ++t) {
+    const int n = n_base + wave * 16 + 4 * (lane >> 4) + t;
+    if (n < N) {
+      const int64_t o = out_trans ? (int64_t(e) * r + j) * N + n : (int64_t(e) * N + n) * r + j;
+      out[o] = sc * acc[t];
+    }
+  }
 }
 
 hipError_t launch_lora_pack(const float *M, int64_t E, int N, int r, float s, bool trans,
@@ -252,7 +267,7 @@ hipError_t launch_lora_wgrad(int u_mode, const uint16_t *src, int64_t ld, int N,
                              const float *topk_w, int64_t E, const float *V, bool v_weighted,
                              int r, float s, bool out_trans, float *out, hipStream_t st) {
   if (E == 0 || N == 0) return hipSuccess;
-  const dim3 grid{uint32_t((N / 2 + 255) / 256), uint32_t(E)};
+  const dim3 grid{uint32_t((N + kWgCols - 1) / kWgCols), uint32_t(E)};
 #define E4B_LW(UM)                                                                             \
   hipLaunchKernelGGL((lora_wgrad_kernel<UM>), grid, dim3(256), 0, st, src, ld, N, I, sorted,   \
                      offsets, topk, topk_w, V, v_weighted, r, s, out_trans, out)

@@ -9,7 +9,7 @@ and stores the packed stack as uint8 ``[E, out*in/2]`` and the scales as
 fp32 ``[E, out*in/blocksize]``; ``_dequantize_expert`` recovers one expert as
 code value times block absmax.
 
-Readings for what the pages leave open (each listed in the design doc):
+Readings for what the pages leave open:
 
 * absmax of a block is max |w| over its 64 consecutive row-major elements,
   stored exactly as fp32;

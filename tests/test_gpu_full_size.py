@@ -109,3 +109,62 @@ def test_decode_full_size(T):
     tol_check(to_np(y), y_ref, f"decode T={T} y")
     yg, _, _, _ = e4b.moe_forward(layer, bf16_tensor(x), cfg.k, topk_idx=idx, topk_w=w, path="grouped")
     tol_check(to_np(yg), y_ref, f"grouped T={T} y")
+
+
+def test_lora_full_size_olmoe_sampled():
+    """LoRA (r=8, alpha=16) on the OLMoE-shaped layer in the benchmark's
+    launch configuration: sampled tokens' y / grad_x / grad_topk_w, and one
+    sampled expert's four adapter gradients (the oracle runs all of that
+    expert's pairs)."""
+    from workloads import gen_lora
+
+    cfg = get_config("olmoe")
+    seed, r, alpha = 0, 8, 16.0
+    announce(f"olmoe lora full size E{cfg.E} H{cfg.H} I{cfg.I} k{cfg.k} T{cfg.T} r{r}")
+    layer = _layer(cfg, seed, "nf4")
+    host = gen_lora(cfg, seed, r)
+    lo = e4b.Lora(*(torch.from_numpy(m).to(DEV) for m in host), alpha=alpha)
+    x = gen_x(cfg, seed)
+    gy = gen_grad_y(cfg, seed)
+    lg = gen_logits(cfg, seed)
+    x_d, gy_d = bf16_tensor(x), bf16_tensor(gy)
+    ws = torch.empty(e4b.lora_workspace_bytes(layer, cfg.T, cfg.k), dtype=torch.uint8, device=DEV)
+    y, idx, w, saved = e4b.moe_lora_forward(layer, lo, x_d, cfg.k, logits=torch.from_numpy(lg).to(DEV),
+                                            save=True, workspace=ws)
+    y = y.clone()
+    gx, gw, grads = e4b.moe_lora_backward(layer, lo, idx, w, x_d, gy_d, saved=saved, workspace=ws)
+    gx2, gw2, grads2 = e4b.moe_lora_backward(layer, lo, idx, w, x_d, gy_d, workspace=ws)
+    torch.cuda.synchronize()
+    for a, b in zip((gx, gw) + grads, (gx2, gw2) + grads2):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+    idx_ref, w_ref = oracle.route(lg, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    rng = np.random.default_rng(321)
+    tokens = np.sort(rng.choice(cfg.T, size=4, replace=False))
+    e_star = int(idx_ref[tokens[0], 0])
+    experts = sorted(set(int(e) for e in idx_ref[tokens].ravel()) | {e_star})
+    announce(f"oracle weights for {len(experts)} experts")
+    st = oracle_expert_stacks(cfg, seed, experts, "nf4")
+    remap = {e: i for i, e in enumerate(experts)}
+    wgu = np.stack([st["gate_up"][e] for e in experts])
+    wdn = np.stack([st["down"][e] for e in experts])
+    ad = [m[experts] for m in host]
+    idx_c = np.vectorize(remap.get)(idx_ref[tokens]).astype(np.int32)
+    y_ref = oracle.lora_forward(x[tokens], idx_c, w_ref[tokens], wgu, wdn, *ad, alpha)
+    gx_ref, gw_ref, *_ = oracle.lora_backward(x[tokens], idx_c, w_ref[tokens], wgu, wdn, *ad, alpha,
+                                              gy[tokens])
+    t_d = torch.from_numpy(tokens).to(DEV)
+    tol_check(to_np(y[t_d]), y_ref, "olmoe lora y")
+    tol_check(to_np(gx[t_d]), gx_ref, "olmoe lora grad_x")
+    tol_check(to_np(gw[t_d]), gw_ref, "olmoe lora grad_topk_w")
+
+    # every pair of expert e_star: (token, slot) with idx == e_star, one slot per token
+    tt, jj = np.nonzero(idx_ref == e_star)
+    announce(f"oracle adapter gradients of expert {e_star} over {tt.size} pairs")
+    i1 = np.full((tt.size, 1), remap[e_star], np.int32)
+    ref = oracle.lora_backward(x[tt], i1, w_ref[tt, jj][:, None], wgu, wdn, *ad, alpha, gy[tt])[2:]
+    for name, got, want in zip(("dA_gu", "dB_gu", "dA_dn", "dB_dn"), grads, ref):
+        tol_check(to_np(got[e_star]), want[remap[e_star]], f"olmoe lora {name}[{e_star}]")
+    del layer, ws, saved
+    torch.cuda.empty_cache()
