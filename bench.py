@@ -15,7 +15,7 @@ Also measured in the same run:
   H=2048, I=768, top-8, Zipf routing) at T=1 and T=8, cold cache (16 layer
   copies rotated), as GB/s of the experts actually touched;
 * the same training step with per-expert LoRA adapters (r=8, alpha=16) over
-  the frozen base (`lora`);
+  the frozen base (`lora`), and on the bf16 passthrough lane (`bf16_lane`);
 * the CPU oracle (numpy float64) on a bounded sample of the same workload.
 
 Prints ONE JSON line. `--gpus N` with N > 1 exits: the library runs on one GPU.
@@ -178,6 +178,29 @@ def bench_lora(args, e4b, torch, cfg, layer, x, lg, gy, base_dt):
     }
 
 
+def bench_bf16_lane(args, e4b, torch, cfg, x, lg, gy, base_dt):
+    """The same training step on the bf16 passthrough lane (weights stored bf16,
+    no dequantization): the fidelity anchor, and the cost of the 4-bit decode."""
+    layer = build_layer(e4b, torch, cfg, args.seed, "bf16")[0]
+    step, keep = train_step_fn(e4b, torch, layer, x, lg, gy, cfg.k)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    tflops = 12.0 * cfg.P * cfg.H * cfg.I / dt / 1e12
+    log(f"bf16 lane: step {dt * 1e3:.3f} ms -> {tflops:.1f} TFLOP/s ({base_dt / dt:.3f} x the "
+        f"{args.codebook} step's speed)")
+    del keep, layer
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(dt * 1e3, 4), "tflops": round(tflops, 1),
+            "weight_bytes": 2 * cfg.E * 3 * cfg.H * cfg.I,
+            "nf4_step_over_bf16_step": round(base_dt / dt, 4)}
+
+
 def time_kernels(e4b, torch, ev, step, names, n):
     """Average duration (ms) of each named kernel over n steps, events on its launch stream."""
     lib = e4b.load()
@@ -282,6 +305,9 @@ def bench_train(args, e4b, torch, ev):
     res = dict(cfg=cfg, dt=dt, tflops=tflops, kernels=kernels, roofline=roofline)
     res["lora"] = None if args.no_lora else bench_lora(args, e4b, torch, cfg, layer, x, lg, gy, dt)
     del keep, layer
+    torch.cuda.empty_cache()
+    res["bf16_lane"] = None if args.no_bf16_lane else bench_bf16_lane(args, e4b, torch, cfg, x, lg,
+                                                                      gy, dt)
     torch.cuda.empty_cache()
     return res
 
@@ -422,6 +448,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-lora", action="store_true")
+    ap.add_argument("--no-bf16-lane", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -478,6 +505,7 @@ def main():
         "kernels": tr["kernels"],
         "decode": dec,
         "lora": tr["lora"],
+        "bf16_lane": tr["bf16_lane"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -21,7 +21,7 @@ import torch
 from . import _lib
 from ._lib import E4bLayer, E4bLora, E4bStack, E4bError, check, load  # noqa: F401
 
-CODEBOOKS = {"nf4": _lib.E4B_CB_NF4, "fp4": _lib.E4B_CB_FP4}
+CODEBOOKS = {"nf4": _lib.E4B_CB_NF4, "fp4": _lib.E4B_CB_FP4, "bf16": _lib.E4B_CB_BF16}
 PATHS = {"auto": _lib.E4B_PATH_AUTO, "grouped": _lib.E4B_PATH_GROUPED, "decode": _lib.E4B_PATH_DECODE}
 
 __all__ = [
@@ -66,10 +66,12 @@ def _need(t, name, dtype, device=None, shape=None):
 
 @dataclass
 class QuantStack:
-    """One quantized fused stack: packed codes + fp32 absmax of an [E, out, in] weight."""
+    """One stored fused stack of an [E, out, in] weight: packed 4-bit codes +
+    fp32 absmax, or (codebook "bf16", the passthrough lane) the bf16 weight as
+    bytes and no absmax."""
 
-    packed: torch.Tensor  # uint8 [E, out*in/2]
-    absmax: torch.Tensor  # float32 [E, out*in/64]
+    packed: torch.Tensor  # uint8 [E, out*in/2]; bf16 lane: uint8 [E, out*in*2]
+    absmax: torch.Tensor  # float32 [E, out*in/64]; bf16 lane: None
     E: int
     out: int
     inn: int
@@ -77,8 +79,8 @@ class QuantStack:
 
     def as_c(self):
         return E4bStack(
-            self.packed.data_ptr(), self.absmax.data_ptr(), self.E, self.out, self.inn, 64,
-            CODEBOOKS[self.codebook],
+            self.packed.data_ptr(), None if self.absmax is None else self.absmax.data_ptr(),
+            self.E, self.out, self.inn, 64, CODEBOOKS[self.codebook],
         )
 
     @property
@@ -114,15 +116,18 @@ class MoELayer:
 
 
 def quantize(w, codebook="nf4"):
-    """Blockwise (64) absmax 4-bit quantization of a float32 [E, out, in] device stack."""
+    """Blockwise (64) absmax 4-bit quantization of a float32 [E, out, in] device stack
+    (codebook "nf4" / "fp4"), or its bf16 passthrough storage (codebook "bf16")."""
     if w.dim() != 3:
         raise ValueError("w must be [E, out, in]")
     _need(w, "w", torch.float32)
     E, out, inn = w.shape
     if codebook not in CODEBOOKS:
         raise ValueError(f"codebook must be one of {sorted(CODEBOOKS)}")
-    packed = torch.empty(E, out * inn // 2, dtype=torch.uint8, device=w.device)
-    absmax = torch.empty(E, out * inn // 64, dtype=torch.float32, device=w.device)
+    bf16 = codebook == "bf16"
+    packed = torch.empty(E, out * inn * 2 if bf16 else out * inn // 2, dtype=torch.uint8,
+                         device=w.device)
+    absmax = None if bf16 else torch.empty(E, out * inn // 64, dtype=torch.float32, device=w.device)
     code = load().e4b_quantize_nf4(
         _vp(w), E, out, inn, 64, CODEBOOKS[codebook], _vp(packed), _vp(absmax), _stream(w)
     )

@@ -22,7 +22,7 @@ E4B_ERR_ALIGN = 7
 E4B_ERR_PATH = 8
 E4B_ERR_HIP = 9
 
-E4B_CB_NF4, E4B_CB_FP4 = 0, 1
+E4B_CB_NF4, E4B_CB_FP4, E4B_CB_BF16 = 0, 1, 2
 E4B_F32, E4B_BF16 = 0, 1
 E4B_PATH_AUTO, E4B_PATH_GROUPED, E4B_PATH_DECODE = 0, 1, 2
 

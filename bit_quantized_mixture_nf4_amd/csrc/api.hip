@@ -27,8 +27,9 @@ GemmArgs base_args(const MoePlan &p, const e4b_stack &st, const PermView &v) {
   a.topk = int32_t(p.k);
   a.Wp = st.packed;
   a.Wa = st.absmax;
-  a.w_e_bytes = st.out * st.in / 2;
-  a.w_e_blocks = st.out * st.in / kBlock;
+  const bool bf16 = st.codebook == E4B_CB_BF16;
+  a.w_e_bytes = bf16 ? st.out * st.in * 2 : st.out * st.in / 2;
+  a.w_e_blocks = bf16 ? 0 : st.out * st.in / kBlock;  // BF16: no absmax buffer
   a.w_in = int32_t(st.in);
   a.I = int32_t(p.I);
   a.offsets = v.offsets;

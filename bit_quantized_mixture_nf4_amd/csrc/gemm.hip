@@ -53,7 +53,8 @@ __device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rc
 // threads, two LDS stages (one workgroup per CU; the two waves of a SIMD run
 // the halves of a K-step in opposite order). WN = 1: 256 threads, one LDS
 // stage, two workgroups per CU hide each other's staging and epilogues.
-template <int AMODE, int BMODE, int EPI, int WN>
+// QB = 1: the bf16 passthrough lane (B is stored bf16 and staged as is).
+template <int AMODE, int BMODE, int EPI, int WN, int QB>
 __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel(GemmArgs g) {
   constexpr int kGemmWavesN = WN;
   constexpr int kThreads = 256 * WN;
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   if (mt >= n_mt) return;
   const int e = tm.x, seg = tm.y, row0 = tm.z, valid_rows = tm.w;
 
-  if (tid < 16) sCode[tid] = codebook_value(g.cb, tid);
+  if (!QB && tid < 16) sCode[tid] = codebook_value(g.cb, tid);
 
   // ---- A rows: column chunk (tid & 7) of rows (tid >> 3) + (kThreads / 8) i.
   // Rows past the segment read the last valid row: their outputs are never
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   // (their outputs are never stored) ----
   const uint8_t *wp = g.Wp + int64_t(e) * g.w_e_bytes;
   const float *wa = g.Wa + int64_t(e) * g.w_e_blocks;
-  const int row_bytes = g.w_in >> 1, row_blocks = g.w_in >> 6;
+  const int row_bytes = QB ? g.w_in * 2 : g.w_in >> 1, row_blocks = g.w_in >> 6;
   // B_NT: thread owns half (32 elements) of one tile column = one weight row
   const int b_c = tid >> 1, b_half = tid & 1;
   int b_row = 0;
@@ -112,13 +113,13 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
       b_row = b_row < g.N ? b_row : 0;
     }
   }
-  const uint8_t *b_src_nt = wp + int64_t(b_row) * row_bytes + b_half * 16;
+  const uint8_t *b_src_nt = wp + int64_t(b_row) * row_bytes + b_half * (QB ? 64 : 16);
   const float *b_am_nt = wa + int64_t(b_row) * row_blocks;
   // B_NN: thread owns a 4 (k) x 8 (n) patch: n group cg, k group kg (16)
   const int b_cg = tid >> 4, b_kg = tid & 15;
   int b_n = nt * kBN + b_cg * 8;
   b_n = b_n < g.N ? b_n : 0;
-  const uint8_t *b_src_nn = wp + int64_t(b_kg * 4) * row_bytes + (b_n >> 1);
+  const uint8_t *b_src_nn = wp + int64_t(b_kg * 4) * row_bytes + (QB ? b_n * 2 : b_n >> 1);
   const float *b_am_nn = wa + int64_t(b_kg * 4) * row_blocks + (b_n >> 6);
 
   u32x4 ra[kAPass];
@@ -126,12 +127,20 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   float ram;
   uint32_t rbn[4];
   float ramn[4];
+  u32x4 rbq[QB ? 4 : 1];  // bf16 lane: B_NT 32 elements of a row, B_NN 4 rows x 8 columns
 
   auto load = [&](int ks) {
 #pragma unroll
     for (int i = 0; i < kAPass; ++i)
       ra[i] = *reinterpret_cast<const u32x4 *>(g.A + a_off[i] + uint32_t(ks * kBK));
-    if (BMODE == B_NT) {
+    if (QB) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        rbq[d] = BMODE == B_NT
+                     ? *reinterpret_cast<const u32x4 *>(b_src_nt + ks * (kBK * 2) + d * 16)
+                     : *reinterpret_cast<const u32x4 *>(b_src_nn +
+                                                        (int64_t(ks) * kBK + d) * row_bytes);
+    } else if (BMODE == B_NT) {
       rb = *reinterpret_cast<const u32x4 *>(b_src_nt + ks * (kBK / 2));
       ram = b_am_nt[ks];
     } else {
@@ -151,7 +160,22 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
       *reinterpret_cast<u32x4 *>(a_dst + ((tid >> 3) + (kThreads / 8) * i) * kLds + a_cc * 8) =
           ra[i];
     uint16_t *b_dst = sB[buf];
-    if (BMODE == B_NT) {
+    if (QB) {
+      if (BMODE == B_NT) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          *reinterpret_cast<u32x4 *>(b_dst + b_c * kLds + b_half * 32 + d * 8) = rbq[d];
+      } else {
+        // column c of the 4 x 8 patch: the 16-bit halves of rows 0..3
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+          *reinterpret_cast<u32x2 *>(b_dst + (b_cg * 8 + c) * kLds + b_kg * 4) =
+              u32x2{__builtin_amdgcn_perm(rbq[1][c >> 1], rbq[0][c >> 1], sel),
+                    __builtin_amdgcn_perm(rbq[3][c >> 1], rbq[2][c >> 1], sel)};
+        }
+      }
+    } else if (BMODE == B_NT) {
       // all 32 codebook reads are issued before the first product; each
       // byte of hi4 / lo4 is the byte offset (4 * nibble) of a table entry
       float c[32];
@@ -459,24 +483,23 @@ hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s) 
   if (a.grid == 0) return hipSuccess;
   const dim3 grid(a.grid);
   timer_before(int(v), s);
+  const bool qb = a.cb == E4B_CB_BF16;
+#define E4B_GEMM(AM, BM, EP, WNV)                                                               \
+  do {                                                                                         \
+    if (qb)                                                                                    \
+      hipLaunchKernelGGL((grouped_gemm_kernel<AM, BM, EP, WNV, 1>), grid, dim3(256 * (WNV)), 0, \
+                         s, a);                                                                \
+    else                                                                                       \
+      hipLaunchKernelGGL((grouped_gemm_kernel<AM, BM, EP, WNV, 0>), grid, dim3(256 * (WNV)), 0, \
+                         s, a);                                                                \
+  } while (0)
   switch (v) {
-    case GEMM_GATE_UP_FWD:
-      hipLaunchKernelGGL((grouped_gemm_kernel<A_GATHER, B_NT, EPI_SWIGLU, kBNWide / 128>), grid,
-                         dim3(2 * kBNWide), 0, s, a);
-      break;
-    case GEMM_DOWN_FWD:
-      hipLaunchKernelGGL((grouped_gemm_kernel<A_DIRECT, B_NT, EPI_STORE, kBNWide / 128>), grid,
-                         dim3(2 * kBNWide), 0, s, a);
-      break;
-    case GEMM_DOWN_DGRAD:
-      hipLaunchKernelGGL((grouped_gemm_kernel<A_GATHER, B_NN, EPI_DSWIGLU, kBNWide / 128>), grid,
-                         dim3(2 * kBNWide), 0, s, a);
-      break;
-    case GEMM_GATE_UP_DGRAD:
-      hipLaunchKernelGGL((grouped_gemm_kernel<A_DIRECT, B_NN, EPI_STORE, kBNNarrow / 128>), grid,
-                         dim3(2 * kBNNarrow), 0, s, a);
-      break;
+    case GEMM_GATE_UP_FWD: E4B_GEMM(A_GATHER, B_NT, EPI_SWIGLU, kBNWide / 128); break;
+    case GEMM_DOWN_FWD: E4B_GEMM(A_DIRECT, B_NT, EPI_STORE, kBNWide / 128); break;
+    case GEMM_DOWN_DGRAD: E4B_GEMM(A_GATHER, B_NN, EPI_DSWIGLU, kBNWide / 128); break;
+    case GEMM_GATE_UP_DGRAD: E4B_GEMM(A_DIRECT, B_NN, EPI_STORE, kBNNarrow / 128); break;
   }
+#undef E4B_GEMM
   const hipError_t err = hipGetLastError();
   timer_after(int(v), s);
   return err;

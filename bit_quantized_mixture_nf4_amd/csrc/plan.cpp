@@ -20,24 +20,28 @@ int bits_for(int64_t n) {
 }  // namespace
 
 e4b_status check_stack(const e4b_stack *st) {
-  if (!st || !st->packed || !st->absmax) return E4B_ERR_NULL;
+  if (!st || !st->packed) return E4B_ERR_NULL;
   if (st->blocksize != kBlock) return E4B_ERR_BLOCKSIZE;
-  if (st->codebook != E4B_CB_NF4 && st->codebook != E4B_CB_FP4) return E4B_ERR_CODEBOOK;
+  if (st->codebook != E4B_CB_NF4 && st->codebook != E4B_CB_FP4 && st->codebook != E4B_CB_BF16)
+    return E4B_ERR_CODEBOOK;
+  const bool bf16 = st->codebook == E4B_CB_BF16;
+  if (!bf16 && !st->absmax) return E4B_ERR_NULL;
   if (st->E <= 0 || st->out <= 0 || st->in <= 0 || st->in % kBlock != 0) return E4B_ERR_SHAPE;
   if (st->out * st->in > kMaxElems32 * 2) return E4B_ERR_SHAPE;
-  if (!aligned16(st->packed) || !aligned16(st->absmax)) return E4B_ERR_ALIGN;
+  if (!aligned16(st->packed) || (!bf16 && !aligned16(st->absmax))) return E4B_ERR_ALIGN;
   return E4B_OK;
 }
 
 e4b_status check_quantize(const float *w, int64_t E, int64_t out, int64_t in,
                           int32_t blocksize, int32_t codebook, const uint8_t *packed,
                           const float *absmax) {
-  if (!w || !packed || !absmax) return E4B_ERR_NULL;
+  const bool bf16 = codebook == E4B_CB_BF16;
+  if (!w || !packed || (!bf16 && !absmax)) return E4B_ERR_NULL;
   if (blocksize != kBlock) return E4B_ERR_BLOCKSIZE;
-  if (codebook != E4B_CB_NF4 && codebook != E4B_CB_FP4) return E4B_ERR_CODEBOOK;
+  if (codebook != E4B_CB_NF4 && codebook != E4B_CB_FP4 && !bf16) return E4B_ERR_CODEBOOK;
   if (E <= 0 || out <= 0 || in <= 0 || in % kBlock != 0) return E4B_ERR_SHAPE;
   if (out * in > kMaxElems32 * 2) return E4B_ERR_SHAPE;
-  if (!aligned16(w) || !aligned16(packed) || !aligned16(absmax)) return E4B_ERR_ALIGN;
+  if (!aligned16(w) || !aligned16(packed) || (!bf16 && !aligned16(absmax))) return E4B_ERR_ALIGN;
   return E4B_OK;
 }
 
@@ -136,7 +140,8 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
 
 bool decode_fits(const MoePlan &p) {
   const int64_t kmax = p.H > p.I ? p.H : p.I;
-  return p.T <= kDecodeMaxT && p.P <= kDecMaxPairs && kmax <= kDecodeMaxK;
+  return p.codebook != E4B_CB_BF16 && p.T <= kDecodeMaxT && p.P <= kDecMaxPairs &&
+         kmax <= kDecodeMaxK;
 }
 
 e4b_status check_forward(const MoePlan &p, const void *x, const float *logits,
@@ -197,7 +202,7 @@ extern "C" const char *e4b_status_string(e4b_status s) {
     case E4B_ERR_DTYPE: return "unknown output dtype";
     case E4B_ERR_WORKSPACE: return "workspace missing or too small";
     case E4B_ERR_ALIGN: return "device buffer not 16-byte aligned";
-    case E4B_ERR_PATH: return "invalid path (decode path needs T <= 8, saved == NULL and max(H, I) <= 4096)";
+    case E4B_ERR_PATH: return "invalid path (decode path needs a 4-bit layer, T <= 8, saved == NULL and max(H, I) <= 4096)";
     case E4B_ERR_HIP: return "HIP kernel launch failed";
   }
   return "unknown status";

@@ -1,4 +1,5 @@
-// quant.hip -- blockwise absmax 4-bit quantize / dequantize of a fused stack.
+// quant.hip -- blockwise absmax 4-bit quantize / dequantize of a fused stack,
+// and the bf16 passthrough lane (round to nearest even / widen).
 //
 // experts4bit-qlora 0.1.0 sdist, _vendor/experts.py: Experts4bit quantizes
 // each expert of an [E, out, in] stack on its own with blocksize 64 and
@@ -83,6 +84,35 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t *__restr
   }
 }
 
+// BF16 passthrough lane: one thread per 8 elements, round to nearest even.
+__global__ __launch_bounds__(256) void quantize_bf16_kernel(const float *__restrict__ w,
+                                                            int64_t ngroups,
+                                                            uint16_t *__restrict__ out) {
+  const int64_t g = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (g >= ngroups) return;
+  const f32x4 *src = reinterpret_cast<const f32x4 *>(w) + 2 * g;
+  const f32x4 a = src[0], b = src[1];
+  reinterpret_cast<u32x4 *>(out)[g] = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                            pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+}
+
+// BF16 stack -> fp32 (exact) or bf16 (copy); one thread per 8 elements.
+template <bool BF16>
+__global__ __launch_bounds__(256) void dequantize_bf16_kernel(const u32x4 *__restrict__ in,
+                                                              int64_t ngroups,
+                                                              void *__restrict__ out) {
+  const int64_t g = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (g >= ngroups) return;
+  const u32x4 q = in[g];
+  if (BF16) {
+    reinterpret_cast<u32x4 *>(out)[g] = q;
+  } else {
+    f32x4 *o = reinterpret_cast<f32x4 *>(out) + 2 * g;
+    o[0] = f32x4{bf16_lo(q[0]), bf16_hi(q[0]), bf16_lo(q[1]), bf16_hi(q[1])};
+    o[1] = f32x4{bf16_lo(q[2]), bf16_hi(q[2]), bf16_lo(q[3]), bf16_hi(q[3])};
+  }
+}
+
 }  // namespace e4b
 
 using namespace e4b;
@@ -92,6 +122,12 @@ extern "C" e4b_status e4b_quantize_nf4(const float *w, int64_t E, int64_t out, i
                                        float *absmax, hipStream_t stream) {
   e4b_status s = check_quantize(w, E, out, in, blocksize, codebook, packed, absmax);
   if (s != E4B_OK) return s;
+  if (codebook == E4B_CB_BF16) {
+    const int64_t ngroups = E * out * in / 8;
+    hipLaunchKernelGGL(quantize_bf16_kernel, dim3(uint32_t((ngroups + 255) / 256)), dim3(256), 0,
+                       stream, w, ngroups, reinterpret_cast<uint16_t *>(packed));
+    return hipGetLastError() == hipSuccess ? E4B_OK : E4B_ERR_HIP;
+  }
   const int64_t nblocks = E * out * in / kBlock;
   const int64_t grid = (nblocks + 3) / 4;
   hipLaunchKernelGGL(quantize_kernel, dim3(uint32_t(grid)), dim3(256), 0, stream, w, nblocks,
@@ -108,6 +144,16 @@ extern "C" e4b_status e4b_dequantize_nf4(const e4b_stack *st, int32_t dtype, voi
   if (!aligned16(w_out)) return E4B_ERR_ALIGN;
   const int64_t ngroups = st->E * st->out * st->in / 8;
   const int64_t grid = (ngroups + 255) / 256;
+  if (st->codebook == E4B_CB_BF16) {
+    const u32x4 *in = reinterpret_cast<const u32x4 *>(st->packed);
+    if (dtype == E4B_BF16)
+      hipLaunchKernelGGL(dequantize_bf16_kernel<true>, dim3(uint32_t(grid)), dim3(256), 0, stream,
+                         in, ngroups, w_out);
+    else
+      hipLaunchKernelGGL(dequantize_bf16_kernel<false>, dim3(uint32_t(grid)), dim3(256), 0, stream,
+                         in, ngroups, w_out);
+    return hipGetLastError() == hipSuccess ? E4B_OK : E4B_ERR_HIP;
+  }
   const uint32_t *pk = reinterpret_cast<const uint32_t *>(st->packed);
   if (dtype == E4B_BF16)
     hipLaunchKernelGGL(dequantize_kernel<true>, dim3(uint32_t(grid)), dim3(256), 0, stream, pk,

@@ -58,14 +58,19 @@ typedef enum {
   E4B_ERR_DTYPE = 5,     /* unknown output dtype */
   E4B_ERR_WORKSPACE = 6, /* workspace NULL or smaller than e4b_moe_workspace_bytes() */
   E4B_ERR_ALIGN = 7,     /* a device buffer is not 16-byte aligned */
-  E4B_ERR_PATH = 8,      /* unknown path, or the decode path was asked for but does not apply (T > 8, saved != NULL, or max(H, I) above 4096) */
+  E4B_ERR_PATH = 8,      /* unknown path, or the decode path was asked for but does not apply (a BF16 layer, T > 8, saved != NULL, or max(H, I) above 4096) */
   E4B_ERR_HIP = 9        /* a kernel launch failed (hipGetLastError after the launch) */
 } e4b_status;
 
-/* The 16-entry codebooks ([sdist] Experts4bit.__init__ quant_type "nf4"/"fp4"):
- * NF4 = the NormalFloat-4 table of the QLoRA paper (arXiv:2305.14314);
- * FP4 = e2m1 (sign bit 3, magnitudes {0,.5,1,1.5,2,3,4,6}/6). */
-typedef enum { E4B_CB_NF4 = 0, E4B_CB_FP4 = 1 } e4b_codebook;
+/* Storage modes. The 16-entry codebooks ([sdist] Experts4bit.__init__
+ * quant_type "nf4"/"fp4"): NF4 = the NormalFloat-4 table of the QLoRA paper
+ * (arXiv:2305.14314); FP4 = e2m1 (sign bit 3, magnitudes {0,.5,1,1.5,2,3,4,6}/6).
+ * BF16 = the 16-bit passthrough lane of the [README] support matrix (the
+ * reference baseline, no absmax buffer): `packed` holds the bf16 weight
+ * [E, out*in] (two bytes per element, round-to-nearest-even of the fp32
+ * weight), `absmax` is unused and may be NULL. A BF16 layer runs the grouped
+ * path only (the decode GEMV reads 4-bit codes). */
+typedef enum { E4B_CB_NF4 = 0, E4B_CB_FP4 = 1, E4B_CB_BF16 = 2 } e4b_codebook;
 
 typedef enum { E4B_F32 = 0, E4B_BF16 = 1 } e4b_dtype;
 
@@ -75,8 +80,8 @@ typedef enum { E4B_PATH_AUTO = 0, E4B_PATH_GROUPED = 1, E4B_PATH_DECODE = 2 } e4
 
 /* One quantized stack (device pointers; the struct itself is host memory). */
 typedef struct {
-  const uint8_t *packed; /* [E, out*in/2] */
-  const float *absmax;   /* [E, out*in/64] */
+  const uint8_t *packed; /* [E, out*in/2]; BF16: [E, out*in] bf16 */
+  const float *absmax;   /* [E, out*in/64]; BF16: unused */
   int64_t E, out, in;
   int32_t blocksize; /* must be 64 */
   int32_t codebook;  /* e4b_codebook */
@@ -98,6 +103,8 @@ typedef struct {
  *   w      : device fp32 [E, out, in], finite (unchecked)
  *   packed : device uint8 [E, out*in/2]   (written)
  *   absmax : device fp32  [E, out*in/64]  (written)
+ * codebook E4B_CB_BF16 writes the bf16 rounding (nearest even) of w to
+ * `packed` ([E, out*in] bf16) and leaves `absmax` (may be NULL) untouched.
  * Errors: NULL, SHAPE (E/out/in <= 0, in % 64 != 0), BLOCKSIZE, CODEBOOK,
  * ALIGN, HIP. */
 e4b_status e4b_quantize_nf4(const float *w, int64_t E, int64_t out, int64_t in,
@@ -106,7 +113,8 @@ e4b_status e4b_quantize_nf4(const float *w, int64_t E, int64_t out, int64_t in,
 
 /* Dequantize a whole stack: w_out[e, r, c] = fl32(code * absmax) (one fp32
  * rounding of the exact product), or its round-to-nearest-even bf16 when
- * dtype == E4B_BF16. [sdist] Experts4bit._dequantize_expert.
+ * dtype == E4B_BF16. [sdist] Experts4bit._dequantize_expert. A BF16 stack
+ * gives its stored values (exact in fp32). 
  *   st    : host descriptor of device buffers
  *   w_out : device [E, out, in] fp32 or bf16 (written)
  * Errors: NULL, SHAPE, BLOCKSIZE, CODEBOOK, DTYPE, ALIGN, HIP. */

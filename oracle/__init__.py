@@ -42,6 +42,7 @@ from .quant import (  # noqa: F401
     bf16_rne_bits,
     bf16_bits_to_f32,
     unpack_codes,
+    stored_weights,
 )
 from .moe import route, permute, moe_forward, moe_dgrad, silu  # noqa: F401
 from .fidelity import rel_fro, reconstruction_errors  # noqa: F401

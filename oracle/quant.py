@@ -138,3 +138,19 @@ def bf16_bits_to_f32(bits):
     """float32 values of bf16 bit patterns."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return b.view(np.float32)
+
+
+def stored_weights(w, kind):
+    """fp32 values that a stack stored in mode ``kind`` represents.
+
+    ``nf4`` / ``fp4``: blockwise quantize then dequantize (above). ``bf16``:
+    the 16-bit passthrough lane of the 0.4.0 README's support matrix (the
+    reference baseline, no absmax): each weight rounded to bf16, nearest
+    even.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    if kind == "bf16":
+        return bf16_bits_to_f32(bf16_rne_bits(w))
+    E, out, inn = w.shape
+    packed, absmax = quantize_blockwise(w, kind)
+    return dequantize(packed, absmax, out, inn, kind)

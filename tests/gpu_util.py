@@ -55,14 +55,11 @@ class Problem:
         self._deq = None
 
     def oracle_weights(self, experts=None):
-        """fp32 dequantized stacks from the oracle's own quantization."""
+        """fp32 stored stacks from the oracle's own quantization (or bf16 rounding)."""
         if self._deq is None:
-            cfg = self.cfg
-            pg, ag = oracle.quantize_blockwise(self.w_gu, self.codebook)
-            pd, ad = oracle.quantize_blockwise(self.w_dn, self.codebook)
             self._deq = (
-                oracle.dequantize(pg, ag, 2 * cfg.I, cfg.H, self.codebook),
-                oracle.dequantize(pd, ad, cfg.H, cfg.I, self.codebook),
+                oracle.stored_weights(self.w_gu, self.codebook),
+                oracle.stored_weights(self.w_dn, self.codebook),
             )
         return self._deq
 
@@ -89,8 +86,7 @@ def oracle_expert_stacks(cfg, seed, experts, kind="nf4", threads=16):
 
     def one(job):
         w, dst, r0, r1 = job
-        p, a = oracle.quantize_blockwise(w[None, r0:r1], kind)
-        dst[r0:r1] = oracle.dequantize(p, a, r1 - r0, w.shape[1], kind)[0]
+        dst[r0:r1] = oracle.stored_weights(w[None, r0:r1], kind)[0]
 
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(one, jobs))

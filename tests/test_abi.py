@@ -55,7 +55,10 @@ def test_quantize_validation():
     assert q(FAKE, 1, 64, 96, 64, 0, FAKE, FAKE, None) == _lib.E4B_ERR_SHAPE
     assert q(FAKE, 0, 64, 64, 64, 0, FAKE, FAKE, None) == _lib.E4B_ERR_SHAPE
     assert q(FAKE, 1, 64, 64, 128, 0, FAKE, FAKE, None) == _lib.E4B_ERR_BLOCKSIZE
-    assert q(FAKE, 1, 64, 64, 64, 2, FAKE, FAKE, None) == _lib.E4B_ERR_CODEBOOK
+    assert q(FAKE, 1, 64, 64, 64, 3, FAKE, FAKE, None) == _lib.E4B_ERR_CODEBOOK
+    # the bf16 lane needs no absmax buffer: NULL passes the pointer check and
+    # the call stops at the next check (nothing is launched)
+    assert q(FAKE, 1, 64, 64, 128, 2, FAKE, None, None) == _lib.E4B_ERR_BLOCKSIZE
     assert q(FAKE + 4, 1, 64, 64, 64, 0, FAKE, FAKE, None) == _lib.E4B_ERR_ALIGN
 
 
@@ -169,3 +172,16 @@ def test_lora_argument_errors():
     assert bwd(ctypes.byref(_lora()), x=None) == _lib.E4B_ERR_NULL
     assert bwd(ctypes.byref(_lora()), dA=None) == _lib.E4B_ERR_NULL
     assert bwd(ctypes.byref(_lora()), dA=FAKE + 4) == _lib.E4B_ERR_ALIGN
+
+
+def test_bf16_lane_validation():
+    bf = _lib.E4bLayer(_stack(4, 128, 64, absmax=None, cb=2), _stack(4, 64, 64, absmax=None, cb=2))
+    # absmax may be NULL; the layer gets as far as the workspace check
+    assert _fwd(bf, ws_bytes=0) == _lib.E4B_ERR_WORKSPACE
+    # the decode GEMV reads 4-bit codes: a bf16 layer takes the grouped path only
+    assert _fwd(bf, T=4, path=2) == _lib.E4B_ERR_PATH
+    # a 4-bit stack still needs its absmax
+    nf = _lib.E4bLayer(_stack(4, 128, 64, absmax=None), _stack(4, 64, 64))
+    assert _fwd(nf) == _lib.E4B_ERR_NULL
+    mixed = _lib.E4bLayer(_stack(4, 128, 64, cb=2), _stack(4, 64, 64, cb=0))
+    assert _fwd(mixed) == _lib.E4B_ERR_CODEBOOK

@@ -46,7 +46,8 @@ def _sampled_oracle(cfg, seed, kind, x, gy, idx_ref, w_ref, tokens):
 
 
 @pytest.mark.parametrize("name,kind,ntok", [("olmoe", "nf4", 6), ("qwen3_prefill", "nf4", 6),
-                                            ("mixtral", "fp4", 24), ("mixtral", "nf4", 24)])
+                                            ("mixtral", "fp4", 24), ("mixtral", "nf4", 24),
+                                            ("olmoe", "bf16", 6)])
 def test_full_size_forward_dgrad_sampled(name, kind, ntok):
     cfg = get_config(name)
     seed = 0
