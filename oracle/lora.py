@@ -44,6 +44,8 @@ from .moe import _check_moe, _pairs_by_expert, _sigmoid, silu
 def _check_lora(w_gu, w_dn, A_gu, B_gu, A_dn, B_dn):
     E, twoI, H = w_gu.shape
     I = twoI // 2
+    if w_dn.shape[2] != I:
+        raise ValueError("LoRA adapters are defined here for gated (SwiGLU) layers")
     A_gu, B_gu, A_dn, B_dn = (np.asarray(m, dtype=np.float64) for m in (A_gu, B_gu, A_dn, B_dn))
     r = A_gu.shape[1]
     if A_gu.shape != (E, r, H) or B_gu.shape != (E, twoI, r):

@@ -3,7 +3,10 @@
 Notation: E experts, H hidden, I intermediate, k experts per token, T tokens,
 P = T*k routed (token, slot) pairs with flat pair id p = t*k + j. Stacks are
 row-major ``[E, out, in]``: gate_up ``[E, 2I, H]`` (rows 0..I-1 gate,
-I..2I-1 up) and down ``[E, H, I]``.
+I..2I-1 up) and down ``[E, H, I]``. An ungated layer (``has_gate=False`` in
+``Experts4bit.__init__``: the projection is a plain up projection of size I)
+has a ``[E, I, H]`` first stack and ``a = act(up)``; the stack shapes select
+the variant.
 
 Sources:
 
@@ -102,12 +105,12 @@ def _check_moe(x, idx, w, w_gu, w_dn):
     x = np.asarray(x, dtype=np.float64)
     idx = np.asarray(idx)
     w = np.asarray(w, dtype=np.float64)
-    E, twoI, H = w_gu.shape
-    if twoI % 2:
-        raise ValueError("gate_up must have 2I rows")
-    I = twoI // 2
-    if w_dn.shape != (E, H, I):
+    E, gu_out, H = w_gu.shape
+    if w_dn.shape[:2] != (E, H):
         raise ValueError("down must be [E, H, I]")
+    I = w_dn.shape[2]
+    if gu_out not in (I, 2 * I):
+        raise ValueError("gate_up must have 2I (gated) or I (ungated) rows")
     if x.ndim != 2 or x.shape[1] != H:
         raise ValueError("x must be [T, H]")
     if idx.shape != w.shape or idx.shape[0] != x.shape[0]:
@@ -116,8 +119,15 @@ def _check_moe(x, idx, w, w_gu, w_dn):
 
 
 def expert_activations(x_rows, w_gu_e, I):
-    """gate, up and a = silu(gate) * up for the rows of one expert (fp64)."""
+    """gate, up and a = silu(gate) * up for the rows of one expert (fp64).
+
+    Ungated stack (I rows): returns (h, None, silu(h)) -- the projection is a
+    plain up projection and the activation applies to it directly
+    (``Experts4bit.forward``, the ``has_gate`` branch).
+    """
     h = x_rows @ np.asarray(w_gu_e, dtype=np.float64).T
+    if h.shape[1] == I:
+        return h, None, silu(h)
     g, u = h[:, :I], h[:, I:]
     return g, u, silu(g) * u
 
@@ -155,6 +165,8 @@ def moe_dgrad(x, idx, w, w_gu, w_dn, grad_y):
     * dg = grad_a * u * s * (1 + g * (1 - s)),  s = sigmoid(g)
     * du = grad_a * g * s
     * grad_x[t] += W_gu[e]^T [dg; du]     (the gate_up projection's dgrad)
+
+    Ungated: dh = grad_a * s * (1 + h * (1 - s)) and grad_x[t] += W_up^T dh.
     """
     x, idx, w, E, H, I = _check_moe(x, idx, w, w_gu, w_dn)
     gy = np.asarray(grad_y, dtype=np.float64)
@@ -170,8 +182,11 @@ def moe_dgrad(x, idx, w, w_gu, w_dn, grad_y):
         grad_w[t, j] = np.sum(G2 * a, axis=1)
         grad_a = w[t, j][:, None] * G2
         s = _sigmoid(g)
-        dg = grad_a * u * s * (1.0 + g * (1.0 - s))
-        du = grad_a * g * s
-        gx = np.concatenate([dg, du], axis=1) @ wgu
-        np.add.at(grad_x, t, gx)
+        if u is None:  # ungated: a = silu(h), d a / d h = s (1 + h (1 - s))
+            gh = grad_a * s * (1.0 + g * (1.0 - s))
+        else:
+            dg = grad_a * u * s * (1.0 + g * (1.0 - s))
+            du = grad_a * g * s
+            gh = np.concatenate([dg, du], axis=1)
+        np.add.at(grad_x, t, gh @ wgu)
     return grad_x, grad_w

@@ -172,3 +172,37 @@ def test_zero_tokens():
     assert moe_forward(x, idx, w, wgu, wdn).shape == (0, 64)
     gx, gw = moe_dgrad(x, idx, w, wgu, wdn, x)
     assert gx.shape == (0, 64) and gw.shape == (0, 2)
+
+
+def _ungated_problem(seed=0, T=9, E=3, H=32, I=24, k=2):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, H))
+    wup = rng.standard_normal((E, I, H)) * 0.2
+    wdn = rng.standard_normal((E, H, I)) * 0.2
+    idx, w = route(rng.standard_normal((T, E)).astype(np.float32), k)
+    return x, idx, w, wup, wdn, rng.standard_normal((T, H))
+
+
+def test_ungated_forward_is_act_of_up_dense_brute_force():
+    """has_gate=False: a = silu(W_up x); dense masked brute force over all experts."""
+    x, idx, w, wup, wdn, _ = _ungated_problem()
+    E = wup.shape[0]
+    G = _gating_matrix(idx, w, E)
+    ref = sum(G[:, e : e + 1] * (silu(x @ wup[e].T) @ wdn[e].T) for e in range(E))
+    y = moe_forward(x, idx, w, wup, wdn)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_ungated_dgrad_matches_torch_autograd():
+    x, idx, w, wup, wdn, gy = _ungated_problem(seed=1)
+    E = wup.shape[0]
+    G = _gating_matrix(idx, w, E)
+    X = torch.tensor(x, requires_grad=True)
+    Gt = torch.tensor(G, requires_grad=True)
+    y = sum(Gt[:, e : e + 1] * (torch.nn.functional.silu(X @ torch.tensor(wup[e]).T)
+                                 @ torch.tensor(wdn[e]).T) for e in range(E))
+    (y * torch.tensor(gy)).sum().backward()
+    gx, gw = moe_dgrad(x, idx, w, wup, wdn, gy)
+    assert np.max(np.abs(gx - X.grad.numpy())) <= 1e-12 * np.max(np.abs(gx))
+    gw_ref = np.take_along_axis(Gt.grad.numpy(), idx.astype(np.int64), axis=1)
+    assert np.max(np.abs(gw - gw_ref)) <= 1e-12 * np.max(np.abs(gw))
