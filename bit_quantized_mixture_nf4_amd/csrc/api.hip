@@ -37,6 +37,8 @@ GemmArgs base_args(const MoePlan &p, const e4b_stack &st, const PermView &v) {
   a.tile_map = v.tile_map;
   a.E = int32_t(p.E);
   a.cb = p.codebook;
+  a.gated = p.gated;
+  a.ldgu = int32_t(p.gu_cols);
   return a;
 }
 
@@ -148,7 +150,7 @@ extern "C" e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t t
   d.n_tiles = int32_t(p.n_tiles_i);
   d.grid = uint32_t(p.m_tiles_bound * p.n_tiles_i);
   d.C = dgu;
-  d.ldc = int32_t(2 * p.I);
+  d.ldc = int32_t(p.gu_cols);
   d.GU = const_cast<uint16_t *>(gu);
   d.topk_w = topk_w;
   d.partial = partial;
@@ -156,9 +158,9 @@ extern "C" e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t t
 
   GemmArgs u = base_args(p, L->gate_up, v);
   u.A = dgu;
-  u.lda = int32_t(2 * p.I);
+  u.lda = int32_t(p.gu_cols);
   u.N = int32_t(p.H);
-  u.K = int32_t(2 * p.I);
+  u.K = int32_t(p.gu_cols);
   u.n_tiles = int32_t(p.n_tiles_h_gud);
   u.grid = uint32_t(p.m_tiles_bound * p.n_tiles_h_gud);
   u.C = gx;
@@ -238,6 +240,7 @@ extern "C" e4b_status e4b_moe_lora_forward(const e4b_moe_layer *L, const e4b_lor
   if (st != E4B_OK) return st;
   st = check_lora(lora);
   if (st != E4B_OK) return st;
+  if (!p.gated) return E4B_ERR_SHAPE;  // adapters are defined for gated layers
   int use_decode = 0;
   st = check_forward(p, x_bf16, router_logits, topk_idx, topk_w, y_bf16, saved, ws, ws_bytes,
                      E4B_PATH_GROUPED, &use_decode);
@@ -292,6 +295,7 @@ extern "C" e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lo
   if (st != E4B_OK) return st;
   st = check_lora(lora);
   if (st != E4B_OK) return st;
+  if (!p.gated) return E4B_ERR_SHAPE;
   st = check_dgrad(p, topk_idx, topk_w, x_bf16, saved, grad_y_bf16, grad_x_bf16, grad_topk_w, ws,
                    ws_bytes);
   if (st != E4B_OK || T == 0) return st;

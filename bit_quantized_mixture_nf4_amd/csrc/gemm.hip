@@ -20,6 +20,8 @@
 //   EPI_STORE   : bf16 store.
 //   EPI_DSWIGLU : dgrad of act(gate) * up scaled by the routing weight, plus
 //                 this tile's share of d y / d routing weight.
+//   EPI_ACT / EPI_DACT : the same for an ungated layer (has_gate=False in
+//                 Experts4bit.__init__: a plain up projection h, a = act(h)).
 //
 // Tile: 256 (pairs) x 128 * WN (columns) x 64 (one quantization block per
 // K-step); 4 x WN waves, each 64 x 128 = 2 x 4 MFMA 32x32x16 tiles. WN = 2
@@ -36,7 +38,7 @@ namespace e4b {
 
 enum { A_GATHER = 0, A_DIRECT = 1 };
 enum { B_NT = 0, B_NN = 1 };
-enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_DSWIGLU = 2 };
+enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_DSWIGLU = 2, EPI_ACT = 3, EPI_DACT = 4 };
 
 
 
@@ -396,14 +398,89 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
                 *reinterpret_cast<u32x2 *>(g.C + grow * g.ldc + pair) =
                     u32x2{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
               if (g.GU) {
-                *reinterpret_cast<u32x2 *>(g.GU + grow * (2 * g.I) + pair) =
+                *reinterpret_cast<u32x2 *>(g.GU + grow * g.ldgu + pair) =
                     u32x2{pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
-                *reinterpret_cast<u32x2 *>(g.GU + grow * (2 * g.I) + g.I + pair) =
+                *reinterpret_cast<u32x2 *>(g.GU + grow * g.ldgu + g.I + pair) =
                     u32x2{pack_bf16x2(uv[0], uv[1]), pack_bf16x2(uv[2], uv[3])};
               }
             }
           }
       }
+    }
+  } else if (EPI == EPI_ACT) {
+    // ungated: h = this tile's columns of the up projection, a = silu(h)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = lrow + i * 32;
+      if (row < valid_rows) {
+        const int64_t grow = seg + row0 + row;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = nt * kBN + lcol + j * 32 + 8 * q;
+            if (col < g.N) {
+              float hv[4], av[4];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                hv[t] = acc[i][j][4 * q + t];
+                av[t] = hv[t] * sigmoidf_(hv[t]);
+              }
+              if (g.C)
+                *reinterpret_cast<u32x2 *>(g.C + grow * g.ldc + col) =
+                    u32x2{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
+              if (g.GU)
+                *reinterpret_cast<u32x2 *>(g.GU + grow * g.ldgu + col) =
+                    u32x2{pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3])};
+            }
+          }
+      }
+    }
+  } else if (EPI == EPI_DACT) {
+    // ungated dgrad: grad_a = w * G2, dh = grad_a * silu'(h), partial sum of G2 * silu(h)
+    float *red = reinterpret_cast<float *>(sA[0]);
+    float part[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = lrow + i * 32;
+      const int64_t grow = seg + row0 + min(row, valid_rows - 1);
+      const float wr = g.topk_w[g.sorted_pair[grow]];
+      const uint16_t *hrow = g.GU + grow * g.ldgu;
+      uint16_t *crow = g.C + grow * g.ldc;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nt * kBN + lcol + j * 32 + 8 * q;
+          const u32x2 hq = *reinterpret_cast<const u32x2 *>(hrow + min(n, g.N - 4));
+          const float hv[4] = {bf16_lo(hq[0]), bf16_hi(hq[0]), bf16_lo(hq[1]), bf16_hi(hq[1])};
+          float dh[4], pq = 0.0f;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float sg = sigmoidf_(hv[t]);
+            const float G2 = acc[i][j][4 * q + t];
+            pq += G2 * (hv[t] * sg);
+            dh[t] = wr * G2 * sg * (1.0f + hv[t] * (1.0f - sg));
+          }
+          if (row < valid_rows && n < g.N) {
+            part[i] += pq;
+            *reinterpret_cast<u32x2 *>(crow + n) =
+                u32x2{pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3])};
+          }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float pr = part[i] + __shfl_xor(part[i], 32);
+      if (lane < 32) red[wn * kBM + lrow + i * 32] = pr;
+    }
+    __syncthreads();
+    for (int r = tid; r < valid_rows; r += kThreads) {
+      const int64_t grow = seg + row0 + r;
+      float sum = red[r];
+#pragma unroll
+      for (int c = 1; c < kGemmWavesN; ++c) sum += red[c * kBM + r];
+      g.partial[grow * g.n_tiles + nt] = sum;
     }
   } else {  // EPI_DSWIGLU
     float *red = reinterpret_cast<float *>(sA[0]);  // [kGemmWavesN][kBM] partial row sums
@@ -420,7 +497,7 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
     u32x2 gg[2][4], uu[2][4];
     auto fetch = [&](int b, int slot) {
       const int i = b >> 2, j = b & 3;
-      const uint16_t *gurow = g.GU + grow[i] * (2 * g.I);
+      const uint16_t *gurow = g.GU + grow[i] * g.ldgu;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = min(nt * kBN + lcol + j * 32 + 8 * q, g.N - 4);
@@ -494,9 +571,15 @@ hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s) 
                          s, a);                                                                \
   } while (0)
   switch (v) {
-    case GEMM_GATE_UP_FWD: E4B_GEMM(A_GATHER, B_NT, EPI_SWIGLU, kBNWide / 128); break;
+    case GEMM_GATE_UP_FWD:
+      if (a.gated) E4B_GEMM(A_GATHER, B_NT, EPI_SWIGLU, kBNWide / 128);
+      else E4B_GEMM(A_GATHER, B_NT, EPI_ACT, kBNWide / 128);
+      break;
     case GEMM_DOWN_FWD: E4B_GEMM(A_DIRECT, B_NT, EPI_STORE, kBNWide / 128); break;
-    case GEMM_DOWN_DGRAD: E4B_GEMM(A_GATHER, B_NN, EPI_DSWIGLU, kBNWide / 128); break;
+    case GEMM_DOWN_DGRAD:
+      if (a.gated) E4B_GEMM(A_GATHER, B_NN, EPI_DSWIGLU, kBNWide / 128);
+      else E4B_GEMM(A_GATHER, B_NN, EPI_DACT, kBNWide / 128);
+      break;
     case GEMM_GATE_UP_DGRAD: E4B_GEMM(A_DIRECT, B_NN, EPI_STORE, kBNNarrow / 128); break;
   }
 #undef E4B_GEMM

@@ -9,7 +9,7 @@
 namespace e4b {
 
 enum GemmVariant {
-  GEMM_GATE_UP_FWD = 0,   // A gathered x,      B = W_gu rows,    SiLU*up epilogue
+  GEMM_GATE_UP_FWD = 0,   // A gathered x,      B = W_gu rows,    SiLU*up (or SiLU) epilogue
   GEMM_DOWN_FWD = 1,      // A sorted a,        B = W_dn rows,    bf16 store
   GEMM_DOWN_DGRAD = 2,    // A gathered grad_y, B = W_dn^T,       SiLU-backward epilogue
   GEMM_GATE_UP_DGRAD = 3  // A sorted dGU,      B = W_gu^T,       bf16 store
@@ -40,6 +40,8 @@ struct GemmArgs {
   uint16_t *GU;  // gate_up fwd: out g|u [row, 2I] (may be null); down dgrad: in g|u
   const float *topk_w;
   float *partial;  // down dgrad: [P, n_tiles]
+  int32_t gated;   // gate_up fwd / down dgrad: 1 SwiGLU pairs, 0 a plain activation of the up rows
+  int32_t ldgu;    // row stride of the saved g|u (gated, 2I) or h (ungated, I)
   // LoRA slice (null: none): per-pair projection fp32 [P, kLoraK] in sorted
   // order, and the bf16 pack of the scaled adapter [E, lora_rows, kLoraK]
   // indexed by the weight row of each output column

@@ -54,10 +54,13 @@ e4b_status check_layer(const e4b_moe_layer *L, MoePlan *p) {
   const e4b_stack &gu = L->gate_up, &dn = L->down;
   if (gu.codebook != dn.codebook) return E4B_ERR_CODEBOOK;
   if (gu.E != dn.E || gu.E > kMaxE) return E4B_ERR_SHAPE;
-  if (gu.out != 2 * dn.in || gu.in != dn.out) return E4B_ERR_SHAPE;
+  // gated (SwiGLU: gate | up, 2I rows) or ungated (a plain up projection, I rows)
+  if ((gu.out != 2 * dn.in && gu.out != dn.in) || gu.in != dn.out) return E4B_ERR_SHAPE;
   p->E = gu.E;
   p->H = gu.in;
   p->I = dn.in;
+  p->gated = gu.out == 2 * dn.in ? 1 : 0;
+  p->gu_cols = gu.out;
   p->codebook = gu.codebook;
   return E4B_OK;
 }
@@ -79,7 +82,9 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   p->nchunks = (P + kPermChunk - 1) / kPermChunk;
   const int64_t busy = P < E ? P : E;  // at most P experts have a pair
   p->m_tiles_bound = (P + busy * (kBM - 1)) / kBM;
-  p->n_tiles_gu = (I + kBNWide / 2 - 1) / (kBNWide / 2);
+  // gated: kBNWide / 2 gate-up pairs per tile; ungated: kBNWide columns of the up projection
+  const int64_t bn_gu = p->gated ? kBNWide / 2 : kBNWide;
+  p->n_tiles_gu = (I + bn_gu - 1) / bn_gu;
   p->n_tiles_h = (H + kBNWide - 1) / kBNWide;
   p->n_tiles_i = (I + kBNWide - 1) / kBNWide;
   p->n_tiles_h_gud = (H + kBNNarrow - 1) / kBNNarrow;
@@ -109,8 +114,8 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   // dgrad region (overlaps the forward region: the two calls never run at once
   // on one workspace)
   off = base;
-  p->off_gu = take(size_t(P) * 2 * I * 2);
-  p->off_dgu = take(size_t(P) * 2 * I * 2);
+  p->off_gu = take(size_t(P) * p->gu_cols * 2);
+  p->off_dgu = take(size_t(P) * p->gu_cols * 2);
   p->off_partial = take(size_t(P) * p->n_tiles_i * 4);
   p->off_gx = take(size_t(P) * H * 2);
   const size_t dgrad_end = off;
@@ -129,7 +134,7 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   p->off_pj_bdn = take(size_t(E) * kLoraK * H * 2);
   p->off_pj_bgu = take(size_t(E) * kLoraK * 2 * I * 2);
   p->lora_ws_bytes = off;
-  p->sv_tile_map = size_t(P) * 2 * I * 2;  // a multiple of 256: I % 64 == 0
+  p->sv_tile_map = align_up(size_t(P) * p->gu_cols * 2, 256);
   p->sv_tile_offsets = p->sv_tile_map + size_t(p->m_tiles_bound) * 16;
   p->sv_offsets = p->sv_tile_offsets + size_t(E + 1) * 4;
   p->sv_sorted = p->sv_offsets + size_t(E + 1) * 4;
@@ -140,7 +145,7 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
 
 bool decode_fits(const MoePlan &p) {
   const int64_t kmax = p.H > p.I ? p.H : p.I;
-  return p.codebook != E4B_CB_BF16 && p.T <= kDecodeMaxT && p.P <= kDecMaxPairs &&
+  return p.codebook != E4B_CB_BF16 && p.gated && p.T <= kDecodeMaxT && p.P <= kDecMaxPairs &&
          kmax <= kDecodeMaxK;
 }
 
@@ -202,7 +207,7 @@ extern "C" const char *e4b_status_string(e4b_status s) {
     case E4B_ERR_DTYPE: return "unknown output dtype";
     case E4B_ERR_WORKSPACE: return "workspace missing or too small";
     case E4B_ERR_ALIGN: return "device buffer not 16-byte aligned";
-    case E4B_ERR_PATH: return "invalid path (decode path needs a 4-bit layer, T <= 8, saved == NULL and max(H, I) <= 4096)";
+    case E4B_ERR_PATH: return "invalid path (decode path needs a gated 4-bit layer, T <= 8, saved == NULL and max(H, I) <= 4096)";
     case E4B_ERR_HIP: return "HIP kernel launch failed";
   }
   return "unknown status";

@@ -31,6 +31,8 @@ constexpr int kLoraK = 16;         // LoRA rank slot: one 16-deep MFMA slice (r 
 struct MoePlan {
   int64_t E, H, I, T, k, P;
   int32_t codebook;
+  int32_t gated;    // 1: gate_up holds gate | up (2I rows); 0: a plain up projection (I rows)
+  int64_t gu_cols;  // rows of the first stack: 2I or I
   int64_t nchunks;        // permutation chunks of kPermChunk pairs
   int64_t m_tiles_bound;  // upper bound of sum_e ceil(count_e / kBM)
   int64_t n_tiles_gu;     // gate_up forward tiles: kBNWide/2 gate-up pairs per tile

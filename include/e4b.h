@@ -88,7 +88,10 @@ typedef struct {
 } e4b_stack;
 
 /* A MoE layer: gate_up (out = 2I, in = H) and down (out = H, in = I), same E,
- * same codebook ([README] "one module, one scheme"). */
+ * same codebook ([README] "one module, one scheme"). A first stack of out = I
+ * rows selects the ungated variant ([sdist] Experts4bit has_gate=False: a
+ * plain up projection h, a = silu(h)); it runs the grouped path and takes no
+ * LoRA adapters. */
 typedef struct {
   e4b_stack gate_up;
   e4b_stack down;
@@ -125,7 +128,8 @@ e4b_status e4b_dequantize_nf4(const e4b_stack *st, int32_t dtype, void *w_out,
  * (token t, slot j) with expert e = topk_idx[t, j],
  *   h = W_gu[e] x_t ; g = h[:I] ; u = h[I:] ; a = silu(g) * u ;
  *   y_t = sum_j topk_w[t, j] * (W_dn[e] a), accumulated in fp32,
- * with W the dequantized stacks (bf16 operands, fp32 accumulation).
+ * with W the dequantized stacks (bf16 operands, fp32 accumulation); an
+ * ungated layer has a = silu(W_up[e] x_t).
  *   x_bf16        : device bf16 [T, H]
  *   router_logits : device fp32 [T, E] or NULL. Given: topk_idx/topk_w are
  *                   OUTPUTS = the top_k largest logits (descending, ties to the
@@ -135,7 +139,7 @@ e4b_status e4b_dequantize_nf4(const e4b_stack *st, int32_t dtype, void *w_out,
  *   topk_w        : device fp32  [T, top_k]
  *   y_bf16        : device bf16 [T, H] (written)
  *   saved         : device buffer of e4b_moe_saved_bytes() or NULL; when given,
- *                   the bf16 gate and up projections of every pair and the
+ *                   the bf16 gate and up projections (ungated: h) of every pair and the
  *                   routing permutation are stored for e4b_moe_dgrad
  *                   (grouped path only)
  *   ws, ws_bytes  : device workspace, >= e4b_moe_workspace_bytes()
@@ -154,7 +158,8 @@ e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t top_k,
  *   G2 = W_dn[e]^T grad_y_t ; grad_topk_w[t, j] = G2 . a ;
  *   grad_a = topk_w[t, j] G2 ; s = sigmoid(g) ;
  *   dg = grad_a u s (1 + g (1 - s)) ; du = grad_a g s ;
- *   grad_x_t = sum_j W_gu[e]^T [dg ; du].
+ *   grad_x_t = sum_j W_gu[e]^T [dg ; du]   (ungated: dh = grad_a s (1 + h (1 - s)),
+ *   grad_x_t = sum_j W_up[e]^T dh).
  *   topk_idx, topk_w : device [T, top_k] (inputs, as used by the forward)
  *   x_bf16           : device bf16 [T, H]; required when saved == NULL
  *                      (the gate/up projections are recomputed), ignored otherwise
@@ -177,7 +182,7 @@ e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t top_k,
  * top_k) (one size serves both); 0 when the arguments are invalid. */
 size_t e4b_moe_workspace_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k);
 
-/* Bytes of the `saved` buffer: bf16 [T*top_k, 2I] followed by the routing
+/* Bytes of the `saved` buffer: bf16 [T*top_k, 2I] ([T*top_k, I] ungated) followed by the routing
  * permutation (int32 arrays over experts, m-tiles and pairs); 0 when invalid. */
 size_t e4b_moe_saved_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k);
 

@@ -185,3 +185,15 @@ def test_bf16_lane_validation():
     assert _fwd(nf) == _lib.E4B_ERR_NULL
     mixed = _lib.E4bLayer(_stack(4, 128, 64, cb=2), _stack(4, 64, 64, cb=0))
     assert _fwd(mixed) == _lib.E4B_ERR_CODEBOOK
+
+
+def test_ungated_layer_validation():
+    ug = _lib.E4bLayer(_stack(4, 64, 64), _stack(4, 64, 64))  # gate_up out = I: has_gate=False
+    assert _fwd(ug, ws_bytes=0) == _lib.E4B_ERR_WORKSPACE  # accepted up to the workspace check
+    assert _fwd(ug, T=4, path=2) == _lib.E4B_ERR_PATH     # decode GEMV is for gated layers
+    bad = _lib.E4bLayer(_stack(4, 96, 64), _stack(4, 64, 64))
+    assert _fwd(bad) == _lib.E4B_ERR_SHAPE
+    lib = e4b.load()
+    lo = _lib.E4bLora(FAKE, FAKE, FAKE, FAKE, 8, 16.0)
+    assert lib.e4b_moe_lora_forward(ctypes.byref(ug), ctypes.byref(lo), 4, 2, FAKE, None, FAKE,
+                                    FAKE, FAKE, None, FAKE, 1 << 40, None) == _lib.E4B_ERR_SHAPE

@@ -21,6 +21,7 @@ class MoEConfig:
     codebooks: tuple = ("nf4",)
     dgrad: bool = True
     weight_std: float = 0.02
+    gated: bool = True  # False: has_gate=False, a plain up projection [E, I, H]
     note: str = ""
 
     @property

@@ -59,9 +59,9 @@ def gen_logits(cfg, seed):
 
 
 def gen_expert_weight(cfg, seed, which, e):
-    """One expert's fp32 weight: ``which`` = "gate_up" -> [2I, H], "down" -> [H, I]."""
+    """One expert's fp32 weight: ``which`` = "gate_up" -> [2I, H] ([I, H] ungated), "down" -> [H, I]."""
     if which == "gate_up":
-        shape, tid = (2 * cfg.I, cfg.H), _W_GU
+        shape, tid = ((2 if cfg.gated else 1) * cfg.I, cfg.H), _W_GU
     elif which == "down":
         shape, tid = (cfg.H, cfg.I), _W_DN
     else:
@@ -74,7 +74,7 @@ def gen_expert_weight(cfg, seed, which, e):
 def gen_weights(cfg, seed, which, experts=None, threads=None):
     """fp32 stack ``[len(experts), out, in]`` (all experts by default)."""
     experts = list(range(cfg.E)) if experts is None else list(experts)
-    shape = (2 * cfg.I, cfg.H) if which == "gate_up" else (cfg.H, cfg.I)
+    shape = ((2 if cfg.gated else 1) * cfg.I, cfg.H) if which == "gate_up" else (cfg.H, cfg.I)
     out = np.empty((len(experts),) + shape, dtype=np.float32)
 
     def fill(i):
