@@ -13,7 +13,8 @@ Also measured in the same run:
   the launch stream (library timer hook), the largest gives `roofline`;
 * the decode dequant-GEMV path on the Qwen3-30B-A3B-shaped layer (E=128,
   H=2048, I=768, top-8, Zipf routing) at T=1 and T=8, cold cache (16 layer
-  copies rotated), as GB/s of the experts actually touched;
+  copies rotated), as GB/s of the experts actually touched, and with the
+  layers streamed from pinned host memory by the layer-granular prefetch;
 * the same training step with per-expert LoRA adapters (r=8, alpha=16) over
   the frozen base (`lora`), and on the bf16 passthrough lane (`bf16_lane`);
 * the CPU oracle (numpy float64) on a bounded sample of the same workload.
@@ -377,9 +378,73 @@ def bench_decode(args, e4b, torch, ev):
             "cache": f"cold ({copies} layer copies rotated)",
         }
         log(f"decode T={T}: {distinct} experts, GEMV {us:.2f} us, {gbps:.0f} GB/s")
+    if not args.no_stream:
+        out["streamed"] = bench_decode_streamed(args, e4b, torch, layers[0])
     del layers
     torch.cuda.empty_cache()
     return out
+
+
+def bench_decode_streamed(args, e4b, torch, layer, n_host=4, steps=8):
+    """Decode with the layers kept in pinned host memory and streamed in with
+    the layer-granular prefetch (two device slots, side-stream copies)."""
+    from workloads import get_config, gen_x, gen_logits
+    from workloads.gen import to_bf16_tensor
+
+    host = []
+    for _ in range(n_host):
+        host.append(e4b.MoELayer(*[
+            e4b.QuantStack(st.packed.cpu().pin_memory(), st.absmax.cpu().pin_memory(), st.E, st.out,
+                           st.inn, st.codebook) for st in (layer.gate_up, layer.down)]))
+    layer_bytes = sum(st.packed.numel() + st.absmax.numel() * 4
+                      for st in (host[0].gate_up, host[0].down))
+    pf = e4b.LayerPrefetcher(host)
+    res = {"host_layers": n_host, "layer_bytes": layer_bytes}
+    # copies alone (no compute)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        pf.prefetch(i % n_host)
+        pf.acquire(i % n_host)
+        pf.release(i % n_host)
+    torch.cuda.synchronize()
+    copy_s = (time.perf_counter() - t0) / steps
+    res["h2d_gbps"] = round(layer_bytes / copy_s / 1e9, 1)
+    for T in (1, 8):
+        cfg = get_config("qwen3_decode", T)
+        x = to_bf16_tensor(gen_x(cfg, args.seed)).cuda()
+        lg = torch.from_numpy(gen_logits(cfg, args.seed)).cuda()
+
+        def fwd(L):
+            e4b.moe_forward(L, x, cfg.k, logits=lg, path="decode")
+
+        for _ in range(2):
+            fwd(layer)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fwd(layer)
+        torch.cuda.synchronize()
+        comp_s = (time.perf_counter() - t0) / steps
+        t0 = time.perf_counter()
+        pf.prefetch(0)
+        for i in range(steps):
+            if i + 1 < steps:
+                pf.prefetch((i + 1) % n_host)
+            L = pf.acquire(i % n_host)
+            fwd(L)
+            pf.release(i % n_host)
+        torch.cuda.synchronize()
+        step_s = (time.perf_counter() - t0) / steps
+        res[f"t{T}"] = {"ms_per_layer": round(step_s * 1e3, 3),
+                        "copy_ms_per_layer": round(copy_s * 1e3, 3),
+                        "compute_ms_per_layer": round(comp_s * 1e3, 4),
+                        "tokens_per_s_per_layer": round(T / step_s, 1),
+                        "overlap": round((copy_s + comp_s) / step_s, 3)}
+        log(f"streamed decode T={T}: {step_s * 1e3:.2f} ms/layer (copy {copy_s * 1e3:.2f}, "
+            f"compute {comp_s * 1e3:.3f}), H2D {res['h2d_gbps']} GB/s")
+    del pf, host
+    return res
 
 
 def cpu_baseline(args, cfg):
@@ -449,6 +514,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-lora", action="store_true")
     ap.add_argument("--no-bf16-lane", action="store_true")
+    ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")

@@ -35,6 +35,7 @@ __all__ = [
     "moe_lora_forward",
     "moe_lora_backward",
     "lora_workspace_bytes",
+    "LayerPrefetcher",
     "workspace_bytes",
     "saved_bytes",
     "E4bError",
@@ -315,3 +316,70 @@ def moe_lora_backward(layer, lora, topk_idx, topk_w, x, grad_y, saved=None, grad
     )
     check("e4b_moe_lora_backward", code)
     return gx, gw, grads
+
+
+def _empty_like_on(t, device):
+    return None if t is None else torch.empty(t.shape, dtype=t.dtype, device=device)
+
+
+class LayerPrefetcher:
+    """Layer-granular prefetch of stored layers kept in pinned host memory.
+
+    Two device slots used in turn: ``prefetch(l)`` copies layer ``l`` into
+    the next slot on a side stream (``e4b_stack_copy_async``) once the
+    compute that last used that slot has finished; ``acquire(l)`` makes the
+    current stream wait for the copy and returns the device layer;
+    ``release(l)`` marks its slot free after the layer's kernels have been
+    enqueued on the current stream. Layers are acquired in prefetch order and
+    at most two are resident. (The 0.4.0 README's "Prefetched expert
+    offload" bullet: layer L+1 copies on a side stream while layer L
+    computes.)
+    """
+
+    def __init__(self, host_layers, device="cuda"):
+        if not host_layers:
+            raise ValueError("no layers")
+        self.host = host_layers
+        dev = torch.device(device)
+        ref = host_layers[0]
+        self.slots = []
+        for _ in range(2):
+            stacks = [QuantStack(_empty_like_on(st.packed, dev), _empty_like_on(st.absmax, dev),
+                                 st.E, st.out, st.inn, st.codebook)
+                      for st in (ref.gate_up, ref.down)]
+            self.slots.append(MoELayer(*stacks))
+        self.stream = torch.cuda.Stream(device=dev)  # default priority
+        self.ready = [torch.cuda.Event() for _ in range(2)]
+        self.free = [torch.cuda.Event() for _ in range(2)]
+        for ev in self.free:
+            ev.record(torch.cuda.current_stream(dev))
+        self.next_slot = 0
+        self.queue = []  # (layer, slot) in prefetch order
+
+    def prefetch(self, l):
+        if len(self.queue) == 2:
+            raise RuntimeError("both slots are in use: release a layer first")
+        s = self.next_slot
+        self.next_slot ^= 1
+        slot, src = self.slots[s], self.host[l]
+        self.stream.wait_event(self.free[s])
+        handle = ctypes.c_void_p(self.stream.cuda_stream)
+        for dst, st in ((slot.gate_up, src.gate_up), (slot.down, src.down)):
+            d, c = dst.as_c(), st.as_c()
+            check("e4b_stack_copy_async",
+                  load().e4b_stack_copy_async(ctypes.byref(d), ctypes.byref(c), handle))
+        self.ready[s].record(self.stream)
+        self.queue.append((l, s))
+
+    def acquire(self, l):
+        if not self.queue or self.queue[0][0] != l:
+            raise RuntimeError(f"layer {l} is not the next prefetched layer")
+        s = self.queue[0][1]
+        torch.cuda.current_stream().wait_event(self.ready[s])
+        return self.slots[s]
+
+    def release(self, l):
+        if not self.queue or self.queue[0][0] != l:
+            raise RuntimeError(f"layer {l} is not the acquired layer")
+        _, s = self.queue.pop(0)
+        self.free[s].record(torch.cuda.current_stream())

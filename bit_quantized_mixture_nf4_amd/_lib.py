@@ -37,6 +37,7 @@ EXPORTS = (
     "e4b_moe_lora_forward",
     "e4b_moe_lora_backward",
     "e4b_moe_lora_workspace_bytes",
+    "e4b_stack_copy_async",
     "e4b_status_string",
     "e4b_set_kernel_timer",
 )
@@ -105,6 +106,7 @@ def load():
         "e4b_moe_lora_backward": (
             i32, [lay, lo, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "e4b_moe_lora_workspace_bytes": (sz, [lay, i64, i32]),
+        "e4b_stack_copy_async": (i32, [st, st, vp]),
         "e4b_status_string": (ctypes.c_char_p, [i32]),
         "e4b_set_kernel_timer": (i32, [i32, vp, vp, i32]),
     }

@@ -163,3 +163,24 @@ extern "C" e4b_status e4b_dequantize_nf4(const e4b_stack *st, int32_t dtype, voi
                        st->absmax, ngroups, int(st->codebook), w_out);
   return hipGetLastError() == hipSuccess ? E4B_OK : E4B_ERR_HIP;
 }
+
+extern "C" e4b_status e4b_stack_copy_async(const e4b_stack *dst, const e4b_stack *src,
+                                           hipStream_t stream) {
+  e4b_status s = check_stack(dst);
+  if (s != E4B_OK) return s;
+  s = check_stack(src);
+  if (s != E4B_OK) return s;
+  if (dst->E != src->E || dst->out != src->out || dst->in != src->in ||
+      dst->codebook != src->codebook)
+    return E4B_ERR_SHAPE;
+  const int64_t n = dst->E * dst->out * dst->in;
+  const bool bf16 = dst->codebook == E4B_CB_BF16;
+  if (hipMemcpyAsync(const_cast<uint8_t *>(dst->packed), src->packed,
+                     size_t(bf16 ? n * 2 : n / 2), hipMemcpyDefault, stream) != hipSuccess)
+    return E4B_ERR_HIP;
+  if (!bf16 && hipMemcpyAsync(const_cast<float *>(dst->absmax), src->absmax,
+                              size_t(n / kBlock) * sizeof(float), hipMemcpyDefault,
+                              stream) != hipSuccess)
+    return E4B_ERR_HIP;
+  return E4B_OK;
+}

@@ -124,6 +124,20 @@ e4b_status e4b_quantize_nf4(const float *w, int64_t E, int64_t out, int64_t in,
 e4b_status e4b_dequantize_nf4(const e4b_stack *st, int32_t dtype, void *w_out,
                               hipStream_t stream);
 
+/* Asynchronous copy of one stored stack (packed codes or bf16 weights, and
+ * the absmax when the mode has one) from `src` to `dst`, on `stream`
+ * (hipMemcpyAsync: host-to-device from pinned host memory, or device-to-
+ * device). It is the transfer of the layer-granular prefetch of the
+ * [README] "Prefetched expert offload" bullet (decode with experts that
+ * exceed device memory): the caller copies layer L+1 into a second set of
+ * device buffers on a side stream while layer L computes, and orders the
+ * two streams with events, so at most two layers are resident.
+ *   dst, src : host descriptors; dst's buffers on the device, src's on the
+ *              device or in pinned host memory; same E, out, in, blocksize
+ *              and codebook
+ * Errors: NULL, SHAPE (descriptors differ), BLOCKSIZE, CODEBOOK, ALIGN, HIP. */
+e4b_status e4b_stack_copy_async(const e4b_stack *dst, const e4b_stack *src, hipStream_t stream);
+
 /* Routed SwiGLU expert forward. [sdist] Experts4bit.forward: for each
  * (token t, slot j) with expert e = topk_idx[t, j],
  *   h = W_gu[e] x_t ; g = h[:I] ; u = h[I:] ; a = silu(g) * u ;

@@ -197,3 +197,12 @@ def test_ungated_layer_validation():
     lo = _lib.E4bLora(FAKE, FAKE, FAKE, FAKE, 8, 16.0)
     assert lib.e4b_moe_lora_forward(ctypes.byref(ug), ctypes.byref(lo), 4, 2, FAKE, None, FAKE,
                                     FAKE, FAKE, None, FAKE, 1 << 40, None) == _lib.E4B_ERR_SHAPE
+
+
+def test_stack_copy_validation():
+    cp = e4b.load().e4b_stack_copy_async
+    a, b = _stack(4, 128, 64), _stack(4, 128, 128)
+    assert cp(ctypes.byref(a), ctypes.byref(b), None) == _lib.E4B_ERR_SHAPE
+    assert cp(ctypes.byref(a), ctypes.byref(_stack(4, 128, 64, cb=1)), None) == _lib.E4B_ERR_SHAPE
+    assert cp(ctypes.byref(_stack(packed=None)), ctypes.byref(a), None) == _lib.E4B_ERR_NULL
+    assert cp(None, ctypes.byref(a), None) == _lib.E4B_ERR_NULL
