@@ -50,19 +50,27 @@ __device__ __forceinline__ int dec_tile_cost8(int np, bool gate_up) {
   return gate_up ? 8 + 2 * (npb - 1) : 8 + 4 * (npb - 1) / 3;
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// v shifted right by N lanes inside each 16-lane row, zero at the row start.
+template <int N>
+__device__ __forceinline__ int row_shr(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x110 + N, 0xF, 0xF, true);
 }
 
+// Inclusive prefix sum over the 64 lanes: DPP shifts inside each row, then
+// the row totals (read from lanes 15, 31, 47) added to the rows after them.
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o);
-    if (lane >= o) v += u;
-  }
-  return v;
+  v += row_shr<1>(v);
+  v += row_shr<2>(v);
+  v += row_shr<4>(v);
+  v += row_shr<8>(v);
+  const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31),
+            t2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row > 0 ? t0 : 0) + (row > 1 ? t1 : 0) + (row > 2 ? t2 : 0);
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+  return __builtin_amdgcn_readlane(wave_inclusive_scan(v, threadIdx.x & 63), 63);
 }
 
 // One workgroup: groups the P <= 256 routed pairs by expert (stable), lists
