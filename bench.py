@@ -357,6 +357,30 @@ def bench_decode(args, e4b, torch, ev):
             step()
         torch.cuda.synchronize()
         call_us = (time.perf_counter() - t0) / n * 1e6
+        # the same calls captured in one HIP graph (one per layer copy) and replayed
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            stream_c = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for c in range(copies):
+                s_ = lib.e4b_moe_forward(ctypes.byref(Ls[c]), T, cfg.k, vp(x), vp(lg), vp(idx),
+                                         vp(w), vp(y), None, vp(ws), ws.numel(), 2, stream_c)
+                if s_:
+                    raise RuntimeError(f"e4b status {s_}")
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(2, n // copies)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_us = (time.perf_counter() - t0) / (reps * copies) * 1e6
+        del graph
         kms = time_kernels(e4b, torch, ev, step, ["decode_gate_up", "decode_down"], n)
         distinct = int(np.unique(idx.cpu().numpy()).size)
         b_gu = distinct * e_gu + T * cfg.H * 2 + T * cfg.k * cfg.I * 2
@@ -375,9 +399,12 @@ def bench_decode(args, e4b, torch, ev):
                      "gbps": round(b_dn / (kms["decode_down"] * 1e-3) / 1e9, 1)},
             "forward_call_us": round(call_us, 2),
             "tokens_per_s": round(T / (call_us * 1e-6), 1),
+            "graph_forward_call_us": round(graph_us, 2),
+            "graph_tokens_per_s": round(T / (graph_us * 1e-6), 1),
             "cache": f"cold ({copies} layer copies rotated)",
         }
-        log(f"decode T={T}: {distinct} experts, GEMV {us:.2f} us, {gbps:.0f} GB/s")
+        log(f"decode T={T}: {distinct} experts, GEMV {us:.2f} us, {gbps:.0f} GB/s; forward call "
+            f"{call_us:.1f} us eager, {graph_us:.1f} us from a HIP graph")
     if not args.no_stream:
         out["streamed"] = bench_decode_streamed(args, e4b, torch, layers[0])
     del layers
