@@ -15,9 +15,11 @@ using namespace e4b;
 
 namespace e4b {
 
+// router_logits may be null (ids and weights given); otherwise the decode
+// prep kernel routes the tokens itself and writes topk_idx / topk_w.
 hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
-                                 const int32_t *idx, const float *w, uint16_t *y, char *ws,
-                                 hipStream_t s);
+                                 const float *logits, int32_t *idx, float *w, uint16_t *y,
+                                 char *ws, hipStream_t s);
 
 namespace {
 
@@ -83,12 +85,12 @@ extern "C" e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t
   const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
   uint16_t *y = static_cast<uint16_t *>(y_bf16);
 
-  if (router_logits)
-    E4B_TRY(launch_route(router_logits, T, int(p.E), top_k, topk_idx, topk_w, stream));
   if (use_decode) {
-    E4B_TRY(launch_decode_forward(p, L, x, topk_idx, topk_w, y, w, stream));
+    E4B_TRY(launch_decode_forward(p, L, x, router_logits, topk_idx, topk_w, y, w, stream));
     return E4B_OK;
   }
+  if (router_logits)
+    E4B_TRY(launch_route(router_logits, T, int(p.E), top_k, topk_idx, topk_w, stream));
   // with a saved buffer the permutation is written there for the dgrad
   const PermView v = saved ? perm_in_saved(p, static_cast<char *>(saved)) : perm_in_workspace(p, w);
   E4B_TRY(launch_permute(p, topk_idx, w, v, stream));

@@ -17,6 +17,7 @@
 // absmax scales each lane's partial sum.
 #include "device.h"
 #include "kernels.h"
+#include "route_dev.h"
 
 namespace e4b {
 
@@ -73,12 +74,16 @@ __device__ __forceinline__ int wave_sum(int v) {
   return __builtin_amdgcn_readlane(wave_inclusive_scan(v, threadIdx.x & 63), 63);
 }
 
-// One workgroup: groups the P <= 256 routed pairs by expert (stable), lists
-// the distinct experts in ascending order and writes the work maps of the
-// two GEMV launches (chunks of tiles of kDecTile units per distinct expert).
-// Ranks come from comparisons of unique (expert, pair) keys, segment starts
-// and the chunk offsets from wave ballots and scans.
-__global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restrict__ idx, int P,
+// One workgroup: routes the tokens when router logits are given (one
+// wavefront per token, the same selection as the router kernel), groups the
+// P <= 256 routed pairs by expert (stable), lists the distinct experts in
+// ascending order and writes the work maps of the two GEMV launches (chunks
+// of tiles of kDecTile units per distinct expert). Ranks come from
+// comparisons of unique (expert, pair) keys, segment starts and the chunk
+// offsets from wave ballots and scans.
+__global__ __launch_bounds__(256) void decode_prep_kernel(const float *__restrict__ logits, int E,
+                                                          int32_t *__restrict__ idx,
+                                                          float *__restrict__ wts, int P,
                                                           int k_route, int tiles_gu, int tiles_dn,
                                                           int target_gu, int target_dn,
                                                           DecodeWs w) {
@@ -89,8 +94,20 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const int32_t *__restr
   __shared__ int32_t s_dseg[kDecMaxPairs + 1];
   __shared__ int32_t s_wsum[5][4];
   const int p = threadIdx.x, lane = p & 63, wv = p >> 6;
+  int e_p = 0;
+  if (logits) {
+    // s_sorted_e doubles as the routed ids until the keys are built
+    const int T = P / k_route;
+    for (int t = wv; t < T; t += kDecMaxPairs / 64)
+      route_token(logits, t, E, k_route, lane, idx, wts, s_sorted_e);
+    __syncthreads();
+    if (p < P) e_p = s_sorted_e[p];
+    __syncthreads();
+  } else if (p < P) {
+    e_p = idx[p];
+  }
   // unique sort key: expert, then pair id (stable)
-  const int key = p < P ? idx[p] * kDecMaxPairs + p : 0x7FFFFFFF;
+  const int key = p < P ? e_p * kDecMaxPairs + p : 0x7FFFFFFF;
   s_key[p] = key;
   __syncthreads();
   int pos = 0;
@@ -437,8 +454,8 @@ static int dec_resident_workgroups(bool gate_up, int bpl) {
 }
 
 hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
-                                 const int32_t *idx, const float *wts, uint16_t *y, char *ws,
-                                 hipStream_t s) {
+                                 const float *logits, int32_t *idx, float *wts, uint16_t *y,
+                                 char *ws, hipStream_t s) {
   DecodeWs w;
   // the decode path reuses the sorted / pos slots of the permutation region
   w.sorted = reinterpret_cast<int32_t *>(ws + p.off_sorted);
@@ -462,7 +479,8 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
   const int target_gu = dec_resident_workgroups(true, bpl_gu);
   const int target_dn = dec_resident_workgroups(false, bpl_dn);
   if (target_gu <= 0 || target_dn <= 0) return hipErrorInvalidDeviceFunction;
-  hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(256), 0, s, idx, P, int(p.k),
+  hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(256), 0, s, logits, int(p.E), idx, wts,
+                     P, int(p.k),
                      I / kDecTile, H / kDecTile, target_gu, target_dn, w);
 
   auto launch = [&](bool gate_up, int K_in, int n_units, const e4b_stack &st,

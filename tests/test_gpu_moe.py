@@ -80,11 +80,16 @@ def test_route_exact_workload_logits(name, T):
     # route through a forward on a tiny stand-in layer with the same E and k
     small = MoEConfig("s", E=cfg.E, H=64, I=64, k=cfg.k, T=cfg.T, routing=cfg.routing)
     pb = Problem(small, seed=0, with_grad=False)
-    e4b.moe_forward(pb.layer, pb.x_d, cfg.k, logits=torch.from_numpy(lg).to(DEV), topk_idx=idx,
-                    topk_w=w, path="grouped")
     idx_ref, w_ref = oracle.route(lg, cfg.k)
-    assert np.array_equal(idx.cpu().numpy(), idx_ref)
-    assert np.max(np.abs(w.cpu().numpy() - w_ref)) <= 1e-6
+    # decode-sized batches are also routed inside the decode prep kernel
+    paths = ["grouped", "decode"] if cfg.T <= 8 else ["grouped"]
+    for path in paths:
+        idx.fill_(-1)
+        w.fill_(0.0)
+        e4b.moe_forward(pb.layer, pb.x_d, cfg.k, logits=torch.from_numpy(lg).to(DEV),
+                        topk_idx=idx, topk_w=w, path=path)
+        assert np.array_equal(idx.cpu().numpy(), idx_ref), path
+        assert np.max(np.abs(w.cpu().numpy() - w_ref)) <= 1e-6, path
     del lib
 
 
