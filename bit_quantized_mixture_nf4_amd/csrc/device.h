@@ -47,14 +47,4 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return uint16_t(pack_bf16x2(f, 0.0f) & 0xFFFFu);
 }
 
-// Hardware dispatch places consecutive workgroup ids on consecutive XCDs
-// (8 per MI355X). Remap so that each XCD receives a contiguous range of
-// logical tile ids, keeping tiles that share operands inside one L2.
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t G) {
-  constexpr uint32_t X = 8;
-  const uint32_t q = G / X, r = G % X;
-  const uint32_t xcd = b % X, idx = b / X;
-  return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-}
-
 }  // namespace e4b

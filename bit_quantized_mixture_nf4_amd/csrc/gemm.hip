@@ -73,13 +73,20 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   const int wave = tid >> 6;
   const int wm = wave / kGemmWavesN, wn = wave % kGemmWavesN;
 
-  // ---- tile -> (expert, m-tile, n-tile) ----
-  const uint32_t L = xcd_remap(blockIdx.x, g.grid);
+  // ---- tile -> (expert, m-tile, n-tile). The grid is sized for the most
+  // m-tiles any routing can produce; the W tiles this routing has are split
+  // into eight contiguous ranges of equal length, one per XCD (dispatch puts
+  // block b on XCD b % 8), so every XCD gets the same share of real tiles
+  // and the n-tiles of one m-tile share that XCD's L2. Blocks past the
+  // ranges exit at once. ----
+  const int n_mt = g.tile_offsets[g.E];
+  const uint32_t W = uint32_t(n_mt) * uint32_t(g.n_tiles);
+  const uint32_t per_xcd = (W + 7) / 8, xi = blockIdx.x / 8;
+  const uint32_t L = (blockIdx.x % 8) * per_xcd + xi;
+  if (xi >= per_xcd || L >= W) return;
   const int mt = int(L / uint32_t(g.n_tiles));
   const int nt = int(L % uint32_t(g.n_tiles));
-  const int n_mt = g.tile_offsets[g.E];
-  const int4 tm = g.tile_map[min(mt, int(g.grid / uint32_t(g.n_tiles)) - 1)];
-  if (mt >= n_mt) return;
+  const int4 tm = g.tile_map[mt];
   const int e = tm.x, seg = tm.y, row0 = tm.z, valid_rows = tm.w;
 
   if (!QB && tid < 16) sCode[tid] = codebook_value(g.cb, tid);
@@ -558,7 +565,8 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
 
 hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s) {
   if (a.grid == 0) return hipSuccess;
-  const dim3 grid(a.grid);
+  // a multiple of 8 blocks: each XCD then has at least ceil(W / 8) of them
+  const dim3 grid((a.grid + 7) / 8 * 8);
   timer_before(int(v), s);
   const bool qb = a.cb == E4B_CB_BF16;
 #define E4B_GEMM(AM, BM, EP, WNV)                                                               \

@@ -73,7 +73,7 @@ PermView perm_in_saved(const MoePlan &p, char *saved);
 hipError_t launch_permute(const MoePlan &p, const int32_t *idx, char *ws, const PermView &v,
                           hipStream_t s);
 
-// grid must equal m_tiles_bound * n_tiles.
+// grid = m_tiles_bound * n_tiles; the launch rounds it up to a multiple of 8.
 hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s);
 
 hipError_t launch_combine_rows(const uint16_t *rows, const int32_t *pos_of_pair, const float *w,
