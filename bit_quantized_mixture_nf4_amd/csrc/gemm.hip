@@ -44,6 +44,20 @@ enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_DSWIGLU = 2, EPI_ACT = 3, EPI_DACT = 4
 
 constexpr int kLds = kBK + 8;  // padded row (bf16 elements): 144 bytes, conflict-free b128 access
 
+// B_NN tile in LDS: 16-byte unit u of a row is stored at unit u ^ ((u >> 3) & 3),
+// which puts the 8 threads writing one row's units on distinct banks
+__device__ __forceinline__ int nn_unit(int u) { return u ^ ((u >> 3) & 3); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+// gfx950 LDS transpose read: within each 16-lane group, lane s supplies the
+// address of 4 bf16 (row s / 4, columns 4 (s % 4) .. + 3 of a 4 x 16 block)
+// and receives column s of the block (rows 0..3)
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(const_cast<uint16_t *>(p)));
+}
+
 // hardware reciprocal (about 1 ulp): the result is rounded to bf16 anyway
 __device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
@@ -63,6 +77,15 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   constexpr int kBN = 128 * WN;
   constexpr int kStages = WN == 1 ? 1 : 2;
   constexpr int kAPass = kBM * 8 / kThreads;  // A rows per thread per K-step
+  // B_NN with 4-bit codes: the dequantized tile is stored [k][n] (64 rows of
+  // kBN columns, row stride kSBn elements = 32 bytes past a multiple of 128,
+  // 16-byte units of a row XOR-swizzled by nn_unit) and the MFMA operand
+  // (8 consecutive k of one n per lane) is read with the LDS transpose read
+  // ds_read_b64_tr_b16, which hands each lane of a 16-lane group 4
+  // consecutive rows of one column of a 4 x 16 block.
+  constexpr bool kNNq = BMODE == B_NN && !QB;
+  constexpr int kSBn = kBN + 16;
+  static_assert(kBK * kSBn <= kBN * kLds, "B_NN tile fits the B stage");
   // the codebook first: its LDS address fits a ds_read's immediate offset
   __shared__ __attribute__((aligned(64))) float sCode[16];
   __shared__ __attribute__((aligned(16))) uint16_t sA[kStages][kBM * kLds];
@@ -124,18 +147,23 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   }
   const uint8_t *b_src_nt = wp + int64_t(b_row) * row_bytes + b_half * (QB ? 64 : 16);
   const float *b_am_nt = wa + int64_t(b_row) * row_blocks;
-  // B_NN: thread owns a 4 (k) x 8 (n) patch: n group cg, k group kg (16)
+  // B_NN, bf16 lane: thread owns a 4 (k) x 8 (n) patch: n group cg, k group kg (16)
   const int b_cg = tid >> 4, b_kg = tid & 15;
   int b_n = nt * kBN + b_cg * 8;
   b_n = b_n < g.N ? b_n : 0;
-  const uint8_t *b_src_nn = wp + int64_t(b_kg * 4) * row_bytes + (QB ? b_n * 2 : b_n >> 1);
-  const float *b_am_nn = wa + int64_t(b_kg * 4) * row_blocks + (b_n >> 6);
+  const uint8_t *b_src_nn = wp + int64_t(b_kg * 4) * row_bytes + b_n * 2;
+  // B_NN, 4-bit codes: thread owns 32 consecutive columns (16 bytes, inside
+  // one absmax block) of one of the K-step's 64 weight rows; the tile is
+  // kept in LDS in the weights' own [k][n] order (row stride kSBn)
+  const int q_row = tid / (kBN / 32), q_c = tid % (kBN / 32);
+  int q_col = nt * kBN + q_c * 32;
+  q_col = q_col < g.N ? q_col : 0;
+  const uint8_t *b_src_q = wp + int64_t(q_row) * row_bytes + (q_col >> 1);
+  const float *b_am_q = wa + int64_t(q_row) * row_blocks + (q_col >> 6);
 
   u32x4 ra[kAPass];
   u32x4 rb;
   float ram;
-  uint32_t rbn[4];
-  float ramn[4];
   u32x4 rbq[QB ? 4 : 1];  // bf16 lane: B_NT 32 elements of a row, B_NN 4 rows x 8 columns
 
   auto load = [&](int ks) {
@@ -153,12 +181,8 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
       rb = *reinterpret_cast<const u32x4 *>(b_src_nt + ks * (kBK / 2));
       ram = b_am_nt[ks];
     } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t k = int64_t(ks) * kBK + r;
-        rbn[r] = *reinterpret_cast<const uint32_t *>(b_src_nn + k * row_bytes);
-        ramn[r] = b_am_nn[k * row_blocks];
-      }
+      rb = *reinterpret_cast<const u32x4 *>(b_src_q + int64_t(ks) * kBK * row_bytes);
+      ram = b_am_q[int64_t(ks) * kBK * row_blocks];
     }
   };
 
@@ -184,7 +208,7 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
                     __builtin_amdgcn_perm(rbq[3][c >> 1], rbq[2][c >> 1], sel)};
         }
       }
-    } else if (BMODE == B_NT) {
+    } else if (BMODE == B_NT || kNNq) {
       // all 32 codebook reads are issued before the first product; each
       // byte of hi4 / lo4 is the byte offset (4 * nibble) of a table entry
       float c[32];
@@ -207,30 +231,13 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = __fmul_rn(c[8 * d + e], ram);
-        *reinterpret_cast<u32x4 *>(b_dst + b_c * kLds + b_half * 32 + d * 8) =
-            u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
-                  pack_bf16x2(v[6], v[7])};
+        const u32x4 q{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7])};
+        if (BMODE == B_NT)
+          *reinterpret_cast<u32x4 *>(b_dst + b_c * kLds + b_half * 32 + d * 8) = q;
+        else
+          *reinterpret_cast<u32x4 *>(b_dst + q_row * kSBn + nn_unit(4 * q_c + d) * 8) = q;
       }
-    } else {
-      float v[4][8];  // [k row r][n col c]
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t w = rbn[r];
-        const uint32_t hi4 = (w >> 2) & 0x3C3C3C3Cu, lo4 = (w << 2) & 0x3C3C3C3Cu;
-        const char *tbl = reinterpret_cast<const char *>(sCode);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const uint32_t sel = 0x0C0C0C00u | uint32_t(b);
-          v[r][2 * b] = __fmul_rn(
-              *reinterpret_cast<const float *>(tbl + __builtin_amdgcn_perm(0u, hi4, sel)), ramn[r]);
-          v[r][2 * b + 1] = __fmul_rn(
-              *reinterpret_cast<const float *>(tbl + __builtin_amdgcn_perm(0u, lo4, sel)), ramn[r]);
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        *reinterpret_cast<u32x2 *>(b_dst + (b_cg * 8 + c) * kLds + b_kg * 4) =
-            u32x2{pack_bf16x2(v[0][c], v[1][c]), pack_bf16x2(v[2][c], v[3][c])};
     }
   };
 
@@ -257,6 +264,19 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   // stores the next stage. Within one barrier interval both orders are safe:
   // the compute reads buffer `cur` (filled before the previous barrier) and
   // the stores fill buffer `cur ^ 1` (last read before the previous barrier).
+  // kNNq fragment addresses: lane (group qg = lane / 16, qs = lane % 16)
+  // reads rows 8 (qg / 2) + qs / 4 (+ 16 kk + 4 r) and the 4 columns
+  // wn * 128 + 32 j + 16 (qg % 2) + 4 (qs % 4) of the [k][n] tile
+  int q_off[4];
+  {
+    const int qg = lane >> 4, qs = lane & 15;
+    const int rrow = 8 * (qg >> 1) + (qs >> 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = wn * 128 + 32 * j + 16 * (qg & 1) + 4 * (qs & 3);
+      q_off[j] = rrow * kSBn + nn_unit(col >> 3) * 8 + (col & 7);
+    }
+  }
   auto compute = [&](int cur) {
     if (!wave_active) return;
     const uint16_t *a_src = sA[cur] + (wm * 64 + (lane & 31)) * kLds + (lane >> 5) * 8;
@@ -270,8 +290,15 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
       for (int i = 0; i < 2; ++i)
         af[slot][i] = *reinterpret_cast<const bf16x8 *>(a_src + i * 32 * kLds + kk * 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[slot][j] = *reinterpret_cast<const bf16x8 *>(b_src + j * 32 * kLds + kk * 16);
+      for (int j = 0; j < 4; ++j) {
+        if (kNNq) {
+          const uint16_t *p = sB[cur] + q_off[j] + kk * 16 * kSBn;
+          const s16x4 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 4 * kSBn);
+          bfr[slot][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          bfr[slot][j] = *reinterpret_cast<const bf16x8 *>(b_src + j * 32 * kLds + kk * 16);
+        }
+      }
     };
     if (kPrefetch) frag(0, 0);
 #pragma unroll
