@@ -25,8 +25,8 @@
 //
 // Tile: 256 (pairs) x 128 * WN (columns) x 64 (one quantization block per
 // K-step); 4 x WN waves, each 64 x 128 = 2 x 4 MFMA 32x32x16 tiles. WN = 2
-// (gate_up forward and both down GEMMs): 512 threads, one workgroup per CU,
-// double-buffered LDS. WN = 1 (gate_up dgrad): 256 threads, one LDS stage,
+// (both gate_up GEMMs and the down forward): 512 threads, one workgroup per
+// CU, double-buffered LDS. WN = 1 (down dgrad): 256 threads, one LDS stage,
 // two workgroups per CU. A and the dequantized B are staged in LDS; B is
 // dequantized once per workgroup (codebook in LDS, fp32 multiply by the block
 // absmax, round-to-nearest-even bf16), i.e. exactly the bf16 view that
@@ -612,10 +612,10 @@ hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s) 
       break;
     case GEMM_DOWN_FWD: E4B_GEMM(A_DIRECT, B_NT, EPI_STORE, kBNWide / 128); break;
     case GEMM_DOWN_DGRAD:
-      if (a.gated) E4B_GEMM(A_GATHER, B_NN, EPI_DSWIGLU, kBNWide / 128);
-      else E4B_GEMM(A_GATHER, B_NN, EPI_DACT, kBNWide / 128);
+      if (a.gated) E4B_GEMM(A_GATHER, B_NN, EPI_DSWIGLU, kBNNarrow / 128);
+      else E4B_GEMM(A_GATHER, B_NN, EPI_DACT, kBNNarrow / 128);
       break;
-    case GEMM_GATE_UP_DGRAD: E4B_GEMM(A_DIRECT, B_NN, EPI_STORE, kBNNarrow / 128); break;
+    case GEMM_GATE_UP_DGRAD: E4B_GEMM(A_DIRECT, B_NN, EPI_STORE, kBNWide / 128); break;
   }
 #undef E4B_GEMM
   const hipError_t err = hipGetLastError();

@@ -86,8 +86,8 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   const int64_t bn_gu = p->gated ? kBNWide / 2 : kBNWide;
   p->n_tiles_gu = (I + bn_gu - 1) / bn_gu;
   p->n_tiles_h = (H + kBNWide - 1) / kBNWide;
-  p->n_tiles_i = (I + kBNWide - 1) / kBNWide;
-  p->n_tiles_h_gud = (H + kBNNarrow - 1) / kBNNarrow;
+  p->n_tiles_i = (I + kBNNarrow - 1) / kBNNarrow;
+  p->n_tiles_h_gud = (H + kBNWide - 1) / kBNWide;
   p->nbits_e = bits_for(E);
 
   size_t off = 0;

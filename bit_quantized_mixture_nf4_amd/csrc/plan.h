@@ -13,9 +13,9 @@ namespace e4b {
 
 // Tile shape shared by every grouped GEMM of the forward and dgrad.
 constexpr int kBM = 256;   // rows (routed pairs) per tile
-// output columns per tile: 256 (8 waves, one workgroup per CU) for the gate_up
-// forward and both down GEMMs, 128 (4 waves, two workgroups per CU) for the
-// gate_up dgrad, each the faster shape for that GEMM
+// output columns per tile: 256 (8 waves, one workgroup per CU) for both
+// gate_up GEMMs and the down forward, 128 (4 waves, two workgroups per CU) for
+// the down dgrad, each the faster shape for that GEMM
 constexpr int kBNWide = 256;
 constexpr int kBNNarrow = 128;
 constexpr int kBK = 64;    // reduction step = one quantization block
@@ -37,8 +37,8 @@ struct MoePlan {
   int64_t m_tiles_bound;  // upper bound of sum_e ceil(count_e / kBM)
   int64_t n_tiles_gu;     // gate_up forward tiles: kBNWide/2 gate-up pairs per tile
   int64_t n_tiles_h;      // down forward tiles over H (kBNWide)
-  int64_t n_tiles_i;      // down dgrad tiles over I (kBNWide)
-  int64_t n_tiles_h_gud;  // gate_up dgrad tiles over H (kBNNarrow)
+  int64_t n_tiles_i;      // down dgrad tiles over I (kBNNarrow)
+  int64_t n_tiles_h_gud;  // gate_up dgrad tiles over H (kBNWide)
   int nbits_e;            // bits needed for an expert id
   // workspace byte offsets
   size_t off_hist, off_chunk_base, off_counts, off_offsets, off_tile_offsets;
