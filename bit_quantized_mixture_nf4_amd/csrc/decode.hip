@@ -93,13 +93,17 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const float *__restric
   __shared__ int32_t s_sorted_p[kDecMaxPairs];
   __shared__ int32_t s_dseg[kDecMaxPairs + 1];
   __shared__ int32_t s_wsum[5][4];
+  __shared__ RouteLds s_route[kDecMaxPairs / 64];
+  __shared__ int4 s_item[kDecMaxPairs];          // distinct expert: id, pairs, segment, tokens
+  __shared__ int32_t s_first[2][kDecMaxPairs + 1];  // its first work item per map
+  __shared__ int32_t s_tpw[2][kDecMaxPairs];        // its tiles per work item per map
   const int p = threadIdx.x, lane = p & 63, wv = p >> 6;
   int e_p = 0;
   if (logits) {
     // s_sorted_e doubles as the routed ids until the keys are built
     const int T = P / k_route;
     for (int t = wv; t < T; t += kDecMaxPairs / 64)
-      route_token(logits, t, E, k_route, lane, idx, wts, s_sorted_e);
+      route_token(logits, t, E, k_route, lane, idx, wts, s_sorted_e, s_route[wv]);
     __syncthreads();
     if (p < P) e_p = s_sorted_e[p];
     __syncthreads();
@@ -169,29 +173,43 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const float *__restric
   }
   __syncthreads();
   // this expert's id, segment and tokens (np <= 8: one token per expert
-  // slot, T <= 8)
-  int e_d = 0, s0 = 0, toks = 0;
+  // slot, T <= 8) and its first work item in each map go to LDS; then all
+  // threads write the items, item b by thread b % 256 (its expert found by a
+  // binary search over the first items)
   if (p < n) {
-    s0 = s_dseg[p];
-    e_d = s_sorted_e[s0];
+    const int s0 = s_dseg[p];
+    int toks = 0;
     for (int q = 0; q < min(np_d, 8); ++q) toks |= (s_sorted_p[s0 + q] / k_route) << (4 * q);
+    s_item[p] = make_int4(s_sorted_e[s0], np_d, s0, toks);
   }
-  int4 *maps[2] = {w.map_gu, w.map_dn};
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     int base = 0;
     for (int v = 0; v < wv; ++v) base += s_wsum[1 + j][v];
-    const int end = base + incl[j];
     if (p < n) {
-      const int c = (tiles[j] + tpw[j] - 1) / tpw[j];
-      const int first_b = end - c;
-      for (int b = first_b; b < end; ++b) {
-        const int tile0 = (b - first_b) * tpw[j];
-        maps[j][b] = dec_item(e_d, np_d, tile0, min(tpw[j], tiles[j] - tile0), s0, toks);
-      }
+      s_first[j][p] = base + incl[j] - (tiles[j] + tpw[j] - 1) / tpw[j];
+      s_tpw[j][p] = tpw[j];
     }
     if (p == 0)
-      w.map_count[j] = s_wsum[1 + j][0] + s_wsum[1 + j][1] + s_wsum[1 + j][2] + s_wsum[1 + j][3];
+      s_first[j][n] = s_wsum[1 + j][0] + s_wsum[1 + j][1] + s_wsum[1 + j][2] + s_wsum[1 + j][3];
+  }
+  __syncthreads();
+  int4 *maps[2] = {w.map_gu, w.map_dn};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int count = s_first[j][n];
+    for (int b = p; b < count; b += kDecMaxPairs) {
+      int lo = 0, hi = n - 1;  // the last expert whose first item is <= b
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_first[j][mid] <= b) lo = mid;
+        else hi = mid - 1;
+      }
+      const int4 it = s_item[lo];
+      const int tile0 = (b - s_first[j][lo]) * s_tpw[j][lo];
+      maps[j][b] = dec_item(it.x, it.y, tile0, min(s_tpw[j][lo], tiles[j] - tile0), it.z, it.w);
+    }
+    if (p == 0) w.map_count[j] = count;
   }
 }
 

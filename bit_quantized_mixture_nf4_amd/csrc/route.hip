@@ -19,10 +19,11 @@ namespace e4b {
 __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ logits, int64_t T,
                                                     int E, int k, int32_t *__restrict__ idx,
                                                     float *__restrict__ wts) {
+  __shared__ RouteLds s_route[4];
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  route_token(logits, t, E, k, lane, idx, wts, nullptr);
+  route_token(logits, t, E, k, lane, idx, wts, nullptr, s_route[threadIdx.x >> 6]);
 }
 
 // hist[e * nchunks + c] = number of pairs of chunk c routed to expert e.
