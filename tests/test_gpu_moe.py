@@ -93,6 +93,28 @@ def test_route_exact_workload_logits(name, T):
     del lib
 
 
+@pytest.mark.parametrize("E,k,levels", [(8, 2, 2), (64, 32, 2), (128, 8, 4), (1024, 32, 1)])
+def test_route_ties(E, k, levels):
+    # logits drawn from a few values: the order among equal logits (lower
+    # expert id first) decides the selection; with one level every logit
+    # ties (more candidates than the parallel form holds: the serial form)
+    rng = np.random.default_rng(E + k)
+    announce(f"route ties E={E} k={k} levels={levels}")
+    small = MoEConfig("s", E=E, H=64, I=64, k=k, T=8, routing="uniform")
+    pb = Problem(small, seed=0, with_grad=False)
+    for T, paths in ((8, ["grouped", "decode"]), (48, ["grouped"])):
+        lg = rng.integers(0, levels, size=(T, E)).astype(np.float32) * 0.5
+        x = torch.zeros(T, 64, dtype=torch.bfloat16, device=DEV)
+        idx_ref, w_ref = oracle.route(lg, k)
+        for path in paths:
+            idx = torch.full((T, k), -1, dtype=torch.int32, device=DEV)
+            w = torch.zeros(T, k, dtype=torch.float32, device=DEV)
+            e4b.moe_forward(pb.layer, x, k, logits=torch.from_numpy(lg).to(DEV), topk_idx=idx,
+                            topk_w=w, path=path)
+            assert np.array_equal(idx.cpu().numpy(), idx_ref), (T, path)
+            assert np.max(np.abs(w.cpu().numpy() - w_ref)) <= 1e-6, (T, path)
+
+
 def test_permutation_exact(tiny):
     cfg = tiny.cfg
     ws = torch.zeros(e4b.workspace_bytes(tiny.layer, cfg.T, cfg.k), dtype=torch.uint8, device=DEV)
