@@ -222,7 +222,7 @@ def time_kernels(e4b, torch, ev, step, names, n):
 
 
 # Kernel sources whose text fixes the grouped GEMMs' memory traffic.
-GEMM_SOURCES = ("gemm.hip", "device.h", "kernels.h")
+GEMM_SOURCES = ("gemm.hip", "device.h", "kernels.h", "plan.h")
 
 
 def gemm_source_digest():
