@@ -17,6 +17,9 @@ What it computes (float64 unless a step fixes another precision):
   storage-fidelity ordering.
 * ``lora``       -- per-expert LoRA adapters over the frozen base: forward,
   dgrad and the adapter weight gradients.
+* ``mx``         -- MXFP4 storage: E2M1 elements with an E8M0 scale per 32
+  elements (the conversion rule of the OCP MX v1.0 specification), and its
+  exact dequantization.
 
 Sources: the experts4bit-qlora / bitsandbytes pages on fused 4-bit expert
 storage (the 0.1.0 sdist's ``_vendor/experts.py`` module ``Experts4bit``; the
@@ -27,7 +30,8 @@ the passage it follows.
 Pin status (see tests/test_oracle_*.py):
 
 * codebooks, quantize, dequantize, bf16 rounding, route, permute, forward,
-  dgrad, fidelity ordering, LoRA forward / backward: pinned by published
+  dgrad, fidelity ordering, LoRA forward / backward, MXFP4 conversion and
+  dequantization: pinned by published
   tables, closed forms (merged weights W + s B A), brute force, finite
   differences and library cross-checks.
 * absolute fidelity magnitudes quoted on the pages (forward relative error
@@ -47,3 +51,4 @@ from .quant import (  # noqa: F401
 from .moe import route, permute, moe_forward, moe_dgrad, silu  # noqa: F401
 from .fidelity import rel_fro, reconstruction_errors  # noqa: F401
 from .lora import lora_forward, lora_backward  # noqa: F401
+from .mx import quantize_mx, dequantize_mx, e2m1_value, e8m0_value  # noqa: F401

@@ -143,7 +143,8 @@ def bf16_bits_to_f32(bits):
 def stored_weights(w, kind):
     """fp32 values that a stack stored in mode ``kind`` represents.
 
-    ``nf4`` / ``fp4``: blockwise quantize then dequantize (above). ``bf16``:
+    ``nf4`` / ``fp4``: blockwise quantize then dequantize (above). ``mxfp4``:
+    the MX conversion and its exact dequantization (``oracle.mx``). ``bf16``:
     the 16-bit passthrough lane of the 0.4.0 README's support matrix (the
     reference baseline, no absmax): each weight rounded to bf16, nearest
     even.
@@ -152,5 +153,9 @@ def stored_weights(w, kind):
     if kind == "bf16":
         return bf16_bits_to_f32(bf16_rne_bits(w))
     E, out, inn = w.shape
+    if kind == "mxfp4":
+        from .mx import quantize_mx, dequantize_mx
+
+        return dequantize_mx(*quantize_mx(w), out, inn)
     packed, absmax = quantize_blockwise(w, kind)
     return dequantize(packed, absmax, out, inn, kind)

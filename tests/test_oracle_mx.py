@@ -1,0 +1,134 @@
+"""Pins of the MXFP4 oracle (oracle/mx.py) against the format definitions of
+the OCP Microscaling Formats (MX) v1.0 specification that the pages' "MXFP4"
+refers to: the E2M1 bit-level decode, the E8M0 scale, the shared-exponent
+rule, round-to-nearest-even with saturation, brute force and round trips."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import mx
+
+
+def _e2m1_from_bits(code):
+    # sign | 2 exponent bits (bias 1) | 1 mantissa bit; exponent 0: subnormal
+    s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    v = m * 0.5 if e == 0 else math.ldexp(1.0 + m / 2.0, e - 1)
+    return -v if s else v
+
+
+def test_e2m1_values_from_the_bit_definition():
+    got = mx.e2m1_value(np.arange(16))
+    want = np.array([_e2m1_from_bits(c) for c in range(16)])
+    assert np.array_equal(got, want)
+    assert list(np.abs(want[:8])) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert np.signbit(got[8]) and got[8] == 0.0  # code 8 is -0
+
+
+def test_e8m0_scale():
+    assert mx.e8m0_value(127) == 1.0
+    assert mx.e8m0_value(0) == 2.0 ** -127
+    assert mx.e8m0_value(254) == 2.0 ** 127
+    with pytest.raises(ValueError):
+        mx.e8m0_value(255)  # NaN code
+
+
+def _one_block(vals):
+    w = np.zeros((1, 1, 32), dtype=np.float32)
+    w[0, 0, : len(vals)] = vals
+    p, s = oracle.quantize_mx(w)
+    q = np.empty(32, dtype=np.int64)
+    q[0::2] = p[0] >> 4
+    q[1::2] = p[0] & 15
+    return q, int(s[0, 0])
+
+
+@pytest.mark.parametrize(
+    "amax,shared",
+    [(6.0, 0), (4.0, 0), (7.99, 0), (1.0, -2), (0.75, -3), (2.0 ** -100, -102), (3.0e38, 125)],
+)
+def test_shared_exponent_rule(amax, shared):
+    # floor(log2(amax)) - 2, by hand
+    q, s = _one_block([amax])
+    assert s - 127 == shared
+    assert shared == math.floor(math.log2(amax)) - 2
+
+
+def test_zero_block_and_negative_zero():
+    q, s = _one_block([0.0])
+    assert s == 0 and np.all(q == 0)
+    q, s = _one_block([4.0, -0.01, -0.0])
+    # scale 2^0: -0.01 rounds to magnitude 0 and keeps its sign (code 8), as does -0.0
+    assert s == 127 and q[0] == 6 and q[1] == 8 and q[2] == 8
+
+
+def test_round_to_nearest_even_and_saturation():
+    # scale 2^0 fixed by the 6.0 in the block; values on every midpoint
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    q, s = _one_block([6.0] + mids + [5.0000005, 4.9999995])
+    assert s == 127
+    # ties go to the even mantissa: 0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0
+    assert list(q[1:8]) == [0, 2, 2, 4, 4, 6, 6]
+    assert q[8] == 7 and q[9] == 6  # just above / below 5
+    q, s = _one_block([7.99, 6.5, -7.0])
+    assert s == 127 and list(q[:3]) == [7, 7, 15]  # saturated to +-6
+
+
+def test_brute_force_nearest_value():
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((3, 8, 96)) * np.exp(rng.uniform(-6, 6, (3, 8, 1)))).astype(np.float32)
+    p, s = oracle.quantize_mx(w)
+    vals = oracle.dequantize_mx(p, s, 8, 96).reshape(-1, 32).astype(np.float64)
+    blocks = w.reshape(-1, 32).astype(np.float64)
+    scale = mx.e8m0_value(s.reshape(-1))
+    cand = np.array([_e2m1_from_bits(c) for c in range(8)])
+    for b in range(blocks.shape[0]):
+        amax = np.abs(blocks[b]).max()
+        assert scale[b] == 2.0 ** (math.floor(math.log2(amax)) - 2)
+        for i in range(32):
+            a = abs(blocks[b, i]) / scale[b]
+            d = np.abs(cand - a)
+            best = np.flatnonzero(d == d.min())
+            idx = best[0] if len(best) == 1 else [k for k in best if k % 2 == 0][0]
+            assert abs(vals[b, i]) == cand[idx] * scale[b]
+            if vals[b, i] != 0.0:
+                assert np.sign(vals[b, i]) == np.sign(blocks[b, i])
+
+
+def test_round_trip_and_exact_dequantization():
+    rng = np.random.default_rng(4)
+    E, out, inn = 2, 6, 64
+    nb = out * inn // 32
+    q = rng.integers(0, 16, size=(E, nb, 32))
+    # a magnitude index of 6 or 7 in every block keeps its shared exponent
+    q[:, :, 5] = rng.choice([6, 7, 14, 15], size=(E, nb))
+    s = rng.integers(1, 253, size=(E, nb)).astype(np.uint8)
+    flat = q.reshape(E, -1)
+    packed = ((flat[:, 0::2] << 4) | flat[:, 1::2]).astype(np.uint8)
+    w = oracle.dequantize_mx(packed, s, out, inn)
+    for e, b, i in [(0, 0, 0), (1, nb - 1, 31), (1, 3, 5)]:
+        assert float(w[e].reshape(-1, 32)[b, i]) == mx.mx_value_exact(int(q[e, b, i]), int(s[e, b]))
+    p2, s2 = oracle.quantize_mx(w)
+    # codes and scales come back bit for bit (-0 keeps its sign through fp32)
+    assert np.array_equal(s2, s)
+    assert np.array_equal(p2, packed)
+
+
+def test_stored_weights_mxfp4_dispatch():
+    rng = np.random.default_rng(5)
+    w = rng.normal(0, 0.02, (2, 4, 64)).astype(np.float32)
+    got = oracle.stored_weights(w, "mxfp4")
+    assert np.array_equal(got, oracle.dequantize_mx(*oracle.quantize_mx(w), 4, 64))
+    # the MX reconstruction is coarser than nf4's on Gaussian weights
+    e_mx = np.linalg.norm(got - w) / np.linalg.norm(w)
+    e_nf4 = np.linalg.norm(oracle.stored_weights(w, "nf4") - w) / np.linalg.norm(w)
+    assert e_mx > e_nf4
+
+
+def test_shape_errors():
+    with pytest.raises(ValueError):
+        oracle.quantize_mx(np.zeros((1, 2, 48), dtype=np.float32))  # in % 32
+    with pytest.raises(ValueError):
+        oracle.quantize_mx(np.zeros((2, 64), dtype=np.float32))
