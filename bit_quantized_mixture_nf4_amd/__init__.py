@@ -1,4 +1,4 @@
-"""MI355X-native fused blockwise-4-bit (NF4 / FP4) Mixture-of-Experts expert MLP.
+"""MI355X-native fused blockwise-4-bit (NF4 / FP4 / MXFP4) Mixture-of-Experts expert MLP.
 
 Thin Python binding over ``libe4b.so`` (C ABI in ``include/e4b.h``). PyTorch is
 used only for device memory and the current HIP stream: every computation runs
@@ -10,7 +10,8 @@ functions below marshal torch tensors into them.
 Layout (the fused-expert storage of the experts4bit-qlora 0.1.0 sdist,
 ``Experts4bit``): gate_up ``[E, 2I, H]`` (gate rows first), down
 ``[E, H, I]``; packed uint8 ``[E, out*in/2]`` (even element in the high
-nibble) and fp32 absmax ``[E, out*in/64]``.
+nibble) and fp32 absmax ``[E, out*in/64]`` (MXFP4: E8M0 scale bytes
+``[E, out*in/32]``).
 """
 
 import ctypes
@@ -21,7 +22,8 @@ import torch
 from . import _lib
 from ._lib import E4bLayer, E4bLora, E4bStack, E4bError, check, load  # noqa: F401
 
-CODEBOOKS = {"nf4": _lib.E4B_CB_NF4, "fp4": _lib.E4B_CB_FP4, "bf16": _lib.E4B_CB_BF16}
+CODEBOOKS = {"nf4": _lib.E4B_CB_NF4, "fp4": _lib.E4B_CB_FP4, "bf16": _lib.E4B_CB_BF16,
+             "mxfp4": _lib.E4B_CB_MXFP4}
 PATHS = {"auto": _lib.E4B_PATH_AUTO, "grouped": _lib.E4B_PATH_GROUPED, "decode": _lib.E4B_PATH_DECODE}
 
 __all__ = [
@@ -68,20 +70,22 @@ def _need(t, name, dtype, device=None, shape=None):
 @dataclass
 class QuantStack:
     """One stored fused stack of an [E, out, in] weight: packed 4-bit codes +
-    fp32 absmax, or (codebook "bf16", the passthrough lane) the bf16 weight as
-    bytes and no absmax."""
+    fp32 absmax, packed E2M1 codes + E8M0 scales (codebook "mxfp4"), or
+    (codebook "bf16", the passthrough lane) the bf16 weight as bytes."""
 
     packed: torch.Tensor  # uint8 [E, out*in/2]; bf16 lane: uint8 [E, out*in*2]
-    absmax: torch.Tensor  # float32 [E, out*in/64]; bf16 lane: None
+    absmax: torch.Tensor  # float32 [E, out*in/64]; bf16 / mxfp4: None
     E: int
     out: int
     inn: int
     codebook: str = "nf4"
+    scales: torch.Tensor = None  # mxfp4: uint8 [E, out*in/32]
 
     def as_c(self):
         return E4bStack(
             self.packed.data_ptr(), None if self.absmax is None else self.absmax.data_ptr(),
-            self.E, self.out, self.inn, 64, CODEBOOKS[self.codebook],
+            self.E, self.out, self.inn, 32 if self.codebook == "mxfp4" else 64,
+            CODEBOOKS[self.codebook], None if self.scales is None else self.scales.data_ptr(),
         )
 
     @property
@@ -118,13 +122,20 @@ class MoELayer:
 
 def quantize(w, codebook="nf4"):
     """Blockwise (64) absmax 4-bit quantization of a float32 [E, out, in] device stack
-    (codebook "nf4" / "fp4"), or its bf16 passthrough storage (codebook "bf16")."""
+    (codebook "nf4" / "fp4"), its MXFP4 conversion (codebook "mxfp4": E2M1 codes and
+    an E8M0 scale per 32 elements), or its bf16 passthrough storage (codebook "bf16")."""
     if w.dim() != 3:
         raise ValueError("w must be [E, out, in]")
     _need(w, "w", torch.float32)
     E, out, inn = w.shape
     if codebook not in CODEBOOKS:
         raise ValueError(f"codebook must be one of {sorted(CODEBOOKS)}")
+    if codebook == "mxfp4":
+        packed = torch.empty(E, out * inn // 2, dtype=torch.uint8, device=w.device)
+        scales = torch.empty(E, out * inn // 32, dtype=torch.uint8, device=w.device)
+        code = load().e4b_quantize_mxfp4(_vp(w), E, out, inn, _vp(packed), _vp(scales), _stream(w))
+        check("e4b_quantize_mxfp4", code)
+        return QuantStack(packed, None, E, out, inn, codebook, scales)
     bf16 = codebook == "bf16"
     packed = torch.empty(E, out * inn * 2 if bf16 else out * inn // 2, dtype=torch.uint8,
                          device=w.device)
@@ -345,7 +356,7 @@ class LayerPrefetcher:
         self.slots = []
         for _ in range(2):
             stacks = [QuantStack(_empty_like_on(st.packed, dev), _empty_like_on(st.absmax, dev),
-                                 st.E, st.out, st.inn, st.codebook)
+                                 st.E, st.out, st.inn, st.codebook, _empty_like_on(st.scales, dev))
                       for st in (ref.gate_up, ref.down)]
             self.slots.append(MoELayer(*stacks))
         self.stream = torch.cuda.Stream(device=dev)  # default priority

@@ -22,13 +22,14 @@ E4B_ERR_ALIGN = 7
 E4B_ERR_PATH = 8
 E4B_ERR_HIP = 9
 
-E4B_CB_NF4, E4B_CB_FP4, E4B_CB_BF16 = 0, 1, 2
+E4B_CB_NF4, E4B_CB_FP4, E4B_CB_BF16, E4B_CB_MXFP4 = 0, 1, 2, 3
 E4B_F32, E4B_BF16 = 0, 1
 E4B_PATH_AUTO, E4B_PATH_GROUPED, E4B_PATH_DECODE = 0, 1, 2
 
 # every function declared in include/e4b.h
 EXPORTS = (
     "e4b_quantize_nf4",
+    "e4b_quantize_mxfp4",
     "e4b_dequantize_nf4",
     "e4b_moe_forward",
     "e4b_moe_dgrad",
@@ -62,6 +63,7 @@ class E4bStack(ctypes.Structure):
         ("in_", ctypes.c_int64),
         ("blocksize", ctypes.c_int32),
         ("codebook", ctypes.c_int32),
+        ("scales", ctypes.c_void_p),
     ]
 
 
@@ -97,6 +99,7 @@ def load():
     st, lay, lo = ctypes.POINTER(E4bStack), ctypes.POINTER(E4bLayer), ctypes.POINTER(E4bLora)
     sigs = {
         "e4b_quantize_nf4": (i32, [vp, i64, i64, i64, i32, i32, vp, vp, vp]),
+        "e4b_quantize_mxfp4": (i32, [vp, i64, i64, i64, vp, vp, vp]),
         "e4b_dequantize_nf4": (i32, [st, i32, vp, vp]),
         "e4b_moe_forward": (i32, [lay, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, i32, vp]),
         "e4b_moe_dgrad": (i32, [lay, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),

@@ -28,10 +28,12 @@ GemmArgs base_args(const MoePlan &p, const e4b_stack &st, const PermView &v) {
   a.sorted_pair = v.sorted;
   a.topk = int32_t(p.k);
   a.Wp = st.packed;
-  a.Wa = st.absmax;
+  a.mx = st.codebook == E4B_CB_MXFP4;
+  a.Wa = a.mx ? nullptr : st.absmax;
+  a.Ws = a.mx ? st.scales : nullptr;
   const bool bf16 = st.codebook == E4B_CB_BF16;
   a.w_e_bytes = bf16 ? st.out * st.in * 2 : st.out * st.in / 2;
-  a.w_e_blocks = bf16 ? 0 : st.out * st.in / kBlock;  // BF16: no absmax buffer
+  a.w_e_blocks = bf16 ? 0 : st.out * st.in / (a.mx ? kMxBlock : kBlock);  // BF16: none
   a.w_in = int32_t(st.in);
   a.I = int32_t(p.I);
   a.offsets = v.offsets;

@@ -277,6 +277,9 @@ struct DecLoad<16> {
 struct DecCtx {
   const uint8_t *wp;   // this expert's packed rows, at the lane's byte offset
   const float *wa;     // this expert's absmax, at the lane's block
+  const uint8_t *ws;   // MXFP4: this expert's E8M0 scales, at the lane's block
+  int sstride;         // scale entries per weight row
+  bool mx;
   int row_bytes, nblk, I, tile0, nt, s0, np, kl, rq, wave, tid;
   int n_active;        // waves with K blocks (the others only meet the barriers)
   bool kvalid, active; // lane holds K bytes; this wave has K blocks
@@ -313,7 +316,7 @@ __device__ __forceinline__ void decode_tiles(const DecCtx &c, const uint32_t *tl
       for (int r = 0; r < NR; ++r) {
         const int64_t row = u + r * c.I;
         wv[ps][r] = *reinterpret_cast<const LT *>(c.wp + row * c.row_bytes);
-        am[ps][r] = c.wa[row * c.nblk];
+        am[ps][r] = c.mx ? e8m0_value(c.ws[row * c.sstride]) : c.wa[row * c.sstride];
       }
     }
   };
@@ -342,7 +345,7 @@ __device__ __forceinline__ void decode_tiles(const DecCtx &c, const uint32_t *tl
           const int u = (c.tile0 + tn) * kDecTile + 4 * ps + c.rq;
           const int64_t row = u + r * c.I;
           wv[ps][r] = *reinterpret_cast<const LT *>(c.wp + row * c.row_bytes);
-          am[ps][r] = c.wa[row * c.nblk];
+          am[ps][r] = c.mx ? e8m0_value(c.ws[row * c.sstride]) : c.wa[row * c.sstride];
         }
         float acc[NP];
 #pragma unroll
@@ -378,7 +381,8 @@ __device__ __forceinline__ void decode_tiles(const DecCtx &c, const uint32_t *tl
 
 template <bool GATE_UP, int BPL>
 __global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(
-    const uint8_t *__restrict__ Wp, const float *__restrict__ Wa, int64_t w_e_bytes,
+    const uint8_t *__restrict__ Wp, const float *__restrict__ Wa, const uint8_t *__restrict__ Ws,
+    int64_t w_e_bytes,
     int64_t w_e_blocks, int K_in, int n_units, int I, const uint16_t *__restrict__ vin,
     int k_route, DecodeWs w, int cb, uint16_t *__restrict__ out, int ldo) {
   constexpr int NR = GATE_UP ? 2 : 1;
@@ -424,7 +428,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(
   c.kvalid = c.kl * BPL < nb * 32;
   const int kbyte = c.kvalid ? b0 * 32 + c.kl * BPL : 0;
   c.wp = Wp + int64_t(e) * w_e_bytes + kbyte;
-  c.wa = Wa + int64_t(e) * w_e_blocks + (kbyte >> 5);
+  // a lane's BPL <= 16 bytes lie inside one 64-element absmax block and,
+  // 16-byte aligned, inside one 32-element MXFP4 block
+  c.mx = Ws != nullptr;
+  c.sstride = c.mx ? K_in >> 5 : c.nblk;
+  c.wa = c.mx ? nullptr : Wa + int64_t(e) * w_e_blocks + (kbyte >> 5);
+  c.ws = c.mx ? Ws + int64_t(e) * w_e_blocks + (kbyte >> 4) : nullptr;
   const int xoff = 2 * kbyte;  // element offset of the lane's input slice
 
 #define E4B_DEC_NP(N)                                                                        \
@@ -506,11 +515,13 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
     const int bpl = bpl_of(K_in);
     const int tiles = n_units / kDecTile;
     const dim3 grid(uint32_t(tiles * ymax));
-    const int64_t eb = st.out * st.in / 2, ea = st.out * st.in / kBlock;
+    const bool mx = st.codebook == E4B_CB_MXFP4;
+    const int64_t eb = st.out * st.in / 2, ea = st.out * st.in / (mx ? kMxBlock : kBlock);
     timer_before(kernel_id, s);
 #define E4B_DEC_LAUNCH(GU, B)                                                                 \
   hipLaunchKernelGGL((decode_gemv_kernel<GU, B>), grid, dim3(kDecThreads), 0, s, st.packed,     \
-                     st.absmax, eb, ea, K_in, n_units, I, vin, int(p.k), w, p.codebook, dst,    \
+                     mx ? nullptr : st.absmax, mx ? st.scales : nullptr, eb, ea, K_in, n_units, I, \
+                     vin, int(p.k), w, p.codebook, dst,                                          \
                      ldo)
     if (gate_up) {
       if (bpl == 4) E4B_DEC_LAUNCH(true, 4);

@@ -130,8 +130,11 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   // ---- B source; columns past N read a valid weight row/column instead
   // (their outputs are never stored) ----
   const uint8_t *wp = g.Wp + int64_t(e) * g.w_e_bytes;
-  const float *wa = g.Wa + int64_t(e) * g.w_e_blocks;
+  // block scales: fp32 absmax per 64 elements, or (MXFP4) an E8M0 byte per 32
+  const float *wa = g.mx ? nullptr : g.Wa + int64_t(e) * g.w_e_blocks;
+  const uint8_t *ws8 = g.mx ? g.Ws + int64_t(e) * g.w_e_blocks : nullptr;
   const int row_bytes = QB ? g.w_in * 2 : g.w_in >> 1, row_blocks = g.w_in >> 6;
+  const int row_mx = g.w_in >> 5;
   // B_NT: thread owns half (32 elements) of one tile column = one weight row
   const int b_c = tid >> 1, b_half = tid & 1;
   int b_row = 0;
@@ -146,7 +149,9 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
     }
   }
   const uint8_t *b_src_nt = wp + int64_t(b_row) * row_bytes + b_half * (QB ? 64 : 16);
-  const float *b_am_nt = wa + int64_t(b_row) * row_blocks;
+  const float *b_am_nt = g.mx ? nullptr : wa + int64_t(b_row) * row_blocks;
+  // MXFP4: the thread's 32 elements of K-step ks are the MX block 2 ks + b_half
+  const uint8_t *b_sc_nt = g.mx ? ws8 + int64_t(b_row) * row_mx + b_half : nullptr;
   // B_NN, bf16 lane: thread owns a 4 (k) x 8 (n) patch: n group cg, k group kg (16)
   const int b_cg = tid >> 4, b_kg = tid & 15;
   int b_n = nt * kBN + b_cg * 8;
@@ -159,7 +164,8 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   int q_col = nt * kBN + q_c * 32;
   q_col = q_col < g.N ? q_col : 0;
   const uint8_t *b_src_q = wp + int64_t(q_row) * row_bytes + (q_col >> 1);
-  const float *b_am_q = wa + int64_t(q_row) * row_blocks + (q_col >> 6);
+  const float *b_am_q = g.mx ? nullptr : wa + int64_t(q_row) * row_blocks + (q_col >> 6);
+  const uint8_t *b_sc_q = g.mx ? ws8 + int64_t(q_row) * row_mx + (q_col >> 5) : nullptr;
 
   u32x4 ra[kAPass];
   u32x4 rb;
@@ -179,10 +185,11 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
                                                         (int64_t(ks) * kBK + d) * row_bytes);
     } else if (BMODE == B_NT) {
       rb = *reinterpret_cast<const u32x4 *>(b_src_nt + ks * (kBK / 2));
-      ram = b_am_nt[ks];
+      ram = g.mx ? e8m0_value(b_sc_nt[2 * ks]) : b_am_nt[ks];
     } else {
       rb = *reinterpret_cast<const u32x4 *>(b_src_q + int64_t(ks) * kBK * row_bytes);
-      ram = b_am_q[int64_t(ks) * kBK * row_blocks];
+      ram = g.mx ? e8m0_value(b_sc_q[int64_t(ks) * kBK * row_mx])
+                 : b_am_q[int64_t(ks) * kBK * row_blocks];
     }
   };
 

@@ -21,9 +21,11 @@ struct GemmArgs {
   const int32_t *sorted_pair;
   int32_t topk;
   const uint8_t *Wp;   // packed stack
-  const float *Wa;     // absmax stack
+  const float *Wa;     // absmax stack (NF4, FP4)
+  const uint8_t *Ws;   // E8M0 scale stack (MXFP4, one byte per 32 elements)
+  int32_t mx;          // 1: MXFP4 (scales in Ws), 0: absmax in Wa
   int64_t w_e_bytes;   // packed bytes per expert
-  int64_t w_e_blocks;  // absmax entries per expert
+  int64_t w_e_blocks;  // absmax (or MXFP4 scale) entries per expert
   int32_t w_in;        // stored in_features
   int32_t N;           // output columns (gate/up: number of gate-up pairs = I)
   int32_t K;           // reduction length (multiple of 64)

@@ -21,14 +21,28 @@ int bits_for(int64_t n) {
 
 e4b_status check_stack(const e4b_stack *st) {
   if (!st || !st->packed) return E4B_ERR_NULL;
-  if (st->blocksize != kBlock) return E4B_ERR_BLOCKSIZE;
-  if (st->codebook != E4B_CB_NF4 && st->codebook != E4B_CB_FP4 && st->codebook != E4B_CB_BF16)
+  if (st->codebook != E4B_CB_NF4 && st->codebook != E4B_CB_FP4 && st->codebook != E4B_CB_BF16 &&
+      st->codebook != E4B_CB_MXFP4)
     return E4B_ERR_CODEBOOK;
-  const bool bf16 = st->codebook == E4B_CB_BF16;
-  if (!bf16 && !st->absmax) return E4B_ERR_NULL;
+  const bool mx = st->codebook == E4B_CB_MXFP4;
+  if (st->blocksize != (mx ? kMxBlock : kBlock)) return E4B_ERR_BLOCKSIZE;
+  // the scale buffer of the mode: fp32 absmax (NF4, FP4), E8M0 bytes (MXFP4), none (BF16)
+  const void *scale = mx ? static_cast<const void *>(st->scales)
+                         : st->codebook == E4B_CB_BF16 ? nullptr : st->absmax;
+  if (st->codebook != E4B_CB_BF16 && !scale) return E4B_ERR_NULL;
+  // rows are whole 64-element K-steps of the GEMMs in every mode
   if (st->E <= 0 || st->out <= 0 || st->in <= 0 || st->in % kBlock != 0) return E4B_ERR_SHAPE;
   if (st->out * st->in > kMaxElems32 * 2) return E4B_ERR_SHAPE;
-  if (!aligned16(st->packed) || (!bf16 && !aligned16(st->absmax))) return E4B_ERR_ALIGN;
+  if (!aligned16(st->packed) || (scale && !aligned16(scale))) return E4B_ERR_ALIGN;
+  return E4B_OK;
+}
+
+e4b_status check_quantize_mx(const float *w, int64_t E, int64_t out, int64_t in,
+                             const uint8_t *packed, const uint8_t *scales) {
+  if (!w || !packed || !scales) return E4B_ERR_NULL;
+  if (E <= 0 || out <= 0 || in <= 0 || in % kMxBlock != 0) return E4B_ERR_SHAPE;
+  if (out * in > kMaxElems32 * 2) return E4B_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(packed) || !aligned16(scales)) return E4B_ERR_ALIGN;
   return E4B_OK;
 }
 
@@ -202,7 +216,7 @@ extern "C" const char *e4b_status_string(e4b_status s) {
     case E4B_OK: return "ok";
     case E4B_ERR_NULL: return "a required pointer is NULL";
     case E4B_ERR_SHAPE: return "invalid shape (dims <= 0, in % 64 != 0, top_k out of range, E > 1024, mismatched stacks or too large)";
-    case E4B_ERR_BLOCKSIZE: return "blocksize must be 64";
+    case E4B_ERR_BLOCKSIZE: return "blocksize must be 64 (MXFP4: 32)";
     case E4B_ERR_CODEBOOK: return "unknown codebook or gate_up/down codebooks differ";
     case E4B_ERR_DTYPE: return "unknown output dtype";
     case E4B_ERR_WORKSPACE: return "workspace missing or too small";

@@ -20,6 +20,7 @@ constexpr int kBNWide = 256;
 constexpr int kBNNarrow = 128;
 constexpr int kBK = 64;    // reduction step = one quantization block
 constexpr int kBlock = 64; // quantization block (elements along `in`)
+constexpr int kMxBlock = 32;  // MXFP4 scale block (elements along `in`)
 constexpr int kPermChunk = 1024;  // pairs per histogram / scatter chunk
 constexpr int kMaxE = 1024;
 constexpr int kMaxTopK = 32;
@@ -72,6 +73,8 @@ e4b_status check_stack(const e4b_stack *st);
 e4b_status check_quantize(const float *w, int64_t E, int64_t out, int64_t in,
                           int32_t blocksize, int32_t codebook, const uint8_t *packed,
                           const float *absmax);
+e4b_status check_quantize_mx(const float *w, int64_t E, int64_t out, int64_t in,
+                             const uint8_t *packed, const uint8_t *scales);
 
 // True when (T, H, I, k) fit the decode GEMV path: T <= 8 and a weight row
 // spans at most 64 lanes of 64 (T <= 2) or 32 (T <= 8) elements.

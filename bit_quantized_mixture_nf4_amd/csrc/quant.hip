@@ -54,10 +54,60 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
   if (lane == 0) absmax[blk] = m;
 }
 
-// One thread per 8 consecutive elements (4 packed bytes).
+// MXFP4 conversion (OCP MX v1.0, the reading of the 0.31.1 project page's
+// MXFP4 experts): one thread per 32-element block. The shared exponent is
+// floor(log2(amax)) - 2 from amax's exponent field (frexpf, exact), clamped
+// to [-127, 127]; w * 2^-shared is exact wherever it matters (a product that
+// underflows to a subnormal is below 0.25 and rounds to zero either way); the
+// E2M1 index is counted against the exact midpoints, with the ties whose lower
+// neighbour has an odd mantissa (0.75, 1.75, 3.5) moved up to the even one.
+__global__ __launch_bounds__(256) void quantize_mx_kernel(const float *__restrict__ w,
+                                                          int64_t nblocks,
+                                                          uint8_t *__restrict__ packed,
+                                                          uint8_t *__restrict__ scales) {
+  const int64_t blk = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (blk >= nblocks) return;
+  const f32x4 *src = reinterpret_cast<const f32x4 *>(w + blk * kMxBlock);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const f32x4 q = src[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[4 * i + j] = q[j];
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  int ex = 0;
+  frexpf(amax, &ex);  // amax = m * 2^ex, 0.5 <= m < 1
+  const int sh = amax == 0.0f ? -127 : min(127, max(-127, ex - 1 - 2));
+  uint32_t q[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float a = fabsf(ldexpf(v[i], -sh));
+    uint32_t m = (a > 0.25f) + (a > 0.75f) + (a > 1.25f) + (a > 1.75f) + (a > 2.5f) +
+                 (a > 3.5f) + (a > 5.0f);
+    m += (a == 0.75f) | (a == 1.75f) | (a == 3.5f);
+    q[i] = m | (signbit(v[i]) ? 8u : 0u);
+  }
+  u32x4 o;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) word |= ((q[8 * d + 2 * b] << 4) | q[8 * d + 2 * b + 1]) << (8 * b);
+    o[d] = word;
+  }
+  reinterpret_cast<u32x4 *>(packed)[blk] = o;
+  scales[blk] = uint8_t(sh + 127);
+}
+
+// One thread per 8 consecutive elements (4 packed bytes). MXFP4 (scales !=
+// nullptr): the block scale is the E8M0 byte of the 32-element block.
 template <bool BF16>
 __global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t *__restrict__ packed,
                                                          const float *__restrict__ absmax,
+                                                         const uint8_t *__restrict__ scales,
                                                          int64_t ngroups, int cb,
                                                          void *__restrict__ out) {
   __shared__ float code[16];
@@ -66,7 +116,8 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t *__restr
   const int64_t g = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (g >= ngroups) return;
   const uint32_t d = packed[g];
-  const float a = absmax[g >> 3];  // 8 groups of 8 elements per 64-block
+  // 8 groups of 8 elements per 64-block; 4 per 32-element MX block
+  const float a = scales ? e8m0_value(scales[g >> 2]) : absmax[g >> 3];
   float v[8];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -135,6 +186,16 @@ extern "C" e4b_status e4b_quantize_nf4(const float *w, int64_t E, int64_t out, i
   return hipGetLastError() == hipSuccess ? E4B_OK : E4B_ERR_HIP;
 }
 
+extern "C" e4b_status e4b_quantize_mxfp4(const float *w, int64_t E, int64_t out, int64_t in,
+                                         uint8_t *packed, uint8_t *scales, hipStream_t stream) {
+  e4b_status s = check_quantize_mx(w, E, out, in, packed, scales);
+  if (s != E4B_OK) return s;
+  const int64_t nblocks = E * out * in / kMxBlock;
+  hipLaunchKernelGGL(quantize_mx_kernel, dim3(uint32_t((nblocks + 255) / 256)), dim3(256), 0,
+                     stream, w, nblocks, packed, scales);
+  return hipGetLastError() == hipSuccess ? E4B_OK : E4B_ERR_HIP;
+}
+
 extern "C" e4b_status e4b_dequantize_nf4(const e4b_stack *st, int32_t dtype, void *w_out,
                                          hipStream_t stream) {
   e4b_status s = check_stack(st);
@@ -155,12 +216,15 @@ extern "C" e4b_status e4b_dequantize_nf4(const e4b_stack *st, int32_t dtype, voi
     return hipGetLastError() == hipSuccess ? E4B_OK : E4B_ERR_HIP;
   }
   const uint32_t *pk = reinterpret_cast<const uint32_t *>(st->packed);
+  const bool mx = st->codebook == E4B_CB_MXFP4;
+  const float *am = mx ? nullptr : st->absmax;
+  const uint8_t *sc = mx ? st->scales : nullptr;
   if (dtype == E4B_BF16)
     hipLaunchKernelGGL(dequantize_kernel<true>, dim3(uint32_t(grid)), dim3(256), 0, stream, pk,
-                       st->absmax, ngroups, int(st->codebook), w_out);
+                       am, sc, ngroups, int(st->codebook), w_out);
   else
     hipLaunchKernelGGL(dequantize_kernel<false>, dim3(uint32_t(grid)), dim3(256), 0, stream, pk,
-                       st->absmax, ngroups, int(st->codebook), w_out);
+                       am, sc, ngroups, int(st->codebook), w_out);
   return hipGetLastError() == hipSuccess ? E4B_OK : E4B_ERR_HIP;
 }
 
@@ -178,9 +242,14 @@ extern "C" e4b_status e4b_stack_copy_async(const e4b_stack *dst, const e4b_stack
   if (hipMemcpyAsync(const_cast<uint8_t *>(dst->packed), src->packed,
                      size_t(bf16 ? n * 2 : n / 2), hipMemcpyDefault, stream) != hipSuccess)
     return E4B_ERR_HIP;
-  if (!bf16 && hipMemcpyAsync(const_cast<float *>(dst->absmax), src->absmax,
-                              size_t(n / kBlock) * sizeof(float), hipMemcpyDefault,
-                              stream) != hipSuccess)
+  if (dst->codebook == E4B_CB_MXFP4) {
+    if (hipMemcpyAsync(const_cast<uint8_t *>(dst->scales), src->scales, size_t(n / kMxBlock),
+                       hipMemcpyDefault, stream) != hipSuccess)
+      return E4B_ERR_HIP;
+  } else if (!bf16 && hipMemcpyAsync(const_cast<float *>(dst->absmax), src->absmax,
+                                     size_t(n / kBlock) * sizeof(float), hipMemcpyDefault,
+                                     stream) != hipSuccess) {
     return E4B_ERR_HIP;
+  }
   return E4B_OK;
 }

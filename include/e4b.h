@@ -53,7 +53,7 @@ typedef enum {
   E4B_ERR_NULL = 1,      /* a required pointer is NULL */
   E4B_ERR_SHAPE = 2,     /* a dimension <= 0, in % 64 != 0, top_k not in [1, min(E, 32)],
                             E > 1024, inconsistent gate_up/down shapes, or a size too large */
-  E4B_ERR_BLOCKSIZE = 3, /* blocksize != 64 */
+  E4B_ERR_BLOCKSIZE = 3, /* blocksize != 64 (MXFP4: != 32) */
   E4B_ERR_CODEBOOK = 4,  /* unknown codebook, or gate_up/down codebooks differ */
   E4B_ERR_DTYPE = 5,     /* unknown output dtype */
   E4B_ERR_WORKSPACE = 6, /* workspace NULL or smaller than e4b_moe_workspace_bytes() */
@@ -62,7 +62,16 @@ typedef enum {
   E4B_ERR_HIP = 9        /* a kernel launch failed (hipGetLastError after the launch) */
 } e4b_status;
 
-/* Storage modes. The 16-entry codebooks ([sdist] Experts4bit.__init__
+/* MXFP4 = the MX storage the [0.31.1] project page names for gpt-oss experts
+ * ("dequantised bit-identically") and for its native MXFP4 row, read as the
+ * OCP Microscaling Formats (MX) v1.0 FP4 format: E2M1 codes (same code layout
+ * and nibble order as FP4, unscaled magnitudes {0,.5,1,1.5,2,3,4,6}) with one
+ * E8M0 scale 2^(s-127) per 32 consecutive elements of a row in `scales`
+ * (uint8 [E, out*in/32]); blocksize 32, `absmax` unused. The dequantized
+ * weight code * 2^(s-127) is exact in fp32 and bf16, so every path (grouped
+ * forward, dgrad, decode GEMV, LoRA) runs on exactly the stored values.
+ *
+ * Storage modes. The 16-entry codebooks ([sdist] Experts4bit.__init__
  * quant_type "nf4"/"fp4"): NF4 = the NormalFloat-4 table of the QLoRA paper
  * (arXiv:2305.14314); FP4 = e2m1 (sign bit 3, magnitudes {0,.5,1,1.5,2,3,4,6}/6).
  * BF16 = the 16-bit passthrough lane of the [README] support matrix (the
@@ -70,7 +79,7 @@ typedef enum {
  * [E, out*in] (two bytes per element, round-to-nearest-even of the fp32
  * weight), `absmax` is unused and may be NULL. A BF16 layer runs the grouped
  * path only (the decode GEMV reads 4-bit codes). */
-typedef enum { E4B_CB_NF4 = 0, E4B_CB_FP4 = 1, E4B_CB_BF16 = 2 } e4b_codebook;
+typedef enum { E4B_CB_NF4 = 0, E4B_CB_FP4 = 1, E4B_CB_BF16 = 2, E4B_CB_MXFP4 = 3 } e4b_codebook;
 
 typedef enum { E4B_F32 = 0, E4B_BF16 = 1 } e4b_dtype;
 
@@ -81,10 +90,11 @@ typedef enum { E4B_PATH_AUTO = 0, E4B_PATH_GROUPED = 1, E4B_PATH_DECODE = 2 } e4
 /* One quantized stack (device pointers; the struct itself is host memory). */
 typedef struct {
   const uint8_t *packed; /* [E, out*in/2]; BF16: [E, out*in] bf16 */
-  const float *absmax;   /* [E, out*in/64]; BF16: unused */
+  const float *absmax;   /* [E, out*in/64]; BF16, MXFP4: unused */
   int64_t E, out, in;
-  int32_t blocksize; /* must be 64 */
+  int32_t blocksize; /* 64; MXFP4: 32 */
   int32_t codebook;  /* e4b_codebook */
+  const uint8_t *scales; /* MXFP4: E8M0 [E, out*in/32]; other modes: unused */
 } e4b_stack;
 
 /* A MoE layer: gate_up (out = 2I, in = H) and down (out = H, in = I), same E,
@@ -114,10 +124,24 @@ e4b_status e4b_quantize_nf4(const float *w, int64_t E, int64_t out, int64_t in,
                             int32_t blocksize, int32_t codebook, uint8_t *packed,
                             float *absmax, hipStream_t stream);
 
+/* MXFP4 conversion of an fp32 [E, out, in] stack (OCP MX v1.0, read for the
+ * [0.31.1] project page's MXFP4 experts): per block of 32 consecutive
+ * elements, shared exponent = floor(log2(max |w|)) - 2 clamped to
+ * [-127, 127] (a block of zeros: -127), scale byte = shared + 127; each
+ * element is w / 2^shared rounded to the nearest E2M1 value (ties to the even
+ * mantissa, beyond 6 saturated), sign bit = sign bit of w.
+ *   w      : device fp32 [E, out, in], finite (unchecked); in % 32 == 0
+ *   packed : device uint8 [E, out*in/2]   (written)
+ *   scales : device uint8 [E, out*in/32]  (written)
+ * Errors: NULL, SHAPE, ALIGN, HIP. */
+e4b_status e4b_quantize_mxfp4(const float *w, int64_t E, int64_t out, int64_t in, uint8_t *packed,
+                              uint8_t *scales, hipStream_t stream);
+
 /* Dequantize a whole stack: w_out[e, r, c] = fl32(code * absmax) (one fp32
  * rounding of the exact product), or its round-to-nearest-even bf16 when
  * dtype == E4B_BF16. [sdist] Experts4bit._dequantize_expert. A BF16 stack
- * gives its stored values (exact in fp32). 
+ * gives its stored values (exact in fp32); an MXFP4 stack gives code *
+ * 2^(s-127) (exact in both dtypes).
  *   st    : host descriptor of device buffers
  *   w_out : device [E, out, in] fp32 or bf16 (written)
  * Errors: NULL, SHAPE, BLOCKSIZE, CODEBOOK, DTYPE, ALIGN, HIP. */

@@ -28,8 +28,8 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
-def _stack(E=4, out=128, inn=64, packed=FAKE, absmax=FAKE, bs=64, cb=0):
-    return _lib.E4bStack(packed, absmax, E, out, inn, bs, cb)
+def _stack(E=4, out=128, inn=64, packed=FAKE, absmax=FAKE, bs=64, cb=0, scales=None):
+    return _lib.E4bStack(packed, absmax, E, out, inn, bs, cb, scales)
 
 
 def _layer(E=4, H=64, I=64, **kw):
@@ -55,6 +55,8 @@ def test_quantize_validation():
     assert q(FAKE, 1, 64, 96, 64, 0, FAKE, FAKE, None) == _lib.E4B_ERR_SHAPE
     assert q(FAKE, 0, 64, 64, 64, 0, FAKE, FAKE, None) == _lib.E4B_ERR_SHAPE
     assert q(FAKE, 1, 64, 64, 128, 0, FAKE, FAKE, None) == _lib.E4B_ERR_BLOCKSIZE
+    assert q(FAKE, 1, 64, 64, 64, 5, FAKE, FAKE, None) == _lib.E4B_ERR_CODEBOOK
+    # MXFP4 has its own entry point (E8M0 scale bytes, not fp32 absmax)
     assert q(FAKE, 1, 64, 64, 64, 3, FAKE, FAKE, None) == _lib.E4B_ERR_CODEBOOK
     # the bf16 lane needs no absmax buffer: NULL passes the pointer check and
     # the call stops at the next check (nothing is launched)
@@ -206,3 +208,28 @@ def test_stack_copy_validation():
     assert cp(ctypes.byref(a), ctypes.byref(_stack(4, 128, 64, cb=1)), None) == _lib.E4B_ERR_SHAPE
     assert cp(ctypes.byref(_stack(packed=None)), ctypes.byref(a), None) == _lib.E4B_ERR_NULL
     assert cp(None, ctypes.byref(a), None) == _lib.E4B_ERR_NULL
+
+
+def test_mxfp4_validation():
+    lib = e4b.load()
+    q = lib.e4b_quantize_mxfp4
+    assert q(None, 1, 64, 64, FAKE, FAKE, None) == _lib.E4B_ERR_NULL
+    assert q(FAKE, 1, 64, 64, FAKE, None, None) == _lib.E4B_ERR_NULL
+    assert q(FAKE, 1, 64, 48, FAKE, FAKE, None) == _lib.E4B_ERR_SHAPE  # in % 32
+    assert q(FAKE, 0, 64, 64, FAKE, FAKE, None) == _lib.E4B_ERR_SHAPE
+    assert q(FAKE, 1, 64, 64, FAKE, FAKE + 1, None) == _lib.E4B_ERR_ALIGN
+
+    def mx(out, inn, bs=32, scales=FAKE, absmax=None):
+        return _stack(4, out, inn, absmax=absmax, bs=bs, cb=3, scales=scales)
+
+    d = lib.e4b_dequantize_nf4
+    assert d(ctypes.byref(mx(128, 64, bs=64)), 0, FAKE, None) == _lib.E4B_ERR_BLOCKSIZE
+    assert d(ctypes.byref(mx(128, 64, scales=None)), 0, FAKE, None) == _lib.E4B_ERR_NULL
+    assert d(ctypes.byref(mx(128, 96)), 0, FAKE, None) == _lib.E4B_ERR_SHAPE  # rows of 64
+    assert d(ctypes.byref(mx(128, 64, scales=FAKE + 8)), 0, FAKE, None) == _lib.E4B_ERR_ALIGN
+    # a valid MXFP4 layer (absmax unused, NULL) gets as far as the workspace check
+    L = _lib.E4bLayer(mx(128, 64), mx(64, 64))
+    assert _fwd(L, ws_bytes=0) == _lib.E4B_ERR_WORKSPACE
+    assert _dgrad(L, ws_bytes=0) == _lib.E4B_ERR_WORKSPACE
+    mixed = _lib.E4bLayer(mx(128, 64), _stack(4, 64, 64))
+    assert _fwd(mixed) == _lib.E4B_ERR_CODEBOOK
