@@ -19,7 +19,8 @@ What it computes (float64 unless a step fixes another precision):
   dgrad and the adapter weight gradients.
 * ``mx``         -- MXFP4 storage: E2M1 elements with an E8M0 scale per 32
   elements (the conversion rule of the OCP MX v1.0 specification), and its
-  exact dequantization.
+  exact dequantization; MXFP8 (E4M3) activation rows and the MX forward that
+  feeds them to the MXFP4 weights.
 
 Sources: the experts4bit-qlora / bitsandbytes pages on fused 4-bit expert
 storage (the 0.1.0 sdist's ``_vendor/experts.py`` module ``Experts4bit``; the
@@ -51,4 +52,13 @@ from .quant import (  # noqa: F401
 from .moe import route, permute, moe_forward, moe_dgrad, silu  # noqa: F401
 from .fidelity import rel_fro, reconstruction_errors  # noqa: F401
 from .lora import lora_forward, lora_backward  # noqa: F401
-from .mx import quantize_mx, dequantize_mx, e2m1_value, e8m0_value  # noqa: F401
+from .mx import (  # noqa: F401
+    quantize_mx,
+    dequantize_mx,
+    e2m1_value,
+    e8m0_value,
+    e4m3_value,
+    quantize_mx8_rows,
+    dequantize_mx8_rows,
+    mx8_forward,
+)

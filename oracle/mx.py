@@ -152,3 +152,96 @@ def mx_value_exact(code, s):
     mag = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0][code & 7]
     v = math.ldexp(mag, int(s) - 127)
     return -v if code & 8 else v
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 activations for the scaled-MFMA forward (the MX forward path)
+#
+# The MX forward feeds the MFMA 8-bit activations: every activation row is
+# converted to MXFP8 (OCP MX v1.0: element FP8 E4M3, scale E8M0 per 32
+# elements) with the same rule as the weights, emax = 8 for E4M3 (448 =
+# 1.75 * 2^8). E4M3 (the OCP 8-bit format): sign, 4 exponent bits (bias 7),
+# 3 mantissa bits; exponent 0 is subnormal (value m / 8 * 2^-6); the only NaN
+# is S.1111.111, there are no infinities, so the largest finite magnitude is
+# 448; conversion rounds to nearest even and saturates at 448.
+# Reading (the pages do not describe the activations of an MXFP4 lane): the
+# gate_up input x and the down input a = bf16(silu(g) * u) are each converted
+# per row; products and sums are exact up to fp32 accumulation.
+
+E4M3_EMAX = 8
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code):
+    """Value of 8-bit E4M3 codes (0x7F / 0xFF are NaN)."""
+    c = np.asarray(code, dtype=np.int64)
+    if np.any((c & 0x7F) == 0x7F):
+        raise ValueError("E4M3 NaN code")
+    e, m = (c >> 3) & 15, c & 7
+    v = np.where(e == 0, np.ldexp(m / 8.0, -6), np.ldexp(1.0 + m / 8.0, e - 7))
+    return np.where(c & 0x80, -v, v)
+
+
+# every finite non-negative E4M3 magnitude, ascending (codes 0x00..0x7E)
+E4M3_MAGS = e4m3_value(np.arange(0x7F))
+
+
+def round_e4m3_magnitude(a):
+    """Code (0..0x7E) of the E4M3 magnitude nearest to ``a >= 0``; ties to
+    the even code (the even mantissa), beyond 448 saturated."""
+    a = np.asarray(a, dtype=np.float64)
+    mids = (E4M3_MAGS[:-1] + E4M3_MAGS[1:]) / 2.0
+    q = np.searchsorted(mids, a, side="left")  # number of midpoints strictly below a
+    tie = (q < len(mids)) & (a == mids[np.minimum(q, len(mids) - 1)]) & (q % 2 == 1)
+    return np.minimum(q + tie, 0x7E)
+
+
+def quantize_mx8_rows(x):
+    """MXFP8 conversion of fp32 rows ``[n, K]`` (K % 32 == 0).
+
+    Returns ``(codes uint8 [n, K], scales uint8 [n, K/32])`` in element order.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    n, K = x.shape
+    if K % MX_BLOCK:
+        raise ValueError("row length must be divisible by 32")
+    if not np.all(np.isfinite(x)):
+        raise ValueError("activations must be finite")
+    blocks = x.reshape(n, K // MX_BLOCK, MX_BLOCK).astype(np.float64)
+    amax = np.abs(blocks).max(axis=2)
+    _, ex = np.frexp(amax)
+    sh = np.where(amax == 0.0, -127, ex.astype(np.int64) - 1 - E4M3_EMAX)
+    sh = np.clip(sh, -127, 127)
+    scaled = blocks / np.ldexp(1.0, sh)[:, :, None]
+    q = round_e4m3_magnitude(np.abs(scaled)) | (np.signbit(blocks).astype(np.int64) << 7)
+    return q.reshape(n, K).astype(np.uint8), (sh + 127).astype(np.uint8)
+
+
+def dequantize_mx8_rows(codes, scales):
+    """fp64 ``[n, K]`` values of MXFP8 rows (exact)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    n, K = codes.shape
+    v = e4m3_value(codes).reshape(n, K // MX_BLOCK, MX_BLOCK)
+    return (v * e8m0_value(scales)[:, :, None]).reshape(n, K)
+
+
+def mx8_forward(x, idx, w, w_gu, w_dn):
+    """The MX forward path: y [T, H] (fp64) of the routed SwiGLU MLP whose
+    expert inputs are MXFP8-converted: x per token row, and a = silu(g) * u
+    rounded to bf16 (as the gate_up epilogue stores it) per pair row. The
+    weights are the stored (MXFP4-dequantized) stacks."""
+    from .moe import _check_moe, _pairs_by_expert, silu
+    from .quant import bf16_rne_bits, bf16_bits_to_f32
+
+    x, idx, w, E, H, I = _check_moe(x, idx, w, w_gu, w_dn)
+    xq = dequantize_mx8_rows(*quantize_mx8_rows(x.astype(np.float32)))
+    T, k = idx.shape
+    y = np.zeros((T, H), dtype=np.float64)
+    for e, t, j in _pairs_by_expert(idx, E):
+        h = xq[t] @ np.asarray(w_gu[e], dtype=np.float64).T
+        a = silu(h[:, :I]) * h[:, I:]
+        a16 = bf16_bits_to_f32(bf16_rne_bits(a.astype(np.float32)))
+        aq = dequantize_mx8_rows(*quantize_mx8_rows(a16))
+        o = aq @ np.asarray(w_dn[e], dtype=np.float64).T
+        np.add.at(y, t, w[t, j][:, None] * o)
+    return y

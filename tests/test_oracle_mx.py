@@ -132,3 +132,82 @@ def test_shape_errors():
         oracle.quantize_mx(np.zeros((1, 2, 48), dtype=np.float32))  # in % 32
     with pytest.raises(ValueError):
         oracle.quantize_mx(np.zeros((2, 64), dtype=np.float32))
+
+
+# ---- MXFP8 (E4M3) activation rows ----
+
+def _e4m3_from_bits(c):
+    s, e, m = (c >> 7) & 1, (c >> 3) & 15, c & 7
+    v = math.ldexp(m / 8.0, -6) if e == 0 else math.ldexp(1.0 + m / 8.0, e - 7)
+    return -v if s else v
+
+
+def test_e4m3_values_by_hand_and_from_bits():
+    got = oracle.e4m3_value(np.arange(0x7F))
+    assert np.array_equal(got, [_e4m3_from_bits(c) for c in range(0x7F)])
+    for code, val in [(0x38, 1.0), (0x7E, 448.0), (0x01, 2.0 ** -9), (0x08, 2.0 ** -6),
+                      (0x77, 240.0), (0x78, 256.0), (0x07, 7 * 2.0 ** -9)]:
+        assert _e4m3_from_bits(code) == val
+        assert oracle.e4m3_value(code) == val
+    assert np.signbit(oracle.e4m3_value(0x80))
+    assert np.all(np.diff(got) > 0)  # codes 0..0x7E are ascending magnitudes
+    with pytest.raises(ValueError):
+        oracle.e4m3_value(0x7F)
+
+
+def _row(vals):
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, : len(vals)] = vals
+    return oracle.quantize_mx8_rows(x)
+
+
+def test_mx8_scale_rule_ties_and_saturation():
+    # 448 pins the shared exponent at 0 (floor(log2 448) - 8)
+    c, s = _row([448.0, 432.0, 440.0, 1.0625, 1.1875, 2.0 ** -10, 3.0 * 2.0 ** -10, 464.0])
+    assert s[0, 0] == 127
+    v = oracle.e4m3_value(c[0])
+    # 432 is the midpoint of 416 (odd mantissa) and 448 (even): 448; 1.0625 between
+    # 1.0 (even) and 1.125: 1.0; 1.1875 between 1.125 and 1.25 (even): 1.25;
+    # 2^-10 between 0 and 2^-9: 0 (even); 3 * 2^-10 between 2^-9 and 2^-8 (even): 2^-8
+    assert list(v[:7]) == [448.0, 448.0, 448.0, 1.0, 1.25, 0.0, 2.0 ** -8]
+    assert v[7] == 448.0  # above the largest finite value: saturated
+    c, s = _row([1.0, -0.5])
+    assert s[0, 0] == 127 - 8 and c[0, 0] == 0x78 and c[0, 1] == 0xF0  # 1.0 / 2^-8 = 256
+    c, s = _row([0.0])
+    assert s[0, 0] == 0 and np.all(c == 0)
+
+
+def test_mx8_brute_force():
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal((6, 128)) * np.exp(rng.uniform(-10, 10, (6, 1)))).astype(np.float32)
+    c, s = oracle.quantize_mx8_rows(x)
+    vals = oracle.dequantize_mx8_rows(c, s)
+    mags = np.array([_e4m3_from_bits(k) for k in range(0x7F)])
+    for r in range(6):
+        for b in range(4):
+            blk = x[r, 32 * b : 32 * b + 32].astype(np.float64)
+            sc = 2.0 ** (math.floor(math.log2(np.abs(blk).max())) - 8)
+            assert int(s[r, b]) - 127 == math.floor(math.log2(np.abs(blk).max())) - 8
+            for i in range(32):
+                a = abs(blk[i]) / sc
+                d = np.abs(mags - a)
+                best = np.flatnonzero(d == d.min())
+                k = best[0] if len(best) == 1 else [q for q in best if q % 2 == 0][0]
+                assert abs(vals[r, 32 * b + i]) == mags[k] * sc
+
+
+def test_mx8_forward_close_to_unquantized_activations():
+    # the activation conversion is a rounding of relative size <= 2^-4 per
+    # element: the MX forward stays within a few percent of the same weights
+    # applied to unrounded activations
+    from workloads import get_config, gen_x, gen_logits, gen_weights
+
+    cfg = get_config("tiny")
+    x, lg = gen_x(cfg, 1), gen_logits(cfg, 1)
+    idx, w = oracle.route(lg, cfg.k)
+    wgu = oracle.stored_weights(gen_weights(cfg, 1, "gate_up"), "mxfp4")
+    wdn = oracle.stored_weights(gen_weights(cfg, 1, "down"), "mxfp4")
+    y_mx = oracle.mx8_forward(x, idx, w, wgu, wdn)
+    y = oracle.moe_forward(x, idx, w, wgu, wdn)
+    err = np.abs(y_mx - y).max() / np.abs(y).max()
+    assert 1e-4 < err < 0.1
