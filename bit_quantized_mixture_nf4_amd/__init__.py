@@ -24,13 +24,15 @@ from ._lib import E4bLayer, E4bLora, E4bStack, E4bError, check, load  # noqa: F4
 
 CODEBOOKS = {"nf4": _lib.E4B_CB_NF4, "fp4": _lib.E4B_CB_FP4, "bf16": _lib.E4B_CB_BF16,
              "mxfp4": _lib.E4B_CB_MXFP4}
-PATHS = {"auto": _lib.E4B_PATH_AUTO, "grouped": _lib.E4B_PATH_GROUPED, "decode": _lib.E4B_PATH_DECODE}
+PATHS = {"auto": _lib.E4B_PATH_AUTO, "grouped": _lib.E4B_PATH_GROUPED, "decode": _lib.E4B_PATH_DECODE,
+         "mx8": _lib.E4B_PATH_MX8}
 
 __all__ = [
     "QuantStack",
     "MoELayer",
     "quantize",
     "dequantize",
+    "mx8_rows",
     "moe_forward",
     "moe_dgrad",
     "Lora",
@@ -145,6 +147,20 @@ def quantize(w, codebook="nf4"):
     )
     check("e4b_quantize_nf4", code)
     return QuantStack(packed, absmax, E, out, inn, codebook)
+
+
+def mx8_rows(x):
+    """MXFP8 conversion of bf16 rows [n, K] (K % 32 == 0) as the MX forward feeds
+    them to the block-scaled MFMA: (codes uint8 [n, K] with the bytes of each
+    element pair swapped, E8M0 scales uint8 [n, K/32])."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [n, K]")
+    n, K = x.shape
+    codes = torch.empty(n, K, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(n, max(K // 32, 1), dtype=torch.uint8, device=x.device)
+    check("e4b_mx8_rows", load().e4b_mx8_rows(_vp(x), n, K, _vp(codes), _vp(scales), _stream(x)))
+    return codes, scales
 
 
 def dequantize(stack, dtype=torch.float32):

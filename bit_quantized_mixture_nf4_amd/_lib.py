@@ -24,12 +24,13 @@ E4B_ERR_HIP = 9
 
 E4B_CB_NF4, E4B_CB_FP4, E4B_CB_BF16, E4B_CB_MXFP4 = 0, 1, 2, 3
 E4B_F32, E4B_BF16 = 0, 1
-E4B_PATH_AUTO, E4B_PATH_GROUPED, E4B_PATH_DECODE = 0, 1, 2
+E4B_PATH_AUTO, E4B_PATH_GROUPED, E4B_PATH_DECODE, E4B_PATH_MX8 = 0, 1, 2, 3
 
 # every function declared in include/e4b.h
 EXPORTS = (
     "e4b_quantize_nf4",
     "e4b_quantize_mxfp4",
+    "e4b_mx8_rows",
     "e4b_dequantize_nf4",
     "e4b_moe_forward",
     "e4b_moe_dgrad",
@@ -100,6 +101,7 @@ def load():
     sigs = {
         "e4b_quantize_nf4": (i32, [vp, i64, i64, i64, i32, i32, vp, vp, vp]),
         "e4b_quantize_mxfp4": (i32, [vp, i64, i64, i64, vp, vp, vp]),
+        "e4b_mx8_rows": (i32, [vp, i64, i64, vp, vp, vp]),
         "e4b_dequantize_nf4": (i32, [st, i32, vp, vp]),
         "e4b_moe_forward": (i32, [lay, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, i32, vp]),
         "e4b_moe_dgrad": (i32, [lay, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),

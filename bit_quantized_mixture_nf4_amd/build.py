@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libe4b.so")
 
-SOURCES = ["plan.cpp", "quant.hip", "route.hip", "gemm.hip", "combine.hip", "decode.hip", "lora.hip", "api.hip"]
+SOURCES = ["plan.cpp", "quant.hip", "route.hip", "gemm.hip", "combine.hip", "decode.hip", "lora.hip", "mx.hip",
+           "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -93,6 +93,54 @@ extern "C" e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t
   }
   if (router_logits)
     E4B_TRY(launch_route(router_logits, T, int(p.E), top_k, topk_idx, topk_w, stream));
+  if (path == E4B_PATH_MX8) {
+    const PermView v = perm_in_workspace(p, w);
+    E4B_TRY(launch_permute(p, topk_idx, w, v, stream));
+    uint8_t *xq = reinterpret_cast<uint8_t *>(w + p.off_mx_xq);
+    uint8_t *xs = reinterpret_cast<uint8_t *>(w + p.off_mx_xs);
+    uint8_t *aq = reinterpret_cast<uint8_t *>(w + p.off_mx_aq);
+    uint8_t *as = reinterpret_cast<uint8_t *>(w + p.off_mx_as);
+    uint16_t *a_buf = reinterpret_cast<uint16_t *>(w + p.off_a);
+    uint16_t *o_buf = reinterpret_cast<uint16_t *>(w + p.off_o);
+    E4B_TRY(launch_mx8_rows(x, T, int(p.H), xq, xs, stream));
+    MxGemmArgs a{};
+    a.sorted_pair = v.sorted;
+    a.topk = top_k;
+    a.Wp = L->gate_up.packed;
+    a.Ws = L->gate_up.scales;
+    a.w_e_bytes = L->gate_up.out * L->gate_up.in / 2;
+    a.w_e_blocks = L->gate_up.out * L->gate_up.in / kMxBlock;
+    a.A = xq;
+    a.As = xs;
+    a.K = int32_t(p.H);
+    a.N = int32_t(p.I);
+    a.I = int32_t(p.I);
+    a.E = int32_t(p.E);
+    a.tile_offsets = v.tile_offsets;
+    a.tile_map = v.tile_map;
+    a.n_tiles = int32_t(p.n_tiles_gu);
+    a.grid = uint32_t(p.m_tiles_bound * p.n_tiles_gu);
+    a.C = a_buf;
+    a.ldc = int32_t(p.I);
+    E4B_TRY(launch_mx_gemm(true, a, stream));
+    E4B_TRY(launch_mx8_rows(a_buf, p.P, int(p.I), aq, as, stream));
+    MxGemmArgs d = a;
+    d.Wp = L->down.packed;
+    d.Ws = L->down.scales;
+    d.w_e_bytes = L->down.out * L->down.in / 2;
+    d.w_e_blocks = L->down.out * L->down.in / kMxBlock;
+    d.A = aq;
+    d.As = as;
+    d.K = int32_t(p.I);
+    d.N = int32_t(p.H);
+    d.n_tiles = int32_t(p.n_tiles_h);
+    d.grid = uint32_t(p.m_tiles_bound * p.n_tiles_h);
+    d.C = o_buf;
+    d.ldc = int32_t(p.H);
+    E4B_TRY(launch_mx_gemm(false, d, stream));
+    E4B_TRY(launch_combine_rows(o_buf, v.pos, topk_w, T, top_k, int(p.H), y, stream));
+    return E4B_OK;
+  }
   // with a saved buffer the permutation is written there for the dgrad
   const PermView v = saved ? perm_in_saved(p, static_cast<char *>(saved)) : perm_in_workspace(p, w);
   E4B_TRY(launch_permute(p, topk_idx, w, v, stream));

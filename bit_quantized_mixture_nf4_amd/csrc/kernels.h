@@ -75,6 +75,29 @@ PermView perm_in_saved(const MoePlan &p, char *saved);
 hipError_t launch_permute(const MoePlan &p, const int32_t *idx, char *ws, const PermView &v,
                           hipStream_t s);
 
+// The MX forward's grouped GEMM (csrc/mx.hip): MXFP4 weights against MXFP8
+// activation rows (codes with the bytes of each element pair swapped, E8M0
+// scale per 32), K a multiple of 128.
+struct MxGemmArgs {
+  const int32_t *sorted_pair;  // gate_up: activation row = token of the sorted pair
+  int32_t topk;
+  const uint8_t *Wp;  // packed E2M1 stack
+  const uint8_t *Ws;  // E8M0 scales of the stack
+  int64_t w_e_bytes, w_e_blocks;
+  const uint8_t *A;   // activation codes [rows, K]
+  const uint8_t *As;  // activation scales [rows, K / 32]
+  int32_t K, N, I, E;
+  const int32_t *tile_offsets;
+  const int4 *tile_map;
+  int32_t n_tiles;
+  uint32_t grid;
+  uint16_t *C;  // gate_up: a [P, I] bf16; down: o [P, H] bf16
+  int32_t ldc;
+};
+hipError_t launch_mx8_rows(const uint16_t *x, int64_t rows, int64_t K, uint8_t *codes,
+                           uint8_t *scales, hipStream_t s);
+hipError_t launch_mx_gemm(bool gate_up, const MxGemmArgs &a, hipStream_t s);
+
 // grid = m_tiles_bound * n_tiles; the launch rounds it up to a multiple of 8.
 hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s);
 

@@ -124,6 +124,12 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   p->off_a = take(size_t(P) * I * 2);
   p->off_o = take(size_t(P) * H * 2);
   p->off_dmap = T <= kDecodeMaxT ? take(16 + size_t(busy) * size_t(H / 16 + I / 16) * 16) : 0;
+  // the MX forward's activation rows (MXFP4 layers): x and a as E4M3 codes + E8M0 scales
+  const bool mx = p->codebook == E4B_CB_MXFP4;
+  p->off_mx_xq = mx ? take(size_t(T) * H) : 0;
+  p->off_mx_xs = mx ? take(size_t(T) * H / kMxBlock) : 0;
+  p->off_mx_aq = mx ? take(size_t(P) * I) : 0;
+  p->off_mx_as = mx ? take(size_t(P) * I / kMxBlock) : 0;
   const size_t fwd_end = off;
   // dgrad region (overlaps the forward region: the two calls never run at once
   // on one workspace)
@@ -167,7 +173,12 @@ e4b_status check_forward(const MoePlan &p, const void *x, const float *logits,
                          const int32_t *idx, const float *w, const void *y,
                          const void *saved, const void *ws, size_t ws_bytes,
                          int32_t path, int *use_decode) {
-  if (path != E4B_PATH_AUTO && path != E4B_PATH_GROUPED && path != E4B_PATH_DECODE)
+  if (path != E4B_PATH_AUTO && path != E4B_PATH_GROUPED && path != E4B_PATH_DECODE &&
+      path != E4B_PATH_MX8)
+    return E4B_ERR_PATH;
+  // the MX forward: an MXFP4 gated layer, K-steps of 128 on both GEMMs, no saved state
+  if (path == E4B_PATH_MX8 && (p.codebook != E4B_CB_MXFP4 || !p.gated || p.H % 128 != 0 ||
+                               p.I % 128 != 0 || saved != nullptr))
     return E4B_ERR_PATH;
   const bool fits = decode_fits(p);
   if (path == E4B_PATH_DECODE && (!fits || saved != nullptr)) return E4B_ERR_PATH;

@@ -47,6 +47,7 @@ struct MoePlan {
   size_t off_tile_map;  // int4 per m-tile: expert, segment start, first row, rows
   size_t off_a, off_o;                          // forward
   size_t off_dmap;                              // forward, decode path: work maps
+  size_t off_mx_xq, off_mx_xs, off_mx_aq, off_mx_as;  // forward, MX path (MXFP4 layers)
   size_t off_gu, off_dgu, off_partial, off_gx;  // dgrad
   size_t ws_bytes;
   // LoRA calls: after the base workspace, fp32 [P, kLoraK] per-pair

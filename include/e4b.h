@@ -84,8 +84,20 @@ typedef enum { E4B_CB_NF4 = 0, E4B_CB_FP4 = 1, E4B_CB_BF16 = 2, E4B_CB_MXFP4 = 3
 typedef enum { E4B_F32 = 0, E4B_BF16 = 1 } e4b_dtype;
 
 /* Forward path selection. AUTO = the decode dequant-GEMV path when T <= 8 and
- * saved == NULL, else the grouped MFMA path. */
-typedef enum { E4B_PATH_AUTO = 0, E4B_PATH_GROUPED = 1, E4B_PATH_DECODE = 2 } e4b_path;
+ * saved == NULL, else the grouped MFMA path. MX8 = the MX forward of an
+ * MXFP4 gated layer on gfx950's block-scaled MFMA ([0.31.1] native MXFP4
+ * row): x and a = bf16(silu(g) * u) are converted per row to MXFP8 (E4M3, an
+ * E8M0 scale per 32; the OCP MX v1.0 rule with emax 8: saturating,
+ * round-to-nearest-even), so the result approximates the exact-weights
+ * forward to about the E4M3 rounding (2^-4 relative per activation); it
+ * needs H % 128 == 0, I % 128 == 0 and saved == NULL (E4B_ERR_PATH
+ * otherwise). */
+typedef enum {
+  E4B_PATH_AUTO = 0,
+  E4B_PATH_GROUPED = 1,
+  E4B_PATH_DECODE = 2,
+  E4B_PATH_MX8 = 3
+} e4b_path;
 
 /* One quantized stack (device pointers; the struct itself is host memory). */
 typedef struct {
@@ -136,6 +148,18 @@ e4b_status e4b_quantize_nf4(const float *w, int64_t E, int64_t out, int64_t in,
  * Errors: NULL, SHAPE, ALIGN, HIP. */
 e4b_status e4b_quantize_mxfp4(const float *w, int64_t E, int64_t out, int64_t in, uint8_t *packed,
                               uint8_t *scales, hipStream_t stream);
+
+/* MXFP8 conversion of bf16 activation rows, as the MX forward (E4B_PATH_MX8)
+ * feeds them to the block-scaled MFMA: per block of 32 consecutive elements
+ * of a row, shared exponent = floor(log2(max |x|)) - 8 clamped to
+ * [-127, 127] (a block of zeros: -127), scale byte = shared + 127, element =
+ * x / 2^shared rounded to E4M3 (nearest even, saturating at 448; sign bit 7).
+ * Layout: codes [rows, K] with the two bytes of every element pair swapped
+ * (byte 2p holds element 2p + 1), scales [rows, K/32].
+ *   x_bf16 : device bf16 [rows, K]; K % 32 == 0
+ * Errors: NULL, SHAPE, ALIGN, HIP. */
+e4b_status e4b_mx8_rows(const void *x_bf16, int64_t rows, int64_t K, uint8_t *codes,
+                        uint8_t *scales, hipStream_t stream);
 
 /* Dequantize a whole stack: w_out[e, r, c] = fl32(code * absmax) (one fp32
  * rounding of the exact product), or its round-to-nearest-even bf16 when

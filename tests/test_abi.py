@@ -233,3 +233,13 @@ def test_mxfp4_validation():
     assert _dgrad(L, ws_bytes=0) == _lib.E4B_ERR_WORKSPACE
     mixed = _lib.E4bLayer(mx(128, 64), _stack(4, 64, 64))
     assert _fwd(mixed) == _lib.E4B_ERR_CODEBOOK
+    # the MX forward (path 3): MXFP4 only, H and I multiples of 128, no saved state
+    assert _fwd(_layer(), path=3) == _lib.E4B_ERR_PATH
+    assert _fwd(L, path=3) == _lib.E4B_ERR_PATH  # H = I = 64
+    L128 = _lib.E4bLayer(mx(256, 128), mx(128, 128))
+    assert _fwd(L128, path=3, ws_bytes=0) == _lib.E4B_ERR_WORKSPACE
+    assert _fwd(L128, path=3, saved=FAKE) == _lib.E4B_ERR_PATH
+    r = lib.e4b_mx8_rows
+    assert r(None, 4, 64, FAKE, FAKE, None) == _lib.E4B_ERR_NULL
+    assert r(FAKE, 4, 48, FAKE, FAKE, None) == _lib.E4B_ERR_SHAPE
+    assert r(FAKE + 2, 4, 64, FAKE, FAKE, None) == _lib.E4B_ERR_ALIGN

@@ -104,3 +104,52 @@ def test_mx_ragged_dgrad_b_nn_blocks():
     gx_ref, gw_ref = oracle.moe_dgrad(pb.x, idx_ref, w_ref, wgu, wdn, pb.grad_y)
     tol_check(to_np(gx), gx_ref, "grad_x mxfp4 ragged")
     tol_check(to_np(gw), gw_ref, "grad_topk_w mxfp4 ragged")
+
+
+# ---- the MX forward (E4B_PATH_MX8): MXFP8 activations on the block-scaled MFMA ----
+
+def _unswap(codes):
+    c = np.asarray(codes).copy()
+    c[:, 0::2], c[:, 1::2] = codes[:, 1::2], codes[:, 0::2]
+    return c
+
+
+def test_mx8_rows_bit_exact():
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((64, 256)) * np.exp(rng.uniform(-8, 8, (64, 1)))).astype(np.float32)
+    # E4M3 midpoints, saturating values, a zero block, -0.0 and tiny values
+    mids = np.array([1.0625, 1.1875, 432.0, 440.0, 464.0, 2.0 ** -10, 3 * 2.0 ** -10, 0.0], np.float32)
+    x[0, :32] = 0.0
+    x[1, :32] = np.concatenate([[448.0], mids, -mids, np.zeros(32 - 17)]).astype(np.float32)
+    x[2, 32:64] = -0.0
+    x[3, 64:96] = np.float32(1e-30)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    announce("mx8 rows 64 x 256")
+    codes, scales = e4b.mx8_rows(xb.to(DEV))
+    c_ref, s_ref = oracle.quantize_mx8_rows(xb.float().numpy())
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(_unswap(codes.cpu().numpy()), c_ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mx_mid"])
+def test_mx8_forward_against_oracle(name, tiny_mx):
+    if name == "tiny":
+        pb = tiny_mx
+    else:
+        cfg = MoEConfig("mx_mid", E=6, H=256, I=384, k=2, T=300, routing="normal")
+        announce("mxfp4 layer E6 H256 I384 k2 T300, mx8 path")
+        pb = Problem(cfg, seed=12, codebook="mxfp4", with_grad=False)
+    cfg = pb.cfg
+    y, idx, w, _ = e4b.moe_forward(pb.layer, pb.x_d, cfg.k, logits=pb.logits_d, path="mx8")
+    idx_ref, w_ref = oracle.route(pb.logits, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    wgu, wdn = pb.oracle_weights()
+    # the oracle converts bf16-rounded x the same way (x is bf16 on the device)
+    xb = torch.from_numpy(pb.x).to(torch.bfloat16).float().numpy()
+    tol_check(to_np(y), oracle.mx8_forward(xb, idx_ref, w_ref, wgu, wdn), f"y mx8 {name}")
+    # against the exact-activation MXFP4 forward: the activation rounding only
+    y2, _, _, _ = e4b.moe_forward(pb.layer, pb.x_d, cfg.k, logits=pb.logits_d, path="grouped")
+    tol_check(to_np(y), to_np(y2).astype(np.float64), f"mx8 vs grouped {name}", rel=0.1)
+    # run to run: bitwise identical
+    y3, _, _, _ = e4b.moe_forward(pb.layer, pb.x_d, cfg.k, logits=pb.logits_d, path="mx8")
+    assert torch.equal(y.view(torch.int16), y3.view(torch.int16))
