@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA (the rate of an fp4 x fp8 product)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 
 
@@ -202,6 +203,58 @@ def bench_bf16_lane(args, e4b, torch, cfg, x, lg, gy, base_dt):
             "nf4_step_over_bf16_step": round(base_dt / dt, 4)}
 
 
+def bench_mx8(args, e4b, torch, ev, cfg, x, lg):
+    """Forward only on an MXFP4 copy of the layer: the MX path (activations
+    converted to MXFP8 rows, both GEMMs on the block-scaled fp4 x fp8 MFMA)
+    against the grouped bf16 path on the same stored weights."""
+    layer = build_layer(e4b, torch, cfg, args.seed, "mxfp4")[0]
+    lib = e4b.load()
+    T, k = x.shape[0], cfg.k
+    dev = x.device
+    idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    y = torch.empty(T, layer.H, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(e4b.workspace_bytes(layer, T, k), dtype=torch.uint8, device=dev)
+    L = layer.as_c()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P, H, I = cfg.P, cfg.H, cfg.I
+    kflops = {"gate_up_fwd": 4.0 * P * H * I, "down_fwd": 2.0 * P * H * I}
+    out = {}
+    for name, path in (("mx8", e4b._lib.E4B_PATH_MX8), ("grouped", e4b._lib.E4B_PATH_GROUPED)):
+        def step():
+            s = lib.e4b_moe_forward(ctypes.byref(L), T, k, vp(x), vp(lg), vp(idx), vp(w), vp(y),
+                                    None, vp(ws), ws.numel(), path, stream)
+            if s:
+                raise RuntimeError(f"e4b status {s}")
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        kms = time_kernels(e4b, torch, ev, step, list(kflops), args.steps)
+        out[name] = {
+            "ms_per_forward": round(dt * 1e3, 4),
+            "tflops": round(6.0 * P * H * I / dt / 1e12, 1),
+            "kernels": {n: {"ms": round(kms[n], 4),
+                            "tflops": round(kflops[n] / (kms[n] * 1e-3) / 1e12, 1)}
+                        for n in kflops},
+        }
+        log(f"mxfp4 layer, {name} forward: {dt * 1e3:.3f} ms -> {out[name]['tflops']} TFLOP/s "
+            f"(gate_up {kms['gate_up_fwd']:.3f} ms, down {kms['down_fwd']:.3f} ms)")
+    gu = out["mx8"]["kernels"]["gate_up_fwd"]["tflops"]
+    out["mx8"]["gate_up_fwd_frac_of_fp8_peak"] = round(gu / MFMA_FP8_PEAK_TFLOPS, 4)
+    out["mx8_over_grouped_speed"] = round(out["grouped"]["ms_per_forward"]
+                                          / out["mx8"]["ms_per_forward"], 4)
+    del layer, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_kernels(e4b, torch, ev, step, names, n):
     """Average duration (ms) of each named kernel over n steps, events on its launch stream."""
     lib = e4b.load()
@@ -303,7 +356,7 @@ def bench_train(args, e4b, torch, ev):
         "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
         "traffic": measured_traffic(dom, "olmoe"),
     }
-    res = dict(cfg=cfg, dt=dt, tflops=tflops, kernels=kernels, roofline=roofline)
+    res = dict(cfg=cfg, dt=dt, tflops=tflops, kernels=kernels, roofline=roofline, x=x, lg=lg)
     res["lora"] = None if args.no_lora else bench_lora(args, e4b, torch, cfg, layer, x, lg, gy, dt)
     del keep, layer
     torch.cuda.empty_cache()
@@ -542,6 +595,7 @@ def main():
     ap.add_argument("--no-lora", action="store_true")
     ap.add_argument("--no-bf16-lane", action="store_true")
     ap.add_argument("--no-stream", action="store_true")
+    ap.add_argument("--no-mx", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -570,6 +624,7 @@ def main():
     e4b.load()
     ev = HipEvents()
     tr = bench_train(args, e4b, torch, ev)
+    mx = None if args.no_mx else bench_mx8(args, e4b, torch, ev, tr["cfg"], tr["x"], tr["lg"])
     dec = None if args.no_decode else bench_decode(args, e4b, torch, ev)
     cfg = tr["cfg"]
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, cfg)
@@ -599,6 +654,7 @@ def main():
         "decode": dec,
         "lora": tr["lora"],
         "bf16_lane": tr["bf16_lane"],
+        "mx8_forward": mx,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
