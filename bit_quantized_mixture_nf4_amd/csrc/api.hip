@@ -100,7 +100,6 @@ extern "C" e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t
     uint8_t *xs = reinterpret_cast<uint8_t *>(w + p.off_mx_xs);
     uint8_t *aq = reinterpret_cast<uint8_t *>(w + p.off_mx_aq);
     uint8_t *as = reinterpret_cast<uint8_t *>(w + p.off_mx_as);
-    uint16_t *a_buf = reinterpret_cast<uint16_t *>(w + p.off_a);
     uint16_t *o_buf = reinterpret_cast<uint16_t *>(w + p.off_o);
     E4B_TRY(launch_mx8_rows(x, T, int(p.H), xq, xs, stream));
     MxGemmArgs a{};
@@ -120,10 +119,9 @@ extern "C" e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t
     a.tile_map = v.tile_map;
     a.n_tiles = int32_t(p.n_tiles_gu);
     a.grid = uint32_t(p.m_tiles_bound * p.n_tiles_gu);
-    a.C = a_buf;
-    a.ldc = int32_t(p.I);
+    a.Cq = aq;
+    a.Cs = as;
     E4B_TRY(launch_mx_gemm(true, a, stream));
-    E4B_TRY(launch_mx8_rows(a_buf, p.P, int(p.I), aq, as, stream));
     MxGemmArgs d = a;
     d.Wp = L->down.packed;
     d.Ws = L->down.scales;

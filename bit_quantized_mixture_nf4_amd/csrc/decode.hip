@@ -279,13 +279,12 @@ struct DecCtx {
   const float *wa;     // this expert's absmax, at the lane's block
   const uint8_t *ws;   // MXFP4: this expert's E8M0 scales, at the lane's block
   int sstride;         // scale entries per weight row
-  bool mx;
   int row_bytes, nblk, I, tile0, nt, s0, np, kl, rq, wave, tid;
   int n_active;        // waves with K blocks (the others only meet the barriers)
   bool kvalid, active; // lane holds K bytes; this wave has K blocks
 };
 
-template <bool GATE_UP, int NP, int BPL>
+template <bool GATE_UP, int NP, int BPL, bool MX>
 __device__ __forceinline__ void decode_tiles(const DecCtx &c, const uint32_t *tl,
                                              const uint16_t *__restrict__ xin, int64_t (&xrow)[NP],
                                              int K_in, float (*s_red)[GATE_UP ? 2 : 1][kDecWaves][kDecTile][8],
@@ -316,7 +315,7 @@ __device__ __forceinline__ void decode_tiles(const DecCtx &c, const uint32_t *tl
       for (int r = 0; r < NR; ++r) {
         const int64_t row = u + r * c.I;
         wv[ps][r] = *reinterpret_cast<const LT *>(c.wp + row * c.row_bytes);
-        am[ps][r] = c.mx ? e8m0_value(c.ws[row * c.sstride]) : c.wa[row * c.sstride];
+        am[ps][r] = MX ? e8m0_value(c.ws[row * c.sstride]) : c.wa[row * c.sstride];
       }
     }
   };
@@ -345,7 +344,7 @@ __device__ __forceinline__ void decode_tiles(const DecCtx &c, const uint32_t *tl
           const int u = (c.tile0 + tn) * kDecTile + 4 * ps + c.rq;
           const int64_t row = u + r * c.I;
           wv[ps][r] = *reinterpret_cast<const LT *>(c.wp + row * c.row_bytes);
-          am[ps][r] = c.mx ? e8m0_value(c.ws[row * c.sstride]) : c.wa[row * c.sstride];
+          am[ps][r] = MX ? e8m0_value(c.ws[row * c.sstride]) : c.wa[row * c.sstride];
         }
         float acc[NP];
 #pragma unroll
@@ -379,7 +378,7 @@ __device__ __forceinline__ void decode_tiles(const DecCtx &c, const uint32_t *tl
   }
 }
 
-template <bool GATE_UP, int BPL>
+template <bool GATE_UP, int BPL, bool MX>
 __global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(
     const uint8_t *__restrict__ Wp, const float *__restrict__ Wa, const uint8_t *__restrict__ Ws,
     int64_t w_e_bytes,
@@ -430,10 +429,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(
   c.wp = Wp + int64_t(e) * w_e_bytes + kbyte;
   // a lane's BPL <= 16 bytes lie inside one 64-element absmax block and,
   // 16-byte aligned, inside one 32-element MXFP4 block
-  c.mx = Ws != nullptr;
-  c.sstride = c.mx ? K_in >> 5 : c.nblk;
-  c.wa = c.mx ? nullptr : Wa + int64_t(e) * w_e_blocks + (kbyte >> 5);
-  c.ws = c.mx ? Ws + int64_t(e) * w_e_blocks + (kbyte >> 4) : nullptr;
+  c.sstride = MX ? K_in >> 5 : c.nblk;
+  c.wa = MX ? nullptr : Wa + int64_t(e) * w_e_blocks + (kbyte >> 5);
+  c.ws = MX ? Ws + int64_t(e) * w_e_blocks + (kbyte >> 4) : nullptr;
   const int xoff = 2 * kbyte;  // element offset of the lane's input slice
 
 #define E4B_DEC_NP(N)                                                                        \
@@ -443,7 +441,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(
       const int qc = min(q, c.np - 1);                                                       \
       xrow[q] = GATE_UP ? int64_t((item.w >> (4 * qc)) & 15) : int64_t(c.s0 + qc);         \
     }                                                                                        \
-    decode_tiles<GATE_UP, N, BPL>(c, tl, vin, xrow, K_in, s_red, out, ldo, xoff);            \
+    decode_tiles<GATE_UP, N, BPL, MX>(c, tl, vin, xrow, K_in, s_red, out, ldo, xoff);        \
   }
   if (c.np <= 1) E4B_DEC_NP(1)
   else if (c.np <= 2) E4B_DEC_NP(2)
@@ -452,25 +450,25 @@ __global__ __launch_bounds__(kDecThreads) void decode_gemv_kernel(
 #undef E4B_DEC_NP
 }
 
+template <bool GATE_UP, bool MX>
+static const void *dec_kernel_fn(int bpl) {
+  return bpl == 4   ? reinterpret_cast<const void *>(&decode_gemv_kernel<GATE_UP, 4, MX>)
+         : bpl == 8 ? reinterpret_cast<const void *>(&decode_gemv_kernel<GATE_UP, 8, MX>)
+                    : reinterpret_cast<const void *>(&decode_gemv_kernel<GATE_UP, 16, MX>);
+}
+
 // Workgroups of one decode GEMV variant resident on the current device at
 // once (occupancy x compute units), cached per device; 0 if the query fails.
-static int dec_resident_workgroups(bool gate_up, int bpl) {
+static int dec_resident_workgroups(bool gate_up, int bpl, bool mx) {
   constexpr int kMaxDev = 64;
-  static int cache[kMaxDev][2][3];  // 0: not yet queried
+  static int cache[kMaxDev][2][2][3];  // 0: not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
   const int vi = bpl == 4 ? 0 : (bpl == 8 ? 1 : 2);
-  int &slot = cache[dev][gate_up ? 1 : 0][vi];
+  int &slot = cache[dev][gate_up ? 1 : 0][mx ? 1 : 0][vi];
   if (slot > 0) return slot;
-  const void *fn = nullptr;
-  if (gate_up)
-    fn = vi == 0 ? reinterpret_cast<const void *>(&decode_gemv_kernel<true, 4>)
-         : vi == 1 ? reinterpret_cast<const void *>(&decode_gemv_kernel<true, 8>)
-                   : reinterpret_cast<const void *>(&decode_gemv_kernel<true, 16>);
-  else
-    fn = vi == 0 ? reinterpret_cast<const void *>(&decode_gemv_kernel<false, 4>)
-         : vi == 1 ? reinterpret_cast<const void *>(&decode_gemv_kernel<false, 8>)
-                   : reinterpret_cast<const void *>(&decode_gemv_kernel<false, 16>);
+  const void *fn = gate_up ? (mx ? dec_kernel_fn<true, true>(bpl) : dec_kernel_fn<true, false>(bpl))
+                           : (mx ? dec_kernel_fn<false, true>(bpl) : dec_kernel_fn<false, false>(bpl));
   int per_cu = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kDecThreads, 0) != hipSuccess)
     return 0;
@@ -503,8 +501,8 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
   };
   const int bpl_gu = bpl_of(H), bpl_dn = bpl_of(I);
   // the workgroups each GEMV kernel keeps resident on the device
-  const int target_gu = dec_resident_workgroups(true, bpl_gu);
-  const int target_dn = dec_resident_workgroups(false, bpl_dn);
+  const int target_gu = dec_resident_workgroups(true, bpl_gu, gu.codebook == E4B_CB_MXFP4);
+  const int target_dn = dec_resident_workgroups(false, bpl_dn, dn.codebook == E4B_CB_MXFP4);
   if (target_gu <= 0 || target_dn <= 0) return hipErrorInvalidDeviceFunction;
   hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(256), 0, s, logits, int(p.E), idx, wts,
                      P, int(p.k),
@@ -518,20 +516,22 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
     const bool mx = st.codebook == E4B_CB_MXFP4;
     const int64_t eb = st.out * st.in / 2, ea = st.out * st.in / (mx ? kMxBlock : kBlock);
     timer_before(kernel_id, s);
-#define E4B_DEC_LAUNCH(GU, B)                                                                 \
-  hipLaunchKernelGGL((decode_gemv_kernel<GU, B>), grid, dim3(kDecThreads), 0, s, st.packed,     \
-                     mx ? nullptr : st.absmax, mx ? st.scales : nullptr, eb, ea, K_in, n_units, I, \
-                     vin, int(p.k), w, p.codebook, dst,                                          \
-                     ldo)
+#define E4B_DEC_LAUNCH(GU, B, MX)                                                             \
+  hipLaunchKernelGGL((decode_gemv_kernel<GU, B, MX>), grid, dim3(kDecThreads), 0, s, st.packed, \
+                     st.absmax, st.scales, eb, ea, K_in, n_units, I, vin, int(p.k), w,          \
+                     p.codebook, dst, ldo)
+#define E4B_DEC_BPL(GU, MX)                                                                   \
+  {                                                                                           \
+    if (bpl == 4) E4B_DEC_LAUNCH(GU, 4, MX);                                                  \
+    else if (bpl == 8) E4B_DEC_LAUNCH(GU, 8, MX);                                             \
+    else E4B_DEC_LAUNCH(GU, 16, MX);                                                          \
+  }
     if (gate_up) {
-      if (bpl == 4) E4B_DEC_LAUNCH(true, 4);
-      else if (bpl == 8) E4B_DEC_LAUNCH(true, 8);
-      else E4B_DEC_LAUNCH(true, 16);
+      if (mx) E4B_DEC_BPL(true, true) else E4B_DEC_BPL(true, false)
     } else {
-      if (bpl == 4) E4B_DEC_LAUNCH(false, 4);
-      else if (bpl == 8) E4B_DEC_LAUNCH(false, 8);
-      else E4B_DEC_LAUNCH(false, 16);
+      if (mx) E4B_DEC_BPL(false, true) else E4B_DEC_BPL(false, false)
     }
+#undef E4B_DEC_BPL
 #undef E4B_DEC_LAUNCH
     timer_after(kernel_id, s);
   };

@@ -91,8 +91,10 @@ struct MxGemmArgs {
   const int4 *tile_map;
   int32_t n_tiles;
   uint32_t grid;
-  uint16_t *C;  // gate_up: a [P, I] bf16; down: o [P, H] bf16
+  uint16_t *C;    // down: o [P, H] bf16
   int32_t ldc;
+  uint8_t *Cq;    // gate_up: a = bf16(silu(g) * u) as MXFP8 codes [P, I], element pairs swapped
+  uint8_t *Cs;    // gate_up: the E8M0 scales of a [P, I / 32]
 };
 hipError_t launch_mx8_rows(const uint16_t *x, int64_t rows, int64_t K, uint8_t *codes,
                            uint8_t *scales, hipStream_t s);

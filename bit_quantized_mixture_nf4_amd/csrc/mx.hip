@@ -29,30 +29,24 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 enum { MX_GATHER = 0, MX_DIRECT = 1 };  // activation rows: by token / by sorted pair
 enum { MX_SWIGLU = 0, MX_STORE = 1 };   // epilogue
 
-// ---- MXFP8 conversion of bf16 rows: one thread per 32-element block ----
-// shared = floor(log2(amax)) - 8 (frexpf, exact), clamped to [-127, 127];
-// element = |v| * 2^-shared rounded to E4M3 (rintf: nearest even) with
-// saturation at 448; code = sign | exponent field | mantissa.
+// ---- MXFP8 conversion: E4M3 codes against a shared E8M0 exponent ----
+// shared = floor(log2(amax)) - 8 (the frexp exponent, exact), clamped to
+// [-127, 127]. For y = |v| * 2^-shared, binade e = max(floor(log2 y), -6)
+// (the subnormals share the lowest; y = 0 takes it too) and n = y / 2^(e-3)
+// rounded to the nearest integer, ties to even (exact: power-of-two scalings
+// and rint). The code is 8 (e + 7) + (n - 8): n in [8, 16] on a normal binade,
+// where n = 16 carries into the next binade's mantissa 0, and n in [0, 8] on
+// the subnormal one (codes 0..8). Saturation is the clamp to 0x7E (448): every
+// y at or above the 448 / 480 midpoint lands on 0x7F or beyond.
+__device__ __forceinline__ int mx8_shared(float amax) {
+  return amax == 0.0f ? -127 : min(127, max(-127, __builtin_amdgcn_frexp_expf(amax) - 1 - 8));
+}
+
 __device__ __forceinline__ uint32_t e4m3_code(float v, int sh) {
   const float y = fabsf(ldexpf(v, -sh));
-  uint32_t c;
-  if (y >= 448.0f) {
-    c = 0x7E;
-  } else {
-    int ex = 0;
-    frexpf(y, &ex);  // y = m * 2^ex, 0.5 <= m < 1 (ex = 0 for y = 0)
-    const int e = max(ex - 1, -6);      // binade, subnormals share the lowest
-    const float quantum = ldexpf(1.0f, e - 3);
-    const float vq = rintf(y / quantum) * quantum;  // exact, nearest even
-    if (vq < 0.015625f) {               // 2^-6: subnormal (or zero)
-      c = uint32_t(vq * 512.0f);        // m / 8 * 2^-6 = m * 2^-9
-    } else {
-      int ex2 = 0;
-      const float m2 = frexpf(vq, &ex2);  // vq = m2 * 2^ex2
-      c = uint32_t((ex2 - 1 + 7) << 3) | uint32_t((m2 * 2.0f - 1.0f) * 8.0f);
-      c = min(c, 0x7Eu);
-    }
-  }
+  const int e = y == 0.0f ? -6 : max(__builtin_amdgcn_frexp_expf(y) - 1, -6);
+  const int n = int(rintf(ldexpf(y, 3 - e)));
+  const uint32_t c = uint32_t(min(8 * e + 48 + n, 0x7E));
   return c | (signbit(v) ? 0x80u : 0u);
 }
 
@@ -76,9 +70,7 @@ __global__ __launch_bounds__(256) void mx8_rows_kernel(const uint16_t *__restric
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  int ex = 0;
-  frexpf(amax, &ex);
-  const int sh = amax == 0.0f ? -127 : min(127, max(-127, ex - 1 - 8));
+  const int sh = mx8_shared(amax);
   u32x4 o[2];
 #pragma unroll
   for (int d = 0; d < 8; ++d) {
@@ -275,27 +267,46 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_kernel(MxGemmArgs g) {
       }
     }
   } else {
+    // a = bf16(silu(g) * u) converted to MXFP8 in place: for (i, jj) a lane
+    // holds pairs 8 q + 4 (lane / 32) + t of one 32-pair MX block of its row,
+    // lane ^ 32 the other sixteen; the block's amax and the stored bytes are
+    // exchanged between the two, and each writes 16 of the block's 32 bytes
+    const int h2 = lane >> 5;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = lrow + i * 32;
-      if (row < valid_rows) {
-        const int64_t grow = seg + row0 + row;
+      const int64_t grow = seg + row0 + row;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+      for (int jj = 0; jj < 2; ++jj) {
+        const int blk0 = nt * (kBN / 2) + wn * 64 + jj * 32;  // 32-aligned, wave-uniform
+        if (blk0 >= g.I) continue;
+        float av[4][4];
+        float amax = 0.0f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int pair = nt * (kBN / 2) + wn * 64 + jj * 32 + 8 * q + 4 * (lane >> 5);
-            if (pair < g.I) {
-              float av[4];
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-              for (int t = 0; t < 4; ++t) {
-                const float gv = acc[i][jj][4 * q + t], uv = acc[i][jj + 2][4 * q + t];
-                av[t] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-              }
-              *reinterpret_cast<u32x2 *>(g.C + grow * g.ldc + pair) =
-                  u32x2{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
-            }
+          for (int t = 0; t < 4; ++t) {
+            const float gv = acc[i][jj][4 * q + t], uv = acc[i][jj + 2][4 * q + t];
+            const float v = bf16_lo(f32_to_bf16(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv));
+            av[q][t] = v;
+            amax = fmaxf(amax, fabsf(v));
           }
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const int sh = mx8_shared(amax);
+        uint32_t wq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)  // bytes of each element pair stored swapped
+          wq[q] = e4m3_code(av[q][1], sh) | e4m3_code(av[q][0], sh) << 8 |
+                  e4m3_code(av[q][3], sh) << 16 | e4m3_code(av[q][2], sh) << 24;
+        // lane h2 = 0 keeps bytes 0..15 (words q = 0, 1 of both lanes),
+        // lane h2 = 1 bytes 16..31 (q = 2, 3)
+        const uint32_t r0 = __shfl_xor(h2 ? wq[0] : wq[2], 32);
+        const uint32_t r1 = __shfl_xor(h2 ? wq[1] : wq[3], 32);
+        const u32x4 outw = h2 ? u32x4{r0, wq[2], r1, wq[3]} : u32x4{wq[0], r0, wq[1], r1};
+        if (row < valid_rows) {
+          *reinterpret_cast<u32x4 *>(g.Cq + grow * g.I + blk0 + 16 * h2) = outw;
+          if (h2 == 0) g.Cs[grow * (g.I >> 5) + (blk0 >> 5)] = uint8_t(sh + 127);
+        }
       }
     }
   }
