@@ -47,7 +47,7 @@ def _sampled_oracle(cfg, seed, kind, x, gy, idx_ref, w_ref, tokens):
 
 @pytest.mark.parametrize("name,kind,ntok", [("olmoe", "nf4", 6), ("qwen3_prefill", "nf4", 6),
                                             ("mixtral", "fp4", 24), ("mixtral", "nf4", 24),
-                                            ("olmoe", "bf16", 6)])
+                                            ("olmoe", "bf16", 6), ("olmoe", "mxfp4", 6)])
 def test_full_size_forward_dgrad_sampled(name, kind, ntok):
     cfg = get_config(name)
     seed = 0
@@ -168,4 +168,43 @@ def test_lora_full_size_olmoe_sampled():
     for name, got, want in zip(("dA_gu", "dB_gu", "dA_dn", "dB_dn"), grads, ref):
         tol_check(to_np(got[e_star]), want[remap[e_star]], f"olmoe lora {name}[{e_star}]")
     del layer, ws, saved
+    torch.cuda.empty_cache()
+
+
+def test_mx8_full_size_olmoe_sampled():
+    """The MX forward (MXFP8 activations on the block-scaled FP4 MFMA) on the
+    OLMoE-shaped MXFP4 layer, in the benchmark's launch configuration:
+    sampled tokens' rows against the oracle's MX forward, the whole output
+    against the exact-activation grouped forward (the activation rounding
+    only), and bitwise run to run."""
+    cfg = get_config("olmoe")
+    seed = 0
+    announce(f"olmoe mxfp4 full size, mx8 path E{cfg.E} H{cfg.H} I{cfg.I} k{cfg.k} T{cfg.T}")
+    layer = _layer(cfg, seed, "mxfp4")
+    x = gen_x(cfg, seed)
+    lg = gen_logits(cfg, seed)
+    x_d, lg_d = bf16_tensor(x), torch.from_numpy(lg).to(DEV)
+    ws = torch.empty(e4b.workspace_bytes(layer, cfg.T, cfg.k), dtype=torch.uint8, device=DEV)
+    y, idx, w, _ = e4b.moe_forward(layer, x_d, cfg.k, logits=lg_d, path="mx8", workspace=ws)
+    y = y.clone()
+    y2, _, _, _ = e4b.moe_forward(layer, x_d, cfg.k, logits=lg_d, path="mx8", workspace=ws)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    yg, _, _, _ = e4b.moe_forward(layer, x_d, cfg.k, logits=lg_d, path="grouped", workspace=ws)
+    tol_check(to_np(y), to_np(yg).astype(np.float64), "olmoe mx8 vs grouped", rel=0.1)
+
+    idx_ref, w_ref = oracle.route(lg, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    rng = np.random.default_rng(77)
+    tokens = np.sort(rng.choice(cfg.T, size=6, replace=False))
+    experts = sorted(set(int(e) for e in idx_ref[tokens].ravel()))
+    announce(f"oracle weights for {len(experts)} experts")
+    st = oracle_expert_stacks(cfg, seed, experts, "mxfp4")
+    remap = {e: i for i, e in enumerate(experts)}
+    wgu = np.stack([st["gate_up"][e] for e in experts])
+    wdn = np.stack([st["down"][e] for e in experts])
+    idx_c = np.vectorize(remap.get)(idx_ref[tokens]).astype(np.int32)
+    # x is bf16-valued as generated: the device converts the same values
+    y_ref = oracle.mx8_forward(x[tokens], idx_c, w_ref[tokens], wgu, wdn)
+    tol_check(to_np(y[torch.from_numpy(tokens).to(DEV)]), y_ref, "olmoe mx8 y")
+    del layer, ws
     torch.cuda.empty_cache()
