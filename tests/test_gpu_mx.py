@@ -153,3 +153,35 @@ def test_mx8_forward_against_oracle(name, tiny_mx):
     # run to run: bitwise identical
     y3, _, _, _ = e4b.moe_forward(pb.layer, pb.x_d, cfg.k, logits=pb.logits_d, path="mx8")
     assert torch.equal(y.view(torch.int16), y3.view(torch.int16))
+
+
+@pytest.mark.parametrize("T", [0, 1, 5])
+def test_mx8_small_batches(tiny_mx, T):
+    # one m-tile per expert with one to five valid rows (or no call at all)
+    pb, cfg = tiny_mx, tiny_mx.cfg
+    x, lg = pb.x_d[:T].contiguous(), pb.logits_d[:T].contiguous()
+    announce(f"mx8 path T={T}")
+    y, idx, w, _ = e4b.moe_forward(pb.layer, x, cfg.k, logits=lg, path="mx8")
+    assert y.shape == (T, cfg.H)
+    if T == 0:
+        return
+    idx_ref, w_ref = oracle.route(pb.logits[:T], cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    wgu, wdn = pb.oracle_weights()
+    xb = torch.from_numpy(pb.x[:T]).to(torch.bfloat16).float().numpy()
+    tol_check(to_np(y), oracle.mx8_forward(xb, idx_ref, w_ref, wgu, wdn), f"y mx8 T={T}")
+
+
+def test_mx8_given_routing_top_k_equals_E():
+    # routing passed in (no logits), every token on every expert
+    cfg = MoEConfig("mx_allE", E=4, H=256, I=128, k=4, T=96, routing="normal")
+    announce("mxfp4 top_k = E E4 H256 I128 T96, mx8 path with given routing")
+    pb = Problem(cfg, seed=9, codebook="mxfp4", with_grad=False)
+    idx_ref, w_ref = oracle.route(pb.logits, cfg.k)
+    idx_d = torch.from_numpy(idx_ref).to(DEV)
+    w_d = torch.from_numpy(w_ref.astype(np.float32)).to(DEV)
+    y, _, _, _ = e4b.moe_forward(pb.layer, pb.x_d, cfg.k, topk_idx=idx_d, topk_w=w_d, path="mx8")
+    wgu, wdn = pb.oracle_weights()
+    xb = torch.from_numpy(pb.x).to(torch.bfloat16).float().numpy()
+    tol_check(to_np(y), oracle.mx8_forward(xb, idx_ref, w_d.cpu().numpy().astype(np.float64), wgu, wdn),
+              "y mx8 top_k=E")
