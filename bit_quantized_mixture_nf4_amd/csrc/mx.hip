@@ -4,8 +4,9 @@
 // The 0.31.1 project page lists MXFP4 experts (gpt-oss) and a native MXFP4
 // row; the formats are the OCP Microscaling Formats (MX) v1.0 ones: E2M1
 // weights and E4M3 activations, each with an E8M0 scale per 32 elements along
-// the reduction. The activations are converted here per row (the pages do not
-// describe them): x before gate_up, a = bf16(silu(g) * u) before down.
+// the reduction. The activations are converted per row (the pages do not
+// describe them): x by mx8_rows_kernel before gate_up, a = bf16(silu(g) * u)
+// inside the gate_up epilogue, which writes it only as MXFP8 rows for down.
 //
 // Operand layout of the instruction (cbsz = 4: A is E2M1, blgp = 0: B is E4M3),
 // established with a probe kernel:
