@@ -20,11 +20,13 @@ __device__ __forceinline__ void route_dpp_best(float &bv, int &bi) {
   }
 }
 
-// Serial form: k rounds of a wave-wide argmax (any k).
+// Serial form: k rounds of a wave-wide argmax (any k). PER >= ceil(E / 64)
+// logits per lane (the register arrays and unrolled loops are sized by it).
+template <int PER>
 __device__ __forceinline__ void route_token_serial(const float *__restrict__ logits, int64_t t, int E,
                                             int k, int lane, int32_t *__restrict__ idx,
                                             float *__restrict__ wts, int32_t *lds_idx) {
-  constexpr int kMaxPer = kMaxE / 64;
+  constexpr int kMaxPer = PER;
   float v[kMaxPer];
   const int per = (E + 63) / 64;
 #pragma unroll
@@ -114,15 +116,16 @@ struct alignas(16) RouteLds {
 //  2. The candidates are compacted into LDS (ballot prefix counts) and each
 //     takes as its slot the number of candidates ordered before it.
 // More than kRouteCand candidates (massive ties) or k > 64 take the serial form.
-__device__ __forceinline__ void route_token(const float *__restrict__ logits, int64_t t, int E,
-                                            int k, int lane, int32_t *__restrict__ idx,
-                                            float *__restrict__ wts, int32_t *lds_idx,
-                                            RouteLds &sc) {
+template <int PER>
+__device__ __forceinline__ void route_token_per(const float *__restrict__ logits, int64_t t, int E,
+                                                int k, int lane, int32_t *__restrict__ idx,
+                                                float *__restrict__ wts, int32_t *lds_idx,
+                                                RouteLds &sc) {
   if (k > 64) {
-    route_token_serial(logits, t, E, k, lane, idx, wts, lds_idx);
+    route_token_serial<PER>(logits, t, E, k, lane, idx, wts, lds_idx);
     return;
   }
-  constexpr int kMaxPer = kMaxE / 64;
+  constexpr int kMaxPer = PER;
   float v[kMaxPer];
   const int per = (E + 63) / 64;
   float m = -INFINITY;
@@ -170,7 +173,7 @@ __device__ __forceinline__ void route_token(const float *__restrict__ logits, in
     C += __popcll(bal);
   }
   if (C > kRouteCand) {
-    route_token_serial(logits, t, E, k, lane, idx, wts, lds_idx);
+    route_token_serial<PER>(logits, t, E, k, lane, idx, wts, lds_idx);
     return;
   }
 #pragma unroll
@@ -216,6 +219,21 @@ __device__ __forceinline__ void route_token(const float *__restrict__ logits, in
     if (lds_idx) lds_idx[t * k + lane] = id;
   }
   __builtin_amdgcn_wave_barrier();
+}
+
+// route_token_per sized for E: entries per lane rounded up to 1, 2, 4, 8 or
+// kMaxE / 64, so a small expert count runs no loop iterations sized for the
+// largest (E is uniform across the grid: every wave takes the same branch).
+__device__ __forceinline__ void route_token(const float *__restrict__ logits, int64_t t, int E,
+                                            int k, int lane, int32_t *__restrict__ idx,
+                                            float *__restrict__ wts, int32_t *lds_idx,
+                                            RouteLds &sc) {
+  static_assert(kMaxE / 64 == 16, "dispatch covers 1..16 logits per lane");
+  if (E <= 64) route_token_per<1>(logits, t, E, k, lane, idx, wts, lds_idx, sc);
+  else if (E <= 128) route_token_per<2>(logits, t, E, k, lane, idx, wts, lds_idx, sc);
+  else if (E <= 256) route_token_per<4>(logits, t, E, k, lane, idx, wts, lds_idx, sc);
+  else if (E <= 512) route_token_per<8>(logits, t, E, k, lane, idx, wts, lds_idx, sc);
+  else route_token_per<16>(logits, t, E, k, lane, idx, wts, lds_idx, sc);
 }
 
 }  // namespace e4b
