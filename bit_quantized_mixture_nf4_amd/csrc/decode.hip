@@ -81,7 +81,11 @@ __device__ __forceinline__ int wave_sum(int v) {
 // of tiles of kDecTile units per distinct expert). Ranks come from
 // comparisons of unique (expert, pair) keys, segment starts and the chunk
 // offsets from wave ballots and scans.
-__global__ __launch_bounds__(256) void decode_prep_kernel(const float *__restrict__ logits, int E,
+// One wave per token routes (kDecodeMaxT waves); the waves past the first
+// kDecMaxPairs threads then exit, and the rest of the kernel runs one thread
+// per routed pair (a barrier waits only for the waves still running).
+constexpr int kPrepThreads = 64 * kDecodeMaxT;
+__global__ __launch_bounds__(kPrepThreads) void decode_prep_kernel(const float *__restrict__ logits, int E,
                                                           int32_t *__restrict__ idx,
                                                           float *__restrict__ wts, int P,
                                                           int k_route, int tiles_gu, int tiles_dn,
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const float *__restric
   __shared__ int32_t s_sorted_p[kDecMaxPairs];
   __shared__ int32_t s_dseg[kDecMaxPairs + 1];
   __shared__ int32_t s_wsum[5][4];
-  __shared__ RouteLds s_route[kDecMaxPairs / 64];
+  __shared__ RouteLds s_route[kDecodeMaxT];
   __shared__ int4 s_item[kDecMaxPairs];          // distinct expert: id, pairs, segment, tokens
   __shared__ int32_t s_first[2][kDecMaxPairs + 1];  // its first work item per map
   __shared__ int32_t s_tpw[2][kDecMaxPairs];        // its tiles per work item per map
@@ -102,13 +106,15 @@ __global__ __launch_bounds__(256) void decode_prep_kernel(const float *__restric
   if (logits) {
     // s_sorted_e doubles as the routed ids until the keys are built
     const int T = P / k_route;
-    for (int t = wv; t < T; t += kDecMaxPairs / 64)
+    for (int t = wv; t < T; t += kDecodeMaxT)
       route_token(logits, t, E, k_route, lane, idx, wts, s_sorted_e, s_route[wv]);
     __syncthreads();
+    if (p >= kDecMaxPairs) return;
     if (p < P) e_p = s_sorted_e[p];
     __syncthreads();
-  } else if (p < P) {
-    e_p = idx[p];
+  } else {
+    if (p >= kDecMaxPairs) return;
+    if (p < P) e_p = idx[p];
   }
   // unique sort key: expert, then pair id (stable)
   const int key = p < P ? e_p * kDecMaxPairs + p : 0x7FFFFFFF;
@@ -504,7 +510,7 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
   const int target_gu = dec_resident_workgroups(true, bpl_gu, gu.codebook == E4B_CB_MXFP4);
   const int target_dn = dec_resident_workgroups(false, bpl_dn, dn.codebook == E4B_CB_MXFP4);
   if (target_gu <= 0 || target_dn <= 0) return hipErrorInvalidDeviceFunction;
-  hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(256), 0, s, logits, int(p.E), idx, wts,
+  hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(kPrepThreads), 0, s, logits, int(p.E), idx, wts,
                      P, int(p.k),
                      I / kDecTile, H / kDecTile, target_gu, target_dn, w);
 
