@@ -217,11 +217,8 @@ extern "C" e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t t
   u.ldc = int32_t(p.H);
   E4B_TRY(launch_grouped_gemm(GEMM_GATE_UP_DGRAD, u, stream));
 
-  const int32_t *pos = v.pos;
-  E4B_TRY(launch_combine_rows(gx, pos, nullptr, T, top_k, int(p.H),
-                              static_cast<uint16_t *>(grad_x_bf16), stream));
-  if (grad_topk_w)
-    E4B_TRY(launch_combine_gradw(partial, int(p.n_tiles_i), pos, p.P, grad_topk_w, stream));
+  E4B_TRY(launch_combine_dgrad(gx, v.pos, T, top_k, int(p.H), static_cast<uint16_t *>(grad_x_bf16),
+                               partial, int(p.n_tiles_i), grad_topk_w, stream));
   return E4B_OK;
 }
 
@@ -422,10 +419,8 @@ extern "C" e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lo
   u.lora_rows = int32_t(p.H);
   E4B_TRY(launch_grouped_gemm(GEMM_GATE_UP_DGRAD, u, stream));
 
-  E4B_TRY(launch_combine_rows(gx, v.pos, nullptr, T, top_k, int(p.H),
-                              static_cast<uint16_t *>(grad_x_bf16), stream));
-  if (grad_topk_w)
-    E4B_TRY(launch_combine_gradw(partial, int(p.n_tiles_i), v.pos, p.P, grad_topk_w, stream));
+  E4B_TRY(launch_combine_dgrad(gx, v.pos, T, top_k, int(p.H), static_cast<uint16_t *>(grad_x_bf16),
+                               partial, int(p.n_tiles_i), grad_topk_w, stream));
 
   // adapter gradients: a A_dn^T from the saved / recomputed g|u, then the
   // four per-expert outer-product sums

@@ -11,18 +11,30 @@
 namespace e4b {
 
 // y[t] = sum_j w[t,j] * O[pos(t,j)]   (weighted)   or   sum_j O[pos(t,j)]
-// rows of H bf16; 8 elements (16 bytes) per thread and step.
+// rows of H bf16; 8 elements (16 bytes) per thread and step. The unweighted
+// form (the dgrad combine) also sums, when gw is given, each pair's routing-
+// weight gradient over the n-tiles of the down dgrad in ascending order:
+// gw[t, j] = sum_i partial[pos(t,j)][i].
 template <bool WEIGHTED>
 __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t *__restrict__ O,
                                                            const int32_t *__restrict__ pos_of_pair,
                                                            const float *__restrict__ wts, int k,
-                                                           int H, uint16_t *__restrict__ y) {
+                                                           int H, uint16_t *__restrict__ y,
+                                                           const float *__restrict__ partial,
+                                                           int n_tiles, float *__restrict__ gw) {
   const int64_t t = blockIdx.x;
   __shared__ int32_t pos[kMaxTopK];
   __shared__ float w[kMaxTopK];
   if (threadIdx.x < k) {
-    pos[threadIdx.x] = pos_of_pair[t * k + threadIdx.x];
+    const int32_t pj = pos_of_pair[t * k + threadIdx.x];
+    pos[threadIdx.x] = pj;
     w[threadIdx.x] = WEIGHTED ? wts[t * k + threadIdx.x] : 1.0f;
+    if (!WEIGHTED && gw) {
+      const float *src = partial + int64_t(pj) * n_tiles;
+      float sum = 0.0f;
+      for (int i = 0; i < n_tiles; ++i) sum += src[i];
+      gw[t * k + threadIdx.x] = sum;
+    }
   }
   __syncthreads();
   for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
@@ -46,36 +58,20 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t *__res
   }
 }
 
-// grad_w[t, j] = sum over n-tiles of partial[pos(t,j)][tile] (ascending tiles).
-__global__ __launch_bounds__(256) void combine_gradw_kernel(const float *__restrict__ partial,
-                                                            int n_tiles,
-                                                            const int32_t *__restrict__ pos_of_pair,
-                                                            int64_t P, float *__restrict__ gw) {
-  const int64_t p = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (p >= P) return;
-  const float *src = partial + int64_t(pos_of_pair[p]) * n_tiles;
-  float s = 0.0f;
-  for (int i = 0; i < n_tiles; ++i) s += src[i];
-  gw[p] = s;
-}
-
 hipError_t launch_combine_rows(const uint16_t *rows, const int32_t *pos_of_pair, const float *w,
                                int64_t T, int k, int H, uint16_t *out, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (w)
-    hipLaunchKernelGGL(combine_rows_kernel<true>, dim3(uint32_t(T)), dim3(256), 0, s, rows,
-                       pos_of_pair, w, k, H, out);
-  else
-    hipLaunchKernelGGL(combine_rows_kernel<false>, dim3(uint32_t(T)), dim3(256), 0, s, rows,
-                       pos_of_pair, w, k, H, out);
+  hipLaunchKernelGGL(combine_rows_kernel<true>, dim3(uint32_t(T)), dim3(256), 0, s, rows,
+                     pos_of_pair, w, k, H, out, nullptr, 0, nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_combine_gradw(const float *partial, int n_tiles, const int32_t *pos_of_pair,
-                                int64_t P, float *gw, hipStream_t s) {
-  if (P == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_gradw_kernel, dim3(uint32_t((P + 255) / 256)), dim3(256), 0, s,
-                     partial, n_tiles, pos_of_pair, P, gw);
+hipError_t launch_combine_dgrad(const uint16_t *rows, const int32_t *pos_of_pair, int64_t T, int k,
+                                int H, uint16_t *out, const float *partial, int n_tiles,
+                                float *gw, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_rows_kernel<false>, dim3(uint32_t(T)), dim3(256), 0, s, rows,
+                     pos_of_pair, nullptr, k, H, out, partial, n_tiles, gw);
   return hipGetLastError();
 }
 

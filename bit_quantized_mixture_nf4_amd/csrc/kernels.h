@@ -103,8 +103,14 @@ hipError_t launch_mx_gemm(bool gate_up, const MxGemmArgs &a, hipStream_t s);
 // grid = m_tiles_bound * n_tiles; the launch rounds it up to a multiple of 8.
 hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s);
 
+// y[t] = sum_j w[t, j] * rows[pos(t, j)] in fp32, slot order.
 hipError_t launch_combine_rows(const uint16_t *rows, const int32_t *pos_of_pair, const float *w,
                                int64_t T, int k, int H, uint16_t *out, hipStream_t s);
+// grad_x[t] = sum_j rows[pos(t, j)], and (gw not null) gw[t, j] = the sum of
+// partial[pos(t, j)][0 .. n_tiles) in ascending order.
+hipError_t launch_combine_dgrad(const uint16_t *rows, const int32_t *pos_of_pair, int64_t T, int k,
+                                int H, uint16_t *out, const float *partial, int n_tiles,
+                                float *gw, hipStream_t s);
 
 // ---- LoRA (lora.hip) ----
 // out[e, n, :] = bf16(s * M[e, n, j]) for j < r, 0 up to kLoraK, where
@@ -137,8 +143,5 @@ hipError_t launch_lora_wgrad(int u_mode, const uint16_t *src, int64_t ld, int N,
                              const int32_t *sorted, const int32_t *offsets, int topk,
                              const float *topk_w, int64_t E, const float *V, bool v_weighted,
                              int r, float s, bool out_trans, float *out, hipStream_t st);
-
-hipError_t launch_combine_gradw(const float *partial, int n_tiles, const int32_t *pos_of_pair,
-                                int64_t P, float *gw, hipStream_t s);
 
 }  // namespace e4b
