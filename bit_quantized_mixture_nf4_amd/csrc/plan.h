@@ -21,7 +21,7 @@ constexpr int kBNNarrow = 128;
 constexpr int kBK = 64;    // reduction step = one quantization block
 constexpr int kBlock = 64; // quantization block (elements along `in`)
 constexpr int kMxBlock = 32;  // MXFP4 scale block (elements along `in`)
-constexpr int kPermChunk = 1024;  // pairs per histogram / scatter chunk
+constexpr int kPermChunk = 256;  // pairs per histogram / scatter chunk
 constexpr int kMaxE = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kDecodeMaxT = 8;

@@ -89,6 +89,15 @@ __global__ __launch_bounds__(64) void perm_scatter_kernel(
   __shared__ int32_t base[kMaxE];
   const int lane = threadIdx.x;
   const int64_t c = blockIdx.x;
+  const int64_t p0 = c * kPermChunk;
+  // the chunk's expert ids, all loads issued before the scan below
+  constexpr int kIt = kPermChunk / 64;
+  int ids[kIt];
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int64_t p = p0 + it * 64 + lane;
+    ids[it] = p < P ? flat_idx[p] : 0;
+  }
   // exclusive scan of counts (and of m-tiles) over experts, 64 at a time
   int32_t carry = 0, tcarry = 0;
   for (int e0 = 0; e0 < E; e0 += 64) {
@@ -127,11 +136,11 @@ __global__ __launch_bounds__(64) void perm_scatter_kernel(
     for (int64_t t = tcarry + lane; t < m_tiles_bound; t += 64) tile_map[t] = int4{0, 0, 0, 0};
   __syncthreads();
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int64_t p0 = c * kPermChunk;
-  for (int it = 0; it < kPermChunk / 64; ++it) {
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
     const int64_t p = p0 + it * 64 + lane;
     const bool valid = p < P;
-    const int e = valid ? flat_idx[p] : 0;
+    const int e = ids[it];
     uint64_t match = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
