@@ -344,7 +344,7 @@ extern "C" e4b_status e4b_mx8_rows(const void *x_bf16, int64_t rows, int64_t K, 
   if (!x_bf16 || !codes || !scales) return E4B_ERR_NULL;
   if (rows < 0 || K <= 0 || K % kMxBlock != 0 || rows * K > (int64_t(1) << 40)) return E4B_ERR_SHAPE;
   if (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales)) return E4B_ERR_ALIGN;
-  return launch_mx8_rows(static_cast<const uint16_t *>(x_bf16), rows, int(K), codes, scales,
+  return launch_mx8_rows(static_cast<const uint16_t *>(x_bf16), rows, K, codes, scales,
                          stream) == hipSuccess
              ? E4B_OK
              : E4B_ERR_HIP;
