@@ -216,7 +216,8 @@ def moe_forward(layer, x, top_k, logits=None, topk_idx=None, topk_w=None, save=F
     y = torch.empty(T, layer.H, dtype=torch.bfloat16, device=dev) if out is None else out
     saved = None
     if save:
-        saved = torch.empty(max(saved_bytes(layer, T, top_k), 16) // 2, dtype=torch.bfloat16, device=dev)
+        # zero-filled: the padding of the blocked g|u layout is never written
+        saved = torch.zeros(max(saved_bytes(layer, T, top_k), 16) // 2, dtype=torch.bfloat16, device=dev)
     ws = _workspace(layer, T, top_k, workspace)
     c = layer.as_c()
     code = load().e4b_moe_forward(
@@ -307,7 +308,8 @@ def moe_lora_forward(layer, lora, x, top_k, logits=None, topk_idx=None, topk_w=N
     y = torch.empty(T, layer.H, dtype=torch.bfloat16, device=dev)
     saved = None
     if save:
-        saved = torch.empty(max(saved_bytes(layer, T, top_k), 16) // 2, dtype=torch.bfloat16, device=dev)
+        # zero-filled: the padding of the blocked g|u layout is never written
+        saved = torch.zeros(max(saved_bytes(layer, T, top_k), 16) // 2, dtype=torch.bfloat16, device=dev)
     ws = _lora_workspace(layer, T, top_k, workspace)
     c, lc = layer.as_c(), lora.as_c()
     code = load().e4b_moe_lora_forward(

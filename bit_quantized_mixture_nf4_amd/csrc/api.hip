@@ -426,13 +426,13 @@ extern "C" e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lo
   // four per-expert outer-product sums
   E4B_TRY(launch_lora_project_mfma(LS_GU_ACT, gu, 2 * p.I, int(p.I), int(p.I), v.sorted, int(p.k),
                                    v, int(p.E), p.m_tiles_bound, l.pj_adn, l.aa, stream));
-  E4B_TRY(launch_lora_wgrad(LS_ROWS, dgu, 2 * p.I, int(2 * p.I), int(p.I), v.sorted, v.offsets,
+  E4B_TRY(launch_lora_wgrad(LS_ROWS, dgu, 2 * p.I, int(2 * p.I), int(p.I), v.sorted, v.offsets, v.tile_offsets,
                             int(p.k), topk_w, p.E, l.xa, false, r, sc, false, dB_gu, stream));
-  E4B_TRY(launch_lora_wgrad(LS_X_GATHER, x, p.H, int(p.H), int(p.I), v.sorted, v.offsets, int(p.k),
+  E4B_TRY(launch_lora_wgrad(LS_X_GATHER, x, p.H, int(p.H), int(p.I), v.sorted, v.offsets, v.tile_offsets, int(p.k),
                             topk_w, p.E, l.hb, false, r, sc, true, dA_gu, stream));
-  E4B_TRY(launch_lora_wgrad(LS_WX_GATHER, gy, p.H, int(p.H), int(p.I), v.sorted, v.offsets,
+  E4B_TRY(launch_lora_wgrad(LS_WX_GATHER, gy, p.H, int(p.H), int(p.I), v.sorted, v.offsets, v.tile_offsets,
                             int(p.k), topk_w, p.E, l.aa, false, r, sc, false, dB_dn, stream));
-  E4B_TRY(launch_lora_wgrad(LS_GU_ACT, gu, 2 * p.I, int(p.I), int(p.I), v.sorted, v.offsets,
+  E4B_TRY(launch_lora_wgrad(LS_GU_ACT, gu, 2 * p.I, int(p.I), int(p.I), v.sorted, v.offsets, v.tile_offsets,
                             int(p.k), topk_w, p.E, l.gb, true, r, sc, true, dA_dn, stream));
   return E4B_OK;
 }

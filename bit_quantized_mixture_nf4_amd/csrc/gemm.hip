@@ -438,11 +438,13 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
               if (g.C)
                 *reinterpret_cast<u32x2 *>(g.C + grow * g.ldc + pair) =
                     u32x2{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
+              static_assert(EPI != EPI_SWIGLU || kBN / 2 == kGuBlockPairs, "one g|u block per tile");
               if (g.GU) {
-                *reinterpret_cast<u32x2 *>(g.GU + grow * g.ldgu + pair) =
-                    u32x2{pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
-                *reinterpret_cast<u32x2 *>(g.GU + grow * g.ldgu + g.I + pair) =
-                    u32x2{pack_bf16x2(uv[0], uv[1]), pack_bf16x2(uv[2], uv[3])};
+                // the tile's 128 pairs are block nt of the blocked g|u
+                const int64_t ch = gu_chunk(mt, nt, g.n_tiles, row, pair - nt * (kBN / 2));
+                *reinterpret_cast<u32x4 *>(g.GU + ch * 8) =
+                    u32x4{pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]),
+                          pack_bf16x2(uv[0], uv[1]), pack_bf16x2(uv[2], uv[3])};
               }
             }
           }
@@ -529,21 +531,29 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
     // batches (row half i, column group j), one batch ahead of its use, with
     // rows and columns clamped into range (out-of-range results are not
     // stored), so the loads of a batch overlap the arithmetic of the previous.
+    static_assert(EPI != EPI_DSWIGLU || kBN == kGuBlockPairs, "one g|u block per tile");
     int64_t grow[2];
+    int rrow[2];
     float wr[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) grow[i] = seg + row0 + min(lrow + i * 32, valid_rows - 1);
+    for (int i = 0; i < 2; ++i) {
+      rrow[i] = min(lrow + i * 32, valid_rows - 1);
+      grow[i] = seg + row0 + rrow[i];
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) wr[i] = g.topk_w[g.sorted_pair[grow[i]]];
     u32x2 gg[2][4], uu[2][4];
+    // pairs of this block the forward wrote: [0, cmax]
+    const int cmax = min(kBN, g.N - nt * kBN) - 4;
     auto fetch = [&](int b, int slot) {
       const int i = b >> 2, j = b & 3;
-      const uint16_t *gurow = g.GU + grow[i] * g.ldgu;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = min(nt * kBN + lcol + j * 32 + 8 * q, g.N - 4);
-        gg[slot][q] = *reinterpret_cast<const u32x2 *>(gurow + n);
-        uu[slot][q] = *reinterpret_cast<const u32x2 *>(gurow + g.I + n);
+        const int c = min(lcol + j * 32 + 8 * q, cmax);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(
+            g.GU + gu_chunk(mt, nt, g.n_tiles, rrow[i], c) * 8);
+        gg[slot][q] = u32x2{v[0], v[1]};
+        uu[slot][q] = u32x2{v[2], v[3]};
       }
     };
     float part[2] = {0.0f, 0.0f};

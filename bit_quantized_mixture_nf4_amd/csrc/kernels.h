@@ -8,6 +8,16 @@
 
 namespace e4b {
 
+// Chunk index (16 bytes: g[4] then u[4], bf16, of 4 consecutive pairs) of row
+// r of m-tile mt and pair c of 128-pair column block pb (npb blocks per
+// m-tile) in a gated layer's saved / recomputed g|u. Within a block, lane
+// r % 32 + 32 ((c % 8) / 4) of run ((r / 32, c / 32), (c % 32) / 8): a wave
+// of the GEMM epilogues that write and read it moves 1 KB per instruction.
+__device__ __forceinline__ int64_t gu_chunk(int mt, int pb, int npb, int r, int c) {
+  return (int64_t(mt) * npb + pb) * kGuBlockChunks +
+         ((((r >> 5) * 4 + (c >> 5)) * 4 + ((c & 31) >> 3)) * 64 + ((c & 7) >> 2) * 32 + (r & 31));
+}
+
 enum GemmVariant {
   GEMM_GATE_UP_FWD = 0,   // A gathered x,      B = W_gu rows,    SiLU*up (or SiLU) epilogue
   GEMM_DOWN_FWD = 1,      // A sorted a,        B = W_dn rows,    bf16 store
@@ -140,7 +150,8 @@ hipError_t launch_lora_project_mfma(int src_mode, const uint16_t *src, int64_t l
 // U(pair)[n] * V(pair)[j] (* topk_w[pair] when v_weighted), written as
 // [E, N, r] (a B-shaped gradient) or [E, r, N] (A-shaped, out_trans).
 hipError_t launch_lora_wgrad(int u_mode, const uint16_t *src, int64_t ld, int N, int I,
-                             const int32_t *sorted, const int32_t *offsets, int topk,
+                             const int32_t *sorted, const int32_t *offsets,
+                             const int32_t *tile_offsets, int topk,
                              const float *topk_w, int64_t E, const float *V, bool v_weighted,
                              int r, float s, bool out_trans, float *out, hipStream_t st);
 

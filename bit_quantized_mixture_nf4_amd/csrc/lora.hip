@@ -89,11 +89,14 @@ __global__ __launch_bounds__(256) void lora_project_mfma_kernel(
   if (wave * 64 >= valid) return;  // no barriers in this kernel
   const int r16 = lane & 15, kb = (lane >> 4) * 8;
   const uint16_t *rowp[4];
+  int rin[4];  // LS_GU_ACT: the row within the m-tile (blocked g|u)
 #pragma unroll
   for (int gi = 0; gi < 4; ++gi) {
-    const int srow = seg + row0 + min(wave * 64 + gi * 16 + r16, valid - 1);
+    rin[gi] = min(wave * 64 + gi * 16 + r16, valid - 1);
+    const int srow = seg + row0 + rin[gi];
     rowp[gi] = (SRC == LS_X_GATHER ? src + int64_t(sorted[srow] / topk) * ld : src + srow * ld) + kb;
   }
+  const int npb = (I + kGuBlockPairs - 1) / kGuBlockPairs;
   const uint16_t *mp = Mj + (int64_t(e) * kLoraK + r16) * K + kb;
   f32x4 acc[4];
 #pragma unroll
@@ -104,8 +107,12 @@ __global__ __launch_bounds__(256) void lora_project_mfma_kernel(
     for (int gi = 0; gi < 4; ++gi) {
       u32x4 q;
       if (SRC == LS_GU_ACT) {
-        const u32x4 gq = *reinterpret_cast<const u32x4 *>(rowp[gi] + k0);
-        const u32x4 uq = *reinterpret_cast<const u32x4 *>(rowp[gi] + I + k0);
+        // pairs k0 + kb .. + 7: two chunks of 4 (g[4], u[4]) of the blocked g|u
+        const int c = k0 + kb, pb = c / kGuBlockPairs, cc = c % kGuBlockPairs;
+        const u32x4 c0 = *reinterpret_cast<const u32x4 *>(src + gu_chunk(mt, pb, npb, rin[gi], cc) * 8);
+        const u32x4 c1 = *reinterpret_cast<const u32x4 *>(src + gu_chunk(mt, pb, npb, rin[gi], cc + 4) * 8);
+        const u32x4 gq{c0[0], c0[1], c1[0], c1[1]};
+        const u32x4 uq{c0[2], c0[3], c1[2], c1[3]};
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           q[t] = pack_bf16x2(silu_f(bf16_lo(gq[t])) * bf16_lo(uq[t]),
@@ -141,7 +148,8 @@ constexpr int kWgPad = kWgChunk + 8;  // LDS row of one column / rank: 32 pairs 
 template <int U>
 __global__ __launch_bounds__(256) void lora_wgrad_kernel(
     const uint16_t *__restrict__ src, int64_t ld, int N, int I, const int32_t *__restrict__ sorted,
-    const int32_t *__restrict__ offsets, int topk, const float *__restrict__ topk_w,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ tile_offsets, int topk,
+    const float *__restrict__ topk_w,
     const float *__restrict__ V, bool v_weighted, int r, float sc, bool out_trans,
     float *__restrict__ out) {
   __shared__ __attribute__((aligned(16))) uint16_t su[kWgCols][kWgPad];  // U^T
@@ -163,14 +171,26 @@ __global__ __launch_bounds__(256) void lora_wgrad_kernel(
     const int p = sorted[s];
     const uint16_t *row = (U == LS_X_GATHER || U == LS_WX_GATHER) ? src + int64_t(p / topk) * ld
                                                                   : src + int64_t(s) * ld;
-    u32x4 q = *reinterpret_cast<const u32x4 *>(row + ncol);
+    u32x4 q;
     if (U == LS_GU_ACT) {
-      const u32x4 uu = *reinterpret_cast<const u32x4 *>(row + I + ncol);
+      // pair s of expert e: row (s - s0) % 256 of m-tile tile_offsets[e] + (s - s0) / 256
+      // of the blocked g|u; columns ncol .. + 7 are two chunks (g[4], u[4])
+      const int rs = s - s0, mt = tile_offsets[e] + rs / kBM;
+      const int npb = (I + kGuBlockPairs - 1) / kGuBlockPairs;
+      const int pb = ncol / kGuBlockPairs, cc = ncol % kGuBlockPairs;
+      const u32x4 c0 = *reinterpret_cast<const u32x4 *>(src + gu_chunk(mt, pb, npb, rs % kBM, cc) * 8);
+      const u32x4 c1 =
+          *reinterpret_cast<const u32x4 *>(src + gu_chunk(mt, pb, npb, rs % kBM, cc + 4) * 8);
+      const u32x4 gq{c0[0], c0[1], c1[0], c1[1]};
+      const u32x4 uu{c0[2], c0[3], c1[2], c1[3]};
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        q[t] = pack_bf16x2(silu_f(bf16_lo(q[t])) * bf16_lo(uu[t]),
-                           silu_f(bf16_hi(q[t])) * bf16_hi(uu[t]));
-    } else if (U == LS_WX_GATHER) {
+        q[t] = pack_bf16x2(silu_f(bf16_lo(gq[t])) * bf16_lo(uu[t]),
+                           silu_f(bf16_hi(gq[t])) * bf16_hi(uu[t]));
+    } else {
+      q = *reinterpret_cast<const u32x4 *>(row + ncol);
+    }
+    if (U == LS_WX_GATHER) {
       const float wp = topk_w[p];
 #pragma unroll
       for (int t = 0; t < 4; ++t) q[t] = pack_bf16x2(wp * bf16_lo(q[t]), wp * bf16_hi(q[t]));
@@ -263,14 +283,15 @@ hipError_t launch_lora_project_mfma(int src_mode, const uint16_t *src, int64_t l
 }
 
 hipError_t launch_lora_wgrad(int u_mode, const uint16_t *src, int64_t ld, int N, int I,
-                             const int32_t *sorted, const int32_t *offsets, int topk,
+                             const int32_t *sorted, const int32_t *offsets,
+                             const int32_t *tile_offsets, int topk,
                              const float *topk_w, int64_t E, const float *V, bool v_weighted,
                              int r, float s, bool out_trans, float *out, hipStream_t st) {
   if (E == 0 || N == 0) return hipSuccess;
   const dim3 grid{uint32_t((N + kWgCols - 1) / kWgCols), uint32_t(E)};
 #define E4B_LW(UM)                                                                             \
   hipLaunchKernelGGL((lora_wgrad_kernel<UM>), grid, dim3(256), 0, st, src, ld, N, I, sorted,   \
-                     offsets, topk, topk_w, V, v_weighted, r, s, out_trans, out)
+                     offsets, tile_offsets, topk, topk_w, V, v_weighted, r, s, out_trans, out)
   switch (u_mode) {
     case LS_X_GATHER: E4B_LW(LS_X_GATHER); break;
     case LS_ROWS: E4B_LW(LS_ROWS); break;

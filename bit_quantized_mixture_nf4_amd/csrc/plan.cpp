@@ -101,6 +101,10 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   p->n_tiles_gu = (I + bn_gu - 1) / bn_gu;
   p->n_tiles_h = (H + kBNWide - 1) / kBNWide;
   p->n_tiles_i = (I + kBNNarrow - 1) / kBNNarrow;
+  // saved / recomputed g|u: gated, blocked per (m-tile, 128 pairs); ungated h [P, I]
+  p->gu_bytes = p->gated ? size_t(p->m_tiles_bound) * size_t((I + kGuBlockPairs - 1) / kGuBlockPairs) *
+                               size_t(kGuBlockChunks) * 16
+                         : size_t(P) * size_t(I) * 2;
   p->n_tiles_h_gud = (H + kBNWide - 1) / kBNWide;
   p->nbits_e = bits_for(E);
 
@@ -134,7 +138,7 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   // dgrad region (overlaps the forward region: the two calls never run at once
   // on one workspace)
   off = base;
-  p->off_gu = take(size_t(P) * p->gu_cols * 2);
+  p->off_gu = take(p->gu_bytes);
   p->off_dgu = take(size_t(P) * p->gu_cols * 2);
   p->off_partial = take(size_t(P) * p->n_tiles_i * 4);
   p->off_gx = take(size_t(P) * H * 2);
@@ -154,7 +158,7 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   p->off_pj_bdn = take(size_t(E) * kLoraK * H * 2);
   p->off_pj_bgu = take(size_t(E) * kLoraK * 2 * I * 2);
   p->lora_ws_bytes = off;
-  p->sv_tile_map = align_up(size_t(P) * p->gu_cols * 2, 256);
+  p->sv_tile_map = align_up(p->gu_bytes, 256);
   p->sv_tile_offsets = p->sv_tile_map + size_t(p->m_tiles_bound) * 16;
   p->sv_offsets = p->sv_tile_offsets + size_t(E + 1) * 4;
   p->sv_sorted = p->sv_offsets + size_t(E + 1) * 4;

@@ -13,6 +13,10 @@ namespace e4b {
 
 // Tile shape shared by every grouped GEMM of the forward and dgrad.
 constexpr int kBM = 256;   // rows (routed pairs) per tile
+// the saved / recomputed g|u of a gated layer is blocked per (m-tile, 128
+// pairs): 256 x 128 pairs of g and u, 128 KB (layout in kernels.h, gu_chunk)
+constexpr int kGuBlockPairs = 128;
+constexpr int kGuBlockChunks = kBM * kGuBlockPairs / 4;  // 16-byte chunks per block
 // output columns per tile: 256 (8 waves, one workgroup per CU) for both
 // gate_up GEMMs and the down forward, 128 (4 waves, two workgroups per CU) for
 // the down dgrad, each the faster shape for that GEMM
@@ -34,6 +38,7 @@ struct MoePlan {
   int32_t codebook;
   int32_t gated;    // 1: gate_up holds gate | up (2I rows); 0: a plain up projection (I rows)
   int64_t gu_cols;  // rows of the first stack: 2I or I
+  size_t gu_bytes;  // the saved / recomputed g|u (gated: blocked) or h
   int64_t nchunks;        // permutation chunks of kPermChunk pairs
   int64_t m_tiles_bound;  // upper bound of sum_e ceil(count_e / kBM)
   int64_t n_tiles_gu;     // gate_up forward tiles: kBNWide/2 gate-up pairs per tile

@@ -244,8 +244,13 @@ e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t top_k,
  * top_k) (one size serves both); 0 when the arguments are invalid. */
 size_t e4b_moe_workspace_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k);
 
-/* Bytes of the `saved` buffer: bf16 [T*top_k, 2I] ([T*top_k, I] ungated) followed by the routing
- * permutation (int32 arrays over experts, m-tiles and pairs); 0 when invalid. */
+/* Bytes of the `saved` buffer (its contents are internal to the library): the
+ * bf16 gate and up projections of every routed pair (gated: in blocks of 256
+ * sorted pairs x 128 intermediate columns, g and u side by side, one block per
+ * m-tile and column block; ungated: h as [T*top_k, I]) followed by the routing
+ * permutation (int32 arrays over experts, m-tiles and pairs); 0 when invalid.
+ * The forward never writes the padding of the blocks (rows past an expert's
+ * pairs, blocks of m-tiles the routing does not produce) and nothing reads it. */
 size_t e4b_moe_saved_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k);
 
 /* Per-expert LoRA adapters over the frozen base (fp32 device buffers).

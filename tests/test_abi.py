@@ -129,11 +129,13 @@ def test_workspace_and_saved_sizes(E, H, I, k, T):
     lib = e4b.load()
     P = T * k
     saved = lib.e4b_moe_saved_bytes(ctypes.byref(L), T, k)
-    # bf16 g|u of every pair, then the permutation: an int4 per m-tile (at most
-    # P / 256 + min(E, P) tiles of 256 pairs), offsets and tile offsets over
-    # E + 1 experts, sorted pairs and pair positions
+    # bf16 g|u in blocks of 256 rows x 128 pairs (g and u) per m-tile (at most
+    # P / 256 + min(E, P) tiles of 256 pairs), then the permutation: an int4 per
+    # m-tile, offsets and tile offsets over E + 1 experts, sorted pairs and
+    # pair positions
     m_tiles = (P + min(E, P) * 255) // 256
-    assert saved == P * 2 * I * 2 + 16 * m_tiles + 8 * (E + 1) + 8 * P
+    gu = m_tiles * -(-I // 128) * 256 * 128 * 2 * 2
+    assert saved == -(-gu // 256) * 256 + 16 * m_tiles + 8 * (E + 1) + 8 * P
     ws = lib.e4b_moe_workspace_bytes(ctypes.byref(L), T, k)
     # at least the dgrad intermediates: g|u, dGU, grad_x rows
     assert ws >= P * (2 * I * 2 * 2 + H * 2)
