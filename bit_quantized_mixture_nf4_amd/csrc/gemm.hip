@@ -527,9 +527,10 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
     }
   } else {  // EPI_DSWIGLU
     float *red = reinterpret_cast<float *>(sA[0]);  // [kGemmWavesN][kBM] partial row sums
-    // The saved g|u of the lane's 2 x 4 x 4 column runs are fetched in eight
-    // batches (row half i, column group j), one batch ahead of its use, with
-    // rows and columns clamped into range (out-of-range results are not
+    // The saved g|u of the lane's 2 x 4 x 4 column runs (one 16-byte chunk of
+    // the tile's g|u block each) are fetched in eight batches (row half i,
+    // column group j), one batch ahead of its use, with rows and columns
+    // clamped to chunks the forward wrote (out-of-range results are not
     // stored), so the loads of a batch overlap the arithmetic of the previous.
     static_assert(EPI != EPI_DSWIGLU || kBN == kGuBlockPairs, "one g|u block per tile");
     int64_t grow[2];
@@ -543,7 +544,7 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
 #pragma unroll
     for (int i = 0; i < 2; ++i) wr[i] = g.topk_w[g.sorted_pair[grow[i]]];
     u32x2 gg[2][4], uu[2][4];
-    // pairs of this block the forward wrote: [0, cmax]
+    // the forward wrote the chunks of pairs 0, 4, ..., cmax of this block
     const int cmax = min(kBN, g.N - nt * kBN) - 4;
     auto fetch = [&](int b, int slot) {
       const int i = b >> 2, j = b & 3;
