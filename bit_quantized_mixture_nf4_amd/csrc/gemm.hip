@@ -398,7 +398,39 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   // so each lane holds runs of 4 consecutive columns of one row.
   const int lrow = wm * 64 + (lane & 31);
   const int lcol = wn * 128 + 4 * (lane >> 5);
-  if (EPI == EPI_STORE) {
+  if (EPI == EPI_STORE && WN == 2) {
+    // Through LDS, so that the stores are whole row segments: rows 0..127 of
+    // the tile go to the A stages, rows 128..255 to the B stages (bf16, row
+    // stride kOut), then every thread writes 16 contiguous bytes, a wave two
+    // 512-byte row segments. The K loop's last barrier has retired every read
+    // of both stages.
+    constexpr int kOut = kBN + 8;
+    static_assert(WN != 2 || (128 * kOut <= kStages * kBM * kLds && 128 * kOut <= kStages * kBN * kLds),
+                  "half a tile fits each stage pair");
+    uint16_t *half = wm < 2 ? sA[0] : sB[0];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = (lrow + i * 32) & 127;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16 &a = acc[i][j];
+          *reinterpret_cast<u32x2 *>(half + r * kOut + lcol + j * 32 + 8 * q) =
+              u32x2{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
+        }
+    }
+    __syncthreads();
+    const int cc = (tid & 31) * 8, col = nt * kBN + cc;
+#pragma unroll 4
+    for (int pass = 0; pass < kBM / 16; ++pass) {
+      const int row = pass * 16 + (tid >> 5);
+      const uint16_t *src = (row < 128 ? sA[0] : sB[0]) + (row & 127) * kOut + cc;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(src);
+      if (row < valid_rows && col < g.N)
+        *reinterpret_cast<u32x4 *>(g.C + int64_t(seg + row0 + row) * g.ldc + col) = v;
+    }
+  } else if (EPI == EPI_STORE) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = lrow + i * 32;
