@@ -250,22 +250,39 @@ __global__ __launch_bounds__(512, 1) void mx_gemm_kernel(MxGemmArgs g) {
   const int lrow = wm * 64 + (lane & 31);
   const int lcol = wn * 128 + 4 * (lane >> 5);
   if (EPI == MX_STORE) {
+    // through LDS in two halves of 128 rows (the activation stages, bf16, row
+    // stride kOut), so that every store is 16 contiguous bytes and a wave
+    // writes two 512-byte row segments; the K loop's last barrier has retired
+    // every read of the stages
+    constexpr int kOut = kBN + 8;
+    static_assert(128 * kOut * 2 <= int(sizeof(sA)), "half a tile fits the activation stages");
+    uint16_t *otile = reinterpret_cast<uint16_t *>(&sA[0][0]);
+    const int cc = (tid & 31) * 8, col = nt * kBN + cc;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = lrow + i * 32;
-      if (row < valid_rows) {
-        uint16_t *crow = g.C + int64_t(seg + row0 + row) * g.ldc;
+    for (int hf = 0; hf < 2; ++hf) {
+      if ((wm >> 1) == hf) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int i = 0; i < 2; ++i) {
+          const int r = (lrow + i * 32) & 127;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int col = nt * kBN + lcol + j * 32 + 8 * q;
-            const f32x16 &a = acc[i][j];
-            if (col < g.N)
-              *reinterpret_cast<u32x2 *>(crow + col) =
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x16 &a = acc[i][j];
+              *reinterpret_cast<u32x2 *>(otile + r * kOut + lcol + j * 32 + 8 * q) =
                   u32x2{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])};
-          }
+            }
+        }
       }
+      __syncthreads();
+#pragma unroll 4
+      for (int pass = 0; pass < 128 / 16; ++pass) {
+        const int r = pass * 16 + (tid >> 5), row = hf * 128 + r;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(otile + r * kOut + cc);
+        if (row < valid_rows && col < g.N)
+          *reinterpret_cast<u32x4 *>(g.C + int64_t(seg + row0 + row) * g.ldc + col) = v;
+      }
+      __syncthreads();
     }
   } else {
     // a = bf16(silu(g) * u) converted to MXFP8 in place: for (i, jj) a lane
