@@ -558,7 +558,15 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
       g.partial[grow * g.n_tiles + nt] = sum;
     }
   } else {  // EPI_DSWIGLU
-    float *red = reinterpret_cast<float *>(sA[0]);  // [kGemmWavesN][kBM] partial row sums
+    float *red = reinterpret_cast<float *>(sB[0]);  // [kGemmWavesN][kBM] partial row sums
+    static_assert(EPI != EPI_DSWIGLU || kGemmWavesN * kBM * 2 <= kStages * kBN * kLds,
+                  "the partial sums fit the B stage");
+    // dGU goes out through LDS in four rounds (row half i, column half jh of
+    // the tile): the four waves' 32 rows each x 64 pairs of dg then du (bf16,
+    // row stride kSt) in the A stage, then 128-byte row segments per store
+    constexpr int kSt = 128 + 8;
+    static_assert(EPI != EPI_DSWIGLU || 128 * kSt <= kStages * kBM * kLds, "a round fits the A stage");
+    uint16_t *stg = sA[0];
     // The saved g|u of the lane's 2 x 4 x 4 column runs (one 16-byte chunk of
     // the tile's g|u block each) are fetched in eight batches (row half i,
     // column group j), one batch ahead of its use, with rows and columns
@@ -596,7 +604,7 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
       if (b + 1 < 8) fetch(b + 1, (b + 1) & 1);
       const int i = b >> 2, j = b & 3, slot = b & 1;
       const bool row_ok = lrow + i * 32 < valid_rows;
-      uint16_t *crow = g.C + grow[i] * g.ldc;
+      uint16_t *srow = stg + (wm * 32 + (lane & 31)) * kSt;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = nt * kBN + lcol + j * 32 + 8 * q;
@@ -614,13 +622,26 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
           dg[t] = ga * uv[t] * s * (1.0f + gv[t] * (1.0f - s));
           du[t] = ga * silu;
         }
-        if (row_ok && n < g.N) {
-          part[i] += pq;
-          *reinterpret_cast<u32x2 *>(crow + n) =
-              u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-          *reinterpret_cast<u32x2 *>(crow + g.I + n) =
-              u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+        if (row_ok && n < g.N) part[i] += pq;
+        const int pr_ = (j & 1) * 32 + 8 * q + 4 * (lane >> 5);  // pair within the round
+        *reinterpret_cast<u32x2 *>(srow + pr_) = u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+        *reinterpret_cast<u32x2 *>(srow + 64 + pr_) =
+            u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+      }
+      if (j & 1) {
+        // round (i, j / 2) staged: 128 rows x 16 chunks of 16 bytes
+        __syncthreads();
+        const int jh = j >> 1;
+#pragma unroll
+        for (int pass = 0; pass < 128 * 16 / kThreads; ++pass) {
+          const int id = pass * kThreads + tid, R = id >> 4, c = id & 15;
+          const int trow = (R >> 5) * 64 + i * 32 + (R & 31);
+          const int n = nt * kBN + jh * 64 + (c & 7) * 8;
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + R * kSt + c * 8);
+          if (trow < valid_rows && n < g.N)
+            *reinterpret_cast<u32x4 *>(g.C + (seg + row0 + trow) * int64_t(g.ldc) + (c < 8 ? 0 : g.I) + n) = v;
         }
+        __syncthreads();
       }
     }
 #pragma unroll
