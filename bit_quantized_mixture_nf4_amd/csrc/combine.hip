@@ -39,16 +39,25 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t *__res
   __syncthreads();
   for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(O + int64_t(pos[j]) * H + h);
+    // up to 8 rows in flight before the first sum; the sums keep slot order
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      u32x4 v[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (WEIGHTED) {
-          acc[2 * q] += w[j] * bf16_lo(v[q]);
-          acc[2 * q + 1] += w[j] * bf16_hi(v[q]);
-        } else {
-          acc[2 * q] += bf16_lo(v[q]);
-          acc[2 * q + 1] += bf16_hi(v[q]);
+      for (int jj = 0; jj < 8; ++jj)
+        if (j0 + jj < k) v[jj] = *reinterpret_cast<const u32x4 *>(O + int64_t(pos[j0 + jj]) * H + h);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (j0 + jj >= k) break;
+        const int j = j0 + jj;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (WEIGHTED) {
+            acc[2 * q] += w[j] * bf16_lo(v[jj][q]);
+            acc[2 * q + 1] += w[j] * bf16_hi(v[jj][q]);
+          } else {
+            acc[2 * q] += bf16_lo(v[jj][q]);
+            acc[2 * q + 1] += bf16_hi(v[jj][q]);
+          }
         }
       }
     }
