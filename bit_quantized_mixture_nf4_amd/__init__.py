@@ -2,10 +2,11 @@
 
 Thin Python binding over ``libe4b.so`` (C ABI in ``include/e4b.h``). PyTorch is
 used only for device memory and the current HIP stream: every computation runs
-in the library's HIP kernels. The raw entry points are available under their C
-names in :mod:`bit_quantized_mixture_nf4_amd.raw` (``e4b_quantize_nf4``,
-``e4b_dequantize_nf4``, ``e4b_moe_forward``, ``e4b_moe_dgrad``, ...); the
-functions below marshal torch tensors into them.
+in the library's HIP kernels. The raw entry points are the ctypes functions of
+``load()`` under their C names (``e4b_quantize_nf4``, ``e4b_dequantize_nf4``,
+``e4b_moe_forward``, ``e4b_moe_dgrad``, ...); the functions below check torch
+tensors (dtype, device, shape, contiguity, buffer sizes) and marshal them into
+those entry points.
 
 Layout (the fused-expert storage of the experts4bit-qlora 0.1.0 sdist,
 ``Experts4bit``): gate_up ``[E, 2I, H]`` (gate rows first), down
@@ -20,7 +21,16 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import E4bLayer, E4bLora, E4bStack, E4bError, check, load  # noqa: F401
+from ._lib import (  # noqa: F401
+    E4bError,
+    E4bKernelEvents,
+    E4bLayer,
+    E4bLora,
+    E4bPermLayout,
+    E4bStack,
+    check,
+    load,
+)
 
 CODEBOOKS = {"nf4": _lib.E4B_CB_NF4, "fp4": _lib.E4B_CB_FP4, "bf16": _lib.E4B_CB_BF16,
              "mxfp4": _lib.E4B_CB_MXFP4}
@@ -42,6 +52,8 @@ __all__ = [
     "LayerPrefetcher",
     "workspace_bytes",
     "saved_bytes",
+    "perm_layout",
+    "check_expert_ids",
     "E4bError",
 ]
 
@@ -67,6 +79,31 @@ def _need(t, name, dtype, device=None, shape=None):
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _need_buffer(t, name, nbytes, device):
+    """A contiguous device byte buffer of at least ``nbytes`` bytes."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, the call needs {nbytes}")
+
+
+def check_expert_ids(topk_idx, E):
+    """Raise ValueError unless every id of ``topk_idx`` lies in [0, E).
+
+    The kernels never index out of bounds with a bad id (they read it as
+    expert 0), but the result is then meaningless; this check costs one
+    device-to-host synchronization, so the calls below run it only when asked
+    (``check_ids=True``).
+    """
+    if topk_idx.numel() and bool(((topk_idx < 0) | (topk_idx >= E)).any()):
+        raise ValueError(f"topk_idx holds an expert id outside [0, {E})")
 
 
 @dataclass
@@ -191,20 +228,33 @@ def _workspace(layer, T, top_k, ws):
     need = workspace_bytes(layer, T, top_k)
     if ws is None:
         return torch.empty(max(need, 256), dtype=torch.uint8, device=layer.device)
+    _need_buffer(ws, "workspace", need, layer.device)
     return ws
 
 
-def moe_forward(layer, x, top_k, logits=None, topk_idx=None, topk_w=None, save=False,
-                path="auto", workspace=None, out=None):
-    """Routed SwiGLU expert forward.
+def _nbytes(t):
+    return t.numel() * t.element_size()
 
-    Either ``logits`` (float32 [T, E]: routing computed on the device) or
-    ``topk_idx`` (int32 [T, k]) and ``topk_w`` (float32 [T, k]) are given.
-    Returns ``(y bf16 [T, H], topk_idx, topk_w, saved or None)``.
-    """
+
+def perm_layout(layer, T, top_k):
+    """Byte offsets of the routing permutation that a grouped forward without
+    saved state leaves in its workspace (``e4b_moe_perm_layout``): a dict with
+    counts, offsets, tile_offsets, sorted_pair, pos_of_pair, tile_map and
+    m_tiles_bound."""
+    c, out = layer.as_c(), E4bPermLayout()
+    check("e4b_moe_perm_layout", load().e4b_moe_perm_layout(ctypes.byref(c), T, top_k, ctypes.byref(out)))
+    return {name: int(getattr(out, name)) for name, _ in E4bPermLayout._fields_}
+
+
+def _check_x(x, name, layer, T=None):
+    _need(x, name, torch.bfloat16, layer.device)
+    if x.dim() != 2 or x.shape[1] != layer.H or (T is not None and x.shape[0] != T):
+        want = f"({'T' if T is None else T}, {layer.H})"
+        raise ValueError(f"{name} must have shape {want}, got {tuple(x.shape)}")
+
+
+def _routing(layer, T, top_k, logits, topk_idx, topk_w, check_ids):
     dev = layer.device
-    _need(x, "x", torch.bfloat16, dev)
-    T = x.shape[0]
     if logits is not None:
         _need(logits, "logits", torch.float32, dev, (T, layer.E))
         topk_idx = torch.empty(T, top_k, dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
@@ -213,37 +263,77 @@ def moe_forward(layer, x, top_k, logits=None, topk_idx=None, topk_w=None, save=F
         raise ValueError("give logits, or both topk_idx and topk_w")
     _need(topk_idx, "topk_idx", torch.int32, dev, (T, top_k))
     _need(topk_w, "topk_w", torch.float32, dev, (T, top_k))
-    y = torch.empty(T, layer.H, dtype=torch.bfloat16, device=dev) if out is None else out
-    saved = None
-    if save:
-        # zero-filled: the padding of the blocked g|u layout is never written
-        saved = torch.zeros(max(saved_bytes(layer, T, top_k), 16) // 2, dtype=torch.bfloat16, device=dev)
+    if logits is None and check_ids:
+        check_expert_ids(topk_idx, layer.E)
+    return topk_idx, topk_w
+
+
+def _saved_buffer(layer, T, top_k, save):
+    # never cleared: the forward writes every byte the dgrad reads
+    return torch.empty(max(saved_bytes(layer, T, top_k), 16), dtype=torch.uint8,
+                       device=layer.device) if save else None
+
+
+def moe_forward(layer, x, top_k, logits=None, topk_idx=None, topk_w=None, save=False,
+                path="auto", workspace=None, out=None, check_ids=False):
+    """Routed SwiGLU expert forward.
+
+    Either ``logits`` (float32 [T, E]: routing computed on the device) or
+    ``topk_idx`` (int32 [T, k]) and ``topk_w`` (float32 [T, k]) are given.
+    ``check_ids`` checks given ids against [0, E) first (one host sync).
+    Returns ``(y bf16 [T, H], topk_idx, topk_w, saved or None)``.
+    """
+    dev = layer.device
+    _check_x(x, "x", layer)
+    T = x.shape[0]
+    if path not in PATHS:
+        raise ValueError(f"path must be one of {sorted(PATHS)}")
+    topk_idx, topk_w = _routing(layer, T, top_k, logits, topk_idx, topk_w, check_ids)
+    if out is None:
+        y = torch.empty(T, layer.H, dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, dev, (T, layer.H))
+        y = out
+    saved = _saved_buffer(layer, T, top_k, save)
     ws = _workspace(layer, T, top_k, workspace)
     c = layer.as_c()
     code = load().e4b_moe_forward(
         ctypes.byref(c), T, top_k, _vp(x), _vp(logits), _vp(topk_idx), _vp(topk_w), _vp(y),
-        _vp(saved), _vp(ws), ws.numel(), PATHS[path], _stream(x),
+        _vp(saved), _vp(ws), _nbytes(ws), PATHS[path], _stream(x),
     )
     check("e4b_moe_forward", code)
     return y, topk_idx, topk_w, saved
 
 
-def moe_dgrad(layer, topk_idx, topk_w, grad_y, x=None, saved=None, grad_w=True, workspace=None):
+def _check_saved(layer, T, top_k, saved):
+    if saved is not None:
+        _need_buffer(saved, "saved", saved_bytes(layer, T, top_k), layer.device)
+
+
+def moe_dgrad(layer, topk_idx, topk_w, grad_y, x=None, saved=None, grad_w=True, workspace=None,
+              check_ids=False):
     """Frozen-base input gradient. Returns ``(grad_x bf16 [T, H], grad_topk_w fp32 [T, k] or None)``."""
     dev = layer.device
-    _need(grad_y, "grad_y", torch.bfloat16, dev)
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [T, k]")
     T, top_k = topk_idx.shape
+    _check_x(grad_y, "grad_y", layer, T)
     _need(topk_idx, "topk_idx", torch.int32, dev, (T, top_k))
     _need(topk_w, "topk_w", torch.float32, dev, (T, top_k))
     if x is not None:
-        _need(x, "x", torch.bfloat16, dev, (T, layer.H))
+        _check_x(x, "x", layer, T)
+    if x is None and saved is None:
+        raise ValueError("give x (recompute) or the saved state of the forward")
+    _check_saved(layer, T, top_k, saved)
+    if check_ids:
+        check_expert_ids(topk_idx, layer.E)
     gx = torch.empty(T, layer.H, dtype=torch.bfloat16, device=dev)
     gw = torch.empty(T, top_k, dtype=torch.float32, device=dev) if grad_w else None
     ws = _workspace(layer, T, top_k, workspace)
     c = layer.as_c()
     code = load().e4b_moe_dgrad(
         ctypes.byref(c), T, top_k, _vp(topk_idx), _vp(topk_w), _vp(x), _vp(saved), _vp(grad_y),
-        _vp(gx), _vp(gw), _vp(ws), ws.numel(), _stream(grad_y),
+        _vp(gx), _vp(gw), _vp(ws), _nbytes(ws), _stream(grad_y),
     )
     check("e4b_moe_dgrad", code)
     return gx, gw
@@ -281,58 +371,54 @@ def lora_workspace_bytes(layer, T, top_k):
 
 
 def _lora_workspace(layer, T, top_k, ws):
+    need = lora_workspace_bytes(layer, T, top_k)
     if ws is None:
-        return torch.empty(max(lora_workspace_bytes(layer, T, top_k), 256), dtype=torch.uint8,
-                           device=layer.device)
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=layer.device)
+    _need_buffer(ws, "workspace", need, layer.device)
     return ws
 
 
 def moe_lora_forward(layer, lora, x, top_k, logits=None, topk_idx=None, topk_w=None, save=False,
-                     workspace=None):
+                     workspace=None, check_ids=False):
     """Forward with per-expert LoRA adapters (grouped path).
 
     Returns ``(y bf16 [T, H], topk_idx, topk_w, saved or None)``.
     """
     dev = layer.device
     lora.check(layer)
-    _need(x, "x", torch.bfloat16, dev)
+    _check_x(x, "x", layer)
     T = x.shape[0]
-    if logits is not None:
-        _need(logits, "logits", torch.float32, dev, (T, layer.E))
-        topk_idx = torch.empty(T, top_k, dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
-        topk_w = torch.empty(T, top_k, dtype=torch.float32, device=dev) if topk_w is None else topk_w
-    if topk_idx is None or topk_w is None:
-        raise ValueError("give logits, or both topk_idx and topk_w")
-    _need(topk_idx, "topk_idx", torch.int32, dev, (T, top_k))
-    _need(topk_w, "topk_w", torch.float32, dev, (T, top_k))
+    topk_idx, topk_w = _routing(layer, T, top_k, logits, topk_idx, topk_w, check_ids)
     y = torch.empty(T, layer.H, dtype=torch.bfloat16, device=dev)
-    saved = None
-    if save:
-        # zero-filled: the padding of the blocked g|u layout is never written
-        saved = torch.zeros(max(saved_bytes(layer, T, top_k), 16) // 2, dtype=torch.bfloat16, device=dev)
+    saved = _saved_buffer(layer, T, top_k, save)
     ws = _lora_workspace(layer, T, top_k, workspace)
     c, lc = layer.as_c(), lora.as_c()
     code = load().e4b_moe_lora_forward(
         ctypes.byref(c), ctypes.byref(lc), T, top_k, _vp(x), _vp(logits), _vp(topk_idx),
-        _vp(topk_w), _vp(y), _vp(saved), _vp(ws), ws.numel(), _stream(x),
+        _vp(topk_w), _vp(y), _vp(saved), _vp(ws), _nbytes(ws), _stream(x),
     )
     check("e4b_moe_lora_forward", code)
     return y, topk_idx, topk_w, saved
 
 
 def moe_lora_backward(layer, lora, topk_idx, topk_w, x, grad_y, saved=None, grad_w=True,
-                      workspace=None):
+                      workspace=None, check_ids=False):
     """Input gradient, routing-weight gradient and adapter gradients.
 
     Returns ``(grad_x bf16 [T, H], grad_topk_w fp32 or None, (dA_gu, dB_gu, dA_dn, dB_dn))``.
     """
     dev = layer.device
     lora.check(layer)
-    _need(grad_y, "grad_y", torch.bfloat16, dev)
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [T, k]")
     T, top_k = topk_idx.shape
+    _check_x(grad_y, "grad_y", layer, T)
     _need(topk_idx, "topk_idx", torch.int32, dev, (T, top_k))
     _need(topk_w, "topk_w", torch.float32, dev, (T, top_k))
-    _need(x, "x", torch.bfloat16, dev, (T, layer.H))
+    _check_x(x, "x", layer, T)
+    _check_saved(layer, T, top_k, saved)
+    if check_ids:
+        check_expert_ids(topk_idx, layer.E)
     gx = torch.empty(T, layer.H, dtype=torch.bfloat16, device=dev)
     gw = torch.empty(T, top_k, dtype=torch.float32, device=dev) if grad_w else None
     grads = tuple(torch.empty_like(t) for t in (lora.A_gu, lora.B_gu, lora.A_dn, lora.B_dn))
@@ -340,7 +426,7 @@ def moe_lora_backward(layer, lora, topk_idx, topk_w, x, grad_y, saved=None, grad
     c, lc = layer.as_c(), lora.as_c()
     code = load().e4b_moe_lora_backward(
         ctypes.byref(c), ctypes.byref(lc), T, top_k, _vp(topk_idx), _vp(topk_w), _vp(x),
-        _vp(saved), _vp(grad_y), _vp(gx), _vp(gw), *(_vp(g) for g in grads), _vp(ws), ws.numel(),
+        _vp(saved), _vp(grad_y), _vp(gx), _vp(gw), *(_vp(g) for g in grads), _vp(ws), _nbytes(ws),
         _stream(grad_y),
     )
     check("e4b_moe_lora_backward", code)

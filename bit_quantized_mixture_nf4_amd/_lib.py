@@ -41,10 +41,12 @@ EXPORTS = (
     "e4b_moe_lora_workspace_bytes",
     "e4b_stack_copy_async",
     "e4b_status_string",
-    "e4b_set_kernel_timer",
+    "e4b_moe_forward_timed",
+    "e4b_moe_dgrad_timed",
+    "e4b_moe_perm_layout",
 )
 
-# e4b_kernel ids for e4b_set_kernel_timer
+# e4b_kernel ids (the slots of e4b_kernel_events)
 KERNELS = {
     "gate_up_fwd": 0,
     "down_fwd": 1,
@@ -52,7 +54,13 @@ KERNELS = {
     "gate_up_dgrad": 3,
     "decode_gate_up": 4,
     "decode_down": 5,
+    "route": 6,
+    "permute": 7,
+    "combine": 8,
+    "combine_dgrad": 9,
+    "decode_prep": 10,
 }
+E4B_K_COUNT = 11
 
 
 class E4bStack(ctypes.Structure):
@@ -80,6 +88,24 @@ class E4bLora(ctypes.Structure):
         ("B_dn", ctypes.c_void_p),
         ("r", ctypes.c_int32),
         ("alpha", ctypes.c_float),
+    ]
+
+
+class E4bKernelEvents(ctypes.Structure):
+    """e4b_kernel_events: start / stop hipEvent_t per kernel id (NULL: not timed)."""
+
+    _fields_ = [("start", ctypes.c_void_p * E4B_K_COUNT), ("stop", ctypes.c_void_p * E4B_K_COUNT)]
+
+
+class E4bPermLayout(ctypes.Structure):
+    _fields_ = [
+        ("counts", ctypes.c_size_t),
+        ("offsets", ctypes.c_size_t),
+        ("tile_offsets", ctypes.c_size_t),
+        ("sorted_pair", ctypes.c_size_t),
+        ("pos_of_pair", ctypes.c_size_t),
+        ("tile_map", ctypes.c_size_t),
+        ("m_tiles_bound", ctypes.c_int64),
     ]
 
 
@@ -113,7 +139,11 @@ def load():
         "e4b_moe_lora_workspace_bytes": (sz, [lay, i64, i32]),
         "e4b_stack_copy_async": (i32, [st, st, vp]),
         "e4b_status_string": (ctypes.c_char_p, [i32]),
-        "e4b_set_kernel_timer": (i32, [i32, vp, vp, i32]),
+        "e4b_moe_forward_timed": (
+            i32, [lay, i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, i32, vp, ctypes.POINTER(E4bKernelEvents)]),
+        "e4b_moe_dgrad_timed": (
+            i32, [lay, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(E4bKernelEvents)]),
+        "e4b_moe_perm_layout": (i32, [lay, i64, i32, ctypes.POINTER(E4bPermLayout)]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)

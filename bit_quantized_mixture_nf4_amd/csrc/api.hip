@@ -19,7 +19,7 @@ namespace e4b {
 // prep kernel routes the tokens itself and writes topk_idx / topk_w.
 hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
                                  const float *logits, int32_t *idx, float *w, uint16_t *y,
-                                 char *ws, hipStream_t s);
+                                 char *ws, hipStream_t s, const e4b_kernel_events *ev);
 
 namespace {
 
@@ -49,7 +49,8 @@ GemmArgs base_args(const MoePlan &p, const e4b_stack &st, const PermView &v) {
 // gate_up projection of every routed pair: writes a = silu(g)*u (if a_out) and
 // the bf16 g|u (if gu_out).
 hipError_t run_gate_up(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
-                       uint16_t *a_out, uint16_t *gu_out, const PermView &v, hipStream_t s) {
+                       uint16_t *a_out, uint16_t *gu_out, const PermView &v, hipStream_t s,
+                       const e4b_kernel_events *ev) {
   GemmArgs a = base_args(p, L->gate_up, v);
   a.A = x;
   a.lda = int32_t(p.H);
@@ -60,7 +61,7 @@ hipError_t run_gate_up(const MoePlan &p, const e4b_moe_layer *L, const uint16_t 
   a.C = a_out;
   a.ldc = int32_t(p.I);
   a.GU = gu_out;
-  return launch_grouped_gemm(GEMM_GATE_UP_FWD, a, s);
+  return launch_grouped_gemm(GEMM_GATE_UP_FWD, a, s, ev);
 }
 
 }  // namespace
@@ -71,11 +72,11 @@ hipError_t run_gate_up(const MoePlan &p, const e4b_moe_layer *L, const uint16_t 
     if ((expr) != hipSuccess) return E4B_ERR_HIP;       \
   } while (0)
 
-extern "C" e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t top_k,
-                                      const void *x_bf16, const float *router_logits,
-                                      int32_t *topk_idx, float *topk_w, void *y_bf16,
-                                      void *saved, void *ws, size_t ws_bytes, int32_t path,
-                                      hipStream_t stream) {
+extern "C" e4b_status e4b_moe_forward_timed(const e4b_moe_layer *L, int64_t T, int32_t top_k,
+                                            const void *x_bf16, const float *router_logits,
+                                            int32_t *topk_idx, float *topk_w, void *y_bf16,
+                                            void *saved, void *ws, size_t ws_bytes, int32_t path,
+                                            hipStream_t stream, const e4b_kernel_events *ev) {
   MoePlan p;
   e4b_status st = plan_moe(L, T, top_k, &p);
   if (st != E4B_OK) return st;
@@ -88,14 +89,14 @@ extern "C" e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t
   uint16_t *y = static_cast<uint16_t *>(y_bf16);
 
   if (use_decode) {
-    E4B_TRY(launch_decode_forward(p, L, x, router_logits, topk_idx, topk_w, y, w, stream));
+    E4B_TRY(launch_decode_forward(p, L, x, router_logits, topk_idx, topk_w, y, w, stream, ev));
     return E4B_OK;
   }
   if (router_logits)
-    E4B_TRY(launch_route(router_logits, T, int(p.E), top_k, topk_idx, topk_w, stream));
+    E4B_TRY(launch_route(router_logits, T, int(p.E), top_k, topk_idx, topk_w, stream, ev));
   if (path == E4B_PATH_MX8) {
     const PermView v = perm_in_workspace(p, w);
-    E4B_TRY(launch_permute(p, topk_idx, w, v, stream));
+    E4B_TRY(launch_permute(p, topk_idx, w, v, stream, ev));
     uint8_t *xq = reinterpret_cast<uint8_t *>(w + p.off_mx_xq);
     uint8_t *xs = reinterpret_cast<uint8_t *>(w + p.off_mx_xs);
     uint8_t *aq = reinterpret_cast<uint8_t *>(w + p.off_mx_aq);
@@ -121,7 +122,7 @@ extern "C" e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t
     a.grid = uint32_t(p.m_tiles_bound * p.n_tiles_gu);
     a.Cq = aq;
     a.Cs = as;
-    E4B_TRY(launch_mx_gemm(true, a, stream));
+    E4B_TRY(launch_mx_gemm(true, a, stream, ev));
     MxGemmArgs d = a;
     d.Wp = L->down.packed;
     d.Ws = L->down.scales;
@@ -135,17 +136,17 @@ extern "C" e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t
     d.grid = uint32_t(p.m_tiles_bound * p.n_tiles_h);
     d.C = o_buf;
     d.ldc = int32_t(p.H);
-    E4B_TRY(launch_mx_gemm(false, d, stream));
-    E4B_TRY(launch_combine_rows(o_buf, v.pos, topk_w, T, top_k, int(p.H), y, stream));
+    E4B_TRY(launch_mx_gemm(false, d, stream, ev));
+    E4B_TRY(launch_combine_rows(o_buf, v.pos, topk_w, T, top_k, int(p.H), y, stream, ev));
     return E4B_OK;
   }
   // with a saved buffer the permutation is written there for the dgrad
   const PermView v = saved ? perm_in_saved(p, static_cast<char *>(saved)) : perm_in_workspace(p, w);
-  E4B_TRY(launch_permute(p, topk_idx, w, v, stream));
+  E4B_TRY(launch_permute(p, topk_idx, w, v, stream, ev));
 
   uint16_t *a_buf = reinterpret_cast<uint16_t *>(w + p.off_a);
   uint16_t *o_buf = reinterpret_cast<uint16_t *>(w + p.off_o);
-  E4B_TRY(run_gate_up(p, L, x, a_buf, static_cast<uint16_t *>(saved), v, stream));
+  E4B_TRY(run_gate_up(p, L, x, a_buf, static_cast<uint16_t *>(saved), v, stream, ev));
 
   GemmArgs d = base_args(p, L->down, v);
   d.A = a_buf;
@@ -156,18 +157,27 @@ extern "C" e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t
   d.grid = uint32_t(p.m_tiles_bound * p.n_tiles_h);
   d.C = o_buf;
   d.ldc = int32_t(p.H);
-  E4B_TRY(launch_grouped_gemm(GEMM_DOWN_FWD, d, stream));
+  E4B_TRY(launch_grouped_gemm(GEMM_DOWN_FWD, d, stream, ev));
 
-  E4B_TRY(launch_combine_rows(o_buf, v.pos, topk_w, T, top_k, int(p.H), y, stream));
+  E4B_TRY(launch_combine_rows(o_buf, v.pos, topk_w, T, top_k, int(p.H), y, stream, ev));
   return E4B_OK;
 }
 
-extern "C" e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t top_k,
-                                    const int32_t *topk_idx, const float *topk_w,
-                                    const void *x_bf16, const void *saved,
-                                    const void *grad_y_bf16, void *grad_x_bf16,
-                                    float *grad_topk_w, void *ws, size_t ws_bytes,
-                                    hipStream_t stream) {
+extern "C" e4b_status e4b_moe_forward(const e4b_moe_layer *L, int64_t T, int32_t top_k,
+                                      const void *x_bf16, const float *router_logits,
+                                      int32_t *topk_idx, float *topk_w, void *y_bf16,
+                                      void *saved, void *ws, size_t ws_bytes, int32_t path,
+                                      hipStream_t stream) {
+  return e4b_moe_forward_timed(L, T, top_k, x_bf16, router_logits, topk_idx, topk_w, y_bf16, saved,
+                               ws, ws_bytes, path, stream, nullptr);
+}
+
+extern "C" e4b_status e4b_moe_dgrad_timed(const e4b_moe_layer *L, int64_t T, int32_t top_k,
+                                          const int32_t *topk_idx, const float *topk_w,
+                                          const void *x_bf16, const void *saved,
+                                          const void *grad_y_bf16, void *grad_x_bf16,
+                                          float *grad_topk_w, void *ws, size_t ws_bytes,
+                                          hipStream_t stream, const e4b_kernel_events *ev) {
   MoePlan p;
   e4b_status st = plan_moe(L, T, top_k, &p);
   if (st != E4B_OK) return st;
@@ -183,9 +193,9 @@ extern "C" e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t t
     v = perm_in_saved(p, static_cast<char *>(const_cast<void *>(saved)));
   } else {
     v = perm_in_workspace(p, w);
-    E4B_TRY(launch_permute(p, topk_idx, w, v, stream));
+    E4B_TRY(launch_permute(p, topk_idx, w, v, stream, ev));
     uint16_t *gu_ws = reinterpret_cast<uint16_t *>(w + p.off_gu);
-    E4B_TRY(run_gate_up(p, L, static_cast<const uint16_t *>(x_bf16), nullptr, gu_ws, v, stream));
+    E4B_TRY(run_gate_up(p, L, static_cast<const uint16_t *>(x_bf16), nullptr, gu_ws, v, stream, ev));
     gu = gu_ws;
   }
   uint16_t *dgu = reinterpret_cast<uint16_t *>(w + p.off_dgu);
@@ -204,7 +214,7 @@ extern "C" e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t t
   d.GU = const_cast<uint16_t *>(gu);
   d.topk_w = topk_w;
   d.partial = partial;
-  E4B_TRY(launch_grouped_gemm(GEMM_DOWN_DGRAD, d, stream));
+  E4B_TRY(launch_grouped_gemm(GEMM_DOWN_DGRAD, d, stream, ev));
 
   GemmArgs u = base_args(p, L->gate_up, v);
   u.A = dgu;
@@ -215,10 +225,36 @@ extern "C" e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t t
   u.grid = uint32_t(p.m_tiles_bound * p.n_tiles_h_gud);
   u.C = gx;
   u.ldc = int32_t(p.H);
-  E4B_TRY(launch_grouped_gemm(GEMM_GATE_UP_DGRAD, u, stream));
+  E4B_TRY(launch_grouped_gemm(GEMM_GATE_UP_DGRAD, u, stream, ev));
 
   E4B_TRY(launch_combine_dgrad(gx, v.pos, T, top_k, int(p.H), static_cast<uint16_t *>(grad_x_bf16),
-                               partial, int(p.n_tiles_i), grad_topk_w, stream));
+                               partial, int(p.n_tiles_i), grad_topk_w, stream, ev));
+  return E4B_OK;
+}
+
+extern "C" e4b_status e4b_moe_dgrad(const e4b_moe_layer *L, int64_t T, int32_t top_k,
+                                    const int32_t *topk_idx, const float *topk_w,
+                                    const void *x_bf16, const void *saved,
+                                    const void *grad_y_bf16, void *grad_x_bf16,
+                                    float *grad_topk_w, void *ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  return e4b_moe_dgrad_timed(L, T, top_k, topk_idx, topk_w, x_bf16, saved, grad_y_bf16,
+                             grad_x_bf16, grad_topk_w, ws, ws_bytes, stream, nullptr);
+}
+
+extern "C" e4b_status e4b_moe_perm_layout(const e4b_moe_layer *L, int64_t T, int32_t top_k,
+                                          e4b_perm_layout *out) {
+  if (!out) return E4B_ERR_NULL;
+  MoePlan p;
+  const e4b_status st = plan_moe(L, T, top_k, &p);
+  if (st != E4B_OK) return st;
+  out->counts = p.off_counts;
+  out->offsets = p.off_offsets;
+  out->tile_offsets = p.off_tile_offsets;
+  out->sorted_pair = p.off_sorted;
+  out->pos_of_pair = p.off_pos;
+  out->tile_map = p.off_tile_map;
+  out->m_tiles_bound = p.m_tiles_bound;
   return E4B_OK;
 }
 
@@ -434,42 +470,5 @@ extern "C" e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lo
                             int(p.k), topk_w, p.E, l.aa, false, r, sc, false, dB_dn, stream));
   E4B_TRY(launch_lora_wgrad(LS_GU_ACT, gu, 2 * p.I, int(p.I), int(p.I), v.sorted, v.offsets, v.tile_offsets,
                             int(p.k), topk_w, p.E, l.gb, true, r, sc, true, dA_dn, stream));
-  return E4B_OK;
-}
-
-// ---- benchmark event hooks ----
-namespace e4b {
-namespace {
-struct KernelTimer {
-  int kernel = -1;
-  hipEvent_t *start = nullptr;
-  hipEvent_t *stop = nullptr;
-  int n = 0;
-  int i = 0;
-} g_timer;
-}  // namespace
-
-void timer_before(int kernel, hipStream_t s) {
-  if (g_timer.n > 0 && kernel == g_timer.kernel)
-    (void)hipEventRecord(g_timer.start[g_timer.i % g_timer.n], s);
-}
-
-void timer_after(int kernel, hipStream_t s) {
-  if (g_timer.n > 0 && kernel == g_timer.kernel) {
-    (void)hipEventRecord(g_timer.stop[g_timer.i % g_timer.n], s);
-    ++g_timer.i;
-  }
-}
-}  // namespace e4b
-
-extern "C" e4b_status e4b_set_kernel_timer(int32_t kernel, hipEvent_t *start, hipEvent_t *stop,
-                                           int32_t n) {
-  if (kernel < 0 || kernel >= E4B_K_COUNT || n < 0) return E4B_ERR_SHAPE;
-  if (n > 0 && (!start || !stop)) return E4B_ERR_NULL;
-  e4b::g_timer.kernel = kernel;
-  e4b::g_timer.start = start;
-  e4b::g_timer.stop = stop;
-  e4b::g_timer.n = n;
-  e4b::g_timer.i = 0;
   return E4B_OK;
 }

@@ -68,20 +68,21 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t *__res
 }
 
 hipError_t launch_combine_rows(const uint16_t *rows, const int32_t *pos_of_pair, const float *w,
-                               int64_t T, int k, int H, uint16_t *out, hipStream_t s) {
+                               int64_t T, int k, int H, uint16_t *out, hipStream_t s,
+                               const e4b_kernel_events *ev) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_rows_kernel<true>, dim3(uint32_t(T)), dim3(256), 0, s, rows,
-                     pos_of_pair, w, k, H, out, nullptr, 0, nullptr);
-  return hipGetLastError();
+  return launch_k(ev, E4B_K_COMBINE, combine_rows_kernel<true>, dim3(uint32_t(T)), dim3(256), s,
+                  rows, pos_of_pair, w, k, H, out, static_cast<const float *>(nullptr), 0,
+                  static_cast<float *>(nullptr));
 }
 
 hipError_t launch_combine_dgrad(const uint16_t *rows, const int32_t *pos_of_pair, int64_t T, int k,
                                 int H, uint16_t *out, const float *partial, int n_tiles,
-                                float *gw, hipStream_t s) {
+                                float *gw, hipStream_t s, const e4b_kernel_events *ev) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_rows_kernel<false>, dim3(uint32_t(T)), dim3(256), 0, s, rows,
-                     pos_of_pair, nullptr, k, H, out, partial, n_tiles, gw);
-  return hipGetLastError();
+  return launch_k(ev, E4B_K_COMBINE_DGRAD, combine_rows_kernel<false>, dim3(uint32_t(T)), dim3(256),
+                  s, rows, pos_of_pair, static_cast<const float *>(nullptr), k, H, out, partial,
+                  n_tiles, gw);
 }
 
 }  // namespace e4b

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kPrepThreads) void decode_prep_kernel(const float *
     __syncthreads();
   } else {
     if (p >= kDecMaxPairs) return;
-    if (p < P) e_p = idx[p];
+    if (p < P) e_p = safe_expert(idx[p], E);
   }
   // unique sort key: expert, then pair id (stable)
   const int key = p < P ? e_p * kDecMaxPairs + p : 0x7FFFFFFF;
@@ -486,7 +486,7 @@ static int dec_resident_workgroups(bool gate_up, int bpl, bool mx) {
 
 hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
                                  const float *logits, int32_t *idx, float *wts, uint16_t *y,
-                                 char *ws, hipStream_t s) {
+                                 char *ws, hipStream_t s, const e4b_kernel_events *ev) {
   DecodeWs w;
   // the decode path reuses the sorted / pos slots of the permutation region
   w.sorted = reinterpret_cast<int32_t *>(ws + p.off_sorted);
@@ -510,9 +510,10 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
   const int target_gu = dec_resident_workgroups(true, bpl_gu, gu.codebook == E4B_CB_MXFP4);
   const int target_dn = dec_resident_workgroups(false, bpl_dn, dn.codebook == E4B_CB_MXFP4);
   if (target_gu <= 0 || target_dn <= 0) return hipErrorInvalidDeviceFunction;
-  hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(kPrepThreads), 0, s, logits, int(p.E), idx, wts,
-                     P, int(p.k),
-                     I / kDecTile, H / kDecTile, target_gu, target_dn, w);
+  hipError_t perr = launch_k(ev, E4B_K_DECODE_PREP, decode_prep_kernel, dim3(1), dim3(kPrepThreads), s,
+                             logits, int(p.E), idx, wts, P, int(p.k), I / kDecTile, H / kDecTile,
+                             target_gu, target_dn, w);
+  if (perr != hipSuccess) return perr;
 
   auto launch = [&](bool gate_up, int K_in, int n_units, const e4b_stack &st,
                     const uint16_t *vin, uint16_t *dst, int ldo, int kernel_id) {
@@ -521,11 +522,10 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
     const dim3 grid(uint32_t(tiles * ymax));
     const bool mx = st.codebook == E4B_CB_MXFP4;
     const int64_t eb = st.out * st.in / 2, ea = st.out * st.in / (mx ? kMxBlock : kBlock);
-    timer_before(kernel_id, s);
 #define E4B_DEC_LAUNCH(GU, B, MX)                                                             \
-  hipLaunchKernelGGL((decode_gemv_kernel<GU, B, MX>), grid, dim3(kDecThreads), 0, s, st.packed, \
-                     st.absmax, st.scales, eb, ea, K_in, n_units, I, vin, int(p.k), w,          \
-                     p.codebook, dst, ldo)
+  (void)launch_k(ev, kernel_id, decode_gemv_kernel<GU, B, MX>, grid, dim3(kDecThreads), s, st.packed, \
+                 st.absmax, st.scales, eb, ea, K_in, n_units, I, vin, int(p.k), w, int(p.codebook), \
+                 dst, ldo)
 #define E4B_DEC_BPL(GU, MX)                                                                   \
   {                                                                                           \
     if (bpl == 4) E4B_DEC_LAUNCH(GU, 4, MX);                                                  \
@@ -539,7 +539,6 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
     }
 #undef E4B_DEC_BPL
 #undef E4B_DEC_LAUNCH
-    timer_after(kernel_id, s);
   };
   // gate_up: I units (gate row u, up row I + u) over K_in = H
   launch(true, H, I, gu, x, a_buf, I, E4B_K_DECODE_GATE_UP);
@@ -547,7 +546,7 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
   launch(false, I, H, dn, a_buf, o_buf, H, E4B_K_DECODE_DOWN);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_combine_rows(o_buf, w.pos, wts, p.T, int(p.k), H, y, s);
+  return launch_combine_rows(o_buf, w.pos, wts, p.T, int(p.k), H, y, s, ev);
 }
 
 }  // namespace e4b

@@ -661,37 +661,28 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   }
 }
 
-hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s) {
+hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s,
+                               const e4b_kernel_events *ev) {
   if (a.grid == 0) return hipSuccess;
   // a multiple of 8 blocks: each XCD then has at least ceil(W / 8) of them
   const dim3 grid((a.grid + 7) / 8 * 8);
-  timer_before(int(v), s);
   const bool qb = a.cb == E4B_CB_BF16;
-#define E4B_GEMM(AM, BM, EP, WNV)                                                               \
-  do {                                                                                         \
-    if (qb)                                                                                    \
-      hipLaunchKernelGGL((grouped_gemm_kernel<AM, BM, EP, WNV, 1>), grid, dim3(256 * (WNV)), 0, \
-                         s, a);                                                                \
-    else                                                                                       \
-      hipLaunchKernelGGL((grouped_gemm_kernel<AM, BM, EP, WNV, 0>), grid, dim3(256 * (WNV)), 0, \
-                         s, a);                                                                \
-  } while (0)
+  const int kid = int(v);  // GemmVariant ids are the e4b_kernel ids of the four GEMMs
+#define E4B_GEMM(AM, BM, EP, WNV)                                                              \
+  return qb ? launch_k(ev, kid, grouped_gemm_kernel<AM, BM, EP, WNV, 1>, grid, dim3(256 * (WNV)), s, a) \
+            : launch_k(ev, kid, grouped_gemm_kernel<AM, BM, EP, WNV, 0>, grid, dim3(256 * (WNV)), s, a)
   switch (v) {
     case GEMM_GATE_UP_FWD:
       if (a.gated) E4B_GEMM(A_GATHER, B_NT, EPI_SWIGLU, kBNWide / 128);
-      else E4B_GEMM(A_GATHER, B_NT, EPI_ACT, kBNWide / 128);
-      break;
-    case GEMM_DOWN_FWD: E4B_GEMM(A_DIRECT, B_NT, EPI_STORE, kBNWide / 128); break;
+      E4B_GEMM(A_GATHER, B_NT, EPI_ACT, kBNWide / 128);
+    case GEMM_DOWN_FWD: E4B_GEMM(A_DIRECT, B_NT, EPI_STORE, kBNWide / 128);
     case GEMM_DOWN_DGRAD:
       if (a.gated) E4B_GEMM(A_GATHER, B_NN, EPI_DSWIGLU, kBNNarrow / 128);
-      else E4B_GEMM(A_GATHER, B_NN, EPI_DACT, kBNNarrow / 128);
-      break;
-    case GEMM_GATE_UP_DGRAD: E4B_GEMM(A_DIRECT, B_NN, EPI_STORE, kBNWide / 128); break;
+      E4B_GEMM(A_GATHER, B_NN, EPI_DACT, kBNNarrow / 128);
+    case GEMM_GATE_UP_DGRAD: E4B_GEMM(A_DIRECT, B_NN, EPI_STORE, kBNWide / 128);
   }
 #undef E4B_GEMM
-  const hipError_t err = hipGetLastError();
-  timer_after(int(v), s);
-  return err;
+  return hipErrorInvalidValue;
 }
 
 }  // namespace e4b

@@ -1,6 +1,7 @@
 // kernels.h -- host-side launchers of the library's kernels (internal).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -62,12 +63,28 @@ struct GemmArgs {
   int32_t lora_rows;
 };
 
-// Benchmark event hooks (e4b_set_kernel_timer): call before / after a launch.
-void timer_before(int kernel, hipStream_t s);
-void timer_after(int kernel, hipStream_t s);
+// Launch of `kernel` on `s`, bracketed by the call's events for kernel id
+// `kid` when the caller passed both (e4b_kernel_events): hipExtLaunchKernelGGL
+// records them at the dispatch's start and end.
+template <typename F, typename... Args>
+inline hipError_t launch_k(const e4b_kernel_events *ev, int kid, F kernel, dim3 grid, dim3 block,
+                           hipStream_t s, Args... args) {
+  hipEvent_t e0 = ev ? ev->start[kid] : nullptr, e1 = ev ? ev->stop[kid] : nullptr;
+  if (e0 && e1)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  return hipGetLastError();
+}
+
+// An expert id as the kernels use it: ids outside [0, E) read as expert 0,
+// so no index derived from a bad id leaves its buffer.
+__device__ __forceinline__ int safe_expert(int32_t id, int E) {
+  return uint32_t(id) < uint32_t(E) ? id : 0;
+}
 
 hipError_t launch_route(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
-                        hipStream_t s);
+                        hipStream_t s, const e4b_kernel_events *ev = nullptr);
 
 // Where the routing permutation lives: in the workspace, or in the saved
 // buffer when the forward keeps it for the dgrad.
@@ -83,7 +100,7 @@ PermView perm_in_saved(const MoePlan &p, char *saved);
 
 // Fills the permutation (histogram scratch and counts in the workspace).
 hipError_t launch_permute(const MoePlan &p, const int32_t *idx, char *ws, const PermView &v,
-                          hipStream_t s);
+                          hipStream_t s, const e4b_kernel_events *ev = nullptr);
 
 // The MX forward's grouped GEMM (csrc/mx.hip): MXFP4 weights against MXFP8
 // activation rows (codes with the bytes of each element pair swapped, E8M0
@@ -108,19 +125,22 @@ struct MxGemmArgs {
 };
 hipError_t launch_mx8_rows(const uint16_t *x, int64_t rows, int64_t K, uint8_t *codes,
                            uint8_t *scales, hipStream_t s);
-hipError_t launch_mx_gemm(bool gate_up, const MxGemmArgs &a, hipStream_t s);
+hipError_t launch_mx_gemm(bool gate_up, const MxGemmArgs &a, hipStream_t s,
+                          const e4b_kernel_events *ev = nullptr);
 
 // grid = m_tiles_bound * n_tiles; the launch rounds it up to a multiple of 8.
-hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s);
+hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s,
+                               const e4b_kernel_events *ev = nullptr);
 
 // y[t] = sum_j w[t, j] * rows[pos(t, j)] in fp32, slot order.
 hipError_t launch_combine_rows(const uint16_t *rows, const int32_t *pos_of_pair, const float *w,
-                               int64_t T, int k, int H, uint16_t *out, hipStream_t s);
+                               int64_t T, int k, int H, uint16_t *out, hipStream_t s,
+                               const e4b_kernel_events *ev = nullptr);
 // grad_x[t] = sum_j rows[pos(t, j)], and (gw not null) gw[t, j] = the sum of
 // partial[pos(t, j)][0 .. n_tiles) in ascending order.
 hipError_t launch_combine_dgrad(const uint16_t *rows, const int32_t *pos_of_pair, int64_t T, int k,
                                 int H, uint16_t *out, const float *partial, int n_tiles,
-                                float *gw, hipStream_t s);
+                                float *gw, hipStream_t s, const e4b_kernel_events *ev = nullptr);
 
 // ---- LoRA (lora.hip) ----
 // out[e, n, :] = bf16(s * M[e, n, j]) for j < r, 0 up to kLoraK, where

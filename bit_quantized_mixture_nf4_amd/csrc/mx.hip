@@ -339,17 +339,13 @@ hipError_t launch_mx8_rows(const uint16_t *x, int64_t rows, int64_t K, uint8_t *
   return hipGetLastError();
 }
 
-hipError_t launch_mx_gemm(bool gate_up, const MxGemmArgs &a, hipStream_t s) {
+hipError_t launch_mx_gemm(bool gate_up, const MxGemmArgs &a, hipStream_t s,
+                          const e4b_kernel_events *ev) {
   if (a.grid == 0) return hipSuccess;
   const dim3 grid{(a.grid + 7) / 8 * 8};
-  timer_before(gate_up ? E4B_K_GATE_UP_FWD : E4B_K_DOWN_FWD, s);
   if (gate_up)
-    hipLaunchKernelGGL((mx_gemm_kernel<MX_GATHER, MX_SWIGLU>), grid, dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL((mx_gemm_kernel<MX_DIRECT, MX_STORE>), grid, dim3(512), 0, s, a);
-  const hipError_t err = hipGetLastError();
-  timer_after(gate_up ? E4B_K_GATE_UP_FWD : E4B_K_DOWN_FWD, s);
-  return err;
+    return launch_k(ev, E4B_K_GATE_UP_FWD, mx_gemm_kernel<MX_GATHER, MX_SWIGLU>, grid, dim3(512), s, a);
+  return launch_k(ev, E4B_K_DOWN_FWD, mx_gemm_kernel<MX_DIRECT, MX_STORE>, grid, dim3(512), s, a);
 }
 
 }  // namespace e4b

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t *__restric
   const int64_t p0 = c * kPermChunk;
   for (int i = threadIdx.x; i < kPermChunk; i += 256) {
     const int64_t p = p0 + i;
-    if (p < P) atomicAdd(&h[flat_idx[p]], 1);
+    if (p < P) atomicAdd(&h[safe_expert(flat_idx[p], E)], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) hist[int64_t(e) * nchunks + c] = h[e];
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(64) void perm_scatter_kernel(
 #pragma unroll
   for (int it = 0; it < kIt; ++it) {
     const int64_t p = p0 + it * 64 + lane;
-    ids[it] = p < P ? flat_idx[p] : 0;
+    ids[it] = p < P ? safe_expert(flat_idx[p], E) : 0;
   }
   // exclusive scan of counts (and of m-tiles) over experts, 64 at a time
   int32_t carry = 0, tcarry = 0;
@@ -162,11 +162,10 @@ __global__ __launch_bounds__(64) void perm_scatter_kernel(
 }
 
 hipError_t launch_route(const float *logits, int64_t T, int E, int k, int32_t *idx, float *w,
-                        hipStream_t s) {
+                        hipStream_t s, const e4b_kernel_events *ev) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(route_kernel, dim3(uint32_t((T + 3) / 4)), dim3(256), 0, s, logits, T, E, k,
-                     idx, w);
-  return hipGetLastError();
+  return launch_k(ev, E4B_K_ROUTE, route_kernel, dim3(uint32_t((T + 3) / 4)), dim3(256), s, logits,
+                  T, E, k, idx, w);
 }
 
 PermView perm_in_workspace(const MoePlan &p, char *ws) {
@@ -190,19 +189,33 @@ PermView perm_in_saved(const MoePlan &p, char *saved) {
 }
 
 hipError_t launch_permute(const MoePlan &p, const int32_t *idx, char *ws, const PermView &v,
-                          hipStream_t s) {
+                          hipStream_t s, const e4b_kernel_events *ev) {
   if (p.P == 0) return hipSuccess;
   int32_t *hist = reinterpret_cast<int32_t *>(ws + p.off_hist);
   int32_t *cbase = reinterpret_cast<int32_t *>(ws + p.off_chunk_base);
   int32_t *counts = reinterpret_cast<int32_t *>(ws + p.off_counts);
   const int E = int(p.E);
-  hipLaunchKernelGGL(perm_hist_kernel, dim3(uint32_t(p.nchunks)), dim3(256), 0, s, idx, p.P, E,
-                     p.nchunks, hist);
+  // E4B_K_PERMUTE spans the three launches: start event on the first, stop on the last
+  hipEvent_t e0 = ev ? ev->start[E4B_K_PERMUTE] : nullptr, e1 = ev ? ev->stop[E4B_K_PERMUTE] : nullptr;
+  const bool timed = e0 && e1;
+  if (timed)
+    hipExtLaunchKernelGGL(perm_hist_kernel, dim3(uint32_t(p.nchunks)), dim3(256), 0, s, e0,
+                          static_cast<hipEvent_t>(nullptr), 0, idx, p.P, E, p.nchunks, hist);
+  else
+    hipLaunchKernelGGL(perm_hist_kernel, dim3(uint32_t(p.nchunks)), dim3(256), 0, s, idx, p.P, E,
+                       p.nchunks, hist);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(uint32_t(E)), dim3(256), 0, s, hist, p.nchunks, cbase,
                      counts);
-  hipLaunchKernelGGL(perm_scatter_kernel, dim3(uint32_t(p.nchunks)), dim3(64), 0, s, idx, p.P, E,
-                     p.nbits_e, p.nchunks, counts, cbase, v.sorted, v.pos, v.offsets,
-                     v.tile_offsets, v.tile_map, p.m_tiles_bound);
+  if (timed)
+    hipExtLaunchKernelGGL(perm_scatter_kernel, dim3(uint32_t(p.nchunks)), dim3(64), 0, s,
+                          static_cast<hipEvent_t>(nullptr), e1, 0, idx, p.P, E, p.nbits_e,
+                          p.nchunks, static_cast<const int32_t *>(counts),
+                          static_cast<const int32_t *>(cbase), v.sorted, v.pos, v.offsets,
+                          v.tile_offsets, v.tile_map, p.m_tiles_bound);
+  else
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(uint32_t(p.nchunks)), dim3(64), 0, s, idx, p.P, E,
+                       p.nbits_e, p.nchunks, counts, cbase, v.sorted, v.pos, v.offsets,
+                       v.tile_offsets, v.tile_map, p.m_tiles_bound);
   return hipGetLastError();
 }
 

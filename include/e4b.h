@@ -35,7 +35,10 @@
  *   "Unsupported" definition): a bad argument is reported, never ignored.
  *   T == 0 is a valid no-op.
  * - Device preconditions that are NOT checked: finite weights and logits;
- *   0 <= topk_idx < E and distinct per token when it is an input.
+ *   0 <= topk_idx < E and distinct per token when it is an input. An id
+ *   outside [0, E) never leads to an out-of-bounds access: every kernel that
+ *   reads ids treats it as expert 0, so the pair's result is meaningless but
+ *   the call stays in bounds (the Python binding can check the ids first).
  */
 #ifndef E4B_H
 #define E4B_H
@@ -302,25 +305,65 @@ e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lora *lora, i
  * adapters' per-pair projections and bf16 operand packs); 0 when invalid. */
 size_t e4b_moe_lora_workspace_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k);
 
-/* Kernels that e4b_set_kernel_timer can bracket with events. */
+/* Kernels of the forward and dgrad calls that the *_timed entry points can
+ * bracket with events (benchmark instrumentation). */
 typedef enum {
-  E4B_K_GATE_UP_FWD = 0,   /* grouped gate_up GEMM + SiLU*up epilogue */
-  E4B_K_DOWN_FWD = 1,      /* grouped down GEMM */
+  E4B_K_GATE_UP_FWD = 0,   /* grouped gate_up GEMM + SiLU*up epilogue (MX path: its MX GEMM) */
+  E4B_K_DOWN_FWD = 1,      /* grouped down GEMM (MX path: its MX GEMM) */
   E4B_K_DOWN_DGRAD = 2,    /* grouped GEMM on W_dn^T + SiLU-backward epilogue */
   E4B_K_GATE_UP_DGRAD = 3, /* grouped GEMM on W_gu^T */
   E4B_K_DECODE_GATE_UP = 4,/* decode dequant-GEMV, gate_up + SiLU*up */
-  E4B_K_DECODE_DOWN = 5,   /* decode dequant-GEMV, down */
-  E4B_K_COUNT = 6
+  E4B_K_DECODE_DOWN = 5,   /* decode dequant-GEMV, down (+ the weighted combine) */
+  E4B_K_ROUTE = 6,         /* top-k routing from logits */
+  E4B_K_PERMUTE = 7,       /* the permutation (the first of its kernels to the last) */
+  E4B_K_COMBINE = 8,       /* forward gather-combine */
+  E4B_K_COMBINE_DGRAD = 9, /* dgrad gather-combine + routing-weight gradient */
+  E4B_K_DECODE_PREP = 10,  /* decode grouping (and routing) */
+  E4B_K_COUNT = 11
 } e4b_kernel;
 
-/* Benchmark instrumentation (not part of the computation): while armed, the
- * i-th launch of `kernel` is bracketed by hipEventRecord(start[i % n]) and
- * hipEventRecord(stop[i % n]) on the stream it is launched on. The event
- * arrays are caller-owned and must stay valid while armed; n == 0 disarms.
- * Process-wide setting, not thread-safe: arm it only from a single-threaded
- * benchmark. Errors: SHAPE (unknown kernel or n < 0), NULL (n > 0 with a
- * NULL array). */
-e4b_status e4b_set_kernel_timer(int32_t kernel, hipEvent_t *start, hipEvent_t *stop, int32_t n);
+/* Per-call kernel timing. For every kernel id whose start and stop events
+ * are both non-NULL, the call launches that kernel with
+ * hipExtLaunchKernelGGL(start, stop), so the two events carry the start and
+ * end time of that dispatch on the launch stream (hipEventElapsedTime gives
+ * the kernel's duration). A kernel launched twice in one call (the gate_up
+ * GEMM recomputed by a dgrad without saved state) records the last launch;
+ * E4B_K_PERMUTE spans its three launches. Events are caller-owned and
+ * created beforehand. The library keeps no reference after the call. */
+typedef struct {
+  hipEvent_t start[E4B_K_COUNT];
+  hipEvent_t stop[E4B_K_COUNT];
+} e4b_kernel_events;
+
+/* e4b_moe_forward / e4b_moe_dgrad with per-call kernel timing (`events` may
+ * be NULL: then identical to the untimed calls). Same arguments, results
+ * and errors. */
+e4b_status e4b_moe_forward_timed(const e4b_moe_layer *L, int64_t T, int32_t top_k,
+                                 const void *x_bf16, const float *router_logits,
+                                 int32_t *topk_idx, float *topk_w, void *y_bf16, void *saved,
+                                 void *ws, size_t ws_bytes, int32_t path, hipStream_t stream,
+                                 const e4b_kernel_events *events);
+e4b_status e4b_moe_dgrad_timed(const e4b_moe_layer *L, int64_t T, int32_t top_k,
+                               const int32_t *topk_idx, const float *topk_w, const void *x_bf16,
+                               const void *saved, const void *grad_y_bf16, void *grad_x_bf16,
+                               float *grad_topk_w, void *ws, size_t ws_bytes, hipStream_t stream,
+                               const e4b_kernel_events *events);
+
+/* Where the grouped forward (saved == NULL) leaves its routing permutation
+ * in the workspace, for inspection (int32 arrays; byte offsets from ws):
+ * counts [E], offsets [E + 1] (first sorted position of each expert),
+ * tile_offsets [E + 1] (first m-tile of each expert, m-tiles of 256 sorted
+ * pairs), sorted_pair [P] (flat pair id t * top_k + j at each sorted
+ * position, stable: ascending within an expert), pos_of_pair [P] (its
+ * inverse), tile_map [m_tiles_bound] (int32 x4 per m-tile: expert, segment
+ * start, first row, rows). Errors as e4b_moe_workspace_bytes' arguments
+ * (NULL for a NULL `out`). */
+typedef struct {
+  size_t counts, offsets, tile_offsets, sorted_pair, pos_of_pair, tile_map;
+  int64_t m_tiles_bound;
+} e4b_perm_layout;
+e4b_status e4b_moe_perm_layout(const e4b_moe_layer *L, int64_t T, int32_t top_k,
+                               e4b_perm_layout *out);
 
 /* Static, human-readable text for a status code. */
 const char *e4b_status_string(e4b_status status);

@@ -91,3 +91,60 @@ def oracle_expert_stacks(cfg, seed, experts, kind="nf4", threads=16):
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(one, jobs))
     return out
+
+
+def oracle_store_expert(w, kind, threads=16):
+    """The oracle's stored form of one expert's fp32 weight ``[out, in]``.
+
+    Quantized on row slices in parallel threads (a block never straddles a
+    row, so row slices give exactly the whole-expert result). Returns
+    ``(stored bytes uint8 [nbytes], scale bytes uint8 [n] or None, dequantized
+    fp32 [out, in])``: nf4 / fp4 -> packed codes and the absmax as its fp32
+    bytes; mxfp4 -> packed codes and the E8M0 bytes; bf16 -> the bf16 bit
+    patterns as bytes and no scales.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    rows, inn = w.shape
+    step = max(1, -(-rows // (4 * threads)))
+    slices = [(r0, min(rows, r0 + step)) for r0 in range(0, rows, step)]
+
+    def one(sl):
+        r0, r1 = sl
+        ws = w[None, r0:r1]
+        if kind == "bf16":
+            bits = oracle.bf16_rne_bits(ws[0])
+            return bits.view(np.uint8).reshape(-1), None, oracle.bf16_bits_to_f32(bits)
+        if kind == "mxfp4":
+            p, s = oracle.quantize_mx(ws)
+            return p[0], s[0], oracle.dequantize_mx(p, s, r1 - r0, inn)[0]
+        p, a = oracle.quantize_blockwise(ws, kind)
+        return p[0], a[0].view(np.uint8), oracle.dequantize(p, a, r1 - r0, inn, kind)[0]
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        parts = list(ex.map(one, slices))
+    codes = np.concatenate([p[0] for p in parts])
+    scales = None if parts[0][1] is None else np.concatenate([p[1] for p in parts])
+    deq = np.concatenate([p[2] for p in parts], axis=0)
+    return codes, scales, deq
+
+
+def stack_bytes(stack):
+    """Host copies of a device stack as bytes per expert: (codes [E, n], scales [E, m] or None)."""
+    codes = stack.packed.cpu().numpy()
+    sc = stack.scales if stack.codebook == "mxfp4" else stack.absmax
+    scales = None if sc is None else sc.cpu().numpy().view(np.uint8).reshape(stack.E, -1)
+    return codes, scales
+
+
+def expert_view(stack, e):
+    """A one-expert QuantStack aliasing expert e of a device stack."""
+    sl = slice(e, e + 1)
+    return e4b.QuantStack(stack.packed[sl], None if stack.absmax is None else stack.absmax[sl], 1,
+                          stack.out, stack.inn, stack.codebook,
+                          None if stack.scales is None else stack.scales[sl])
+
+
+def routed_pairs(idx, e):
+    """(tokens, slots) of the pairs routed to expert e, in token order."""
+    return np.nonzero(np.asarray(idx) == e)

@@ -20,23 +20,30 @@ from gpu_util import DEV, Problem, announce, tol_check, to_np, bf16_tensor
 pytestmark = pytest.mark.gpu
 
 
-def _align(v, a=256):
-    return (v + a - 1) // a * a
-
-
-def _perm_layout(E, P):
-    """Byte offsets of the permutation outputs in the workspace (mirrors the planner)."""
-    nchunks = (P + 1023) // 1024
-    off, out = 0, {}
-    for name, n in (("hist", E * nchunks), ("cbase", E * nchunks), ("counts", E),
-                    ("offsets", E + 1), ("tiles", E + 1), ("sorted", P), ("pos", P)):
-        out[name] = (off, n)
-        off = _align(off + 4 * n)
-    return out
-
-
 def _read_i32(ws, off, n):
     return ws[off : off + 4 * n].view(torch.int32).cpu().numpy()
+
+
+def _check_permutation(layer, ws, idx, E, P):
+    """Every array of the permutation in the workspace equals the oracle's, as
+    exact integers, at the offsets the library reports (e4b_moe_perm_layout)."""
+    T, k = idx.shape
+    lay = e4b.perm_layout(layer, T, k)
+    counts, offsets, sp, pos = oracle.permute(idx, E)
+    assert np.array_equal(_read_i32(ws, lay["counts"], E), counts)
+    assert np.array_equal(_read_i32(ws, lay["offsets"], E + 1), offsets)
+    assert np.array_equal(_read_i32(ws, lay["sorted_pair"], P), sp)
+    assert np.array_equal(_read_i32(ws, lay["pos_of_pair"], P), pos)
+    mt = (counts + 255) // 256
+    tiles = np.concatenate([[0], np.cumsum(mt)])
+    assert np.array_equal(_read_i32(ws, lay["tile_offsets"], E + 1), tiles)
+    # m-tile map: (expert, segment start, first row, rows) per real m-tile, zero past them
+    want = np.zeros((lay["m_tiles_bound"], 4), np.int64)
+    for e in range(E):
+        for t in range(mt[e]):
+            want[tiles[e] + t] = (e, offsets[e], 256 * t, min(256, counts[e] - 256 * t))
+    got = _read_i32(ws, lay["tile_map"], 4 * lay["m_tiles_bound"]).reshape(-1, 4)
+    assert np.array_equal(got, want)
 
 
 def _oracle_fwd(pb, idx, w, tokens=None):
@@ -121,14 +128,36 @@ def test_permutation_exact(tiny):
     _, idx, _, _ = e4b.moe_forward(tiny.layer, tiny.x_d, cfg.k, logits=tiny.logits_d,
                                    path="grouped", workspace=ws)
     torch.cuda.synchronize()
-    counts, offsets, sp, pos = oracle.permute(idx.cpu().numpy(), cfg.E)
-    lay = _perm_layout(cfg.E, cfg.P)
-    assert np.array_equal(_read_i32(ws, *lay["counts"]), counts)
-    assert np.array_equal(_read_i32(ws, *lay["offsets"]), offsets)
-    assert np.array_equal(_read_i32(ws, *lay["sorted"]), sp)
-    assert np.array_equal(_read_i32(ws, *lay["pos"]), pos)
-    tiles = np.concatenate([[0], np.cumsum((counts + 255) // 256)])
-    assert np.array_equal(_read_i32(ws, *lay["tiles"]), tiles)
+    _check_permutation(tiny.layer, ws, idx.cpu().numpy(), cfg.E, cfg.P)
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 700), ("olmoe", None), ("qwen3_prefill", None),
+                                    ("mixtral", None)])
+def test_permutation_exact_multi_chunk(name, T):
+    """Many 256-pair chunks (the per-chunk histogram, the carried scan and the
+    per-chunk scatter base), up to the Zipf-routed Qwen3 prefill batch
+    (P = 131072, its hottest expert spanning dozens of m-tiles)."""
+    from workloads import gen_logits
+
+    cfg = get_config(name, T)
+    lg = gen_logits(cfg, 0)
+    announce(f"permutation {name} E={cfg.E} k={cfg.k} T={cfg.T} P={cfg.P}")
+    # routed through a forward on a small stand-in layer with the same E, k and T
+    small = MoEConfig("s", E=cfg.E, H=64, I=64, k=cfg.k, T=cfg.T, routing=cfg.routing)
+    pb = Problem(small, seed=0, with_grad=False)
+    ws = torch.zeros(e4b.workspace_bytes(pb.layer, cfg.T, cfg.k), dtype=torch.uint8, device=DEV)
+    _, idx, _, _ = e4b.moe_forward(pb.layer, pb.x_d, cfg.k, logits=torch.from_numpy(lg).to(DEV),
+                                   path="grouped", workspace=ws)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    assert np.array_equal(idx_np, oracle.route(lg, cfg.k)[0])
+    _check_permutation(pb.layer, ws, idx_np, cfg.E, cfg.P)
+    # given ids (no logits): the same permutation from the caller's buffer
+    ws.zero_()
+    e4b.moe_forward(pb.layer, pb.x_d, cfg.k, topk_idx=idx, topk_w=torch.full_like(idx, 0.5, dtype=torch.float32),
+                    path="grouped", workspace=ws)
+    torch.cuda.synchronize()
+    _check_permutation(pb.layer, ws, idx_np, cfg.E, cfg.P)
 
 
 def test_forward_tiny_grouped(tiny):
@@ -175,7 +204,9 @@ def test_runs_are_bitwise_deterministic(tiny):
         y, idx, w, saved = e4b.moe_forward(tiny.layer, tiny.x_d, cfg.k, logits=tiny.logits_d, save=True)
         gx, gw = e4b.moe_dgrad(tiny.layer, idx, w, tiny.grad_y_d, saved=saved)
         torch.cuda.synchronize()
-        outs.append([t.clone() for t in (y, idx, w, saved, gx, gw)])
+        # the outputs; the saved buffer's padding is never written, so only
+        # what the dgrad reads from it enters the comparison (through gx, gw)
+        outs.append([t.clone() for t in (y, idx, w, gx, gw)])
     for a, b in zip(*outs):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 

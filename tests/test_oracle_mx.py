@@ -211,3 +211,114 @@ def test_mx8_forward_close_to_unquantized_activations():
     y = oracle.moe_forward(x, idx, w, wgu, wdn)
     err = np.abs(y_mx - y).max() / np.abs(y).max()
     assert 1e-4 < err < 0.1
+
+
+# ---- exact pin of the MX forward's composition ----------------------------
+# An independent recomputation in rational arithmetic (fractions.Fraction,
+# with silu from decimal at 60 digits): every conversion is a brute-force
+# nearest search over the E4M3 values built from the bit definition, the bf16
+# rounding of a goes through its fp32 value (the gate_up epilogue computes a
+# in fp32 and stores it as bf16, nearest even), and the contractions are exact.
+
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+
+def _e4m3_mags_exact():
+    out = []
+    for c in range(0x7F):
+        e, m = c >> 3, c & 7
+        out.append(Fraction(m, 8) * Fraction(1, 64) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7))
+    return out
+
+
+_MAGS = _e4m3_mags_exact()
+
+
+def _floor_log2(q):
+    q = abs(q)
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    while Fraction(2) ** e > q:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= q:
+        e += 1
+    return e
+
+
+def _mx8_round_row(vals):
+    """MXFP8 values of one row of Fractions (blocks of 32), by brute force."""
+    out = []
+    for b in range(0, len(vals), 32):
+        blk = vals[b:b + 32]
+        amax = max(abs(v) for v in blk)
+        sh = -127 if amax == 0 else max(-127, min(127, _floor_log2(amax) - 8))
+        sc = Fraction(2) ** sh
+        for v in blk:
+            a = abs(v) / sc
+            d = [abs(m - a) for m in _MAGS]
+            best = [k for k in range(len(_MAGS)) if d[k] == min(d)]
+            k = best[0] if len(best) == 1 else [q for q in best if q % 2 == 0][0]
+            out.append((-1 if v < 0 else 1) * _MAGS[k] * sc)
+    return out
+
+
+def _round_bits(q, bits, emin):
+    """Nearest binary value of q with `bits` significant bits (ties to even), exponent >= emin."""
+    if q == 0:
+        return Fraction(0)
+    s = -1 if q < 0 else 1
+    q = abs(q)
+    e = max(_floor_log2(q), emin)
+    ulp = Fraction(2) ** (e - bits + 1)
+    n, r = divmod(q, ulp)
+    if r > ulp / 2 or (r == ulp / 2 and n % 2 == 1):
+        n += 1
+    return s * n * ulp
+
+
+def _silu_exact(g):
+    getcontext().prec = 60
+    gd = Decimal(g.numerator) / Decimal(g.denominator)
+    return Fraction(gd / (1 + (-gd).exp()))
+
+
+def test_mx8_forward_equals_exact_rational_recomputation():
+    rng = np.random.default_rng(20)
+    E, H, I, T, k = 2, 64, 64, 3, 2
+    # MXFP4-stored weights: E2M1 values times a power of two per 32-block
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+    def mx_weights(out, inn):
+        v = mags[rng.integers(0, 8, (E, out, inn))] * np.where(rng.random((E, out, inn)) < 0.5, -1, 1)
+        s = rng.integers(-9, -5, (E, out, inn // 32))
+        return (v * np.ldexp(1.0, np.repeat(s, 32, axis=2))).astype(np.float32)
+
+    wgu, wdn = mx_weights(2 * I, H), mx_weights(H, I)
+    x = oracle.bf16_bits_to_f32(oracle.bf16_rne_bits(
+        (rng.standard_normal((T, H)) * np.exp(rng.uniform(-3, 3, (T, 1)))).astype(np.float32)))
+    idx = np.array([[0, 1], [1, 0], [1, 0]], np.int32)
+    w = rng.random((T, k))
+    w /= w.sum(1, keepdims=True)
+
+    def reference(round_a_to_bf16):
+        y = [[Fraction(0)] * H for _ in range(T)]
+        for t in range(T):
+            xq = _mx8_round_row([Fraction(float(v)) for v in x[t]])
+            for j in range(k):
+                e = int(idx[t, j])
+                h = [sum(Fraction(float(wgu[e, n, c])) * xq[c] for c in range(H)) for n in range(2 * I)]
+                a = [_silu_exact(h[n]) * h[I + n] for n in range(I)]
+                if round_a_to_bf16:
+                    a = [_round_bits(_round_bits(v, 24, -126), 8, -126) for v in a]
+                aq = _mx8_round_row(a)
+                for n in range(H):
+                    o = sum(Fraction(float(wdn[e, n, c])) * aq[c] for c in range(I))
+                    y[t][n] += Fraction(float(w[t, j])) * o
+        return np.array([[float(v) for v in row] for row in y])
+
+    ref = reference(True)
+    got = oracle.mx8_forward(x, idx, w, wgu, wdn)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+    # the case tells the bf16 rounding of a apart: without it the E4M3
+    # decisions of some elements of a change
+    assert np.max(np.abs(reference(False) - ref)) > 1e-6 * np.max(np.abs(ref))
