@@ -36,7 +36,6 @@ import ctypes
 import json
 import os
 import statistics
-import subprocess
 import sys
 import time
 
@@ -643,14 +642,6 @@ def host_info(torch):
         info["gpu"] = torch.cuda.get_device_properties(0).gcnArchName
     except Exception:  # noqa: BLE001 - metadata only
         info["gpu"] = None
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        d = json.loads(r.stdout) if r.returncode == 0 else {}
-        card = next(iter(d.values())) if d else {}
-        info["sclk"] = next((v for k_, v in card.items() if "sclk" in k_.lower()), None)
-        info["mclk"] = next((v for k_, v in card.items() if "mclk" in k_.lower()), None)
-    except Exception:  # noqa: BLE001 - metadata only
-        info["sclk"] = None
     return info
 
 

@@ -31,35 +31,9 @@
 // dequantized once per workgroup (codebook in LDS, fp32 multiply by the block
 // absmax, round-to-nearest-even bf16), i.e. exactly the bf16 view that
 // e4b_dequantize_nf4 returns.
-#include "device.h"
-#include "kernels.h"
+#include "gemm_dev.h"
 
 namespace e4b {
-
-enum { A_GATHER = 0, A_DIRECT = 1 };
-enum { B_NT = 0, B_NN = 1 };
-enum { EPI_SWIGLU = 0, EPI_STORE = 1, EPI_DSWIGLU = 2, EPI_ACT = 3, EPI_DACT = 4 };
-
-
-
-constexpr int kLds = kBK + 8;  // padded row (bf16 elements): 144 bytes, conflict-free b128 access
-
-// B_NN tile in LDS: 16-byte unit u of a row is stored at unit u ^ ((u >> 3) & 3),
-// which puts the 8 threads writing one row's units on distinct banks
-__device__ __forceinline__ int nn_unit(int u) { return u ^ ((u >> 3) & 3); }
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-// gfx950 LDS transpose read: within each 16-lane group, lane s supplies the
-// address of 4 bf16 (row s / 4, columns 4 (s % 4) .. + 3 of a 4 x 16 block)
-// and receives column s of the block (rows 0..3)
-__device__ __forceinline__ s16x4 lds_read_tr16(const uint16_t *p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4 *)(const_cast<uint16_t *>(p)));
-}
-
-// hardware reciprocal (about 1 ulp): the result is rounded to bf16 anyway
-__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Waves are laid out 4 (M) x 2 (N); wave w -> (wm = w / 2, wn = w % 2), so the
 // waves holding the first 128 rows sit on all four SIMDs and a tile whose
@@ -673,13 +647,11 @@ hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s,
             : launch_k(ev, kid, grouped_gemm_kernel<AM, BM, EP, WNV, 0>, grid, dim3(256 * (WNV)), s, a)
   switch (v) {
     case GEMM_GATE_UP_FWD:
-      if (a.gated) E4B_GEMM(A_GATHER, B_NT, EPI_SWIGLU, kBNWide / 128);
-      E4B_GEMM(A_GATHER, B_NT, EPI_ACT, kBNWide / 128);
-    case GEMM_DOWN_FWD: E4B_GEMM(A_DIRECT, B_NT, EPI_STORE, kBNWide / 128);
+    case GEMM_DOWN_FWD:
+    case GEMM_GATE_UP_DGRAD: return launch_gemm_wide(v, a, s, ev);
     case GEMM_DOWN_DGRAD:
       if (a.gated) E4B_GEMM(A_GATHER, B_NN, EPI_DSWIGLU, kBNNarrow / 128);
       E4B_GEMM(A_GATHER, B_NN, EPI_DACT, kBNNarrow / 128);
-    case GEMM_GATE_UP_DGRAD: E4B_GEMM(A_DIRECT, B_NN, EPI_STORE, kBNWide / 128);
   }
 #undef E4B_GEMM
   return hipErrorInvalidValue;
