@@ -44,7 +44,11 @@ EXPORTS = (
     "e4b_moe_forward_timed",
     "e4b_moe_dgrad_timed",
     "e4b_moe_perm_layout",
+    "e4b_moe_forward_noalloc",
 )
+
+# bytes of the per-GPU array that e4b_moe_forward_noalloc uses as its workspace
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # e4b_kernel ids (the slots of e4b_kernel_events)
 KERNELS = {
@@ -144,6 +148,7 @@ def load():
         "e4b_moe_dgrad_timed": (
             i32, [lay, i64, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(E4bKernelEvents)]),
         "e4b_moe_perm_layout": (i32, [lay, i64, i32, ctypes.POINTER(E4bPermLayout)]),
+        "e4b_moe_forward_noalloc": (i32, [lay, i64, i32, vp, vp, vp, vp, vp, vp, i32, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)

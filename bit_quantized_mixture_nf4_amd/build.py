@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libe4b.so")
 
 SOURCES = ["plan.cpp", "quant.hip", "route.hip", "gemm.hip", "gemm_wide.hip", "combine.hip", "decode.hip", "lora.hip", "mx.hip",
-           "api.hip"]
+           "api.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

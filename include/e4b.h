@@ -256,6 +256,25 @@ size_t e4b_moe_workspace_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k)
  * pairs, blocks of m-tiles the routing does not produce) and nothing reads it. */
 size_t e4b_moe_saved_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k);
 
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): e4b_moe_forward with its workspace in a fixed per-GPU device
+ * array of the library (E4B_NOALLOC_SCRATCH_BYTES) instead of a caller
+ * buffer; the other arguments are those of e4b_moe_forward. Each GPU holds
+ * its own copy of the array until the process ends; every call on that GPU
+ * shares it and it keeps the last call's contents (no kernel of the forward
+ * reads a workspace byte that the same call did not write, so nothing is
+ * cleared). Calls that overlap on one GPU (two streams or two threads) race
+ * on the array: the caller serializes them. No call allocates; the first
+ * call on a device looks up the array's device address once.
+ * Errors: as e4b_moe_forward; WORKSPACE when e4b_moe_workspace_bytes(L, T,
+ * top_k) exceeds E4B_NOALLOC_SCRATCH_BYTES; HIP when the address lookup fails. */
+#define E4B_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+e4b_status e4b_moe_forward_noalloc(const e4b_moe_layer *L, int64_t T, int32_t top_k,
+                                   const void *x_bf16, const float *router_logits,
+                                   int32_t *topk_idx, float *topk_w, void *y_bf16, void *saved,
+                                   int32_t path, hipStream_t stream);
+
 /* Per-expert LoRA adapters over the frozen base (fp32 device buffers).
  * [README] Quickstart: ExpertsLoRA(base, r=8, alpha=16) attaches trainable
  * per-expert LoRA to a frozen 4-bit stack; only the adapters train. The
