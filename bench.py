@@ -203,7 +203,7 @@ def kernel_times(e4b, torch, ev, step, names, n):
 
 
 # Kernel sources whose text fixes the grouped GEMMs' memory traffic.
-GEMM_SOURCES = ("gemm.hip", "device.h", "kernels.h", "plan.h")
+GEMM_SOURCES = ("gemm.hip", "gemm_wide.hip", "gemm_dev.h", "device.h", "kernels.h", "plan.h")
 
 
 def gemm_source_digest():
@@ -427,7 +427,7 @@ def bench_decode(args, e4b, torch, ev):
     out = {}
     e_gu = 2 * cfg0.I * cfg0.H // 2 + 2 * cfg0.I * cfg0.H // 64 * 4  # packed + absmax per expert
     e_dn = cfg0.H * cfg0.I // 2 + cfg0.H * cfg0.I // 64 * 4
-    names = ["decode_prep", "decode_gate_up", "decode_down", "combine"]
+    names = ["decode_gate_up", "decode_down"]
     for T in (1, 8):
         cfg = get_config("qwen3_decode", T)
         x = to_bf16_tensor(gen_x(cfg, 0)).cuda()

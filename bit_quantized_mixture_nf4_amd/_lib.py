@@ -62,9 +62,8 @@ KERNELS = {
     "permute": 7,
     "combine": 8,
     "combine_dgrad": 9,
-    "decode_prep": 10,
 }
-E4B_K_COUNT = 11
+E4B_K_COUNT = 10
 
 
 class E4bStack(ctypes.Structure):

@@ -19,7 +19,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // (arXiv:2305.14314, appendix "NormalFloat 4-bit data type"). FP4: e2m1
 // magnitudes {0,.5,1,1.5,2,3,4,6}/6, bit 3 = sign (code 8 = -0.0). Row 2
 // (BF16) has no table. MXFP4: the unscaled E2M1 values (OCP MX v1.0).
-__constant__ static const uint32_t kCodebookBits[4][16] = {
+// Usable from host and device code.
+static constexpr uint32_t kCodebookBits[4][16] = {
     {0xBF800000u, 0xBF3239B1u, 0xBF066B30u, 0xBECA32A0u, 0xBE91A24Du, 0xBE3D353Fu,
      0xBDBA7871u, 0x00000000u, 0x3DA2FAFFu, 0x3E24CAE3u, 0x3E7C04DDu, 0x3EAD033Au,
      0x3EE1A4B8u, 0x3F1007ABu, 0x3F3913B3u, 0x3F800000u},

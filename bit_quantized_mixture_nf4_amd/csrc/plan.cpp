@@ -127,7 +127,7 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   // forward region
   p->off_a = take(size_t(P) * I * 2);
   p->off_o = take(size_t(P) * H * 2);
-  p->off_dmap = T <= kDecodeMaxT ? take(16 + size_t(busy) * size_t(H / 16 + I / 16) * 16) : 0;
+  p->off_dmap = T <= kDecodeMaxT ? take(kDecPlanBytes) : 0;
   // the MX forward's activation rows (MXFP4 layers): x and a as E4M3 codes + E8M0 scales
   const bool mx = p->codebook == E4B_CB_MXFP4;
   p->off_mx_xq = mx ? take(size_t(T) * H) : 0;
@@ -236,7 +236,7 @@ extern "C" const char *e4b_status_string(e4b_status s) {
     case E4B_ERR_DTYPE: return "unknown output dtype";
     case E4B_ERR_WORKSPACE: return "workspace missing or too small";
     case E4B_ERR_ALIGN: return "device buffer not 16-byte aligned";
-    case E4B_ERR_PATH: return "invalid path (decode path needs a gated 4-bit layer, T <= 8, saved == NULL and max(H, I) <= 4096)";
+    case E4B_ERR_PATH: return "invalid path (decode path needs a gated 4-bit layer, T <= 8, saved == NULL and max(H, I) <= 16384)";
     case E4B_ERR_HIP: return "HIP kernel launch failed";
   }
   return "unknown status";

@@ -30,7 +30,8 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kDecodeMaxT = 8;
 constexpr int kDecMaxPairs = kDecodeMaxT * kMaxTopK;
-constexpr int kDecodeMaxK = 4096;  // max(H, I) on the decode path
+constexpr int kDecodeMaxK = 16384; // max(H, I) on the decode path
+constexpr size_t kDecPlanBytes = 5376;  // decode: the grouping the gate_up launch leaves for the down launch
 constexpr int kLoraK = 16;         // LoRA rank slot: one 16-deep MFMA slice (r <= 16)
 
 struct MoePlan {
@@ -51,7 +52,7 @@ struct MoePlan {
   size_t off_sorted, off_pos;
   size_t off_tile_map;  // int4 per m-tile: expert, segment start, first row, rows
   size_t off_a, off_o;                          // forward
-  size_t off_dmap;                              // forward, decode path: work maps
+  size_t off_dmap;  // forward, decode path: the grouping the gate_up launch leaves for the down launch
   size_t off_mx_xq, off_mx_xs, off_mx_aq, off_mx_as;  // forward, MX path (MXFP4 layers)
   size_t off_gu, off_dgu, off_partial, off_gx;  // dgrad
   size_t ws_bytes;

@@ -61,7 +61,7 @@ typedef enum {
   E4B_ERR_DTYPE = 5,     /* unknown output dtype */
   E4B_ERR_WORKSPACE = 6, /* workspace NULL or smaller than e4b_moe_workspace_bytes() */
   E4B_ERR_ALIGN = 7,     /* a device buffer is not 16-byte aligned */
-  E4B_ERR_PATH = 8,      /* unknown path, or the decode path was asked for but does not apply (a BF16 layer, T > 8, saved != NULL, or max(H, I) above 4096) */
+  E4B_ERR_PATH = 8,      /* unknown path, or the decode path was asked for but does not apply (a BF16 layer, T > 8, saved != NULL, or max(H, I) above 16384) */
   E4B_ERR_HIP = 9        /* a kernel launch failed (hipGetLastError after the launch) */
 } e4b_status;
 
@@ -331,14 +331,13 @@ typedef enum {
   E4B_K_DOWN_FWD = 1,      /* grouped down GEMM (MX path: its MX GEMM) */
   E4B_K_DOWN_DGRAD = 2,    /* grouped GEMM on W_dn^T + SiLU-backward epilogue */
   E4B_K_GATE_UP_DGRAD = 3, /* grouped GEMM on W_gu^T */
-  E4B_K_DECODE_GATE_UP = 4,/* decode dequant-GEMV, gate_up + SiLU*up */
+  E4B_K_DECODE_GATE_UP = 4,/* decode dequant-GEMV, gate_up + SiLU*up (routes and groups the pairs too) */
   E4B_K_DECODE_DOWN = 5,   /* decode dequant-GEMV, down (+ the weighted combine) */
   E4B_K_ROUTE = 6,         /* top-k routing from logits */
   E4B_K_PERMUTE = 7,       /* the permutation (the first of its kernels to the last) */
   E4B_K_COMBINE = 8,       /* forward gather-combine */
   E4B_K_COMBINE_DGRAD = 9, /* dgrad gather-combine + routing-weight gradient */
-  E4B_K_DECODE_PREP = 10,  /* decode grouping (and routing) */
-  E4B_K_COUNT = 11
+  E4B_K_COUNT = 10
 } e4b_kernel;
 
 /* Per-call kernel timing. For every kernel id whose start and stop events

@@ -107,8 +107,8 @@ def test_forward_and_dgrad_argument_errors():
     assert _fwd(L, path=3) == _lib.E4B_ERR_PATH
     assert _fwd(L, T=9, path=2) == _lib.E4B_ERR_PATH  # decode path needs T <= 8
     assert _fwd(L, T=4, path=2, saved=FAKE) == _lib.E4B_ERR_PATH
-    big = _layer(E=4, H=8192, I=64)
-    assert _fwd(big, T=8, path=2) == _lib.E4B_ERR_PATH  # staging would exceed 64 KiB
+    big = _layer(E=4, H=32768, I=64)
+    assert _fwd(big, T=8, path=2) == _lib.E4B_ERR_PATH  # decode path needs max(H, I) <= 16384
     assert _dgrad(L, gy=None) == _lib.E4B_ERR_NULL
     assert _dgrad(L, x=None, saved=None) == _lib.E4B_ERR_NULL
     assert _dgrad(L, ws_bytes=need - 1) == _lib.E4B_ERR_WORKSPACE

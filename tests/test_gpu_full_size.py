@@ -39,13 +39,15 @@ def _layer(cfg, seed, kind):
     return e4b.MoELayer(*stacks)
 
 
-def _oracle_experts(cfg, seed, kind, layer):
+def _oracle_experts(cfg, seed, kind, layer, experts=None):
     """Yields (e, W_gu[e], W_dn[e]) as the oracle stores them (fp32 dequantized),
     after checking the GPU's stored bytes and dequantized weights of expert e
-    against the oracle's bit for bit."""
+    against the oracle's bit for bit (every expert, or those in `experts`)."""
     host = {"gate_up": stack_bytes(layer.gate_up), "down": stack_bytes(layer.down)}
     t0 = time.time()
     for e in range(cfg.E):
+        if experts is not None and e not in experts:
+            continue
         if e % max(1, cfg.E // 8) == 0:
             announce(f"  oracle expert {e}/{cfg.E} ({time.time() - t0:.0f} s)")
         out = []
@@ -65,14 +67,16 @@ def _oracle_experts(cfg, seed, kind, layer):
         yield e, out[0], out[1]
 
 
-def _oracle_whole(cfg, seed, kind, layer, x, gy, idx, w):
-    """Whole y, grad_x [T, H] and grad_topk_w [T, k] from the oracle, run one expert at a time."""
+def _oracle_whole(cfg, seed, kind, layer, x, gy, idx, w, routed_only=False):
+    """Whole y, grad_x [T, H] and grad_topk_w [T, k] from the oracle, run one expert at a time
+    (with routed_only, the experts without tokens are skipped)."""
     T, H, k = cfg.T, cfg.H, cfg.k
     y = np.zeros((T, H))
     gx = np.zeros((T, H)) if gy is not None else None
     gw = np.zeros((T, k)) if gy is not None else None
     t0 = time.time()
-    for e, wgu, wdn in _oracle_experts(cfg, seed, kind, layer):
+    only = set(np.unique(idx).tolist()) if routed_only else None
+    for e, wgu, wdn in _oracle_experts(cfg, seed, kind, layer, only):
         t, j = routed_pairs(idx, e)
         if t.size == 0:
             continue
@@ -161,11 +165,11 @@ def test_mixtral_fidelity_ordering_from_gpu_outputs():
     assert rw["bf16"] < rw["nf4"] < rw["fp4"], rw
 
 
-@pytest.mark.parametrize("T", [1, 8])
-def test_decode_full_size(T):
-    cfg = get_config("qwen3_decode", T)
+@pytest.mark.parametrize("name,T", [("qwen3_decode", 1), ("qwen3_decode", 8), ("mixtral", 1), ("mixtral", 8)])
+def test_decode_full_size(name, T):
+    cfg = get_config(name, T)
     seed = 0
-    announce(f"qwen3 decode full size T={T}")
+    announce(f"{name} decode full size E{cfg.E} H{cfg.H} I{cfg.I} k{cfg.k} T={T}")
     layer = _layer(cfg, seed, "nf4")
     x = gen_x(cfg, seed)
     lg = gen_logits(cfg, seed)
@@ -174,7 +178,7 @@ def test_decode_full_size(T):
     idx_ref, w_ref = oracle.route(lg, cfg.k)
     assert np.array_equal(idx.cpu().numpy(), idx_ref)
     assert np.max(np.abs(w.cpu().numpy() - w_ref)) <= 1e-6
-    y_ref, _, _ = _oracle_whole(cfg, seed, "nf4", layer, x, None, idx_ref, w_ref)
+    y_ref, _, _ = _oracle_whole(cfg, seed, "nf4", layer, x, None, idx_ref, w_ref, routed_only=True)
     tol_check(to_np(y), y_ref, f"decode T={T} y")
     yg, _, _, _ = e4b.moe_forward(layer, bf16_tensor(x), cfg.k, topk_idx=idx, topk_w=w, path="grouped")
     tol_check(to_np(yg), y_ref, f"grouped T={T} y")

@@ -276,8 +276,8 @@ def test_single_expert_top1_is_dense_swiglu():
 def _decode_case(cfg, idx, seed=1, kind="nf4", path="decode"):
     """One forward path vs the oracle with given routing ids (weights drawn here)."""
     T, k = idx.shape
-    # ids are a precondition the kernels do not check: in range, distinct per token
-    assert idx.min() >= 0 and idx.max() < cfg.E and all(len(set(r)) == k for r in idx.tolist())
+    # ids in range are a precondition the kernels do not check
+    assert idx.min() >= 0 and idx.max() < cfg.E
     pb = Problem(cfg, seed=seed, codebook=kind, with_grad=False)
     w = np.random.default_rng(seed).random((T, k)).astype(np.float32) + 0.1
     idx_d = torch.from_numpy(np.ascontiguousarray(idx, np.int32)).to(DEV)
@@ -296,7 +296,8 @@ def test_decode_all_tokens_share_experts(kind):
 
 
 def test_decode_mixed_token_counts():
-    """Experts with 1, 2, 3, 5 and 8 tokens in one call (every bucket of the GEMV)."""
+    """Experts with 1, 2, 3, 5 and 8 tokens in one call (every vector bucket of the
+    GEMV, and experts with more pairs than one pass takes)."""
     cfg = MoEConfig("mixed", E=32, H=1024, I=512, k=4, T=8, routing="normal")
     announce("decode mixed counts E32 H1024 I512 k4 T8")
     idx = np.zeros((8, 4), np.int32)
@@ -306,12 +307,23 @@ def test_decode_mixed_token_counts():
     _decode_case(cfg, idx)
 
 
+@pytest.mark.parametrize("H,I", [(16384, 64), (64, 16384)])
 @pytest.mark.parametrize("path", ["decode", "grouped"])
-def test_longest_and_shortest_rows(path):
-    """in_features 4096 (the decode limit: 16 bytes per lane) and 64 (one block)."""
-    cfg = MoEConfig("long", E=4, H=4096, I=64, k=2, T=5, routing="normal")
-    announce(f"{path} long rows E4 H4096 I64 k2 T5")
+def test_longest_and_shortest_rows(path, H, I):
+    """in_features 16384 (the decode limit) and 64 (one block), on either projection."""
+    cfg = MoEConfig("long", E=4, H=H, I=I, k=2, T=5, routing="normal")
+    announce(f"{path} long rows E4 H{H} I{I} k2 T5")
     idx = np.array([[0, 1], [1, 2], [3, 0], [2, 3], [0, 2]], np.int32)
+    _decode_case(cfg, idx, path=path)
+
+
+@pytest.mark.parametrize("path", ["decode", "grouped"])
+def test_expert_repeated_within_tokens(path):
+    """Given ids may repeat an expert within a token: each slot is its own pair
+    (here 16 pairs on expert 5, more than one GEMV pass takes, and 3 on 1)."""
+    cfg = MoEConfig("repeat", E=8, H=512, I=320, k=3, T=8, routing="normal")
+    announce(f"{path} repeated experts E8 H512 I320 k3 T8")
+    idx = np.array([[5, 5, t % 3] for t in range(8)], np.int32)
     _decode_case(cfg, idx, path=path)
 
 
