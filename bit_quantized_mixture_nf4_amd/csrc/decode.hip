@@ -28,15 +28,14 @@
 namespace e4b {
 
 constexpr int kDecThreads = 256;
-constexpr int kTblCopies = 32;   // LDS table copies: the lanes of a half-wave read distinct banks
-constexpr int kDecVec = 4;       // input vectors per GEMV pass (more pairs of an expert: passes of 4)
-constexpr int kRows = 4;         // weight rows per workgroup block (both launches)
-constexpr int kGuUnits = kRows / 2;  // gate_up: units per block (a gate row and an up row each)
-constexpr int kDnRows = kRows;       // down: rows of H per block
+constexpr int kTblCopies = 32;   // LDS table copies (lane l reads copy l % kTblCopies)
+constexpr int kDecVec = 2;       // input vectors per GEMV pass (more pairs of an expert: passes of 2)
+constexpr int kGuRows = 2;       // gate_up: weight rows per workgroup block (one unit's gate and up rows)
+constexpr int kGuUnits = kGuRows / 2;
+constexpr int kDnRows = 4;       // down: rows of H per workgroup block
 constexpr int kPartFloats = 2048;    // LDS partial sums: K parts x pairs x rows
 constexpr int kDecWgPerCu = 3;       // resident workgroups per CU the launch grid is sized for
 constexpr int kRouteWaves = kDecThreads / 64;
-constexpr int kMulti = 2;            // single-pair items a lane group keeps in flight at once
 
 // The grouping that the gate_up launch leaves in the workspace.
 struct DecodePlan {
@@ -95,22 +94,30 @@ struct DecCodebook {
 // the element order in memory (the even element sits in the high nibble).
 // Entry (byte, copy) at byte * kTblCopies + copy. The copies of a byte are
 // equal: thread tid writes four with each 16-byte store u = tid + 256 i
-// (i < 8), whose byte u / 8 has the low nibble q = (tid >> 3) & 15 and the
-// high nibble 2 i + (tid >> 7). The low nibble's value is picked from the
-// pairs by a select tree on q's bits (no register array indexed at run time).
+// (i < kTblCopies / 4), whose byte is u >> S (S = log2(kTblCopies / 4)):
+// low nibble (tid >> S) & 15, high nibble i * (256 >> (S + 4)) + (tid >> (S +
+// 4)). Values are picked from the pairs by select trees on those bits (no
+// register array indexed at run time).
 __device__ __forceinline__ void fill_code_table(uint32_t *tbl, const DecCodebook &cb) {
-  static_assert(kTblCopies == 32 && kDecThreads == 256, "fill layout");
+  static_assert((kTblCopies == 16 || kTblCopies == 32) && kDecThreads == 256, "fill layout");
+  constexpr int S = kTblCopies == 32 ? 3 : 2;
   const int tid = threadIdx.x;
-  const uint32_t q = (tid >> 3) & 15;
+  const uint32_t q = (tid >> S) & 15;
   const uint32_t a0 = (q & 2) ? cb.pair[1] : cb.pair[0], a1 = (q & 2) ? cb.pair[3] : cb.pair[2];
   const uint32_t a2 = (q & 2) ? cb.pair[5] : cb.pair[4], a3 = (q & 2) ? cb.pair[7] : cb.pair[6];
   const uint32_t b0 = (q & 4) ? a1 : a0, b1 = (q & 4) ? a3 : a2;
   const uint32_t c = (q & 8) ? b1 : b0;
   const uint32_t lo = (q & 1) ? (c >> 16) : (c & 0xFFFFu);
-  const bool odd = tid >> 7;
+  const uint32_t t = tid >> (S + 4);  // high nibble within the store's group of codes
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t hi = odd ? (cb.pair[i] >> 16) : (cb.pair[i] & 0xFFFFu);
+  for (int i = 0; i < kTblCopies / 4; ++i) {
+    uint32_t pr;
+    if constexpr (kTblCopies == 32) {
+      pr = cb.pair[i];  // codes 2 i, 2 i + 1
+    } else {
+      pr = (t & 2) ? cb.pair[2 * i + 1] : cb.pair[2 * i];  // codes 4 i .. 4 i + 3
+    }
+    const uint32_t hi = (t & 1) ? (pr >> 16) : (pr & 0xFFFFu);
     const uint32_t v = hi | (lo << 16);
     reinterpret_cast<u32x4 *>(tbl)[tid + kDecThreads * i] = u32x4{v, v, v, v};
   }
@@ -132,14 +139,12 @@ __host__ __device__ inline int lanes_per_row(int K) {
   return cpr > 32 ? 64 : (cpr > 16 ? 32 : (cpr > 8 ? 16 : (cpr > 4 ? 8 : 4)));
 }
 
-// The grouping every workgroup reads: distinct experts d < n (ascending id),
-// their first sorted position first[d] (first[n] = P), and per sorted
-// position s the row of its input vector.
+// The grouping every workgroup reads: distinct experts d < n (ascending id)
+// and their first sorted position first[d] (first[n] = P).
 struct DecodeGroups {
   int32_t n;
   int32_t expert[kDecMaxPairs];
   int32_t first[kDecMaxPairs + 1];
-  int32_t vrow[kDecMaxPairs];  // gate_up: the pair's token; down: s itself
 };
 
 // Weights of one projection stack.
@@ -150,213 +155,205 @@ struct DecStack {
   int64_t e_bytes, e_blocks;
 };
 
-// One item: kRows weight rows of expert e (tile row r is weight row
-// row_of(r), or none when row_of(r) < 0) against np <= NPB input vectors
-// (vector q at vin + vrow(q) * K), over the chunks [c_lo, c_hi); the LPR lanes
-// of a group take the chunks c_lo + li, c_lo + li + LPR, .... Lane 0 of the
-// group writes the sums of its K part: part_out[q * part_stride + r].
-template <int LPR, int NPB, bool MX, typename RowOf, typename VRow>
-__device__ __forceinline__ void gemv_item(const DecStack &W, int e, int K, RowOf row_of, int np,
-                                          const uint16_t *__restrict__ vin, VRow vrow, int c_lo, int c_hi,
-                                          int li, const uint32_t *tl, float *part_out, int part_stride) {
+// The operands of one step: ROWS weight rows' 16 code bytes of chunk c and
+// their block scales, and the chunk of up to kDecVec input vectors.
+template <int ROWS>
+struct WChunk {
+  u32x4 cw[ROWS];
+  float sc[ROWS];
+  u32x4 xv[kDecVec][4];
+};
+
+template <int ROWS, bool MX>
+__device__ __forceinline__ void load_wchunk(const DecStack &W, int e, int K, const int64_t (&wrow)[ROWS], int c,
+                                            const uint16_t *__restrict__ vin, const int64_t (&vr)[kDecVec], int np,
+                                            WChunk<ROWS> &o) {
   const uint8_t *wp = W.packed + int64_t(e) * W.e_bytes;
-  const int CPR = K >> 5;
   const int64_t row_bytes = K >> 1;
-  int64_t wrow[kRows];
+  const int CPR = K >> 5;
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) {
-    const int w = row_of(r);
-    wrow[r] = w < 0 ? 0 : w;  // a row without weights reads row 0; its sum is not kept
-  }
-  int64_t vr[NPB];
-#pragma unroll
-  for (int q = 0; q < NPB; ++q) vr[q] = int64_t(vrow(q < np ? q : 0)) * K;
-  float part[kRows][NPB];
-#pragma unroll
-  for (int r = 0; r < kRows; ++r)
-#pragma unroll
-    for (int q = 0; q < NPB; ++q) part[r][q] = 0.0f;
-  for (int c = c_lo + li; c < c_hi; c += LPR) {
-    u32x4 cw[kRows];
-    float sc[kRows];
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      cw[r] = *reinterpret_cast<const u32x4 *>(wp + wrow[r] * row_bytes + c * 16);
-      sc[r] = MX ? e8m0_value(W.scales[int64_t(e) * W.e_blocks + wrow[r] * CPR + c])
+  for (int r = 0; r < ROWS; ++r) {
+    o.cw[r] = *reinterpret_cast<const u32x4 *>(wp + wrow[r] * row_bytes + c * 16);
+    o.sc[r] = MX ? e8m0_value(W.scales[int64_t(e) * W.e_blocks + wrow[r] * CPR + c])
                  : W.absmax[int64_t(e) * W.e_blocks + wrow[r] * (K >> 6) + (c >> 1)];
-    }
-    u32x4 xv[NPB][4];
-#pragma unroll
-    for (int q = 0; q < NPB; ++q) {
-      const u32x4 *src = reinterpret_cast<const u32x4 *>(vin + vr[q] + c * 32);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xv[q][i] = q < np ? src[i] : u32x4{0u, 0u, 0u, 0u};
-    }
-    // a row's 16 lookups are issued together, the next row's under this
-    // row's products (the scheduler would otherwise wait on each lookup)
-    uint32_t v[2][16];
-    lookup_chunk(tl, cw[0], v[0]);
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      if (r + 1 < kRows) lookup_chunk(tl, cw[r + 1], v[(r + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < NPB; ++q) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc = dot2_bf16(v[r & 1][i], xv[q][i >> 2][i & 3], acc);
-        part[r][q] += acc * sc[r];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
   }
 #pragma unroll
-  for (int r = 0; r < kRows; ++r)
+  for (int q = 0; q < kDecVec; ++q) {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(vin + vr[q] + c * 32);
 #pragma unroll
-    for (int q = 0; q < NPB; ++q) part[r][q] = group_sum<LPR>(part[r][q]);
-  if (li == 0) {
-#pragma unroll
-    for (int r = 0; r < kRows; ++r)
-#pragma unroll
-      for (int q = 0; q < NPB; ++q)
-        if (q < np) part_out[q * part_stride + r] = part[r][q];
+    for (int i = 0; i < 4; ++i) o.xv[q][i] = q < np ? src[i] : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
 // K parts per expert: the groups of a workgroup split one expert's chunks
 // when there are fewer experts than groups (a power of two, at least one
 // chunk per lane, and the partial sums fit kPartFloats).
+template <int ROWS>
 __device__ __forceinline__ int k_parts(int n, int P, int groups, int cpr, int lpr) {
   int kp = 1;
-  while (2 * kp * n <= groups && 2 * kp * lpr <= cpr && 2 * kp * P * kRows <= kPartFloats) kp *= 2;
+  while (2 * kp * n <= groups && 2 * kp * lpr <= cpr && 2 * kp * P * ROWS <= kPartFloats) kp *= 2;
   return kp;
 }
 
-// NI items of experts with a single pair each, over the same chunks [c_lo,
-// c_hi): all their weight and input loads are issued before any product, so a
-// lane keeps NI items' bytes in flight (the common case at small T, where an
-// expert serves one token). Item j: expert e[j], input vector row vr[j], sums
-// to out[j][r].
-template <int LPR, int NI, bool MX, typename RowOf>
-__device__ __forceinline__ void gemv_multi(const DecStack &W, const int (&e)[4], int K, RowOf row_of,
-                                           const uint16_t *__restrict__ vin, const int (&vr)[4], int c_lo,
-                                           int c_hi, int li, const uint32_t *tl, float *const (&out)[4]) {
-  const int CPR = K >> 5;
-  const int64_t row_bytes = K >> 1;
-  int64_t wrow[kRows];
+// A lane group's position in its work: item i (expert d = i >> kps, K part
+// kp = i & (KP - 1), KP = 1 << kps), the pass over the expert's pairs
+// starting at pair q0 (passes of kDecVec), and the step j over the part's
+// chunks (the lane's chunk c_lo + li + j * LPR).
+struct DecCursor {
+  int i, q0, j;
+};
+
+struct DecItem {
+  int e, s0, cnt, c_lo, c_hi, steps;
+};
+
+template <int LPR>
+__device__ __forceinline__ DecItem dec_item(const DecodeGroups &G, int i, int kps, int CPR) {
+  const int d = i >> kps, kp = i & ((1 << kps) - 1);
+  DecItem it;
+  it.e = G.expert[d];
+  it.s0 = G.first[d];
+  it.cnt = G.first[d + 1] - it.s0;
+  it.c_lo = (kp * CPR) >> kps;
+  it.c_hi = ((kp + 1) * CPR) >> kps;
+  it.steps = (it.c_hi - it.c_lo + LPR - 1) / LPR;
+  return it;
+}
+
+// Input vector rows (times K) of the pairs q0 .. q0 + np - 1 of item it.
+template <typename VRow>
+__device__ __forceinline__ void vec_rows(const DecItem &it, int q0, int K, VRow vrow, int64_t (&vr)[kDecVec],
+                                         int &np) {
+  np = min(kDecVec, it.cnt - q0);
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) {
-    const int w = row_of(r);
-    wrow[r] = w < 0 ? 0 : w;  // a row without weights reads row 0; its sum is not kept
-  }
-  float part[NI][kRows];
+  for (int q = 0; q < kDecVec; ++q) vr[q] = int64_t(vrow(it.s0 + q0 + (q < np ? q : 0))) * K;
+}
+
+// One pass (item it, pairs q0 .. q0 + np - 1, np <= NPB) over all of its
+// steps. The operands of the current step arrive in w (loaded one step
+// ahead); each step first issues the loads of the cursor's next step (the
+// next chunk, or the first chunk of the next pass or item) into w, then
+// computes. Lane 0 of the group writes the pass's sums of its K part:
+// part_out[q * ROWS + r].
+template <int LPR, int ROWS, int NPB, bool MX, typename VRow>
+__device__ __forceinline__ void gemv_pass(const DecStack &W, int K, const int64_t (&wrow)[ROWS],
+                                          const DecodeGroups &G, int kps, int total, int CPR, const DecItem &it,
+                                          DecCursor &cur, WChunk<ROWS> &w, int np,
+                                          const uint16_t *__restrict__ vin, VRow vrow, int li, const uint32_t *tl,
+                                          float *part_out) {
+  constexpr int kGroups = kDecThreads / LPR;
+  float part[ROWS][NPB];
 #pragma unroll
-  for (int j = 0; j < NI; ++j)
+  for (int r = 0; r < ROWS; ++r)
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) part[j][r] = 0.0f;
-  for (int c = c_lo + li; c < c_hi; c += LPR) {
-    u32x4 cw[NI][kRows];
-    float sc[NI][kRows];
-    u32x4 xv[NI][4];
+    for (int q = 0; q < NPB; ++q) part[r][q] = 0.0f;
+  for (int j = 0; j < it.steps; ++j) {
+    const bool valid = it.c_lo + li + j * LPR < it.c_hi;
+    // the next step's operands
+    DecCursor nx = cur;
+    if (j + 1 < it.steps) {
+      nx.j = j + 1;
+    } else if (cur.q0 + kDecVec < it.cnt) {
+      nx.q0 = cur.q0 + kDecVec;
+      nx.j = 0;
+    } else {
+      nx.i = cur.i + kGroups;
+      nx.q0 = 0;
+      nx.j = 0;
+    }
+    const WChunk<ROWS> cw = w;
+    if (nx.i < total) {
+      const DecItem ni = nx.i == cur.i ? it : dec_item<LPR>(G, nx.i, kps, CPR);
+      const int cn = ni.c_lo + li + nx.j * LPR;
+      int64_t vr[kDecVec];
+      int nnp;
+      vec_rows(ni, nx.q0, K, vrow, vr, nnp);
+      load_wchunk<ROWS, MX>(W, ni.e, K, wrow, cn < ni.c_hi ? cn : ni.c_lo, vin, vr, nnp, w);
+    }
+    if (valid) {
+      // a row's 16 lookups are issued together, the next row's under this
+      // row's products (the scheduler would otherwise wait on each lookup)
+      uint32_t v[2][16];
+      lookup_chunk(tl, cw.cw[0], v[0]);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      const uint8_t *wp = W.packed + int64_t(e[j]) * W.e_bytes;
+      for (int r = 0; r < ROWS; ++r) {
+        if (r + 1 < ROWS) lookup_chunk(tl, cw.cw[r + 1], v[(r + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) {
-        cw[j][r] = *reinterpret_cast<const u32x4 *>(wp + wrow[r] * row_bytes + c * 16);
-        sc[j][r] = MX ? e8m0_value(W.scales[int64_t(e[j]) * W.e_blocks + wrow[r] * CPR + c])
-                      : W.absmax[int64_t(e[j]) * W.e_blocks + wrow[r] * (K >> 6) + (c >> 1)];
+        for (int q = 0; q < NPB; ++q) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc = dot2_bf16(v[r & 1][i], cw.xv[q][i >> 2][i & 3], acc);
+          part[r][q] += acc * cw.sc[r];
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const u32x4 *src = reinterpret_cast<const u32x4 *>(vin + int64_t(vr[j]) * K + c * 32);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xv[j][i] = src[i];
     }
-    // the lookups of the next (item, row) are issued under this one's products
-    uint32_t v[2][16];
-    lookup_chunk(tl, cw[0][0], v[0]);
-#pragma unroll
-    for (int jr = 0; jr < NI * kRows; ++jr) {
-      const int j = jr / kRows, r = jr % kRows;
-      if (jr + 1 < NI * kRows) lookup_chunk(tl, cw[(jr + 1) / kRows][(jr + 1) % kRows], v[(jr + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      float acc = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc = dot2_bf16(v[jr & 1][i], xv[j][i >> 2][i & 3], acc);
-      part[j][r] += acc * sc[j][r];
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    if (j + 1 == it.steps) cur = nx;
   }
 #pragma unroll
-  for (int j = 0; j < NI; ++j)
+  for (int r = 0; r < ROWS; ++r)
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) part[j][r] = group_sum<LPR>(part[j][r]);
+    for (int q = 0; q < NPB; ++q) part[r][q] = group_sum<LPR>(part[r][q]);
   if (li == 0) {
 #pragma unroll
-    for (int j = 0; j < NI; ++j)
+    for (int r = 0; r < ROWS; ++r)
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) out[j][r] = part[j][r];
+      for (int q = 0; q < NPB; ++q)
+        if (q < np) part_out[q * ROWS + r] = part[r][q];
   }
 }
 
-// The block's GEMV for every distinct expert: items (expert d, K part kp),
-// item i to lane group i % groups. Partial sums go to
-// part[(kp * P + s) * kRows + r] for sorted position s and tile row r. Runs
-// of up to four items of a group whose experts have one pair go through
-// gemv_multi; the others one at a time, their pairs in passes of kDecVec.
-template <int LPR, bool MX, typename RowOf>
+// The block's GEMV for every distinct expert: ROWS weight rows (tile row r is
+// weight row row_of(r), or none when row_of(r) < 0) of each expert against
+// its pairs' input vectors (pair at sorted position s: vin + vrow(s) * K).
+// Items (expert d, K part kp) go to lane group i % groups; each group walks
+// its items, passes and chunk steps with the next step's operands in flight.
+// Partial sums go to part[(kp * P + s) * ROWS + r].
+template <int LPR, int ROWS, bool MX, typename RowOf, typename VRow>
 __device__ __forceinline__ void gemv_block(const DecStack &W, int K, int P, const DecodeGroups &G, RowOf row_of,
-                                           const uint16_t *__restrict__ vin, const uint32_t *tbl, float *part,
-                                           int KP) {
-  constexpr int kGroups = kDecThreads / LPR;
+                                           const uint16_t *__restrict__ vin, VRow vrow, const uint32_t *tbl,
+                                           float *part, int KP) {
   const int tid = threadIdx.x, g = tid / LPR, li = tid % LPR;
   const int CPR = K >> 5;
   const int total = G.n * KP;
+  const int kps = __builtin_ctz(KP);
   const uint32_t *tl = tbl + (tid & (kTblCopies - 1));
-  int i = g;
-  while (i < total) {
-    // kGroups is a multiple of KP: the items i + j * kGroups share i's K part
-    const int kp = i % KP;
-    const int c_lo = kp * CPR / KP, c_hi = (kp + 1) * CPR / KP;
-    int e[4], vr[4], m = 0;
-    float *out[4];
-    bool run = true;
+  int64_t wrow[ROWS];
 #pragma unroll
-    for (int j = 0; j < kMulti; ++j) {
-      const int it = i + j * kGroups;
-      const int d = it / KP;
-      run = run && it < total && G.first[d + 1] - G.first[d] == 1;
-      const int s = run ? G.first[d] : 0;
-      e[j] = run ? G.expert[d] : 0;
-      vr[j] = run ? G.vrow[s] : 0;
-      out[j] = part + (kp * P + s) * kRows;
-      m += run;
-    }
-    if (m > 0) {
-      if (m == 1) gemv_multi<LPR, 1, MX>(W, e, K, row_of, vin, vr, c_lo, c_hi, li, tl, out);
-      else if (m == 2) gemv_multi<LPR, 2, MX>(W, e, K, row_of, vin, vr, c_lo, c_hi, li, tl, out);
-      else gemv_multi<LPR, 2, MX>(W, e, K, row_of, vin, vr, c_lo, c_hi, li, tl, out);
-      i += m * kGroups;
-      continue;
-    }
-    const int d = i / KP;
-    const int s0 = G.first[d], cnt = G.first[d + 1] - s0, ex = G.expert[d];
-    for (int q0 = 0; q0 < cnt; q0 += kDecVec) {
-      const int np = min(kDecVec, cnt - q0);
-      auto vrow = [&](int q) { return G.vrow[s0 + q0 + q]; };
-      float *o = part + (kp * P + s0 + q0) * kRows;
-      static_assert(kDecVec == 4, "buckets 1, 2, 4");
-      if (np <= 1) gemv_item<LPR, 1, MX>(W, ex, K, row_of, np, vin, vrow, c_lo, c_hi, li, tl, o, kRows);
-      else if (np <= 2) gemv_item<LPR, 2, MX>(W, ex, K, row_of, np, vin, vrow, c_lo, c_hi, li, tl, o, kRows);
-      else gemv_item<LPR, 4, MX>(W, ex, K, row_of, np, vin, vrow, c_lo, c_hi, li, tl, o, kRows);
-    }
-    i += kGroups;
+  for (int r = 0; r < ROWS; ++r) {
+    const int w = row_of(r);
+    wrow[r] = w < 0 ? 0 : w;  // a row without weights reads row 0; its sum is not kept
+  }
+  DecCursor cur{g, 0, 0};
+  if (cur.i >= total) return;
+  WChunk<ROWS> w;
+  {
+    const DecItem it = dec_item<LPR>(G, cur.i, kps, CPR);
+    const int c = it.c_lo + li;
+    int64_t vr[kDecVec];
+    int np;
+    vec_rows(it, 0, K, vrow, vr, np);
+    load_wchunk<ROWS, MX>(W, it.e, K, wrow, c < it.c_hi ? c : it.c_lo, vin, vr, np, w);
+  }
+  while (cur.i < total) {
+    const DecItem it = dec_item<LPR>(G, cur.i, kps, CPR);
+    const int kp = cur.i & (KP - 1);
+    const int np = min(kDecVec, it.cnt - cur.q0);
+    float *out = part + (kp * P + it.s0 + cur.q0) * ROWS;
+    static_assert(kDecVec == 2, "buckets 1, 2");
+    if (np <= 1)
+      gemv_pass<LPR, ROWS, 1, MX>(W, K, wrow, G, kps, total, CPR, it, cur, w, np, vin, vrow, li, tl, out);
+    else
+      gemv_pass<LPR, ROWS, 2, MX>(W, K, wrow, G, kps, total, CPR, it, cur, w, np, vin, vrow, li, tl, out);
   }
 }
 
 // Sum of the K parts of sorted position s, tile row r (fixed order).
+template <int ROWS>
 __device__ __forceinline__ float part_sum(const float *part, int KP, int P, int s, int r) {
-  float v = part[s * kRows + r];
-  for (int kp = 1; kp < KP; ++kp) v += part[(kp * P + s) * kRows + r];
+  float v = part[s * ROWS + r];
+  for (int kp = 1; kp < KP; ++kp) v += part[(kp * P + s) * ROWS + r];
   return v;
 }
 
@@ -366,6 +363,7 @@ __device__ __forceinline__ float part_sum(const float *part, int KP, int P, int 
 struct DecodeGuLds {
   uint32_t tbl[256 * kTblCopies];
   DecodeGroups groups;
+  int32_t vrow[kDecMaxPairs];  // the token of the pair at each sorted position
   int32_t idx[kDecMaxPairs];  // routed expert of flat pair t * k + j
   float w[kDecMaxPairs];      // its weight
   int32_t sp[kDecMaxPairs];   // pair at sorted position
@@ -411,7 +409,7 @@ __device__ __forceinline__ void decode_group(const float *__restrict__ logits, i
     L.sp[pos] = p;
     L.se[pos] = key / kDecMaxPairs;
     L.pos[p] = pos;
-    L.groups.vrow[pos] = p / k;
+    L.vrow[pos] = p / k;
   }
   __syncthreads();
   // distinct experts: sorted position p starts a segment
@@ -467,7 +465,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(kDe
     }
     __syncthreads();  // pos is read above; the partial sums share its space
   }
-  const int KP = k_parts(n, P, kDecThreads / LPR, H >> 5, LPR);
+  const int KP = k_parts<kGuRows>(n, P, kDecThreads / LPR, H >> 5, LPR);
   const int nblk = (I + kGuUnits - 1) / kGuUnits;
   for (int b = int(blockIdx.x); b < nblk; b += int(gridDim.x)) {
     const int u0 = b * kGuUnits;
@@ -476,12 +474,13 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(kDe
       const int u = u0 + (r % kGuUnits);
       return u < I ? (r < kGuUnits ? u : I + u) : -1;
     };
-    gemv_block<LPR, MX>(W, H, P, L.groups, row_of, x, L.tbl, L.part, KP);
+    gemv_block<LPR, kGuRows, MX>(W, H, P, L.groups, row_of, x, [&](int s) { return L.vrow[s]; }, L.tbl, L.part,
+                                 KP);
     __syncthreads();
     if (tid < P * kGuUnits) {
       const int s = tid / kGuUnits, i = tid % kGuUnits;
       if (u0 + i < I) {
-        const float g = part_sum(L.part, KP, P, s, i), u = part_sum(L.part, KP, P, s, kGuUnits + i);
+        const float g = part_sum<kGuRows>(L.part, KP, P, s, i), u = part_sum<kGuRows>(L.part, KP, P, s, kGuUnits + i);
         a[int64_t(s) * I + u0 + i] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
       }
     }
@@ -520,17 +519,16 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(kDe
     L.groups.first[n] = P;
   }
   if (pt) {
-    L.groups.vrow[tid] = tid;
     L.weight[tid] = wt;
     L.pos[tid] = ps;
   }
   __syncthreads();
-  const int KP = k_parts(n, P, kDecThreads / LPR, I >> 5, LPR);
+  const int KP = k_parts<kDnRows>(n, P, kDecThreads / LPR, I >> 5, LPR);
   const int nblk = (H + kDnRows - 1) / kDnRows;
   for (int b = int(blockIdx.x); b < nblk; b += int(gridDim.x)) {
     const int r0 = b * kDnRows;
     auto row_of = [&](int r) { return r0 + r < H ? r0 + r : -1; };
-    gemv_block<LPR, MX>(W, I, P, L.groups, row_of, a, L.tbl, L.part, KP);
+    gemv_block<LPR, kDnRows, MX>(W, I, P, L.groups, row_of, a, [](int s) { return s; }, L.tbl, L.part, KP);
     __syncthreads();
     // y rows of this block: each token's pairs in slot order
     if (tid < T * kDnRows) {
@@ -539,7 +537,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(kDe
         float acc = 0.0f;
         for (int j = 0; j < k; ++j) {
           const int s = L.pos[t * k + j];
-          acc += L.weight[s] * part_sum(L.part, KP, P, s, r);
+          acc += L.weight[s] * part_sum<kDnRows>(L.part, KP, P, s, r);
         }
         y[int64_t(t) * H + r0 + r] = f32_to_bf16(acc);
       }
@@ -551,7 +549,8 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(kDe
 hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
                                  const float *logits, int32_t *idx, float *wts, uint16_t *y,
                                  char *ws, hipStream_t s, const e4b_kernel_events *ev) {
-  static_assert(kDecMaxPairs * kRows <= kPartFloats, "one K part always fits");
+  static_assert(kDecMaxPairs * kGuRows <= kPartFloats && kDecMaxPairs * kDnRows <= kPartFloats,
+                "one K part always fits");
   DecodePlan *plan = reinterpret_cast<DecodePlan *>(ws + p.off_dmap);
   uint16_t *a = reinterpret_cast<uint16_t *>(ws + p.off_a);
   const int H = int(p.H), I = int(p.I), T = int(p.T), k = int(p.k), E = int(p.E);
