@@ -657,6 +657,8 @@ def main():
     ap.add_argument("--cpu-min-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only run the decode measurement and print its JSON object")
     ap.add_argument("--no-lora", action="store_true")
     ap.add_argument("--no-bf16-lane", action="store_true")
     ap.add_argument("--no-stream", action="store_true")
@@ -693,6 +695,9 @@ def main():
         return
     e4b.load()
     ev = HipEvents()
+    if args.decode_only:
+        print(json.dumps({"decode": bench_decode(args, e4b, torch, ev)}), flush=True)
+        return
     results = {k: bench_workload(args, e4b, torch, ev, k) for k in keys}
     head = results[keys[0]]
     olmoe_ms = results["olmoe_nf4"]["ms_per_step"] * 1e-3 if "olmoe_nf4" in results else None
