@@ -1,25 +1,26 @@
-// gemm_wide.hip -- grouped GEMM on 256 x 256 tiles with four waves of
-// 128 x 128: the gate_up and down forward projections and the gate_up dgrad.
+// gemm_wide.hip -- grouped GEMM on 256 x 256 tiles, software-pipelined inside
+// each wave: the gate_up and down forward projections and the gate_up dgrad.
 //
 // Same operation, operands, tile schedule and epilogues as the kernel in
 // gemm.hip (the grouped-nf4-gemm design of the 0.31.1 project page: one
 // launch over the packed stacks, the 4-bit weight decoded inside the GEMM,
 // fp32 accumulation); what differs is the work inside a workgroup:
 //
-// * One wave per SIMD holds 4 x 4 MFMA 32x32x16 bf16 tiles (256 fp32
-//   accumulators per lane). A K-step of 64 reads 128 KB of LDS fragments per
-//   workgroup for 256 MFMAs, a third less per MFMA than 64 x 128 waves.
-// * The K loop is software-pipelined inside each wave. While the 64 MFMAs of
+// * The launches use 8 waves of 64 x 128 (two per SIMD, 2 x 4 MFMA 32x32x16
+//   bf16 tiles and 128 fp32 accumulators per lane), so one wave's MFMAs run
+//   while the other waits for memory; the 4-wave shape (128 x 128 per wave,
+//   a third fewer LDS fragment bytes per MFMA) is kept as Shape<2>.
+// * The K loop is software-pipelined inside each wave. While the MFMAs of
 //   K-step ks run from LDS stage ks & 1, the wave stages K-step ks + 1 into
 //   the other stage -- LDS stores of the A rows it loaded one step earlier,
 //   and the B tile's dequantization (codebook lookups in LDS, one fp32
 //   multiply by the block scale, round to bf16, LDS stores) -- and issues
 //   the global loads of later K-steps (A: ks + 2; B: ks + 3, two register
-//   sets). The instruction stream of a K-step is cut into 64 slots of one
-//   MFMA each; every slot carries a fixed share of that work and a
-//   scheduling barrier closes it, so the compiler keeps the work between the
-//   MFMAs instead of clustering it, and the lookups' LDS latency elapses
-//   under the MFMAs that follow.
+//   sets). The instruction stream of a K-step is cut into slots of one MFMA
+//   each (32 per wave and K-step); every slot carries a fixed share of that
+//   work and a scheduling barrier closes it, so the compiler keeps the work
+//   between the MFMAs instead of clustering it, and the lookups' LDS latency
+//   elapses under the MFMAs that follow.
 // * B is dequantized exactly as in gemm.hip: bf16(fl32(code * scale)), the
 //   bf16 view that e4b_dequantize_nf4 returns.
 #include <type_traits>

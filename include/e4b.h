@@ -35,10 +35,11 @@
  *   "Unsupported" definition): a bad argument is reported, never ignored.
  *   T == 0 is a valid no-op.
  * - Device preconditions that are NOT checked: finite weights and logits;
- *   0 <= topk_idx < E and distinct per token when it is an input. An id
- *   outside [0, E) never leads to an out-of-bounds access: every kernel that
- *   reads ids treats it as expert 0, so the pair's result is meaningless but
- *   the call stays in bounds (the Python binding can check the ids first).
+ *   0 <= topk_idx < E when it is an input. An id outside [0, E) never leads
+ *   to an out-of-bounds access: every kernel that reads ids treats it as
+ *   expert 0, so the pair's result is meaningless but the call stays in
+ *   bounds (the Python binding can check the ids first). Given ids may
+ *   repeat an expert within a token: each slot is a pair of its own.
  */
 #ifndef E4B_H
 #define E4B_H
