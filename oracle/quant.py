@@ -153,6 +153,10 @@ def stored_weights(w, kind):
     if kind == "bf16":
         return bf16_bits_to_f32(bf16_rne_bits(w))
     E, out, inn = w.shape
+    if kind in ("int8", "fp8"):
+        from .quant8 import quantize_blockwise8, dequantize8
+
+        return dequantize8(*quantize_blockwise8(w, kind), out, inn, kind)
     if kind == "mxfp4":
         from .mx import quantize_mx, dequantize_mx
 

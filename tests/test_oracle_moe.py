@@ -125,11 +125,13 @@ def test_dgrad_matches_torch_autograd_on_tiny_config():
     assert np.allclose(y.detach().numpy(), yo, rtol=1e-10, atol=1e-12)
 
 
-def test_fidelity_ordering_bf16_nf4_fp4():
+def test_fidelity_ordering_bf16_int8_fp8_nf4_fp4():
+    """The support matrix's test-pinned ordering (0.4.0 README, storage modes):
+    bf16 < int8 < fp8 < nf4 < fp4 reconstruction error (fp16 is not a lane)."""
     cfg = get_config("tiny")
     for w in (gen_weights(cfg, 0, "gate_up"), gen_weights(cfg, 0, "down")):
         r = reconstruction_errors(w)
-        assert r["bf16"] < r["nf4"] < r["fp4"], r
+        assert r["bf16"] < r["int8"] < r["fp8"] < r["nf4"] < r["fp4"], r
     # forward-output fidelity on the tiny layer
     x = gen_x(cfg, 0)
     wgu, wdn = gen_weights(cfg, 0, "gate_up"), gen_weights(cfg, 0, "down")
@@ -151,7 +153,11 @@ def test_fidelity_ordering_bf16_nf4_fp4():
                 x, idx, w, dequantize(pg, ag, 2 * cfg.I, cfg.H, kind), dequantize(pd, ad, cfg.H, cfg.I, kind)
             ),
         )
-    assert errs["bf16"] < errs["nf4"] < errs["fp4"], errs
+    from oracle.quant import stored_weights
+
+    for kind in ("int8", "fp8"):
+        errs[kind] = rel_fro(y_ref, moe_forward(x, idx, w, stored_weights(wgu, kind), stored_weights(wdn, kind)))
+    assert errs["bf16"] < errs["int8"] < errs["fp8"] < errs["nf4"] < errs["fp4"], errs
 
 
 def test_fidelity_ordering_mixtral_shaped_rows():
@@ -160,7 +166,7 @@ def test_fidelity_ordering_mixtral_shaped_rows():
     rng = np.random.default_rng(0)
     w = (rng.standard_normal((1, 64, cfg.H)) * cfg.weight_std).astype(np.float32)
     r = reconstruction_errors(w)
-    assert r["bf16"] < r["nf4"] < r["fp4"], r
+    assert r["bf16"] < r["int8"] < r["fp8"] < r["nf4"] < r["fp4"], r
 
 
 def test_zero_tokens():
