@@ -33,7 +33,7 @@ from ._lib import (  # noqa: F401
 )
 
 CODEBOOKS = {"nf4": _lib.E4B_CB_NF4, "fp4": _lib.E4B_CB_FP4, "bf16": _lib.E4B_CB_BF16,
-             "mxfp4": _lib.E4B_CB_MXFP4}
+             "mxfp4": _lib.E4B_CB_MXFP4, "int8": _lib.E4B_CB_INT8, "fp8": _lib.E4B_CB_FP8}
 PATHS = {"auto": _lib.E4B_PATH_AUTO, "grouped": _lib.E4B_PATH_GROUPED, "decode": _lib.E4B_PATH_DECODE,
          "mx8": _lib.E4B_PATH_MX8}
 
@@ -109,10 +109,11 @@ def check_expert_ids(topk_idx, E):
 @dataclass
 class QuantStack:
     """One stored fused stack of an [E, out, in] weight: packed 4-bit codes +
-    fp32 absmax, packed E2M1 codes + E8M0 scales (codebook "mxfp4"), or
-    (codebook "bf16", the passthrough lane) the bf16 weight as bytes."""
+    fp32 absmax, packed E2M1 codes + E8M0 scales (codebook "mxfp4"), one code
+    byte per element + fp32 absmax (codebooks "int8", "fp8"), or (codebook
+    "bf16", the passthrough lane) the bf16 weight as bytes."""
 
-    packed: torch.Tensor  # uint8 [E, out*in/2]; bf16 lane: uint8 [E, out*in*2]
+    packed: torch.Tensor  # uint8 [E, out*in/2]; int8/fp8: [E, out*in]; bf16 lane: [E, out*in*2]
     absmax: torch.Tensor  # float32 [E, out*in/64]; bf16 / mxfp4: None
     E: int
     out: int
@@ -160,9 +161,10 @@ class MoELayer:
 
 
 def quantize(w, codebook="nf4"):
-    """Blockwise (64) absmax 4-bit quantization of a float32 [E, out, in] device stack
-    (codebook "nf4" / "fp4"), its MXFP4 conversion (codebook "mxfp4": E2M1 codes and
-    an E8M0 scale per 32 elements), or its bf16 passthrough storage (codebook "bf16")."""
+    """Blockwise (64) absmax quantization of a float32 [E, out, in] device stack: 4-bit
+    (codebook "nf4" / "fp4") or 8-bit (codebook "int8": the dynamic tree map; "fp8": an
+    E4M3 codebook), its MXFP4 conversion (codebook "mxfp4": E2M1 codes and an E8M0
+    scale per 32 elements), or its bf16 passthrough storage (codebook "bf16")."""
     if w.dim() != 3:
         raise ValueError("w must be [E, out, in]")
     _need(w, "w", torch.float32)
@@ -176,8 +178,8 @@ def quantize(w, codebook="nf4"):
         check("e4b_quantize_mxfp4", code)
         return QuantStack(packed, None, E, out, inn, codebook, scales)
     bf16 = codebook == "bf16"
-    packed = torch.empty(E, out * inn * 2 if bf16 else out * inn // 2, dtype=torch.uint8,
-                         device=w.device)
+    nbytes = out * inn * 2 if bf16 else out * inn if codebook in ("int8", "fp8") else out * inn // 2
+    packed = torch.empty(E, nbytes, dtype=torch.uint8, device=w.device)
     absmax = None if bf16 else torch.empty(E, out * inn // 64, dtype=torch.float32, device=w.device)
     code = load().e4b_quantize_nf4(
         _vp(w), E, out, inn, 64, CODEBOOKS[codebook], _vp(packed), _vp(absmax), _stream(w)

@@ -22,7 +22,7 @@ E4B_ERR_ALIGN = 7
 E4B_ERR_PATH = 8
 E4B_ERR_HIP = 9
 
-E4B_CB_NF4, E4B_CB_FP4, E4B_CB_BF16, E4B_CB_MXFP4 = 0, 1, 2, 3
+E4B_CB_NF4, E4B_CB_FP4, E4B_CB_BF16, E4B_CB_MXFP4, E4B_CB_INT8, E4B_CB_FP8 = 0, 1, 2, 3, 4, 5
 E4B_F32, E4B_BF16 = 0, 1
 E4B_PATH_AUTO, E4B_PATH_GROUPED, E4B_PATH_DECODE, E4B_PATH_MX8 = 0, 1, 2, 3
 

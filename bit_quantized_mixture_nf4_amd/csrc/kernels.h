@@ -125,6 +125,8 @@ struct MxGemmArgs {
 };
 hipError_t launch_mx8_rows(const uint16_t *x, int64_t rows, int64_t K, uint8_t *codes,
                            uint8_t *scales, hipStream_t s);
+// An INT8 / FP8 stack dequantized to bf16 (bf16 == true) or fp32 [E, out, in].
+hipError_t launch_dequantize8(const e4b_stack &st, bool bf16, void *out, hipStream_t s);
 hipError_t launch_mx_gemm(bool gate_up, const MxGemmArgs &a, hipStream_t s,
                           const e4b_kernel_events *ev = nullptr);
 

@@ -21,9 +21,7 @@ int bits_for(int64_t n) {
 
 e4b_status check_stack(const e4b_stack *st) {
   if (!st || !st->packed) return E4B_ERR_NULL;
-  if (st->codebook != E4B_CB_NF4 && st->codebook != E4B_CB_FP4 && st->codebook != E4B_CB_BF16 &&
-      st->codebook != E4B_CB_MXFP4)
-    return E4B_ERR_CODEBOOK;
+  if (st->codebook < E4B_CB_NF4 || st->codebook > E4B_CB_FP8) return E4B_ERR_CODEBOOK;
   const bool mx = st->codebook == E4B_CB_MXFP4;
   if (st->blocksize != (mx ? kMxBlock : kBlock)) return E4B_ERR_BLOCKSIZE;
   // the scale buffer of the mode: fp32 absmax (NF4, FP4), E8M0 bytes (MXFP4), none (BF16)
@@ -52,7 +50,9 @@ e4b_status check_quantize(const float *w, int64_t E, int64_t out, int64_t in,
   const bool bf16 = codebook == E4B_CB_BF16;
   if (!w || !packed || (!bf16 && !absmax)) return E4B_ERR_NULL;
   if (blocksize != kBlock) return E4B_ERR_BLOCKSIZE;
-  if (codebook != E4B_CB_NF4 && codebook != E4B_CB_FP4 && !bf16) return E4B_ERR_CODEBOOK;
+  if (codebook != E4B_CB_NF4 && codebook != E4B_CB_FP4 && codebook != E4B_CB_INT8 &&
+      codebook != E4B_CB_FP8 && !bf16)
+    return E4B_ERR_CODEBOOK;
   if (E <= 0 || out <= 0 || in <= 0 || in % kBlock != 0) return E4B_ERR_SHAPE;
   if (out * in > kMaxElems32 * 2) return E4B_ERR_SHAPE;
   if (!aligned16(w) || !aligned16(packed) || (!bf16 && !aligned16(absmax))) return E4B_ERR_ALIGN;
@@ -123,6 +123,10 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   p->off_sorted = take(size_t(P) * 4);
   p->off_pos = take(size_t(P) * 4);
   p->off_tile_map = take(size_t(p->m_tiles_bound) * 16);
+  // an 8-bit layer's stacks expanded to bf16, which the call's GEMMs read
+  const bool w8 = p->codebook == E4B_CB_INT8 || p->codebook == E4B_CB_FP8;
+  p->off_w8_gu = w8 ? take(size_t(E) * size_t(p->gu_cols) * size_t(H) * 2) : 0;
+  p->off_w8_dn = w8 ? take(size_t(E) * size_t(H) * size_t(I) * 2) : 0;
   const size_t base = off;
   // forward region
   p->off_a = take(size_t(P) * I * 2);
@@ -169,7 +173,8 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
 
 bool decode_fits(const MoePlan &p) {
   const int64_t kmax = p.H > p.I ? p.H : p.I;
-  return p.codebook != E4B_CB_BF16 && p.gated && p.T <= kDecodeMaxT && p.P <= kDecMaxPairs &&
+  const bool four_bit = p.codebook == E4B_CB_NF4 || p.codebook == E4B_CB_FP4 || p.codebook == E4B_CB_MXFP4;
+  return four_bit && p.gated && p.T <= kDecodeMaxT && p.P <= kDecMaxPairs &&
          kmax <= kDecodeMaxK;
 }
 
@@ -236,7 +241,7 @@ extern "C" const char *e4b_status_string(e4b_status s) {
     case E4B_ERR_DTYPE: return "unknown output dtype";
     case E4B_ERR_WORKSPACE: return "workspace missing or too small";
     case E4B_ERR_ALIGN: return "device buffer not 16-byte aligned";
-    case E4B_ERR_PATH: return "invalid path (decode path needs a gated 4-bit layer, T <= 8, saved == NULL and max(H, I) <= 16384)";
+    case E4B_ERR_PATH: return "invalid path (decode path needs a gated 4-bit layer (NF4, FP4, MXFP4), T <= 8, saved == NULL and max(H, I) <= 16384)";
     case E4B_ERR_HIP: return "HIP kernel launch failed";
   }
   return "unknown status";

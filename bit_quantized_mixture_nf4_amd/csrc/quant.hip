@@ -1,11 +1,12 @@
-// quant.hip -- blockwise absmax 4-bit quantize / dequantize of a fused stack,
-// and the bf16 passthrough lane (round to nearest even / widen).
+// quant.hip -- blockwise absmax 4-bit and 8-bit quantize / dequantize of a
+// fused stack, and the bf16 passthrough lane (round to nearest even / widen).
 //
 // experts4bit-qlora 0.1.0 sdist, _vendor/experts.py: Experts4bit quantizes
 // each expert of an [E, out, in] stack on its own with blocksize 64 and
 // dequantizes one expert as code value times block absmax. Blocks are 64
 // consecutive row-major elements, so the flat index of an element determines
 // its block across the whole contiguous [E, out*in/64] absmax array.
+#include "codebook8.h"
 #include "device.h"
 #include "plan.h"
 
@@ -135,6 +136,79 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t *__restr
   }
 }
 
+// 8-bit lanes (INT8, FP8): one wavefront per 64-element block, one element
+// per lane. The index of |w| / absmax among the 128 ascending magnitudes is
+// the number of midpoints m below it, counted by a binary search on the
+// exact fp64 products absmax * m (the midpoints of adjacent fp32 magnitudes
+// need at most 28 bits), so ties go to the smaller magnitude; the sign bit is
+// w's. One code byte per element.
+__global__ __launch_bounds__(256) void quantize8_kernel(const float *__restrict__ w, int64_t nblocks,
+                                                        int lane8, uint8_t *__restrict__ codes,
+                                                        float *__restrict__ absmax) {
+  const int lane = threadIdx.x & 63;
+  const int64_t blk = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (blk >= nblocks) return;  // whole wave exits together
+  const float v = w[blk * 64 + lane];
+  float m = fabsf(v);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  const double amax = double(m), a = fabs(double(v));
+  const float *mag = kMag8[lane8].v;
+  int lo = 0, hi = 127;  // the count of midpoints below a lies in [lo, hi]
+#pragma unroll
+  for (int it = 0; it < 7; ++it) {
+    const int mid = (lo + hi) >> 1;  // midpoint between magnitudes mid and mid + 1
+    const double mp = (double(mag[mid]) + double(mag[mid + 1])) * 0.5;
+    if (a > amax * mp) lo = mid + 1;
+    else hi = mid;
+  }
+  codes[blk * 64 + lane] = uint8_t(lo | (signbit(v) ? 0x80 : 0));
+  if (lane == 0) absmax[blk] = m;
+}
+
+// 8-bit lanes: one thread per 8 consecutive elements (8 code bytes);
+// fl32(value(code) * absmax), or its bf16 rounding.
+template <bool BF16>
+__global__ __launch_bounds__(256) void dequantize8_kernel(const u32x2 *__restrict__ codes,
+                                                          const float *__restrict__ absmax,
+                                                          int64_t ngroups, int lane8,
+                                                          void *__restrict__ out) {
+  __shared__ float val[256];
+  {
+    const float mg = kMag8[lane8].v[threadIdx.x & 127];
+    val[threadIdx.x] = threadIdx.x < 128 ? mg : -mg;
+  }
+  __syncthreads();
+  const int64_t g = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (g >= ngroups) return;
+  const u32x2 c = codes[g];
+  const float a = absmax[g >> 3];
+  float v[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) v[b] = __fmul_rn(val[(c[b >> 2] >> (8 * (b & 3))) & 255u], a);
+  if (BF16) {
+    u32x4 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+               pack_bf16x2(v[6], v[7])};
+    reinterpret_cast<u32x4 *>(out)[g] = o;
+  } else {
+    f32x4 *o = reinterpret_cast<f32x4 *>(out) + 2 * g;
+    o[0] = f32x4{v[0], v[1], v[2], v[3]};
+    o[1] = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
+hipError_t launch_dequantize8(const e4b_stack &st, bool bf16, void *out, hipStream_t s) {
+  const int64_t ngroups = st.E * st.out * st.in / 8;
+  const dim3 grid(uint32_t((ngroups + 255) / 256));
+  const u32x2 *c = reinterpret_cast<const u32x2 *>(st.packed);
+  const int lane8 = int(st.codebook) - E4B_CB_INT8;
+  if (bf16)
+    hipLaunchKernelGGL(dequantize8_kernel<true>, grid, dim3(256), 0, s, c, st.absmax, ngroups, lane8, out);
+  else
+    hipLaunchKernelGGL(dequantize8_kernel<false>, grid, dim3(256), 0, s, c, st.absmax, ngroups, lane8, out);
+  return hipGetLastError();
+}
+
 // BF16 passthrough lane: one thread per 8 elements, round to nearest even.
 __global__ __launch_bounds__(256) void quantize_bf16_kernel(const float *__restrict__ w,
                                                             int64_t ngroups,
@@ -181,8 +255,12 @@ extern "C" e4b_status e4b_quantize_nf4(const float *w, int64_t E, int64_t out, i
   }
   const int64_t nblocks = E * out * in / kBlock;
   const int64_t grid = (nblocks + 3) / 4;
-  hipLaunchKernelGGL(quantize_kernel, dim3(uint32_t(grid)), dim3(256), 0, stream, w, nblocks,
-                     int(codebook), packed, absmax);
+  if (codebook == E4B_CB_INT8 || codebook == E4B_CB_FP8)
+    hipLaunchKernelGGL(quantize8_kernel, dim3(uint32_t(grid)), dim3(256), 0, stream, w, nblocks,
+                       int(codebook) - E4B_CB_INT8, packed, absmax);
+  else
+    hipLaunchKernelGGL(quantize_kernel, dim3(uint32_t(grid)), dim3(256), 0, stream, w, nblocks,
+                       int(codebook), packed, absmax);
   return hipGetLastError() == hipSuccess ? E4B_OK : E4B_ERR_HIP;
 }
 
@@ -215,6 +293,8 @@ extern "C" e4b_status e4b_dequantize_nf4(const e4b_stack *st, int32_t dtype, voi
                          in, ngroups, w_out);
     return hipGetLastError() == hipSuccess ? E4B_OK : E4B_ERR_HIP;
   }
+  if (st->codebook == E4B_CB_INT8 || st->codebook == E4B_CB_FP8)
+    return launch_dequantize8(*st, dtype == E4B_BF16, w_out, stream) == hipSuccess ? E4B_OK : E4B_ERR_HIP;
   const uint32_t *pk = reinterpret_cast<const uint32_t *>(st->packed);
   const bool mx = st->codebook == E4B_CB_MXFP4;
   const float *am = mx ? nullptr : st->absmax;
@@ -239,8 +319,9 @@ extern "C" e4b_status e4b_stack_copy_async(const e4b_stack *dst, const e4b_stack
     return E4B_ERR_SHAPE;
   const int64_t n = dst->E * dst->out * dst->in;
   const bool bf16 = dst->codebook == E4B_CB_BF16;
+  const bool w8 = dst->codebook == E4B_CB_INT8 || dst->codebook == E4B_CB_FP8;
   if (hipMemcpyAsync(const_cast<uint8_t *>(dst->packed), src->packed,
-                     size_t(bf16 ? n * 2 : n / 2), hipMemcpyDefault, stream) != hipSuccess)
+                     size_t(bf16 ? n * 2 : w8 ? n : n / 2), hipMemcpyDefault, stream) != hipSuccess)
     return E4B_ERR_HIP;
   if (dst->codebook == E4B_CB_MXFP4) {
     if (hipMemcpyAsync(const_cast<uint8_t *>(dst->scales), src->scales, size_t(n / kMxBlock),

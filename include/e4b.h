@@ -62,7 +62,7 @@ typedef enum {
   E4B_ERR_DTYPE = 5,     /* unknown output dtype */
   E4B_ERR_WORKSPACE = 6, /* workspace NULL or smaller than e4b_moe_workspace_bytes() */
   E4B_ERR_ALIGN = 7,     /* a device buffer is not 16-byte aligned */
-  E4B_ERR_PATH = 8,      /* unknown path, or the decode path was asked for but does not apply (a BF16 layer, T > 8, saved != NULL, or max(H, I) above 16384) */
+  E4B_ERR_PATH = 8,      /* unknown path, or the decode path was asked for but does not apply (a BF16, INT8 or FP8 layer, T > 8, saved != NULL, or max(H, I) above 16384) */
   E4B_ERR_HIP = 9        /* a kernel launch failed (hipGetLastError after the launch) */
 } e4b_status;
 
@@ -83,12 +83,28 @@ typedef enum {
  * [E, out*in] (two bytes per element, round-to-nearest-even of the fp32
  * weight), `absmax` is unused and may be NULL. A BF16 layer runs the grouped
  * path only (the decode GEMV reads 4-bit codes). */
-typedef enum { E4B_CB_NF4 = 0, E4B_CB_FP4 = 1, E4B_CB_BF16 = 2, E4B_CB_MXFP4 = 3 } e4b_codebook;
+/* Storage modes ([README] "Storage modes: the support matrix"): the 4-bit
+ * codebooks NF4 and FP4 (two codes per byte), the bf16 passthrough lane, MXFP4
+ * (E2M1 codes + E8M0 scales), and the 8-bit blockwise lanes INT8 (the
+ * dynamic tree map) and FP8 (an E4M3 codebook), one code byte per element:
+ * sign bit 7 | index into 128 ascending magnitudes from 0 to 1 (the tables
+ * are defined in csrc/codebook8.h). As on the pages, the 8-bit lanes have no
+ * GEMV: their forward and dgrad dequantize both stacks to bf16 in the
+ * workspace and run the bf16 lane's GEMMs. */
+typedef enum {
+  E4B_CB_NF4 = 0,
+  E4B_CB_FP4 = 1,
+  E4B_CB_BF16 = 2,
+  E4B_CB_MXFP4 = 3,
+  E4B_CB_INT8 = 4,
+  E4B_CB_FP8 = 5
+} e4b_codebook;
 
 typedef enum { E4B_F32 = 0, E4B_BF16 = 1 } e4b_dtype;
 
-/* Forward path selection. AUTO = the decode dequant-GEMV path when T <= 8 and
- * saved == NULL, else the grouped MFMA path. MX8 = the MX forward of an
+/* Forward path selection. AUTO = the decode dequant-GEMV path when T <= 8,
+ * saved == NULL and the layer is a gated 4-bit one (NF4, FP4, MXFP4), else
+ * the grouped MFMA path. MX8 = the MX forward of an
  * MXFP4 gated layer on gfx950's block-scaled MFMA ([0.31.1] native MXFP4
  * row): x and a = bf16(silu(g) * u) are converted per row to MXFP8 (E4M3, an
  * E8M0 scale per 32; the OCP MX v1.0 rule with emax 8: saturating,
@@ -105,7 +121,7 @@ typedef enum {
 
 /* One quantized stack (device pointers; the struct itself is host memory). */
 typedef struct {
-  const uint8_t *packed; /* [E, out*in/2]; BF16: [E, out*in] bf16 */
+  const uint8_t *packed; /* [E, out*in/2]; BF16: [E, out*in] bf16; INT8, FP8: [E, out*in] codes */
   const float *absmax;   /* [E, out*in/64]; BF16, MXFP4: unused */
   int64_t E, out, in;
   int32_t blocksize; /* 64; MXFP4: 32 */
@@ -128,9 +144,11 @@ typedef struct {
  * no double quantization; [PR] "Non-goals" keeps absmax a plain fp32 buffer).
  * absmax = max |w| over each 64-block; code = nearest codebook entry to
  * w/absmax decided exactly (ties: NF4 lower code, FP4 smaller magnitude; FP4
- * sign bit = sign bit of w); an NF4 block of zeros stores code 7.
+ * sign bit = sign bit of w); an NF4 block of zeros stores code 7. INT8 and
+ * FP8: the magnitude nearest |w|/absmax (ties: the smaller one), sign bit 7 =
+ * sign bit of w, one code byte per element.
  *   w      : device fp32 [E, out, in], finite (unchecked)
- *   packed : device uint8 [E, out*in/2]   (written)
+ *   packed : device uint8 [E, out*in/2]; INT8, FP8: [E, out*in]   (written)
  *   absmax : device fp32  [E, out*in/64]  (written)
  * codebook E4B_CB_BF16 writes the bf16 rounding (nearest even) of w to
  * `packed` ([E, out*in] bf16) and leaves `absmax` (may be NULL) untouched.

@@ -100,8 +100,9 @@ def oracle_store_expert(w, kind, threads=16):
     row, so row slices give exactly the whole-expert result). Returns
     ``(stored bytes uint8 [nbytes], scale bytes uint8 [n] or None, dequantized
     fp32 [out, in])``: nf4 / fp4 -> packed codes and the absmax as its fp32
-    bytes; mxfp4 -> packed codes and the E8M0 bytes; bf16 -> the bf16 bit
-    patterns as bytes and no scales.
+    bytes; int8 / fp8 -> one code byte per element and the absmax bytes;
+    mxfp4 -> packed codes and the E8M0 bytes; bf16 -> the bf16 bit patterns as
+    bytes and no scales.
     """
     from concurrent.futures import ThreadPoolExecutor
 
@@ -118,6 +119,11 @@ def oracle_store_expert(w, kind, threads=16):
         if kind == "mxfp4":
             p, s = oracle.quantize_mx(ws)
             return p[0], s[0], oracle.dequantize_mx(p, s, r1 - r0, inn)[0]
+        if kind in ("int8", "fp8"):
+            from oracle import quant8
+
+            c, a = quant8.quantize_blockwise8(ws, kind)
+            return c[0], a[0].view(np.uint8), quant8.dequantize8(c, a, r1 - r0, inn, kind)[0]
         p, a = oracle.quantize_blockwise(ws, kind)
         return p[0], a[0].view(np.uint8), oracle.dequantize(p, a, r1 - r0, inn, kind)[0]
 

@@ -55,7 +55,11 @@ def test_quantize_validation():
     assert q(FAKE, 1, 64, 96, 64, 0, FAKE, FAKE, None) == _lib.E4B_ERR_SHAPE
     assert q(FAKE, 0, 64, 64, 64, 0, FAKE, FAKE, None) == _lib.E4B_ERR_SHAPE
     assert q(FAKE, 1, 64, 64, 128, 0, FAKE, FAKE, None) == _lib.E4B_ERR_BLOCKSIZE
-    assert q(FAKE, 1, 64, 64, 64, 5, FAKE, FAKE, None) == _lib.E4B_ERR_CODEBOOK
+    assert q(FAKE, 1, 64, 64, 64, 6, FAKE, FAKE, None) == _lib.E4B_ERR_CODEBOOK
+    assert q(FAKE, 1, 64, 64, 64, -1, FAKE, FAKE, None) == _lib.E4B_ERR_CODEBOOK
+    # the 8-bit lanes need an absmax buffer like the 4-bit ones
+    assert q(FAKE, 1, 64, 64, 64, _lib.E4B_CB_INT8, FAKE, None, None) == _lib.E4B_ERR_NULL
+    assert q(FAKE, 1, 64, 64, 128, _lib.E4B_CB_FP8, FAKE, FAKE, None) == _lib.E4B_ERR_BLOCKSIZE
     # MXFP4 has its own entry point (E8M0 scale bytes, not fp32 absmax)
     assert q(FAKE, 1, 64, 64, 64, 3, FAKE, FAKE, None) == _lib.E4B_ERR_CODEBOOK
     # the bf16 lane needs no absmax buffer: NULL passes the pointer check and
@@ -71,7 +75,7 @@ def test_dequantize_validation():
     assert d(ctypes.byref(st), 7, FAKE, None) == _lib.E4B_ERR_DTYPE
     assert d(ctypes.byref(st), 0, FAKE + 8, None) == _lib.E4B_ERR_ALIGN
     assert d(ctypes.byref(_stack(bs=32)), 0, FAKE, None) == _lib.E4B_ERR_BLOCKSIZE
-    assert d(ctypes.byref(_stack(cb=5)), 0, FAKE, None) == _lib.E4B_ERR_CODEBOOK
+    assert d(ctypes.byref(_stack(cb=6)), 0, FAKE, None) == _lib.E4B_ERR_CODEBOOK
     assert d(ctypes.byref(_stack(inn=100)), 0, FAKE, None) == _lib.E4B_ERR_SHAPE
     assert d(ctypes.byref(_stack(packed=None)), 0, FAKE, None) == _lib.E4B_ERR_NULL
     assert d(None, 0, FAKE, None) == _lib.E4B_ERR_NULL
@@ -189,6 +193,23 @@ def test_bf16_lane_validation():
     assert _fwd(nf) == _lib.E4B_ERR_NULL
     mixed = _lib.E4bLayer(_stack(4, 128, 64, cb=2), _stack(4, 64, 64, cb=0))
     assert _fwd(mixed) == _lib.E4B_ERR_CODEBOOK
+
+
+def test_8bit_lane_validation():
+    for cb in (_lib.E4B_CB_INT8, _lib.E4B_CB_FP8):
+        L = _lib.E4bLayer(_stack(4, 128, 64, cb=cb), _stack(4, 64, 64, cb=cb))
+        # the call reaches the workspace check; the workspace holds both stacks in bf16
+        assert _fwd(L, ws_bytes=0) == _lib.E4B_ERR_WORKSPACE
+        nf4 = _lib.E4bLayer(_stack(4, 128, 64), _stack(4, 64, 64))
+        lib = e4b.load()
+        w8 = lib.e4b_moe_workspace_bytes(ctypes.byref(L), 4, 2)
+        w4 = lib.e4b_moe_workspace_bytes(ctypes.byref(nf4), 4, 2)
+        assert w8 >= w4 + 2 * (4 * 128 * 64 + 4 * 64 * 64)
+        # no GEMV for the 8-bit lanes: the decode path is refused
+        assert _fwd(L, T=4, path=2) == _lib.E4B_ERR_PATH
+        # the 8-bit stacks need their absmax
+        bad = _lib.E4bLayer(_stack(4, 128, 64, absmax=None, cb=cb), _stack(4, 64, 64, cb=cb))
+        assert _fwd(bad) == _lib.E4B_ERR_NULL
 
 
 def test_ungated_layer_validation():

@@ -93,7 +93,8 @@ def _oracle_whole(cfg, seed, kind, layer, x, gy, idx, w, routed_only=False):
 
 
 @pytest.mark.parametrize("name,kind", [("olmoe", "nf4"), ("qwen3_prefill", "nf4"), ("mixtral", "nf4"),
-                                       ("mixtral", "fp4"), ("olmoe", "bf16"), ("olmoe", "mxfp4")])
+                                       ("mixtral", "fp4"), ("olmoe", "bf16"), ("olmoe", "mxfp4"),
+                                       ("olmoe", "int8"), ("olmoe", "fp8")])
 def test_full_size_forward_dgrad_whole(name, kind):
     cfg = get_config(name)
     seed = 0
