@@ -290,6 +290,7 @@ namespace {
 
 struct LoraWs {
   float *xa, *aa, *gb, *hb;
+  uint16_t *a;                                  // recomputed a [P, I] (backward without saved state)
   uint16_t *pk_bgu, *pk_bdn, *pk_agu, *pk_adn;  // GEMM slices: scaled, by output column
   uint16_t *pj_agu, *pj_adn, *pj_bdn, *pj_bgu;  // projections: j-major
 };
@@ -300,6 +301,7 @@ LoraWs lora_ws(const MoePlan &p, char *w) {
   l.aa = reinterpret_cast<float *>(w + p.off_l_aa);
   l.gb = reinterpret_cast<float *>(w + p.off_l_gb);
   l.hb = reinterpret_cast<float *>(w + p.off_l_hb);
+  l.a = reinterpret_cast<uint16_t *>(w + p.off_l_a);
   l.pk_bgu = reinterpret_cast<uint16_t *>(w + p.off_pk_bgu);
   l.pk_bdn = reinterpret_cast<uint16_t *>(w + p.off_pk_bdn);
   l.pk_agu = reinterpret_cast<uint16_t *>(w + p.off_pk_agu);
@@ -313,12 +315,37 @@ LoraWs lora_ws(const MoePlan &p, char *w) {
 
 float lora_scale(const e4b_lora *lo) { return lo->alpha / float(lo->r); }
 
-// x A_gu^T per pair, then the gate_up GEMM with the s B_gu slice.
+void add_pack(LoraPackJobs &jobs, const float *M, int64_t E, int N, int type, float s,
+              uint16_t *out) {
+  LoraPackJob &J = jobs.j[jobs.n++];
+  J.M = M;
+  J.out = out;
+  J.E = E;
+  J.items = 0;
+  J.N = N;
+  J.type = type;
+  J.s = s;
+}
+
+void add_wgrad(LoraWgJobs &jobs, int mode, const uint16_t *src, int64_t ld, int N, const float *V,
+               bool v_weighted, bool out_trans, float *out) {
+  LoraWgJob &J = jobs.j[jobs.n++];
+  J.src = src;
+  J.V = V;
+  J.out = out;
+  J.ld = ld;
+  J.N = N;
+  J.mode = mode;
+  J.v_weighted = v_weighted;
+  J.out_trans = out_trans;
+}
+
+// x A_gu^T per pair into xa, then the gate_up GEMM with the s B_gu slice.
 hipError_t lora_gate_up(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
                         uint16_t *a_out, uint16_t *gu_out, const PermView &v, const LoraWs &l,
-                        hipStream_t s) {
-  hipError_t err = launch_lora_project_mfma(LS_X_GATHER, x, p.H, int(p.H), int(p.I), v.sorted,
-                                            int(p.k), v, int(p.E), p.m_tiles_bound, l.pj_agu, l.xa, s);
+                        float *xa, hipStream_t s) {
+  hipError_t err = launch_lora_proj(LS_X_GATHER, x, p.H, int(p.H), v.sorted, int(p.k), v, int(p.E),
+                                    p.m_tiles_bound, l.pj_agu, xa, s);
   if (err != hipSuccess) return err;
   GemmArgs a = base_args(p, L->gate_up, v);
   a.A = x;
@@ -330,7 +357,7 @@ hipError_t lora_gate_up(const MoePlan &p, const e4b_moe_layer *L, const uint16_t
   a.C = a_out;
   a.ldc = int32_t(p.I);
   a.GU = gu_out;
-  a.lora_p = l.xa;
+  a.lora_p = xa;
   a.lora_w = l.pk_bgu;
   a.lora_rows = int32_t(2 * p.I);
   return launch_grouped_gemm(GEMM_GATE_UP_FWD, a, s);
@@ -366,16 +393,23 @@ extern "C" e4b_status e4b_moe_lora_forward(const e4b_moe_layer *L, const e4b_lor
     E4B_TRY(launch_route(router_logits, T, int(p.E), top_k, topk_idx, topk_w, stream));
   const PermView v = saved ? perm_in_saved(p, static_cast<char *>(saved)) : perm_in_workspace(p, w);
   E4B_TRY(launch_permute(p, topk_idx, w, v, stream));
-  E4B_TRY(launch_lora_pack(lora->B_gu, p.E, int(2 * p.I), lora->r, sc, false, l.pk_bgu, stream));
-  E4B_TRY(launch_lora_pack(lora->B_dn, p.E, int(p.H), lora->r, sc, false, l.pk_bdn, stream));
-  E4B_TRY(launch_lora_pack_jk(lora->A_gu, p.E, int(p.H), lora->r, false, l.pj_agu, stream));
-  E4B_TRY(launch_lora_pack_jk(lora->A_dn, p.E, int(p.I), lora->r, false, l.pj_adn, stream));
+  LoraPackJobs packs{};
+  packs.r = lora->r;
+  add_pack(packs, lora->B_gu, p.E, int(2 * p.I), LP_COLS, sc, l.pk_bgu);
+  add_pack(packs, lora->B_dn, p.E, int(p.H), LP_COLS, sc, l.pk_bdn);
+  add_pack(packs, lora->A_gu, p.E, int(p.H), LP_JK_A, 1.0f, l.pj_agu);
+  add_pack(packs, lora->A_dn, p.E, int(p.I), LP_JK_A, 1.0f, l.pj_adn);
+  E4B_TRY(launch_lora_packs(packs, stream));
 
+  // with saved state, the two forward rank projections are kept for the backward
+  char *sv = static_cast<char *>(saved);
+  float *xa = saved ? reinterpret_cast<float *>(sv + p.sv_xa) : l.xa;
+  float *aa = saved ? reinterpret_cast<float *>(sv + p.sv_aa) : l.aa;
   uint16_t *a_buf = reinterpret_cast<uint16_t *>(w + p.off_a);
   uint16_t *o_buf = reinterpret_cast<uint16_t *>(w + p.off_o);
-  E4B_TRY(lora_gate_up(p, L, x, a_buf, static_cast<uint16_t *>(saved), v, l, stream));
-  E4B_TRY(launch_lora_project_mfma(LS_ROWS, a_buf, p.I, int(p.I), int(p.I), v.sorted, int(p.k), v,
-                                   int(p.E), p.m_tiles_bound, l.pj_adn, l.aa, stream));
+  E4B_TRY(lora_gate_up(p, L, x, a_buf, static_cast<uint16_t *>(saved), v, l, xa, stream));
+  E4B_TRY(launch_lora_proj(LS_ROWS, a_buf, p.I, int(p.I), v.sorted, int(p.k), v, int(p.E),
+                           p.m_tiles_bound, l.pj_adn, aa, stream));
   GemmArgs d = base_args(p, L->down, v);
   d.A = a_buf;
   d.lda = int32_t(p.I);
@@ -385,7 +419,7 @@ extern "C" e4b_status e4b_moe_lora_forward(const e4b_moe_layer *L, const e4b_lor
   d.grid = uint32_t(p.m_tiles_bound * p.n_tiles_h);
   d.C = o_buf;
   d.ldc = int32_t(p.H);
-  d.lora_p = l.aa;
+  d.lora_p = aa;
   d.lora_w = l.pk_bdn;
   d.lora_rows = int32_t(p.H);
   E4B_TRY(launch_grouped_gemm(GEMM_DOWN_FWD, d, stream));
@@ -423,34 +457,46 @@ extern "C" e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lo
   const float sc = lora_scale(lora);
   const int r = lora->r;
 
+  LoraPackJobs packs{};
+  packs.r = r;
+  add_pack(packs, lora->B_dn, p.E, int(p.H), LP_JK_B, 1.0f, l.pj_bdn);
+  add_pack(packs, lora->B_gu, p.E, int(2 * p.I), LP_JK_B, 1.0f, l.pj_bgu);
+  add_pack(packs, lora->A_dn, p.E, int(p.I), LP_COLS_T, sc, l.pk_adn);
+  add_pack(packs, lora->A_gu, p.E, int(p.H), LP_COLS_T, sc, l.pk_agu);
+  if (!saved) {  // the recomputed forward's operands
+    add_pack(packs, lora->B_gu, p.E, int(2 * p.I), LP_COLS, sc, l.pk_bgu);
+    add_pack(packs, lora->A_gu, p.E, int(p.H), LP_JK_A, 1.0f, l.pj_agu);
+    add_pack(packs, lora->A_dn, p.E, int(p.I), LP_JK_A, 1.0f, l.pj_adn);
+  }
+  E4B_TRY(launch_lora_packs(packs, stream));
   const uint16_t *gu = static_cast<const uint16_t *>(saved);
-  E4B_TRY(launch_lora_pack_jk(lora->A_gu, p.E, int(p.H), r, false, l.pj_agu, stream));
-  E4B_TRY(launch_lora_pack_jk(lora->A_dn, p.E, int(p.I), r, false, l.pj_adn, stream));
-  E4B_TRY(launch_lora_pack_jk(lora->B_dn, p.E, int(p.H), r, true, l.pj_bdn, stream));
-  E4B_TRY(launch_lora_pack_jk(lora->B_gu, p.E, int(2 * p.I), r, true, l.pj_bgu, stream));
+  const float *xa, *aa;
   PermView v;
   if (saved) {
-    v = perm_in_saved(p, static_cast<char *>(const_cast<void *>(saved)));
-    // x A_gu^T for dB_gu (the forward's copy may have been overwritten)
-    E4B_TRY(launch_lora_project_mfma(LS_X_GATHER, x, p.H, int(p.H), int(p.I), v.sorted, int(p.k),
-                                     v, int(p.E), p.m_tiles_bound, l.pj_agu, l.xa, stream));
+    // the permutation, g|u and the forward's rank projections x A_gu^T, a A_dn^T
+    const char *sv = static_cast<const char *>(saved);
+    v = perm_in_saved(p, const_cast<char *>(sv));
+    xa = reinterpret_cast<const float *>(sv + p.sv_xa);
+    aa = reinterpret_cast<const float *>(sv + p.sv_aa);
   } else {
+    // recompute them exactly as the forward does
     v = perm_in_workspace(p, w);
     E4B_TRY(launch_permute(p, topk_idx, w, v, stream));
-    E4B_TRY(launch_lora_pack(lora->B_gu, p.E, int(2 * p.I), r, sc, false, l.pk_bgu, stream));
     uint16_t *gu_ws = reinterpret_cast<uint16_t *>(w + p.off_gu);
-    E4B_TRY(lora_gate_up(p, L, x, nullptr, gu_ws, v, l, stream));
+    E4B_TRY(lora_gate_up(p, L, x, l.a, gu_ws, v, l, l.xa, stream));
+    E4B_TRY(launch_lora_proj(LS_ROWS, l.a, p.I, int(p.I), v.sorted, int(p.k), v, int(p.E),
+                             p.m_tiles_bound, l.pj_adn, l.aa, stream));
     gu = gu_ws;
+    xa = l.xa;
+    aa = l.aa;
   }
-  E4B_TRY(launch_lora_pack(lora->A_dn, p.E, int(p.I), r, sc, true, l.pk_adn, stream));
-  E4B_TRY(launch_lora_pack(lora->A_gu, p.E, int(p.H), r, sc, true, l.pk_agu, stream));
   uint16_t *dgu = reinterpret_cast<uint16_t *>(w + p.off_dgu);
   float *partial = reinterpret_cast<float *>(w + p.off_partial);
   uint16_t *gx = reinterpret_cast<uint16_t *>(w + p.off_gx);
 
   // grad_y B_dn per pair, then the down dgrad GEMM with the s A_dn^T slice
-  E4B_TRY(launch_lora_project_mfma(LS_X_GATHER, gy, p.H, int(p.H), int(p.I), v.sorted, int(p.k),
-                                   v, int(p.E), p.m_tiles_bound, l.pj_bdn, l.gb, stream));
+  E4B_TRY(launch_lora_proj(LS_X_GATHER, gy, p.H, int(p.H), v.sorted, int(p.k), v, int(p.E),
+                           p.m_tiles_bound, l.pj_bdn, l.gb, stream));
   GemmArgs d = base_args(p, L->down, v);
   d.A = gy;
   d.lda = int32_t(p.H);
@@ -469,8 +515,8 @@ extern "C" e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lo
   E4B_TRY(launch_grouped_gemm(GEMM_DOWN_DGRAD, d, stream));
 
   // dGU B_gu per pair, then the gate_up dgrad GEMM with the s A_gu^T slice
-  E4B_TRY(launch_lora_project_mfma(LS_ROWS, dgu, 2 * p.I, int(2 * p.I), int(p.I), v.sorted,
-                                   int(p.k), v, int(p.E), p.m_tiles_bound, l.pj_bgu, l.hb, stream));
+  E4B_TRY(launch_lora_proj(LS_ROWS, dgu, 2 * p.I, int(2 * p.I), v.sorted, int(p.k), v, int(p.E),
+                           p.m_tiles_bound, l.pj_bgu, l.hb, stream));
   GemmArgs u = base_args(p, L->gate_up, v);
   u.A = dgu;
   u.lda = int32_t(2 * p.I);
@@ -488,17 +534,13 @@ extern "C" e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lo
   E4B_TRY(launch_combine_dgrad(gx, v.pos, T, top_k, int(p.H), static_cast<uint16_t *>(grad_x_bf16),
                                partial, int(p.n_tiles_i), grad_topk_w, stream));
 
-  // adapter gradients: a A_dn^T from the saved / recomputed g|u, then the
-  // four per-expert outer-product sums
-  E4B_TRY(launch_lora_project_mfma(LS_GU_ACT, gu, 2 * p.I, int(p.I), int(p.I), v.sorted, int(p.k),
-                                   v, int(p.E), p.m_tiles_bound, l.pj_adn, l.aa, stream));
-  E4B_TRY(launch_lora_wgrad(LS_ROWS, dgu, 2 * p.I, int(2 * p.I), int(p.I), v.sorted, v.offsets, v.tile_offsets,
-                            int(p.k), topk_w, p.E, l.xa, false, r, sc, false, dB_gu, stream));
-  E4B_TRY(launch_lora_wgrad(LS_X_GATHER, x, p.H, int(p.H), int(p.I), v.sorted, v.offsets, v.tile_offsets, int(p.k),
-                            topk_w, p.E, l.hb, false, r, sc, true, dA_gu, stream));
-  E4B_TRY(launch_lora_wgrad(LS_WX_GATHER, gy, p.H, int(p.H), int(p.I), v.sorted, v.offsets, v.tile_offsets,
-                            int(p.k), topk_w, p.E, l.aa, false, r, sc, false, dB_dn, stream));
-  E4B_TRY(launch_lora_wgrad(LS_GU_ACT, gu, 2 * p.I, int(p.I), int(p.I), v.sorted, v.offsets, v.tile_offsets,
-                            int(p.k), topk_w, p.E, l.gb, true, r, sc, true, dA_dn, stream));
+  // the four per-expert outer-product sums, one launch
+  LoraWgJobs g{};
+  add_wgrad(g, LS_ROWS, dgu, 2 * p.I, int(2 * p.I), xa, false, false, dB_gu);
+  add_wgrad(g, LS_X_GATHER, x, p.H, int(p.H), l.hb, false, true, dA_gu);
+  add_wgrad(g, LS_WX_GATHER, gy, p.H, int(p.H), aa, false, false, dB_dn);
+  add_wgrad(g, LS_GU_ACT, gu, 2 * p.I, int(p.I), l.gb, true, true, dA_dn);
+  E4B_TRY(launch_lora_wgrads(g, int(p.I), v.sorted, v.offsets, v.tile_offsets, int(p.k), topk_w,
+                             p.E, r, sc, stream));
   return E4B_OK;
 }

@@ -149,36 +149,65 @@ hipError_t launch_combine_dgrad(const uint16_t *rows, const int32_t *pos_of_pair
                                 float *gw, hipStream_t s, const e4b_kernel_events *ev = nullptr);
 
 // ---- LoRA (lora.hip) ----
-// out[e, n, :] = bf16(s * M[e, n, j]) for j < r, 0 up to kLoraK, where
-// M = B [E, N, r] (trans = false) or M[e, n, j] = A[e, j, n] for A [E, r, N].
-hipError_t launch_lora_pack(const float *M, int64_t E, int N, int r, float s, bool trans,
-                            uint16_t *out, hipStream_t st);
+// Operand packs of the adapters, with zeros for r <= j < kLoraK:
+//   LP_COLS   : out[e, n, :] = bf16(s * B[e, n, j])   (B [E, N, r]; GEMM slice)
+//   LP_COLS_T : out[e, n, :] = bf16(s * A[e, j, n])   (A [E, r, N]; GEMM slice)
+//   LP_JK_A   : out[e, j, k] = bf16(A[e, j, k])       (A [E, r, K]; projection, N = K)
+//   LP_JK_B   : out[e, j, k] = bf16(B[e, k, j])       (B [E, K, r]; projection, N = K)
+enum LoraPackType { LP_COLS = 0, LP_COLS_T = 1, LP_JK_A = 2, LP_JK_B = 3 };
+struct LoraPackJob {
+  const float *M;
+  uint16_t *out;
+  int64_t E;
+  int64_t items;  // set by the launcher
+  int32_t N;
+  int32_t type;
+  float s;
+};
+constexpr int kLoraPackJobs = 8;
+struct LoraPackJobs {
+  LoraPackJob j[kLoraPackJobs];
+  int64_t first_block[kLoraPackJobs];  // set by the launcher
+  int32_t n;
+  int32_t r;
+};
+// All packs of one call in one launch (jobs.n <= kLoraPackJobs).
+hipError_t launch_lora_packs(LoraPackJobs jobs, hipStream_t st);
 
 // Source rows of a per-pair projection / of an adapter gradient.
 enum LoraSrc {
   LS_X_GATHER = 0,  // src[token(sorted pair)]           (x or grad_y, [T, ld])
   LS_ROWS = 1,      // src[sorted position]               (a or dGU, [P, ld])
-  LS_GU_ACT = 2,    // silu(g) * u from g|u [P, 2I] rows  (the activation a)
-  LS_WX_GATHER = 3  // topk_w[pair] * src[token(pair)]    (the weighted grad_y)
+  LS_GU_ACT = 2,    // silu(g) * u from g|u [P, 2I] rows  (the activation a; gradients only)
+  LS_WX_GATHER = 3  // topk_w[pair] * src[token(pair)]    (the weighted grad_y; gradients only)
 };
-// j-major bf16 pack [E, kLoraK, K] of an adapter for the MFMA projection.
-hipError_t launch_lora_pack_jk(const float *M, int64_t E, int K, int r, bool m_is_b,
-                               uint16_t *out, hipStream_t st);
 // out[s, j] = sum_k src(s)[k] M(e(s), k, j) (j < r, zero up to kLoraK), fp32
 // [P, kLoraK], on MFMA over the m-tiles of the permutation (rows of a tile
-// share one expert); Mj is the j-major pack of the adapter (M = A [E, r, K]
-// or B [E, K, r] packed by launch_lora_pack_jk).
-hipError_t launch_lora_project_mfma(int src_mode, const uint16_t *src, int64_t ld, int K, int I,
-                                    const int32_t *sorted, int topk, const PermView &v, int E,
-                                    int64_t m_tiles_bound, const uint16_t *Mj, float *out,
-                                    hipStream_t st);
+// share one expert); Mj is the j-major pack [E, kLoraK, K] of the adapter
+// (LP_JK_A / LP_JK_B). src_mode LS_X_GATHER or LS_ROWS; K % 64 == 0.
+hipError_t launch_lora_proj(int src_mode, const uint16_t *src, int64_t ld, int K,
+                            const int32_t *sorted, int topk, const PermView &v, int E,
+                            int64_t m_tiles_bound, const uint16_t *Mj, float *out, hipStream_t st);
 // Adapter gradient of expert e: G[n, j] = s * sum over e's sorted pairs of
 // U(pair)[n] * V(pair)[j] (* topk_w[pair] when v_weighted), written as
-// [E, N, r] (a B-shaped gradient) or [E, r, N] (A-shaped, out_trans).
-hipError_t launch_lora_wgrad(int u_mode, const uint16_t *src, int64_t ld, int N, int I,
-                             const int32_t *sorted, const int32_t *offsets,
-                             const int32_t *tile_offsets, int topk,
-                             const float *topk_w, int64_t E, const float *V, bool v_weighted,
-                             int r, float s, bool out_trans, float *out, hipStream_t st);
+// [E, N, r] (a B-shaped gradient) or [E, r, N] (A-shaped, out_trans); U
+// comes from src in `mode` (LoraSrc). Up to four gradients per launch.
+struct LoraWgJob {
+  const uint16_t *src;
+  const float *V;
+  float *out;
+  int64_t ld;
+  int32_t N;
+  int32_t mode;
+  int32_t v_weighted;
+  int32_t out_trans;
+};
+struct LoraWgJobs {
+  LoraWgJob j[4];
+  int32_t n;
+};
+hipError_t launch_lora_wgrads(const LoraWgJobs &jobs, int I, const int32_t *sorted,
+                              const int32_t *offsets, const int32_t *tile_offsets, int topk,
+                              const float *topk_w, int64_t E, int r, float s, hipStream_t st);
 
 }  // namespace e4b

@@ -153,6 +153,7 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   p->off_l_aa = take(size_t(P) * kLoraK * 4);
   p->off_l_gb = take(size_t(P) * kLoraK * 4);
   p->off_l_hb = take(size_t(P) * kLoraK * 4);
+  p->off_l_a = take(size_t(P) * I * 2);
   p->off_pk_bgu = take(size_t(E) * 2 * I * kLoraK * 2);
   p->off_pk_bdn = take(size_t(E) * H * kLoraK * 2);
   p->off_pk_agu = take(size_t(E) * H * kLoraK * 2);
@@ -167,7 +168,9 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   p->sv_offsets = p->sv_tile_offsets + size_t(E + 1) * 4;
   p->sv_sorted = p->sv_offsets + size_t(E + 1) * 4;
   p->sv_pos = p->sv_sorted + size_t(P) * 4;
-  p->saved_bytes = p->sv_pos + size_t(P) * 4;
+  p->sv_xa = align_up(p->sv_pos + size_t(P) * 4, 256);
+  p->sv_aa = p->sv_xa + size_t(P) * kLoraK * 4;
+  p->saved_bytes = p->sv_aa + size_t(P) * kLoraK * 4;
   return E4B_OK;
 }
 

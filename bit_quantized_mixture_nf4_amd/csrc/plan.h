@@ -61,13 +61,15 @@ struct MoePlan {
   // projections (x A_gu^T, a A_dn^T, grad_y B_dn, dGU B_gu) and bf16
   // [E, rows, kLoraK] operand packs (s B_gu, s B_dn, s A_gu^T, s A_dn^T)
   size_t off_l_xa, off_l_aa, off_l_gb, off_l_hb;
+  size_t off_l_a;  // bf16 a [P, I] of the backward's recomputed forward
   size_t off_pk_bgu, off_pk_bdn, off_pk_agu, off_pk_adn;
   // j-major bf16 [E, kLoraK, K] packs for the projections: A_gu, A_dn, B_dn^T, B_gu^T
   size_t off_pj_agu, off_pj_adn, off_pj_bdn, off_pj_bgu;
   size_t lora_ws_bytes;
-  // saved buffer (dense): bf16 g|u [P, 2I], then the forward's permutation
-  // (tile map, tile offsets, offsets, sorted pairs, pair positions)
-  size_t sv_tile_map, sv_tile_offsets, sv_offsets, sv_sorted, sv_pos;
+  // saved buffer: bf16 g|u (blocked), then the forward's permutation (tile
+  // map, tile offsets, offsets, sorted pairs, pair positions), then the LoRA
+  // forward's fp32 [P, kLoraK] rank projections x A_gu^T and a A_dn^T
+  size_t sv_tile_map, sv_tile_offsets, sv_offsets, sv_sorted, sv_pos, sv_xa, sv_aa;
   size_t saved_bytes;
 };
 

@@ -270,9 +270,11 @@ size_t e4b_moe_workspace_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k)
  * bf16 gate and up projections of every routed pair (gated: in blocks of 256
  * sorted pairs x 128 intermediate columns, g and u side by side, one block per
  * m-tile and column block; ungated: h as [T*top_k, I]) followed by the routing
- * permutation (int32 arrays over experts, m-tiles and pairs); 0 when invalid.
- * The forward never writes the padding of the blocks (rows past an expert's
- * pairs, blocks of m-tiles the routing does not produce) and nothing reads it. */
+ * permutation (int32 arrays over experts, m-tiles and pairs) and room for the
+ * LoRA forward's two per-pair rank projections (fp32 [T*top_k, 16] each; the
+ * base forward leaves it unwritten); 0 when invalid. The forward never writes
+ * the padding of the blocks (rows past an expert's pairs, blocks of m-tiles
+ * the routing does not produce) and nothing reads it. */
 size_t e4b_moe_saved_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k);
 
 /* Allocation-free forward, for callers that cannot allocate device memory
@@ -311,7 +313,8 @@ typedef struct {
 } e4b_lora;
 
 /* Forward of e4b_moe_forward with LoRA adapters; always the grouped path
- * (saved, when given, is filled exactly as by e4b_moe_forward).
+ * (saved, when given, is filled as by e4b_moe_forward, with the adapted g|u,
+ * plus the rank projections x A_gu^T and a A_dn^T that the backward reuses).
  * ws must hold e4b_moe_lora_workspace_bytes(). Errors as e4b_moe_forward,
  * plus NULL / SHAPE for the adapter descriptor (r outside [1, 16]). */
 e4b_status e4b_moe_lora_forward(const e4b_moe_layer *L, const e4b_lora *lora, int64_t T,
@@ -327,7 +330,9 @@ e4b_status e4b_moe_lora_forward(const e4b_moe_layer *L, const e4b_lora *lora, in
  *   grad_h = [dg ; du] from grad_a     grad_x_t += W_gu^T grad_h + s A_gu^T (B_gu^T grad_h)
  *   dB_gu += s grad_h (A_gu x_t)^T     dA_gu += s (B_gu^T grad_h) x_t^T
  *   x_bf16   : device bf16 [T, H], required (the adapter gradients use it)
- *   saved    : as e4b_moe_dgrad (NULL recomputes the gate/up projections)
+ *   saved    : the buffer filled by e4b_moe_lora_forward with the same
+ *              adapters, or NULL (recomputes the forward's projections,
+ *              bitwise equal to the saved ones)
  *   dA_gu, dB_gu, dA_dn, dB_dn : device fp32, adapter shapes (written, not
  *              accumulated); each sum runs over an expert's pairs in sorted
  *              order, so results are deterministic

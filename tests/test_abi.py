@@ -136,10 +136,11 @@ def test_workspace_and_saved_sizes(E, H, I, k, T):
     # bf16 g|u in blocks of 256 rows x 128 pairs (g and u) per m-tile (at most
     # P / 256 + min(E, P) tiles of 256 pairs), then the permutation: an int4 per
     # m-tile, offsets and tile offsets over E + 1 experts, sorted pairs and
-    # pair positions
+    # pair positions; then the LoRA forward's two fp32 [P, 16] rank projections
     m_tiles = (P + min(E, P) * 255) // 256
     gu = m_tiles * -(-I // 128) * 256 * 128 * 2 * 2
-    assert saved == -(-gu // 256) * 256 + 16 * m_tiles + 8 * (E + 1) + 8 * P
+    perm_end = -(-gu // 256) * 256 + 16 * m_tiles + 8 * (E + 1) + 8 * P
+    assert saved == -(-perm_end // 256) * 256 + 2 * P * 16 * 4
     ws = lib.e4b_moe_workspace_bytes(ctypes.byref(L), T, k)
     # at least the dgrad intermediates: g|u, dGU, grad_x rows
     assert ws >= P * (2 * I * 2 * 2 + H * 2)
