@@ -110,7 +110,8 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
   constexpr bool kQ = SK != SK_BF16;
   constexpr bool kMX = SK == SK_MX;
   constexpr bool kNN = BMODE == B_NN;
-  static_assert(EPI == EPI_SWIGLU || EPI == EPI_ACT || EPI == EPI_STORE, "forward / gate_up dgrad epilogues");
+  static_assert(EPI == EPI_SWIGLU || EPI == EPI_ACT || EPI == EPI_STORE || EPI == EPI_DSWIGLU,
+                "forward / dgrad epilogues");
   // the codebook first: its LDS address fits a ds_read's immediate offset
   __shared__ __attribute__((aligned(64))) float sCode[16];
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kLds];
@@ -512,6 +513,78 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
           }
       }
     }
+  } else if (EPI == EPI_DSWIGLU) {
+    // down dgrad of a gated layer: the wave's 128 columns are the pairs of
+    // g|u block blk = 2 nt + wn. Per pair, from the saved g|u and the routing
+    // weight w: grad_a = w G2, dg = grad_a u silu'(g), du = grad_a silu(g)
+    // (bf16 into dGU [row, g | u]); per row, the block's share of
+    // d y / d w = sum of G2 silu(g) u over its pairs.
+    static_assert(EPI != EPI_DSWIGLU || kBN == 2 * kGuBlockPairs, "two g|u blocks per tile");
+    const int npb = (g.I + kGuBlockPairs - 1) / kGuBlockPairs;
+    const int blk = 2 * nt + wn;
+    const int cmax = min(kGuBlockPairs, g.I - blk * kGuBlockPairs) - 4;  // last chunk the forward wrote
+    if (cmax >= 0) {  // uniform over the wave
+      // the lane's 4 chunks of batch b = (row tile i, column tile j) = (b / 4, b % 4)
+      // (g[4], u[4] of 4 consecutive pairs each), clamped to chunks the forward
+      // wrote (results past I are not stored); batch b + 1 is in flight while
+      // batch b is used
+      int rr[kMI];
+      float wr[kMI];
+#pragma unroll
+      for (int i = 0; i < kMI; ++i) rr[i] = min(lrow + i * 32, valid_rows - 1);
+#pragma unroll
+      for (int i = 0; i < kMI; ++i) wr[i] = g.topk_w[g.sorted_pair[seg + row0 + rr[i]]];
+      u32x4 v[2][4];
+      auto fetch = [&](int b, int slot) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = min((b & 3) * 32 + 8 * q + 4 * (lane >> 5), cmax);
+          v[slot][q] = *reinterpret_cast<const u32x4 *>(g.GU + gu_chunk(mt, blk, npb, rr[b >> 2], c) * 8);
+        }
+      };
+      float part[kMI];
+#pragma unroll
+      for (int i = 0; i < kMI; ++i) part[i] = 0.0f;
+      fetch(0, 0);
+#pragma unroll
+      for (int b = 0; b < 4 * kMI; ++b) {
+        if (b + 1 < 4 * kMI) fetch(b + 1, (b + 1) & 1);
+        const int i = b >> 2, j = b & 3;
+        const int row = lrow + i * 32;
+        uint16_t *crow = g.C + (seg + row0 + rr[i]) * int64_t(g.ldc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = j * 32 + 8 * q + 4 * (lane >> 5);
+          const int n = blk * kGuBlockPairs + c;
+          const u32x4 cv4 = v[b & 1][q];
+          const float gv[4] = {bf16_lo(cv4[0]), bf16_hi(cv4[0]), bf16_lo(cv4[1]), bf16_hi(cv4[1])};
+          const float uv[4] = {bf16_lo(cv4[2]), bf16_hi(cv4[2]), bf16_lo(cv4[3]), bf16_hi(cv4[3])};
+          float dg[4], du[4], pq = 0.0f;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float sg = sigmoidf_(gv[t]);
+            const float silu = gv[t] * sg;
+            const float G2 = acc[i][j][4 * q + t];
+            pq += G2 * (silu * uv[t]);
+            const float ga = wr[i] * G2;
+            dg[t] = ga * uv[t] * sg * (1.0f + gv[t] * (1.0f - sg));
+            du[t] = ga * silu;
+          }
+          if (row < valid_rows && c <= cmax) {
+            part[i] += pq;
+            *reinterpret_cast<u32x2 *>(crow + n) = u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+            *reinterpret_cast<u32x2 *>(crow + g.I + n) =
+                u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kMI; ++i) {
+        // the two half-waves hold the two column halves of the same rows
+        const float pr = part[i] + __shfl_xor(part[i], 32);
+        if (lane < 32 && lrow + i * 32 < valid_rows) g.partial[(seg + row0 + rr[i]) * int64_t(npb) + blk] = pr;
+      }
+    }
   } else {  // EPI_ACT: ungated, h = this tile's columns of the up projection, a = silu(h)
 #pragma unroll
     for (int i = 0; i < kMI; ++i) {
@@ -564,6 +637,7 @@ hipError_t launch_gemm_wide(GemmVariant v, const GemmArgs &a, hipStream_t s, con
       E4B_WIDE(A_GATHER, B_NT, EPI_ACT);
     case GEMM_DOWN_FWD: E4B_WIDE(A_DIRECT, B_NT, EPI_STORE);
     case GEMM_GATE_UP_DGRAD: E4B_WIDE(A_DIRECT, B_NN, EPI_STORE);
+    case GEMM_DOWN_DGRAD: E4B_WIDE(A_GATHER, B_NN, EPI_DSWIGLU);
     default: break;
   }
 #undef E4B_WIDE_SK

@@ -340,3 +340,23 @@ def test_grouped_topk_equals_E():
     gx_ref, gw_ref = _oracle_dgrad(pb, idx_ref, w_ref)
     tol_check(to_np(gx), gx_ref, "grad_x top_k=E")
     tol_check(to_np(gw), gw_ref, "grad_w top_k=E")
+
+
+@pytest.mark.parametrize("kind", ["nf4", "mxfp4", "bf16"])
+@pytest.mark.parametrize("I", [256, 320])
+def test_down_dgrad_wide_tile(kind, I):
+    """H = 4096 puts the down dgrad on the 256-column tile: two g|u blocks per
+    tile (I = 256), and a tile whose second block lies past I (I = 320)."""
+    cfg = MoEConfig("wide_dgrad", E=4, H=4096, I=I, k=2, T=300, routing="uniform")
+    announce(f"wide down dgrad {kind} E4 H4096 I{I} k2 T300")
+    pb = Problem(cfg, seed=7, codebook=kind)
+    y, idx, w, saved = e4b.moe_forward(pb.layer, pb.x_d, cfg.k, logits=pb.logits_d, save=True,
+                                       path="grouped")
+    idx_ref, w_ref = oracle.route(pb.logits, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    gx, gw = e4b.moe_dgrad(pb.layer, idx, w, pb.grad_y_d, saved=saved)
+    gx2, gw2 = e4b.moe_dgrad(pb.layer, idx, w, pb.grad_y_d, x=pb.x_d)
+    assert torch.equal(gx.view(torch.uint8), gx2.view(torch.uint8)) and torch.equal(gw, gw2)
+    gx_ref, gw_ref = _oracle_dgrad(pb, idx_ref, w_ref)
+    tol_check(to_np(gx), gx_ref, f"grad_x wide {kind}")
+    tol_check(to_np(gw), gw_ref, f"grad_w wide {kind}")
