@@ -353,20 +353,25 @@ def bench_lora(args, e4b, torch, base_dt):
             "lora_flops_per_step": lora_flops, "vs_frozen_base_step": round(dt / base_dt, 4)}
 
 
-def bench_bf16_lane(args, e4b, torch, base_dt):
-    """The OLMoE-shaped training step on the bf16 passthrough lane (weights
-    stored bf16, no dequantization): the fidelity anchor."""
+def bench_lane(args, e4b, torch, base_dt, kind):
+    """The OLMoE-shaped training step on another storage lane: bf16
+    passthrough (weights stored bf16, no dequantization: the fidelity
+    anchor), or the int8 / fp8 blockwise lanes (one code byte per weight,
+    dequantized to bf16 in the workspace at each call, then the bf16-lane
+    GEMMs)."""
     cfg, x, gy, lg = olmoe_inputs(e4b, torch)
-    layer = build_layer(e4b, torch, cfg, 0, "bf16")[0]
+    layer = build_layer(e4b, torch, cfg, 0, kind)[0]
     step, keep = train_step_fn(e4b, torch, layer, x, lg, gy, cfg.k)
     dt = timed_steps(torch, step, args.warmup, args.steps)
     tflops = 12.0 * cfg.P * cfg.H * cfg.I / dt / 1e12
-    log(f"bf16 lane: step {dt * 1e3:.3f} ms -> {tflops:.1f} TFLOP/s ({base_dt / dt:.3f} x the nf4 "
+    log(f"{kind} lane: step {dt * 1e3:.3f} ms -> {tflops:.1f} TFLOP/s ({base_dt / dt:.3f} x the nf4 "
         "step's speed)")
     del keep, layer
     torch.cuda.empty_cache()
-    return {"workload": "olmoe_bf16", "ms_per_step": round(dt * 1e3, 4), "tflops": round(tflops, 1),
-            "weight_bytes": 2 * cfg.E * 3 * cfg.H * cfg.I, "nf4_step_over_bf16_step": round(base_dt / dt, 4)}
+    per_weight = {"bf16": 2.0, "int8": 1.0 + 4.0 / 64, "fp8": 1.0 + 4.0 / 64}[kind]
+    return {"workload": f"olmoe_{kind}", "ms_per_step": round(dt * 1e3, 4), "tflops": round(tflops, 1),
+            "weight_bytes": int(per_weight * cfg.E * 3 * cfg.H * cfg.I),
+            f"nf4_step_over_{kind}_step": round(base_dt / dt, 4)}
 
 
 def bench_mx8(args, e4b, torch, ev):
@@ -661,6 +666,7 @@ def main():
                     help="only run the decode measurement and print its JSON object")
     ap.add_argument("--no-lora", action="store_true")
     ap.add_argument("--no-bf16-lane", action="store_true")
+    ap.add_argument("--no-8bit-lanes", action="store_true")
     ap.add_argument("--no-stream", action="store_true")
     ap.add_argument("--no-mx", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -702,7 +708,9 @@ def main():
     head = results[keys[0]]
     olmoe_ms = results["olmoe_nf4"]["ms_per_step"] * 1e-3 if "olmoe_nf4" in results else None
     lora = None if args.no_lora or olmoe_ms is None else bench_lora(args, e4b, torch, olmoe_ms)
-    bf16 = None if args.no_bf16_lane or olmoe_ms is None else bench_bf16_lane(args, e4b, torch, olmoe_ms)
+    bf16 = None if args.no_bf16_lane or olmoe_ms is None else bench_lane(args, e4b, torch, olmoe_ms, "bf16")
+    lanes8 = None if args.no_8bit_lanes or olmoe_ms is None else {
+        kind: bench_lane(args, e4b, torch, olmoe_ms, kind) for kind in ("int8", "fp8")}
     mx = None if args.no_mx else bench_mx8(args, e4b, torch, ev)
     dec = None if args.no_decode else bench_decode(args, e4b, torch, ev)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, keys[0])
@@ -728,6 +736,7 @@ def main():
         "decode": dec,
         "lora": lora,
         "bf16_lane": bf16,
+        "lanes_8bit": lanes8,
         "mx8_forward": mx,
         "cpu_baseline": cpu,
         "host": host_info(torch),
