@@ -32,7 +32,8 @@ GemmArgs base_args(const MoePlan &p, const e4b_stack &st, const PermView &v) {
   a.Wa = a.mx ? nullptr : st.absmax;
   a.Ws = a.mx ? st.scales : nullptr;
   const bool bf16 = st.codebook == E4B_CB_BF16;
-  a.w_e_bytes = bf16 ? st.out * st.in * 2 : st.out * st.in / 2;
+  const bool c8 = st.codebook == E4B_CB_INT8 || st.codebook == E4B_CB_FP8;
+  a.w_e_bytes = bf16 ? st.out * st.in * 2 : (c8 ? st.out * st.in : st.out * st.in / 2);
   a.w_e_blocks = bf16 ? 0 : st.out * st.in / (a.mx ? kMxBlock : kBlock);  // BF16: none
   a.w_in = int32_t(st.in);
   a.I = int32_t(p.I);
@@ -64,28 +65,6 @@ hipError_t run_gate_up(const MoePlan &p, const e4b_moe_layer *L, const uint16_t 
   return launch_grouped_gemm(GEMM_GATE_UP_FWD, a, s, ev);
 }
 
-// An INT8 / FP8 layer runs as the bf16 lane on its stacks dequantized into
-// the workspace ([README] support matrix: these lanes' inference
-// dequantizes, no GEMV): both stacks are expanded to bf16(fl32(code * absmax))
-// and the call continues on a bf16 view of the layer.
-hipError_t stage_8bit(MoePlan &p, const e4b_moe_layer *&L, e4b_moe_layer &view, char *w,
-                      hipStream_t s) {
-  if (p.codebook != E4B_CB_INT8 && p.codebook != E4B_CB_FP8) return hipSuccess;
-  uint8_t *gu = reinterpret_cast<uint8_t *>(w + p.off_w8_gu);
-  uint8_t *dn = reinterpret_cast<uint8_t *>(w + p.off_w8_dn);
-  hipError_t err = launch_dequantize8(L->gate_up, true, gu, s);
-  if (err == hipSuccess) err = launch_dequantize8(L->down, true, dn, s);
-  if (err != hipSuccess) return err;
-  view = *L;
-  view.gate_up.packed = gu;
-  view.down.packed = dn;
-  view.gate_up.absmax = view.down.absmax = nullptr;
-  view.gate_up.codebook = view.down.codebook = E4B_CB_BF16;
-  p.codebook = E4B_CB_BF16;
-  L = &view;
-  return hipSuccess;
-}
-
 }  // namespace
 }  // namespace e4b
 
@@ -114,8 +93,6 @@ extern "C" e4b_status e4b_moe_forward_timed(const e4b_moe_layer *L, int64_t T, i
     E4B_TRY(launch_decode_forward(p, L, x, router_logits, topk_idx, topk_w, y, w, stream, ev));
     return E4B_OK;
   }
-  e4b_moe_layer view;
-  E4B_TRY(stage_8bit(p, L, view, w, stream));
   if (router_logits)
     E4B_TRY(launch_route(router_logits, T, int(p.E), top_k, topk_idx, topk_w, stream, ev));
   if (path == E4B_PATH_MX8) {
@@ -209,8 +186,6 @@ extern "C" e4b_status e4b_moe_dgrad_timed(const e4b_moe_layer *L, int64_t T, int
                    ws_bytes);
   if (st != E4B_OK || T == 0) return st;
   char *w = static_cast<char *>(ws);
-  e4b_moe_layer view;
-  E4B_TRY(stage_8bit(p, L, view, w, stream));
   // the saved buffer holds the forward's permutation; without it the
   // permutation and the gate_up projection are recomputed
   const uint16_t *gu = static_cast<const uint16_t *>(saved);
@@ -386,8 +361,6 @@ extern "C" e4b_status e4b_moe_lora_forward(const e4b_moe_layer *L, const e4b_lor
   const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
   const LoraWs l = lora_ws(p, w);
   const float sc = lora_scale(lora);
-  e4b_moe_layer view;
-  E4B_TRY(stage_8bit(p, L, view, w, stream));
 
   if (router_logits)
     E4B_TRY(launch_route(router_logits, T, int(p.E), top_k, topk_idx, topk_w, stream));
@@ -449,8 +422,6 @@ extern "C" e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lo
     return E4B_ERR_ALIGN;
   if (ws_bytes < p.lora_ws_bytes) return E4B_ERR_WORKSPACE;
   char *w = static_cast<char *>(ws);
-  e4b_moe_layer view;
-  E4B_TRY(stage_8bit(p, L, view, w, stream));
   const uint16_t *x = static_cast<const uint16_t *>(x_bf16);
   const uint16_t *gy = static_cast<const uint16_t *>(grad_y_bf16);
   const LoraWs l = lora_ws(p, w);

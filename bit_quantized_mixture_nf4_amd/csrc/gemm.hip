@@ -31,6 +31,7 @@
 // dequantized once per workgroup (codebook in LDS, fp32 multiply by the block
 // absmax, round-to-nearest-even bf16), i.e. exactly the bf16 view that
 // e4b_dequantize_nf4 returns.
+#include "codebook8.h"
 #include "gemm_dev.h"
 
 namespace e4b {
@@ -44,6 +45,8 @@ namespace e4b {
 // the halves of a K-step in opposite order). WN = 1: 256 threads, one LDS
 // stage, two workgroups per CU hide each other's staging and epilogues.
 // QB = 1: the bf16 passthrough lane (B is stored bf16 and staged as is).
+// QB = 2: the int8 / fp8 lanes (one code byte per weight, fp32 absmax per 64,
+// decoded through a 256-entry table like the 4-bit codes).
 template <int AMODE, int BMODE, int EPI, int WN, int QB>
 __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel(GemmArgs g) {
   constexpr int kGemmWavesN = WN;
@@ -57,11 +60,12 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   // (8 consecutive k of one n per lane) is read with the LDS transpose read
   // ds_read_b64_tr_b16, which hands each lane of a 16-lane group 4
   // consecutive rows of one column of a 4 x 16 block.
-  constexpr bool kNNq = BMODE == B_NN && !QB;
+  constexpr bool kNNq = BMODE == B_NN && QB != 1;
+  constexpr bool kC8 = QB == 2;
   constexpr int kSBn = kBN + 16;
   static_assert(kBK * kSBn <= kBN * kLds, "B_NN tile fits the B stage");
   // the codebook first: its LDS address fits a ds_read's immediate offset
-  __shared__ __attribute__((aligned(64))) float sCode[16];
+  __shared__ __attribute__((aligned(64))) float sCode[kC8 ? 256 : 16];
   __shared__ __attribute__((aligned(16))) uint16_t sA[kStages][kBM * kLds];
   __shared__ __attribute__((aligned(16))) uint16_t sB[kStages][kBN * kLds];
 
@@ -87,6 +91,10 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   const int e = tm.x, seg = tm.y, row0 = tm.z, valid_rows = tm.w;
 
   if (!QB && tid < 16) sCode[tid] = codebook_value(g.cb, tid);
+  if (kC8 && tid < 256) {
+    const float mg = kMag8[g.cb - E4B_CB_INT8].v[tid & 127];
+    sCode[tid] = tid < 128 ? mg : -mg;  // code byte = sign bit 7 | magnitude index
+  }
 
   // ---- A rows: column chunk (tid & 7) of rows (tid >> 3) + (kThreads / 8) i.
   // Rows past the segment read the last valid row: their outputs are never
@@ -107,7 +115,7 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   // block scales: fp32 absmax per 64 elements, or (MXFP4) an E8M0 byte per 32
   const float *wa = g.mx ? nullptr : g.Wa + int64_t(e) * g.w_e_blocks;
   const uint8_t *ws8 = g.mx ? g.Ws + int64_t(e) * g.w_e_blocks : nullptr;
-  const int row_bytes = QB ? g.w_in * 2 : g.w_in >> 1, row_blocks = g.w_in >> 6;
+  const int row_bytes = QB == 1 ? g.w_in * 2 : (kC8 ? g.w_in : g.w_in >> 1), row_blocks = g.w_in >> 6;
   const int row_mx = g.w_in >> 5;
   // B_NT: thread owns half (32 elements) of one tile column = one weight row
   const int b_c = tid >> 1, b_half = tid & 1;
@@ -122,7 +130,7 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
       b_row = b_row < g.N ? b_row : 0;
     }
   }
-  const uint8_t *b_src_nt = wp + int64_t(b_row) * row_bytes + b_half * (QB ? 64 : 16);
+  const uint8_t *b_src_nt = wp + int64_t(b_row) * row_bytes + b_half * (QB == 1 ? 64 : (kC8 ? 32 : 16));
   const float *b_am_nt = g.mx ? nullptr : wa + int64_t(b_row) * row_blocks;
   // MXFP4: the thread's 32 elements of K-step ks are the MX block 2 ks + b_half
   const uint8_t *b_sc_nt = g.mx ? ws8 + int64_t(b_row) * row_mx + b_half : nullptr;
@@ -137,20 +145,20 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
   const int q_row = tid / (kBN / 32), q_c = tid % (kBN / 32);
   int q_col = nt * kBN + q_c * 32;
   q_col = q_col < g.N ? q_col : 0;
-  const uint8_t *b_src_q = wp + int64_t(q_row) * row_bytes + (q_col >> 1);
+  const uint8_t *b_src_q = wp + int64_t(q_row) * row_bytes + (kC8 ? q_col : q_col >> 1);
   const float *b_am_q = g.mx ? nullptr : wa + int64_t(q_row) * row_blocks + (q_col >> 6);
   const uint8_t *b_sc_q = g.mx ? ws8 + int64_t(q_row) * row_mx + (q_col >> 5) : nullptr;
 
   u32x4 ra[kAPass];
-  u32x4 rb;
+  u32x4 rb, rb2;  // codes of the thread's 32 weights (8-bit: 32 bytes)
   float ram;
-  u32x4 rbq[QB ? 4 : 1];  // bf16 lane: B_NT 32 elements of a row, B_NN 4 rows x 8 columns
+  u32x4 rbq[QB == 1 ? 4 : 1];  // bf16 lane: B_NT 32 elements of a row, B_NN 4 rows x 8 columns
 
   auto load = [&](int ks) {
 #pragma unroll
     for (int i = 0; i < kAPass; ++i)
       ra[i] = *reinterpret_cast<const u32x4 *>(g.A + a_off[i] + uint32_t(ks * kBK));
-    if (QB) {
+    if (QB == 1) {
 #pragma unroll
       for (int d = 0; d < 4; ++d)
         rbq[d] = BMODE == B_NT
@@ -158,10 +166,12 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
                      : *reinterpret_cast<const u32x4 *>(b_src_nn +
                                                         (int64_t(ks) * kBK + d) * row_bytes);
     } else if (BMODE == B_NT) {
-      rb = *reinterpret_cast<const u32x4 *>(b_src_nt + ks * (kBK / 2));
+      rb = *reinterpret_cast<const u32x4 *>(b_src_nt + ks * (kC8 ? kBK : kBK / 2));
+      if (kC8) rb2 = *reinterpret_cast<const u32x4 *>(b_src_nt + ks * kBK + 16);
       ram = g.mx ? e8m0_value(b_sc_nt[2 * ks]) : b_am_nt[ks];
     } else {
       rb = *reinterpret_cast<const u32x4 *>(b_src_q + int64_t(ks) * kBK * row_bytes);
+      if (kC8) rb2 = *reinterpret_cast<const u32x4 *>(b_src_q + int64_t(ks) * kBK * row_bytes + 16);
       ram = g.mx ? e8m0_value(b_sc_q[int64_t(ks) * kBK * row_mx])
                  : b_am_q[int64_t(ks) * kBK * row_blocks];
     }
@@ -174,7 +184,7 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
       *reinterpret_cast<u32x4 *>(a_dst + ((tid >> 3) + (kThreads / 8) * i) * kLds + a_cc * 8) =
           ra[i];
     uint16_t *b_dst = sB[buf];
-    if (QB) {
+    if (QB == 1) {
       if (BMODE == B_NT) {
 #pragma unroll
         for (int d = 0; d < 4; ++d)
@@ -194,8 +204,17 @@ __global__ __launch_bounds__(256 * WN, WN == 1 ? 2 : 1) void grouped_gemm_kernel
       // byte of hi4 / lo4 is the byte offset (4 * nibble) of a table entry
       float c[32];
       const char *tbl = reinterpret_cast<const char *>(sCode);
+      if (kC8) {
+        // byte j of the 32 is weight j: its table offset is 4 * byte
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
+        for (int d = 0; d < 8; ++d)
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            c[4 * d + b] = *reinterpret_cast<const float *>(
+                tbl + (__builtin_amdgcn_perm(0u, d < 4 ? rb[d] : rb2[d - 4], 0x0C0C0C00u | uint32_t(b)) << 2));
+      }
+#pragma unroll
+      for (int d = 0; d < 4 && !kC8; ++d) {
         const uint32_t hi4 = (rb[d] >> 2) & 0x3C3C3C3Cu, lo4 = (rb[d] << 2) & 0x3C3C3C3Cu;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -640,11 +659,12 @@ hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s,
   if (a.grid == 0) return hipSuccess;
   // a multiple of 8 blocks: each XCD then has at least ceil(W / 8) of them
   const dim3 grid((a.grid + 7) / 8 * 8);
-  const bool qb = a.cb == E4B_CB_BF16;
+  const int qb = a.cb == E4B_CB_BF16 ? 1 : (a.cb == E4B_CB_INT8 || a.cb == E4B_CB_FP8 ? 2 : 0);
   const int kid = int(v);  // GemmVariant ids are the e4b_kernel ids of the four GEMMs
 #define E4B_GEMM(AM, BM, EP, WNV)                                                              \
-  return qb ? launch_k(ev, kid, grouped_gemm_kernel<AM, BM, EP, WNV, 1>, grid, dim3(256 * (WNV)), s, a) \
-            : launch_k(ev, kid, grouped_gemm_kernel<AM, BM, EP, WNV, 0>, grid, dim3(256 * (WNV)), s, a)
+  return qb == 1   ? launch_k(ev, kid, grouped_gemm_kernel<AM, BM, EP, WNV, 1>, grid, dim3(256 * (WNV)), s, a) \
+         : qb == 2 ? launch_k(ev, kid, grouped_gemm_kernel<AM, BM, EP, WNV, 2>, grid, dim3(256 * (WNV)), s, a) \
+                   : launch_k(ev, kid, grouped_gemm_kernel<AM, BM, EP, WNV, 0>, grid, dim3(256 * (WNV)), s, a)
   switch (v) {
     case GEMM_GATE_UP_FWD:
     case GEMM_DOWN_FWD:

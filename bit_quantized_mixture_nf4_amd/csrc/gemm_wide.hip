@@ -25,12 +25,15 @@
 //   bf16 view that e4b_dequantize_nf4 returns.
 #include <type_traits>
 
+#include "codebook8.h"
 #include "gemm_dev.h"
 
 namespace e4b {
 
 // storage of the weight operand
-enum { SK_ABSMAX = 0, SK_MX = 1, SK_BF16 = 2 };
+// SK_CODE8: one code byte per weight (the int8 / fp8 lanes) and an fp32
+// absmax per 64, decoded through a 256-entry table exactly like the 4-bit codes
+enum { SK_ABSMAX = 0, SK_MX = 1, SK_BF16 = 2, SK_CODE8 = 3 };
 
 // the tile shape the launches use (waves along M; see wide::Shape)
 constexpr int kWideWM = 4;
@@ -109,11 +112,12 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
   constexpr int kNE = S::kNE, kNP = S::kNP, kRowsW = 32 * kMI;
   constexpr bool kQ = SK != SK_BF16;
   constexpr bool kMX = SK == SK_MX;
+  constexpr bool kC8 = SK == SK_CODE8;
   constexpr bool kNN = BMODE == B_NN;
   static_assert(EPI == EPI_SWIGLU || EPI == EPI_ACT || EPI == EPI_STORE || EPI == EPI_DSWIGLU,
                 "forward / dgrad epilogues");
   // the codebook first: its LDS address fits a ds_read's immediate offset
-  __shared__ __attribute__((aligned(64))) float sCode[16];
+  __shared__ __attribute__((aligned(64))) float sCode[kC8 ? 256 : 16];
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kLds];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kLds];
   static_assert(kBK * kSBn <= kBN * kLds, "B_NN tile fits the B stage");
@@ -141,7 +145,11 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
   const int4 tm = g.tile_map[mt];
   const int e = tm.x, seg = tm.y, row0 = tm.z, valid_rows = tm.w;
 
-  if (kQ && tid < 16) sCode[tid] = codebook_value(g.cb, tid);
+  if (kQ && !kC8 && tid < 16) sCode[tid] = codebook_value(g.cb, tid);
+  if (kC8 && tid < 256) {
+    const float mg = kMag8[g.cb - E4B_CB_INT8].v[tid & 127];
+    sCode[tid] = tid < 128 ? mg : -mg;  // code byte = sign bit 7 | magnitude index
+  }
 
   // ---- A: column chunk tid & 7 of rows (tid >> 3) + (kThreads / 8) i; rows
   // past the segment read the last valid row (their outputs are never stored) ----
@@ -157,9 +165,9 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
 
   // ---- B source; columns past N read a valid weight row / column instead ----
   const uint8_t *wp = g.Wp + int64_t(e) * g.w_e_bytes;
-  const float *wa = SK == SK_ABSMAX ? g.Wa + int64_t(e) * g.w_e_blocks : nullptr;
+  const float *wa = SK == SK_ABSMAX || kC8 ? g.Wa + int64_t(e) * g.w_e_blocks : nullptr;
   const uint8_t *ws8 = kMX ? g.Ws + int64_t(e) * g.w_e_blocks : nullptr;
-  const int row_bytes = kQ ? g.w_in >> 1 : g.w_in * 2;
+  const int row_bytes = kC8 ? g.w_in : (kQ ? g.w_in >> 1 : g.w_in * 2);
   const int row_blocks = g.w_in >> 6, row_mx = g.w_in >> 5;
   // B_NT: the thread owns tile column b_c = one weight row; its kNU units
   // are the 32-weight halves b_h0 .. b_h0 + kNU - 1 of the row's 64-step
@@ -195,8 +203,8 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
     q_c[h] = u & 7;
     int col = nt * kBN + q_c[h] * 32;
     col = col < g.N ? col : 0;
-    b_nnq[h] = wp + int64_t(q_row[h]) * row_bytes + (col >> 1);
-    b_nna[h] = SK == SK_ABSMAX ? wa + int64_t(q_row[h]) * row_blocks + (col >> 6) : nullptr;
+    b_nnq[h] = wp + int64_t(q_row[h]) * row_bytes + (kC8 ? col : col >> 1);
+    b_nna[h] = SK == SK_ABSMAX || kC8 ? wa + int64_t(q_row[h]) * row_blocks + (col >> 6) : nullptr;
     b_nns[h] = kMX ? ws8 + int64_t(q_row[h]) * row_mx + (col >> 5) : nullptr;
     p_cg[h] = u >> 4;
     p_kg[h] = u & 15;
@@ -210,6 +218,7 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
   // ---- registers of the staging pipeline ----
   u32x4 ra[kAP];                    // A rows of K-step ks + 1
   u32x4 rb[2][kNU];                 // 4-bit B: codes of two K-steps (sets by parity)
+  u32x4 rb2[2][kNU];                // 8-bit B: the second 16 code bytes of each unit
   float rs[2][kNU];                 // their block scales (per unit)
   u32x4 rq[4 * kNU];                // bf16 B of K-step ks + 1
 
@@ -224,10 +233,15 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
   // 4-bit B of K-step ks into register set st
   auto load_b = [&](int ks, int st) {
     if (!kNN) {
-      const u32x4 *src = reinterpret_cast<const u32x4 *>(b_nt + ks * (kBK / 2));
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(b_nt + ks * (kC8 ? kBK : kBK / 2));
 #pragma unroll
       for (int h = 0; h < kNU; ++h) {
-        rb[st][h] = src[b_h0 + h];
+        if (kC8) {
+          rb[st][h] = src[2 * (b_h0 + h)];
+          rb2[st][h] = src[2 * (b_h0 + h) + 1];
+        } else {
+          rb[st][h] = src[b_h0 + h];
+        }
         // a 64-step is one absmax block, or two MX blocks (one per half)
         rs[st][h] = kMX ? e8m0_value(ws8[int64_t(b_row) * row_mx + 2 * ks + b_h0 + h])
                         : wa[int64_t(b_row) * row_blocks + ks];
@@ -236,6 +250,7 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
 #pragma unroll
       for (int h = 0; h < kNU; ++h) {
         rb[st][h] = *reinterpret_cast<const u32x4 *>(b_nnq[h] + int64_t(ks) * kBK * row_bytes);
+        if (kC8) rb2[st][h] = *reinterpret_cast<const u32x4 *>(b_nnq[h] + int64_t(ks) * kBK * row_bytes + 16);
         rs[st][h] = kMX ? e8m0_value(b_nns[h][int64_t(ks) * kBK * row_mx])
                         : b_nna[h][int64_t(ks) * kBK * row_blocks];
       }
@@ -278,10 +293,18 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
   const char *tbl = reinterpret_cast<const char *>(sCode);
   float cv[kNE];
   auto lookup = [&](int st, int el) {
-    const uint32_t word = rb[st][el >> 5][(el >> 3) & 3];
-    const uint32_t sh = (el & 1) ? (word << 2) : (word >> 2);
-    const uint32_t off = __builtin_amdgcn_perm(0u, sh & 0x3C3C3C3Cu, 0x0C0C0C00u | uint32_t((el >> 1) & 3));
-    cv[el] = *reinterpret_cast<const float *>(tbl + off);
+    if constexpr (kC8) {
+      // byte el & 31 of the unit: the table offset 4 * byte
+      const int b = el & 31;
+      const uint32_t word = (b < 16 ? rb[st][el >> 5] : rb2[st][el >> 5])[(b >> 2) & 3];
+      const uint32_t off = __builtin_amdgcn_perm(0u, word, 0x0C0C0C00u | uint32_t(b & 3)) << 2;
+      cv[el] = *reinterpret_cast<const float *>(tbl + off);
+    } else {
+      const uint32_t word = rb[st][el >> 5][(el >> 3) & 3];
+      const uint32_t sh = (el & 1) ? (word << 2) : (word >> 2);
+      const uint32_t off = __builtin_amdgcn_perm(0u, sh & 0x3C3C3C3Cu, 0x0C0C0C00u | uint32_t((el >> 1) & 3));
+      cv[el] = *reinterpret_cast<const float *>(tbl + off);
+    }
   };
   uint32_t bq[kNP];
   auto mul_pair = [&](int st, int p) {
@@ -621,10 +644,12 @@ hipError_t launch_gemm_wide(GemmVariant v, const GemmArgs &a, hipStream_t s, con
   // a multiple of 8 blocks: each XCD then has at least ceil(W / 8) of them
   const dim3 grid((a.grid + 7) / 8 * 8), block(wide::Shape<kWideWM>::kThreads);
   const int kid = int(v);
-  const int sk = a.cb == E4B_CB_BF16 ? SK_BF16 : (a.mx ? SK_MX : SK_ABSMAX);
+  const bool c8 = a.cb == E4B_CB_INT8 || a.cb == E4B_CB_FP8;
+  const int sk = a.cb == E4B_CB_BF16 ? SK_BF16 : (a.mx ? SK_MX : (c8 ? SK_CODE8 : SK_ABSMAX));
 #define E4B_WIDE_SK(AM, BM, EP, LO)                                                                          \
-  return sk == SK_BF16 ? launch_k(ev, kid, gemm_wide_kernel<AM, BM, EP, SK_BF16, LO, kWideWM>, grid, block, s, a) \
-         : sk == SK_MX ? launch_k(ev, kid, gemm_wide_kernel<AM, BM, EP, SK_MX, LO, kWideWM>, grid, block, s, a)   \
+  return sk == SK_BF16    ? launch_k(ev, kid, gemm_wide_kernel<AM, BM, EP, SK_BF16, LO, kWideWM>, grid, block, s, a)  \
+         : sk == SK_CODE8 ? launch_k(ev, kid, gemm_wide_kernel<AM, BM, EP, SK_CODE8, LO, kWideWM>, grid, block, s, a) \
+         : sk == SK_MX    ? launch_k(ev, kid, gemm_wide_kernel<AM, BM, EP, SK_MX, LO, kWideWM>, grid, block, s, a)    \
                        : launch_k(ev, kid, gemm_wide_kernel<AM, BM, EP, SK_ABSMAX, LO, kWideWM>, grid, block, s, a)
 #define E4B_WIDE(AM, BM, EP)                     \
   do {                                           \

@@ -123,10 +123,6 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   p->off_sorted = take(size_t(P) * 4);
   p->off_pos = take(size_t(P) * 4);
   p->off_tile_map = take(size_t(p->m_tiles_bound) * 16);
-  // an 8-bit layer's stacks expanded to bf16, which the call's GEMMs read
-  const bool w8 = p->codebook == E4B_CB_INT8 || p->codebook == E4B_CB_FP8;
-  p->off_w8_gu = w8 ? take(size_t(E) * size_t(p->gu_cols) * size_t(H) * 2) : 0;
-  p->off_w8_dn = w8 ? take(size_t(E) * size_t(H) * size_t(I) * 2) : 0;
   const size_t base = off;
   // forward region
   p->off_a = take(size_t(P) * I * 2);

@@ -58,7 +58,6 @@ struct MoePlan {
   size_t off_hist, off_chunk_base, off_counts, off_offsets, off_tile_offsets;
   size_t off_sorted, off_pos;
   size_t off_tile_map;  // int4 per m-tile: expert, segment start, first row, rows
-  size_t off_w8_gu, off_w8_dn;  // INT8 / FP8 layers: both stacks dequantized to bf16 for the call
   size_t off_a, off_o;                          // forward
   size_t off_dmap;  // forward, decode path: the grouping the gate_up launch leaves for the down launch
   size_t off_mx_xq, off_mx_xs, off_mx_aq, off_mx_as;  // forward, MX path (MXFP4 layers)

@@ -88,9 +88,10 @@ typedef enum {
  * (E2M1 codes + E8M0 scales), and the 8-bit blockwise lanes INT8 (the
  * dynamic tree map) and FP8 (an E4M3 codebook), one code byte per element:
  * sign bit 7 | index into 128 ascending magnitudes from 0 to 1 (the tables
- * are defined in csrc/codebook8.h). As on the pages, the 8-bit lanes have no
- * GEMV: their forward and dgrad dequantize both stacks to bf16 in the
- * workspace and run the bf16 lane's GEMMs. */
+ * are defined in csrc/codebook8.h). The grouped GEMMs decode the code bytes
+ * in their weight staging through a 256-entry table, as they decode the 4-bit
+ * codes (bf16(fl32(value * absmax))); as on the pages, the 8-bit lanes have
+ * no decode GEMV. */
 typedef enum {
   E4B_CB_NF4 = 0,
   E4B_CB_FP4 = 1,

@@ -342,7 +342,7 @@ def test_grouped_topk_equals_E():
     tol_check(to_np(gw), gw_ref, "grad_w top_k=E")
 
 
-@pytest.mark.parametrize("kind", ["nf4", "mxfp4", "bf16"])
+@pytest.mark.parametrize("kind", ["nf4", "mxfp4", "bf16", "int8", "fp8"])
 @pytest.mark.parametrize("I", [256, 320])
 def test_down_dgrad_wide_tile(kind, I):
     """H = 4096 puts the down dgrad on the 256-column tile: two g|u blocks per

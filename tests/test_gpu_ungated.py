@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("E,H,I,k,T,kind", [(8, 256, 128, 2, 64, "nf4"), (6, 192, 320, 2, 300, "nf4"),
-                                            (6, 192, 320, 2, 300, "bf16"), (4, 128, 64, 2, 5, "fp4")])
+                                            (6, 192, 320, 2, 300, "bf16"), (4, 128, 64, 2, 5, "fp4"),
+                                            (6, 192, 320, 2, 300, "int8"), (6, 192, 320, 2, 300, "fp8")])
 def test_ungated_forward_dgrad(E, H, I, k, T, kind):
     cfg = MoEConfig("ungated", E=E, H=H, I=I, k=k, T=T, routing="normal", gated=False)
     announce(f"ungated {kind} E{E} H{H} I{I} k{k} T{T}")
