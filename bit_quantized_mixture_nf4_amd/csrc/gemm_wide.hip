@@ -41,7 +41,11 @@ constexpr int kWideWM = 4;
 namespace wide {
 
 constexpr int kBN = 256;
-constexpr int kSBn = kBN + 16;   // B_NN [k][n] tile row stride (elements)
+// B_NN [k][n] tile row stride (elements): 576 bytes, 16 banks past a multiple
+// of 64, so that the four rows x 16 columns of the two 16-lane groups that a
+// transpose read serves in one pass fall on distinct banks (a 272-element
+// stride put their rows 8 banks apart: 2-way conflicts)
+constexpr int kSBn = kBN + 32;
 constexpr uint32_t kGroupM = 4;  // m-tiles per group of the tile order
 
 // The two shapes of the 256 x 256 tile: WM waves along M (2 along N).
