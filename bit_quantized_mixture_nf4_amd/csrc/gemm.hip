@@ -670,7 +670,7 @@ hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s,
     case GEMM_DOWN_FWD:
     case GEMM_GATE_UP_DGRAD: return launch_gemm_wide(v, a, s, ev);
     case GEMM_DOWN_DGRAD:
-      if (a.gated && a.K >= kWideDgradMinK) {
+      if (a.gated) {
         // 256-column tiles: the same m-tiles, half as many n-tiles; the
         // partials keep one entry per 128-pair block
         GemmArgs w = a;
@@ -678,7 +678,6 @@ hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s,
         w.grid = a.grid / uint32_t(a.n_tiles) * uint32_t(w.n_tiles);
         return launch_gemm_wide(v, w, s, ev);
       }
-      if (a.gated) E4B_GEMM(A_GATHER, B_NN, EPI_DSWIGLU, kBNNarrow / 128);
       E4B_GEMM(A_GATHER, B_NN, EPI_DACT, kBNNarrow / 128);
   }
 #undef E4B_GEMM

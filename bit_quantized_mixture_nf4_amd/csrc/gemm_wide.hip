@@ -545,11 +545,20 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
     // g|u block blk = 2 nt + wn. Per pair, from the saved g|u and the routing
     // weight w: grad_a = w G2, dg = grad_a u silu'(g), du = grad_a silu(g)
     // (bf16 into dGU [row, g | u]); per row, the block's share of
-    // d y / d w = sum of G2 silu(g) u over its pairs.
+    // d y / d w = sum of G2 silu(g) u over its pairs. Each row tile of the
+    // wave (32 rows x 128 dg | 128 du) is staged in the wave's own LDS rows
+    // and leaves as 256-byte row segments.
     static_assert(EPI != EPI_DSWIGLU || kBN == 2 * kGuBlockPairs, "two g|u blocks per tile");
+    constexpr int kDgSt = 2 * kGuBlockPairs + 8;  // staging row: dg | du of 128 pairs (bf16) + pad
+    static_assert(4 * 32 * kDgSt <= 2 * kBM * kLds && 4 * 32 * kDgSt <= 2 * kBN * kLds,
+                  "four waves' staging rows fit each stage pair");
     const int npb = (g.I + kGuBlockPairs - 1) / kGuBlockPairs;
     const int blk = 2 * nt + wn;
-    const int cmax = min(kGuBlockPairs, g.I - blk * kGuBlockPairs) - 4;  // last chunk the forward wrote
+    const int nvalid = min(kGuBlockPairs, g.I - blk * kGuBlockPairs);  // pairs of this block (a multiple of 64)
+    const int cmax = nvalid - 4;                                        // last chunk the forward wrote
+    // every wave has read its last fragments of the stages before they are reused
+    __syncthreads();
+    uint16_t *stg = (wave < 4 ? sA[0] : sB[0]) + (wave & 3) * 32 * kDgSt;
     if (cmax >= 0) {  // uniform over the wave
       // the lane's 4 chunks of batch b = (row tile i, column tile j) = (b / 4, b % 4)
       // (g[4], u[4] of 4 consecutive pairs each), clamped to chunks the forward
@@ -572,17 +581,16 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
       float part[kMI];
 #pragma unroll
       for (int i = 0; i < kMI; ++i) part[i] = 0.0f;
+      uint16_t *srow = stg + (lane & 31) * kDgSt;
       fetch(0, 0);
 #pragma unroll
       for (int b = 0; b < 4 * kMI; ++b) {
         if (b + 1 < 4 * kMI) fetch(b + 1, (b + 1) & 1);
         const int i = b >> 2, j = b & 3;
         const int row = lrow + i * 32;
-        uint16_t *crow = g.C + (seg + row0 + rr[i]) * int64_t(g.ldc);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int c = j * 32 + 8 * q + 4 * (lane >> 5);
-          const int n = blk * kGuBlockPairs + c;
           const u32x4 cv4 = v[b & 1][q];
           const float gv[4] = {bf16_lo(cv4[0]), bf16_hi(cv4[0]), bf16_lo(cv4[1]), bf16_hi(cv4[1])};
           const float uv[4] = {bf16_lo(cv4[2]), bf16_hi(cv4[2]), bf16_lo(cv4[3]), bf16_hi(cv4[3])};
@@ -597,11 +605,23 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
             dg[t] = ga * uv[t] * sg * (1.0f + gv[t] * (1.0f - sg));
             du[t] = ga * silu;
           }
-          if (row < valid_rows && c <= cmax) {
-            part[i] += pq;
-            *reinterpret_cast<u32x2 *>(crow + n) = u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
-            *reinterpret_cast<u32x2 *>(crow + g.I + n) =
-                u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+          if (row < valid_rows && c <= cmax) part[i] += pq;
+          *reinterpret_cast<u32x2 *>(srow + c) = u32x2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+          *reinterpret_cast<u32x2 *>(srow + kGuBlockPairs + c) =
+              u32x2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+        }
+        if (j == 3) {
+          // row tile i staged (the wave's own rows: LDS keeps one wave's
+          // operations in order): two rows per instruction, each as a
+          // 256-byte dg segment and a 256-byte du segment
+#pragma unroll 4
+          for (int it = 0; it < 16; ++it) {
+            const int r = 2 * it + (lane >> 5), half = (lane >> 4) & 1, ch = lane & 15;
+            const int trow = wm * kRowsW + i * 32 + r;
+            const u32x4 o = *reinterpret_cast<const u32x4 *>(stg + r * kDgSt + half * kGuBlockPairs + ch * 8);
+            if (trow < valid_rows && ch * 8 < nvalid)
+              *reinterpret_cast<u32x4 *>(g.C + (seg + row0 + trow) * int64_t(g.ldc) + (half ? g.I : 0) +
+                                         blk * kGuBlockPairs + ch * 8) = o;
           }
         }
       }

@@ -17,18 +17,11 @@ constexpr int kBM = 256;   // rows (routed pairs) per tile
 // pairs): 256 x 128 pairs of g and u, 128 KB (layout in kernels.h, gu_chunk)
 constexpr int kGuBlockPairs = 128;
 constexpr int kGuBlockChunks = kBM * kGuBlockPairs / 4;  // 16-byte chunks per block
-// output columns per tile: 256 (8 waves, one workgroup per CU) for both
-// gate_up GEMMs and the down forward, 128 (4 waves, two workgroups per CU) for
-// the down dgrad unless its reduction is long (below), each the faster shape
-// for that GEMM
+// output columns per tile: 256 (8 waves, one workgroup per CU) for every GEMM
+// of a gated layer; 128 (4 waves, two workgroups per CU) for the down dgrad of
+// an ungated layer
 constexpr int kBNWide = 256;
 constexpr int kBNNarrow = 128;
-// The down dgrad of a gated layer runs on the wide 256 x 256 tile (one
-// workgroup per CU) when its reduction H is at least this long; below it the
-// epilogue's g|u reads and dGU writes, which no second workgroup overlaps,
-// cost more than the wide tile saves, and the 256 x 128 tile (two
-// workgroups per CU) is used.
-constexpr int kWideDgradMinK = 4096;
 constexpr int kBK = 64;    // reduction step = one quantization block
 constexpr int kBlock = 64; // quantization block (elements along `in`)
 constexpr int kMxBlock = 32;  // MXFP4 scale block (elements along `in`)
