@@ -507,16 +507,24 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
         *reinterpret_cast<u32x4 *>(g.C + int64_t(seg + row0 + row) * g.ldc + col) = v;
     }
   } else if (EPI == EPI_SWIGLU) {
+    // a = silu(g) u of the wave's 64 pairs goes out through the wave's own LDS
+    // rows (one row tile of 32 rows at a time) as 128-byte row segments; the
+    // g|u chunks are stored directly (a wave writes 1 KB per instruction)
+    constexpr int kASt = 64 + 8;  // staging row: 64 pairs of a (bf16) + pad
+    static_assert(4 * 32 * kASt <= 2 * kBM * kLds, "four waves' staging rows fit a stage pair");
+    if (g.C) __syncthreads();  // uniform: every wave has read its last fragments of the stages
+    uint16_t *stg = (wave < 4 ? sA[0] : sB[0]) + (wave & 3) * 32 * kASt;
+    uint16_t *srow = stg + (lane & 31) * kASt;
 #pragma unroll
     for (int i = 0; i < kMI; ++i) {
       const int row = lrow + i * 32;
       if (row < valid_rows) {
-        const int64_t grow = seg + row0 + row;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int pair = nt * (kBN / 2) + wn * 64 + jj * 32 + 8 * q + 4 * (lane >> 5);
+            const int pw = jj * 32 + 8 * q + 4 * (lane >> 5);  // pair within the wave's 64
+            const int pair = nt * (kBN / 2) + wn * 64 + pw;
             if (pair < g.I) {
               float gv[4], uv[4], av[4];
 #pragma unroll
@@ -526,8 +534,7 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
                 av[t] = gv[t] * sigmoidf_(gv[t]) * uv[t];
               }
               if (g.C)
-                *reinterpret_cast<u32x2 *>(g.C + grow * g.ldc + pair) =
-                    u32x2{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
+                *reinterpret_cast<u32x2 *>(srow + pw) = u32x2{pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3])};
               static_assert(EPI != EPI_SWIGLU || kBN / 2 == kGuBlockPairs, "one g|u block per tile");
               if (g.GU) {
                 // the tile's 128 pairs are block nt of the blocked g|u
@@ -538,6 +545,19 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
               }
             }
           }
+      }
+      if (g.C) {
+        // row tile i staged (the wave's own rows: LDS keeps one wave's
+        // operations in order): eight rows of 128 bytes per instruction
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int r = 8 * it + (lane >> 3), ch = lane & 7;
+          const int trow = wm * kRowsW + i * 32 + r;
+          const int pair0 = nt * (kBN / 2) + wn * 64 + ch * 8;
+          const u32x4 o = *reinterpret_cast<const u32x4 *>(stg + r * kASt + ch * 8);
+          if (trow < valid_rows && pair0 < g.I)
+            *reinterpret_cast<u32x4 *>(g.C + (seg + row0 + trow) * int64_t(g.ldc) + pair0) = o;
+        }
       }
     }
   } else if (EPI == EPI_DSWIGLU) {
