@@ -203,7 +203,7 @@ def kernel_times(e4b, torch, ev, step, names, n):
 
 
 # Kernel sources whose text fixes the grouped GEMMs' memory traffic.
-GEMM_SOURCES = ("gemm.hip", "gemm_wide.hip", "gemm_dev.h", "device.h", "kernels.h", "plan.h")
+GEMM_SOURCES = ("gemm_wide.hip", "gemm_dev.h", "device.h", "kernels.h", "plan.h")
 
 
 def gemm_source_digest():

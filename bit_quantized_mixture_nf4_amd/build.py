@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libe4b.so")
 
-SOURCES = ["plan.cpp", "quant.hip", "route.hip", "gemm.hip", "gemm_wide.hip", "combine.hip", "decode.hip", "lora.hip", "mx.hip",
+SOURCES = ["plan.cpp", "quant.hip", "route.hip", "gemm_wide.hip", "combine.hip", "decode.hip", "lora.hip", "mx.hip",
            "api.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

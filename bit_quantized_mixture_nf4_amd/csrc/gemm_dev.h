@@ -1,4 +1,4 @@
-// gemm_dev.h -- device helpers shared by the grouped GEMM kernels.
+// gemm_dev.h -- device helpers of the grouped GEMM (gemm_wide.hip) and the LoRA kernels.
 #pragma once
 
 #include "device.h"

@@ -1,15 +1,36 @@
-// gemm_wide.hip -- grouped GEMM on 256 x 256 tiles, software-pipelined inside
-// each wave: the gate_up and down forward projections and the gate_up dgrad.
+// gemm_wide.hip -- the grouped GEMMs over routed pairs, with the stored
+// weight decoded on the fly (bf16 MFMA, fp32 accumulation): the gate_up and
+// down forward projections and both dgrad projections.
 //
-// Same operation, operands, tile schedule and epilogues as the kernel in
-// gemm.hip (the grouped-nf4-gemm design of the 0.31.1 project page: one
-// launch over the packed stacks, the 4-bit weight decoded inside the GEMM,
-// fp32 accumulation); what differs is the work inside a workgroup:
+// One launch covers every expert (the grouped-nf4-gemm design the 0.31.1
+// project page describes: one launch over the packed stacks, decode in the
+// kernel, fp32 accumulation). Rows of a tile are routed pairs of one expert in
+// sorted order; the tile schedule is read from device-side offsets, so the
+// host never synchronizes.
 //
-// * The launches use 8 waves of 64 x 128 (two per SIMD, 2 x 4 MFMA 32x32x16
-//   bf16 tiles and 128 fp32 accumulators per lane), so one wave's MFMAs run
-//   while the other waits for memory; the 4-wave shape (128 x 128 per wave,
-//   a third fewer LDS fragment bytes per MFMA) is kept as Shape<2>.
+// Operand modes
+//   A_GATHER : A[m] = src[token(sorted_pair[row])]   (x or grad_y, [T, lda])
+//   A_DIRECT : A[m] = src[row]                       (a or dGU, sorted rows)
+//   B_NT     : B[n][k] = W[n][k]   weight rows are output columns (forward)
+//   B_NN     : B[n][k] = W[k][n]   weight rows are the reduction (dgrad:
+//              grad_output @ W, bitsandbytes PR #1965 recompute bullet)
+// Epilogues
+//   EPI_SWIGLU  : columns are gate/up pairs; a = silu(g) * u -> bf16, and the
+//                 bf16 g, u are optionally stored for the backward
+//                 (0.1.0 sdist, Experts4bit.forward: chunk into gate | up).
+//   EPI_STORE   : bf16 store.
+//   EPI_DSWIGLU : dgrad of act(gate) * up scaled by the routing weight, plus
+//                 the tile's share of d y / d routing weight.
+//   EPI_ACT / EPI_DACT : the same for an ungated layer (has_gate=False in
+//                 Experts4bit.__init__: a plain up projection h, a = act(h)).
+//
+// Tile: 256 pairs x 256 columns x 64 (one quantization block per K-step).
+// * 8 waves of 64 x 128 (two per SIMD, 2 x 4 MFMA 32x32x16 bf16 tiles and
+//   128 fp32 accumulators per lane), so one wave's MFMAs run while the other
+//   waits for memory; the 4-wave shape (128 x 128 per wave, a third fewer LDS
+//   fragment bytes per MFMA) is kept as Shape<2>. The dequantized weight is
+//   the MFMA A operand, so a lane's accumulators hold runs of 4 consecutive
+//   output columns of one pair.
 // * The K loop is software-pipelined inside each wave. While the MFMAs of
 //   K-step ks run from LDS stage ks & 1, the wave stages K-step ks + 1 into
 //   the other stage -- LDS stores of the A rows it loaded one step earlier,
@@ -21,8 +42,17 @@
 //   work and a scheduling barrier closes it, so the compiler keeps the work
 //   between the MFMAs instead of clustering it, and the lookups' LDS latency
 //   elapses under the MFMAs that follow.
-// * B is dequantized exactly as in gemm.hip: bf16(fl32(code * scale)), the
-//   bf16 view that e4b_dequantize_nf4 returns.
+// * B is dequantized once per workgroup: bf16(fl32(code value * block
+//   scale)), the bf16 view that e4b_dequantize_nf4 returns. For B_NN the
+//   dequantized tile is kept in the weights' own [k][n] order (16-byte units
+//   of a row XOR-swizzled by nn_unit) and the MFMA operand (8 consecutive k
+//   of one n per lane) is read with the LDS transpose read ds_read_b64_tr_b16,
+//   which hands each lane of a 16-lane group 4 consecutive rows of one column
+//   of a 4 x 16 block.
+// * LoRA: one more 16-deep MFMA slice after the K loop, pair side = the
+//   per-pair rank projection (fp32 [P, 16], rounded to bf16), weight side =
+//   the bf16 pack of the scaled adapter [E, rows, 16] at the weight row of
+//   each tile column; the epilogues then see the adapted product.
 #include <type_traits>
 
 #include "codebook8.h"
@@ -118,7 +148,8 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
   constexpr bool kMX = SK == SK_MX;
   constexpr bool kC8 = SK == SK_CODE8;
   constexpr bool kNN = BMODE == B_NN;
-  static_assert(EPI == EPI_SWIGLU || EPI == EPI_ACT || EPI == EPI_STORE || EPI == EPI_DSWIGLU,
+  static_assert(EPI == EPI_SWIGLU || EPI == EPI_ACT || EPI == EPI_STORE || EPI == EPI_DSWIGLU ||
+                    EPI == EPI_DACT,
                 "forward / dgrad epilogues");
   // the codebook first: its LDS address fits a ds_read's immediate offset
   __shared__ __attribute__((aligned(64))) float sCode[kC8 ? 256 : 16];
@@ -324,7 +355,10 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
   };
 
   // ---- fragments: A rows wm * kRowsW + 32 i, B columns wn * 128 + 32 j ----
-  int q_off[4];  // B_NN: transpose-read addresses (see gemm.hip)
+  // B_NN transpose-read addresses: lane (group qg = lane / 16, qs = lane % 16)
+  // reads rows 8 (qg / 2) + qs / 4 (+ 16 kk + 4 r) and the 4 columns
+  // wn * 128 + 32 j + 16 (qg % 2) + 4 (qs % 4) of the [k][n] tile
+  int q_off[4];
   {
     const int qg = lane >> 4, qs = lane & 15;
     const int rrow = 8 * (qg >> 1) + (qs >> 2);
@@ -436,7 +470,7 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
   }
   if (ks < nK) kstep(std::integral_constant<int, 0>{}, ks);
 
-  // ---- LoRA: one more 16-deep slice (see gemm.hip) ----
+  // ---- LoRA: one more 16-deep slice ----
   if constexpr (LORA) {
     const int kh = lane >> 5;
     bf16x8 pf[kMI], wf[4];
@@ -652,6 +686,84 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
         if (lane < 32 && lrow + i * 32 < valid_rows) g.partial[(seg + row0 + rr[i]) * int64_t(npb) + blk] = pr;
       }
     }
+  } else if (EPI == EPI_DACT) {
+    // down dgrad of an ungated layer: the wave's 128 columns are the
+    // intermediate units of block blk = 2 nt + wn. Per unit, from the saved h
+    // and the routing weight w: dh = w G2 silu'(h) (bf16 into dH [row, unit]);
+    // per row, the block's share of d y / d w = sum of G2 silu(h). Each row
+    // tile of the wave (32 rows x 128 units) is staged in the wave's own LDS
+    // rows and leaves as 256-byte row segments.
+    constexpr int kDhSt = kGuBlockPairs + 8;  // staging row: 128 units of dh (bf16) + pad
+    static_assert(4 * 32 * kDhSt <= 2 * kBM * kLds, "four waves' staging rows fit a stage pair");
+    const int npb = (g.I + kGuBlockPairs - 1) / kGuBlockPairs;
+    const int blk = 2 * nt + wn;
+    const int nvalid = min(kGuBlockPairs, g.I - blk * kGuBlockPairs);  // units of this block (a multiple of 64)
+    __syncthreads();  // every wave has read its last fragments of the stages
+    uint16_t *stg = (wave < 4 ? sA[0] : sB[0]) + (wave & 3) * 32 * kDhSt;
+    if (nvalid > 0) {  // uniform over the wave
+      int rr[kMI];
+      float wr[kMI];
+#pragma unroll
+      for (int i = 0; i < kMI; ++i) rr[i] = min(lrow + i * 32, valid_rows - 1);
+#pragma unroll
+      for (int i = 0; i < kMI; ++i) wr[i] = g.topk_w[g.sorted_pair[seg + row0 + rr[i]]];
+      // h of batch b = (row tile i, column tile j): the lane's 4 runs of 4
+      // units, clamped to units below I; batch b + 1 is in flight while b is used
+      u32x2 v[2][4];
+      auto fetch = [&](int b, int slot) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = min((b & 3) * 32 + 8 * q + 4 * (lane >> 5), nvalid - 4);
+          v[slot][q] = *reinterpret_cast<const u32x2 *>(g.GU + (seg + row0 + rr[b >> 2]) * int64_t(g.ldgu) +
+                                                        blk * kGuBlockPairs + c);
+        }
+      };
+      float part[kMI];
+#pragma unroll
+      for (int i = 0; i < kMI; ++i) part[i] = 0.0f;
+      uint16_t *srow = stg + (lane & 31) * kDhSt;
+      fetch(0, 0);
+#pragma unroll
+      for (int b = 0; b < 4 * kMI; ++b) {
+        if (b + 1 < 4 * kMI) fetch(b + 1, (b + 1) & 1);
+        const int i = b >> 2, j = b & 3;
+        const int row = lrow + i * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = j * 32 + 8 * q + 4 * (lane >> 5);
+          const u32x2 hq = v[b & 1][q];
+          const float hv[4] = {bf16_lo(hq[0]), bf16_hi(hq[0]), bf16_lo(hq[1]), bf16_hi(hq[1])};
+          float dh[4], pq = 0.0f;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float sg = sigmoidf_(hv[t]);
+            const float G2 = acc[i][j][4 * q + t];
+            pq += G2 * (hv[t] * sg);
+            dh[t] = wr[i] * G2 * sg * (1.0f + hv[t] * (1.0f - sg));
+          }
+          if (row < valid_rows && c < nvalid) part[i] += pq;
+          *reinterpret_cast<u32x2 *>(srow + c) = u32x2{pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3])};
+        }
+        if (j == 3) {
+          // row tile i staged (the wave's own rows: LDS keeps one wave's
+          // operations in order): four rows of 256 bytes per instruction
+#pragma unroll
+          for (int it = 0; it < 8; ++it) {
+            const int r = 4 * it + (lane >> 4), ch = lane & 15;
+            const int trow = wm * kRowsW + i * 32 + r;
+            const u32x4 o = *reinterpret_cast<const u32x4 *>(stg + r * kDhSt + ch * 8);
+            if (trow < valid_rows && ch * 8 < nvalid)
+              *reinterpret_cast<u32x4 *>(g.C + (seg + row0 + trow) * int64_t(g.ldc) + blk * kGuBlockPairs + ch * 8) = o;
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kMI; ++i) {
+        // the two half-waves hold the two column halves of the same rows
+        const float pr = part[i] + __shfl_xor(part[i], 32);
+        if (lane < 32 && lrow + i * 32 < valid_rows) g.partial[(seg + row0 + rr[i]) * int64_t(npb) + blk] = pr;
+      }
+    }
   } else {  // EPI_ACT: ungated, h = this tile's columns of the up projection, a = silu(h)
 #pragma unroll
     for (int i = 0; i < kMI; ++i) {
@@ -683,6 +795,7 @@ __global__ __launch_bounds__(wide::Shape<WM>::kThreads, 1) void gemm_wide_kernel
   }
 }
 
+namespace {
 hipError_t launch_gemm_wide(GemmVariant v, const GemmArgs &a, hipStream_t s, const e4b_kernel_events *ev) {
   if (a.grid == 0) return hipSuccess;
   // a multiple of 8 blocks: each XCD then has at least ceil(W / 8) of them
@@ -706,12 +819,27 @@ hipError_t launch_gemm_wide(GemmVariant v, const GemmArgs &a, hipStream_t s, con
       E4B_WIDE(A_GATHER, B_NT, EPI_ACT);
     case GEMM_DOWN_FWD: E4B_WIDE(A_DIRECT, B_NT, EPI_STORE);
     case GEMM_GATE_UP_DGRAD: E4B_WIDE(A_DIRECT, B_NN, EPI_STORE);
-    case GEMM_DOWN_DGRAD: E4B_WIDE(A_GATHER, B_NN, EPI_DSWIGLU);
+    case GEMM_DOWN_DGRAD:
+      if (a.gated) E4B_WIDE(A_GATHER, B_NN, EPI_DSWIGLU);
+      E4B_WIDE(A_GATHER, B_NN, EPI_DACT);
     default: break;
   }
 #undef E4B_WIDE_SK
 #undef E4B_WIDE
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s, const e4b_kernel_events *ev) {
+  if (v != GEMM_DOWN_DGRAD) return launch_gemm_wide(v, a, s, ev);
+  // the down dgrad arrives planned per 128-unit block (the routing-weight
+  // partials keep one entry per block); its tiles are 256 columns wide: the
+  // same m-tiles, half as many n-tiles
+  GemmArgs w = a;
+  w.n_tiles = (a.N + 2 * kGuBlockPairs - 1) / (2 * kGuBlockPairs);
+  w.grid = a.n_tiles > 0 ? a.grid / uint32_t(a.n_tiles) * uint32_t(w.n_tiles) : 0;
+  return launch_gemm_wide(v, w, s, ev);
 }
 
 }  // namespace e4b

@@ -130,13 +130,11 @@ hipError_t launch_dequantize8(const e4b_stack &st, bool bf16, void *out, hipStre
 hipError_t launch_mx_gemm(bool gate_up, const MxGemmArgs &a, hipStream_t s,
                           const e4b_kernel_events *ev = nullptr);
 
-// grid = m_tiles_bound * n_tiles; the launch rounds it up to a multiple of 8.
+// The grouped GEMMs (gemm_wide.hip, 256 x 256 tiles). grid = m_tiles_bound *
+// n_tiles; the launch rounds it up to a multiple of 8. The down dgrad is given
+// n_tiles over 128-unit blocks (the routing-weight partials' granularity).
 hipError_t launch_grouped_gemm(GemmVariant v, const GemmArgs &a, hipStream_t s,
                                const e4b_kernel_events *ev = nullptr);
-// The 256 x 256-tile kernel of the gate_up and down forward GEMMs and the
-// gate_up dgrad (gemm_wide.hip); launch_grouped_gemm routes those there.
-hipError_t launch_gemm_wide(GemmVariant v, const GemmArgs &a, hipStream_t s,
-                            const e4b_kernel_events *ev);
 
 // y[t] = sum_j w[t, j] * rows[pos(t, j)] in fp32, slot order.
 hipError_t launch_combine_rows(const uint16_t *rows, const int32_t *pos_of_pair, const float *w,

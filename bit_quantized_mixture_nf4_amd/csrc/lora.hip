@@ -10,7 +10,7 @@
 //     rows of an m-tile (rows of a tile share one expert), fp32, written as
 //     [P, 16] in sorted-pair order;
 //   * one extra 16-deep MFMA slice inside the grouped GEMM that already
-//     produces the projection (gemm.hip), against a bf16 pack of the scaled
+//     produces the projection (gemm_wide.hip), against a bf16 pack of the scaled
 //     adapter laid out by output column;
 //   * the four adapter gradients in one launch: per expert, a fixed-order sum
 //     over its pairs of outer products, on MFMA with the pairs as the

@@ -100,7 +100,7 @@ e4b_status plan_moe(const e4b_moe_layer *L, int64_t T, int32_t top_k, MoePlan *p
   const int64_t bn_gu = p->gated ? kBNWide / 2 : kBNWide;
   p->n_tiles_gu = (I + bn_gu - 1) / bn_gu;
   p->n_tiles_h = (H + kBNWide - 1) / kBNWide;
-  p->n_tiles_i = (I + kBNNarrow - 1) / kBNNarrow;
+  p->n_tiles_i = (I + kGuBlockPairs - 1) / kGuBlockPairs;
   // saved / recomputed g|u: gated, blocked per (m-tile, 128 pairs); ungated h [P, I]
   p->gu_bytes = p->gated ? size_t(p->m_tiles_bound) * size_t((I + kGuBlockPairs - 1) / kGuBlockPairs) *
                                size_t(kGuBlockChunks) * 16

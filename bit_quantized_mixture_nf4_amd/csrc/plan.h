@@ -17,11 +17,8 @@ constexpr int kBM = 256;   // rows (routed pairs) per tile
 // pairs): 256 x 128 pairs of g and u, 128 KB (layout in kernels.h, gu_chunk)
 constexpr int kGuBlockPairs = 128;
 constexpr int kGuBlockChunks = kBM * kGuBlockPairs / 4;  // 16-byte chunks per block
-// output columns per tile: 256 (8 waves, one workgroup per CU) for every GEMM
-// of a gated layer; 128 (4 waves, two workgroups per CU) for the down dgrad of
-// an ungated layer
+// output columns per tile of every grouped GEMM (8 waves, one workgroup per CU)
 constexpr int kBNWide = 256;
-constexpr int kBNNarrow = 128;
 constexpr int kBK = 64;    // reduction step = one quantization block
 constexpr int kBlock = 64; // quantization block (elements along `in`)
 constexpr int kMxBlock = 32;  // MXFP4 scale block (elements along `in`)
@@ -44,7 +41,7 @@ struct MoePlan {
   int64_t m_tiles_bound;  // upper bound of sum_e ceil(count_e / kBM)
   int64_t n_tiles_gu;     // gate_up forward tiles: kBNWide/2 gate-up pairs per tile
   int64_t n_tiles_h;      // down forward tiles over H (kBNWide)
-  int64_t n_tiles_i;      // down dgrad tiles over I (kBNNarrow)
+  int64_t n_tiles_i;      // down dgrad: blocks of kGuBlockPairs units over I (one partial each)
   int64_t n_tiles_h_gud;  // gate_up dgrad tiles over H (kBNWide)
   int nbits_e;            // bits needed for an expert id
   // workspace byte offsets
