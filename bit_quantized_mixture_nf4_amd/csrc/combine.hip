@@ -13,8 +13,9 @@ namespace e4b {
 // y[t] = sum_j w[t,j] * O[pos(t,j)]   (weighted)   or   sum_j O[pos(t,j)]
 // rows of H bf16; 8 elements (16 bytes) per thread and step. The unweighted
 // form (the dgrad combine) also sums, when gw is given, each pair's routing-
-// weight gradient over the n-tiles of the down dgrad in ascending order:
-// gw[t, j] = sum_i partial[pos(t,j)][i].
+// weight gradient over the blocks of the down dgrad: gw[t, j] = sum_i
+// partial[pos(t,j)][i], one wave per pair, lane l summing blocks l, l + 64,
+// ... in ascending order and the 64 lane sums added by a fixed butterfly.
 template <bool WEIGHTED>
 __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t *__restrict__ O,
                                                            const int32_t *__restrict__ pos_of_pair,
@@ -26,17 +27,21 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t *__res
   __shared__ int32_t pos[kMaxTopK];
   __shared__ float w[kMaxTopK];
   if (threadIdx.x < k) {
-    const int32_t pj = pos_of_pair[t * k + threadIdx.x];
-    pos[threadIdx.x] = pj;
+    pos[threadIdx.x] = pos_of_pair[t * k + threadIdx.x];
     w[threadIdx.x] = WEIGHTED ? wts[t * k + threadIdx.x] : 1.0f;
-    if (!WEIGHTED && gw) {
-      const float *src = partial + int64_t(pj) * n_tiles;
-      float sum = 0.0f;
-      for (int i = 0; i < n_tiles; ++i) sum += src[i];
-      gw[t * k + threadIdx.x] = sum;
-    }
   }
   __syncthreads();
+  if (!WEIGHTED && gw) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int j = wave; j < k; j += 4) {
+      const float *src = partial + int64_t(pos[j]) * n_tiles;
+      float sum = 0.0f;
+      for (int i = lane; i < n_tiles; i += 64) sum += src[i];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+      if (lane == 0) gw[t * k + j] = sum;
+    }
+  }
   for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     // up to 8 rows in flight before the first sum; the sums keep slot order
