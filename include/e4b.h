@@ -346,7 +346,9 @@ e4b_status e4b_moe_lora_backward(const e4b_moe_layer *L, const e4b_lora *lora, i
                                  size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes of the two LoRA calls (the base workspace plus the
- * adapters' per-pair projections and bf16 operand packs); 0 when invalid. */
+ * adapters' per-pair projections, their bf16 operand packs and, for a
+ * backward without saved state, the recomputed bf16 a [T*top_k, I]); 0 when
+ * invalid. */
 size_t e4b_moe_lora_workspace_bytes(const e4b_moe_layer *L, int64_t T, int32_t top_k);
 
 /* Kernels of the forward and dgrad calls that the *_timed entry points can
