@@ -15,12 +15,6 @@ using namespace e4b;
 
 namespace e4b {
 
-// router_logits may be null (ids and weights given); otherwise the decode
-// prep kernel routes the tokens itself and writes topk_idx / topk_w.
-hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
-                                 const float *logits, int32_t *idx, float *w, uint16_t *y,
-                                 char *ws, hipStream_t s, const e4b_kernel_events *ev);
-
 namespace {
 
 GemmArgs base_args(const MoePlan &p, const e4b_stack &st, const PermView &v) {

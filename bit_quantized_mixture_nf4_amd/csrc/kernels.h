@@ -125,8 +125,6 @@ struct MxGemmArgs {
 };
 hipError_t launch_mx8_rows(const uint16_t *x, int64_t rows, int64_t K, uint8_t *codes,
                            uint8_t *scales, hipStream_t s);
-// An INT8 / FP8 stack dequantized to bf16 (bf16 == true) or fp32 [E, out, in].
-hipError_t launch_dequantize8(const e4b_stack &st, bool bf16, void *out, hipStream_t s);
 hipError_t launch_mx_gemm(bool gate_up, const MxGemmArgs &a, hipStream_t s,
                           const e4b_kernel_events *ev = nullptr);
 
@@ -145,6 +143,18 @@ hipError_t launch_combine_rows(const uint16_t *rows, const int32_t *pos_of_pair,
 hipError_t launch_combine_dgrad(const uint16_t *rows, const int32_t *pos_of_pair, int64_t T, int k,
                                 int H, uint16_t *out, const float *partial, int n_tiles,
                                 float *gw, hipStream_t s, const e4b_kernel_events *ev = nullptr);
+
+// An INT8 / FP8 stack dequantized to bf16 (bf16 == true) or fp32 [E, out, in]
+// (quant.hip).
+hipError_t launch_dequantize8(const e4b_stack &st, bool bf16, void *out, hipStream_t s);
+
+// The decode forward for T <= 8 (decode.hip): two launches, gate_up (routing
+// when logits is not null, grouping, GEMV, SiLU*up) and down (GEMV and the
+// weighted combine). With logits null the ids and weights in idx / w are
+// used; otherwise the gate_up launch routes the tokens and writes them there.
+hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
+                                 const float *logits, int32_t *idx, float *w, uint16_t *y,
+                                 char *ws, hipStream_t s, const e4b_kernel_events *ev);
 
 // ---- LoRA (lora.hip) ----
 // Operand packs of the adapters, with zeros for r <= j < kLoraK:

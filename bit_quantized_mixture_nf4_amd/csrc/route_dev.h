@@ -1,5 +1,5 @@
 // route_dev.h -- top-k selection and softmax of one token's router logits by
-// one wavefront (shared by the router kernel and the decode prep kernel).
+// one wavefront (shared by the router kernel and the decode gate_up launch).
 #pragma once
 
 #include "device.h"

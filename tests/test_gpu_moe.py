@@ -88,7 +88,7 @@ def test_route_exact_workload_logits(name, T):
     small = MoEConfig("s", E=cfg.E, H=64, I=64, k=cfg.k, T=cfg.T, routing=cfg.routing)
     pb = Problem(small, seed=0, with_grad=False)
     idx_ref, w_ref = oracle.route(lg, cfg.k)
-    # decode-sized batches are also routed inside the decode prep kernel
+    # decode-sized batches are also routed inside the decode gate_up launch
     paths = ["grouped", "decode"] if cfg.T <= 8 else ["grouped"]
     for path in paths:
         idx.fill_(-1)
