@@ -21,11 +21,25 @@
 // it. No MFMA: each code byte is expanded through an LDS table into two bf16
 // codebook values and contracted with bf16 inputs by v_dot2_f32_bf16 in fp32;
 // a 32-element chunk's partial sum is multiplied by its block scale.
+#include <algorithm>
+#include <utility>
+
 #include "device.h"
 #include "kernels.h"
 #include "route_dev.h"
 
 namespace e4b {
+
+// f(std::integral_constant<int, i>) for i = 0 .. N - 1 (register sets
+// indexed by constants)
+template <typename F, int... Is>
+__device__ __forceinline__ void dec_static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void dec_static_for(F &&f) {
+  dec_static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 constexpr int kDecThreads = 256;
 constexpr int kTblCopies = 32;   // LDS table copies (lane l reads copy l % kTblCopies)
@@ -380,15 +394,32 @@ struct DecodeGuLds {
 };
 
 // Routing (when given logits) and grouping of the P <= kDecMaxPairs pairs:
-// pairs sorted by (expert, flat pair id).
+// pairs sorted by (expert, flat pair id). NT threads (a multiple of 256):
+// wave t routes token t, thread p < kDecMaxPairs handles pair p, and every
+// thread takes part in the barriers.
+// MAXE: the largest expert count the caller routes (E <= MAXE); at most 256
+// keeps only the router instances of up to four logits per lane.
+template <int NT, int MAXE, typename Lds>
 __device__ __forceinline__ void decode_group(const float *__restrict__ logits, int E, int k, int T,
                                              const int32_t *__restrict__ idx_in, const float *__restrict__ w_in,
-                                             DecodeGuLds &L) {
-  static_assert(kDecThreads == kDecMaxPairs, "one thread per routed pair");
+                                             Lds &L) {
+  static_assert(NT % kDecMaxPairs == 0 && kDecMaxPairs % 64 == 0, "every pair has a thread");
+  constexpr int kWaves = NT / 64, kPairWaves = kDecMaxPairs / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int P = T * k;
   if (logits) {
-    for (int t = wv; t < T; t += kRouteWaves) route_token(logits, t, E, k, lane, L.idx, L.w, nullptr, L.route[wv]);
+    for (int t = wv; t < T; t += kWaves) {
+      if constexpr (MAXE <= 256) {
+        if (E <= 64)
+          route_token_per<1>(logits, t, E, k, lane, L.idx, L.w, nullptr, L.route[wv]);
+        else if (E <= 128)
+          route_token_per<2>(logits, t, E, k, lane, L.idx, L.w, nullptr, L.route[wv]);
+        else
+          route_token_per<4>(logits, t, E, k, lane, L.idx, L.w, nullptr, L.route[wv]);
+      } else {
+        route_token(logits, t, E, k, lane, L.idx, L.w, nullptr, L.route[wv]);
+      }
+    }
   } else if (tid < P) {
     L.idx[tid] = safe_expert(idx_in[tid], E);
     L.w[tid] = w_in[tid];
@@ -397,7 +428,7 @@ __device__ __forceinline__ void decode_group(const float *__restrict__ logits, i
   const int p = tid;
   // unique sort key: expert, then pair id (stable)
   const int key = p < P ? L.idx[p] * kDecMaxPairs + p : 0x7FFFFFFF;
-  L.key[p] = key;
+  if (NT == kDecMaxPairs || p < kDecMaxPairs) L.key[p] = key;
   __syncthreads();
   int pos = 0;
   const int4 *k4 = reinterpret_cast<const int4 *>(L.key);
@@ -416,10 +447,10 @@ __device__ __forceinline__ void decode_group(const float *__restrict__ logits, i
   const bool starts = p < P && (p == 0 || L.se[p - 1] != L.se[p]);
   const uint64_t fm = __ballot(starts);
   int d = __popcll(fm & ((1ull << lane) - 1));
-  if (lane == 0) L.wsum[wv] = __popcll(fm);
+  if (lane == 0 && wv < kPairWaves) L.wsum[wv] = __popcll(fm);
   __syncthreads();
   int n = 0;
-  for (int v = 0; v < kDecThreads / 64; ++v) {
+  for (int v = 0; v < kPairWaves; ++v) {
     d += v < wv ? L.wsum[v] : 0;
     n += L.wsum[v];
   }
@@ -434,6 +465,30 @@ __device__ __forceinline__ void decode_group(const float *__restrict__ logits, i
   __syncthreads();
 }
 
+// Workgroup 0's copy of the grouping for the down launch, and the routing
+// outputs (ids and weights by flat pair) when the launch routed.
+template <typename Lds>
+__device__ __forceinline__ void decode_write_plan(const Lds &L, int P, int n, bool routed, int32_t *__restrict__ idx_io,
+                                                  float *__restrict__ w_io, DecodePlan *__restrict__ plan) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    plan->n = n;
+    plan->first[n] = P;
+  }
+  if (tid < n) {
+    plan->expert[tid] = L.groups.expert[tid];
+    plan->first[tid] = L.groups.first[tid];
+  }
+  if (tid < P) {
+    plan->weight[tid] = L.w[L.sp[tid]];
+    plan->pos[tid] = L.pos[tid];
+    if (routed) {
+      idx_io[tid] = L.idx[tid];
+      w_io[tid] = L.w[tid];
+    }
+  }
+}
+
 template <int LPR, bool MX>
 __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(kDecWgPerCu))) void decode_gate_up_kernel(const float *__restrict__ logits, int E, int k,
                                                                      int T, int32_t *__restrict__ idx_io,
@@ -443,26 +498,10 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(kDe
                                                                      uint16_t *__restrict__ a) {
   __shared__ DecodeGuLds L;
   fill_code_table(L.tbl, cb);  // its stores overlap the routing's loads
-  decode_group(logits, E, k, T, logits ? nullptr : idx_io, w_io, L);
+  decode_group<kDecThreads, kMaxE>(logits, E, k, T, logits ? nullptr : idx_io, w_io, L);
   const int tid = threadIdx.x, P = T * k, n = L.groups.n;
   if (blockIdx.x == 0) {
-    // the grouping for the down launch, and the routing outputs
-    if (tid == 0) {
-      plan->n = n;
-      plan->first[n] = P;
-    }
-    if (tid < n) {
-      plan->expert[tid] = L.groups.expert[tid];
-      plan->first[tid] = L.groups.first[tid];
-    }
-    if (tid < P) {
-      plan->weight[tid] = L.w[L.sp[tid]];
-      plan->pos[tid] = L.pos[tid];
-      if (logits) {
-        idx_io[tid] = L.idx[tid];
-        w_io[tid] = L.w[tid];
-      }
-    }
+    decode_write_plan(L, P, n, logits != nullptr, idx_io, w_io, plan);
     __syncthreads();  // pos is read above; the partial sums share its space
   }
   const int KP = k_parts<kGuRows>(n, P, kDecThreads / LPR, H >> 5, LPR);
@@ -483,6 +522,156 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(kDe
         const float g = part_sum<kGuRows>(L.part, KP, P, s, i), u = part_sum<kGuRows>(L.part, KP, P, s, kGuUnits + i);
         a[int64_t(s) * I + u0 + i] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
       }
+    }
+    __syncthreads();
+  }
+}
+
+// ---- gate_up for rows of H = 2048: one 32-element chunk per lane of a wave ----
+// One workgroup of 1024 threads per CU instead of three of 256: one code
+// table, and the tokens' x rows staged in LDS once, so a step loads only the
+// two weight rows' codes and scales (into one of kRingDepth register sets,
+// statically indexed: the sets are reloaded in place, not copied). A
+// workgroup block is `units` gate/up units; item (expert d, unit u) of a
+// block goes to wave i % 16. Per pair the arithmetic is the 256-thread
+// kernel's with 64 lanes per row (the same products, chunk scaling and
+// lane sums), so both give the same bits.
+constexpr int kRingThreads = 1024;
+constexpr int kRingWaves = kRingThreads / 64;
+constexpr int kRingH = 2048;       // the row length (H) this kernel covers
+constexpr int kRingX4 = kRingH / 8;  // 16-byte units of an x row
+constexpr int kRingMaxUnits = 4;   // units per workgroup block
+constexpr int kRingDepth = 4;      // weight register sets per wave
+constexpr int kRingMaxE = 256;     // expert counts this kernel routes
+
+struct DecodeRingLds {
+  uint32_t tbl[256 * kTblCopies];
+  // x of token t: unit g (elements 8 g .. 8 g + 7) of the row at
+  // t * kRingX4 + (g % 4) * 64 + g / 4, so lane l reads its chunk's four
+  // units at l, l + 64, l + 128, l + 192 (consecutive lanes, no conflicts)
+  u32x4 xs[kDecodeMaxT * kRingX4];
+  DecodeGroups groups;
+  int32_t vrow[kDecMaxPairs];
+  int32_t idx[kDecMaxPairs];
+  float w[kDecMaxPairs];
+  int32_t sp[kDecMaxPairs];
+  int32_t pos[kDecMaxPairs];
+  union {
+    RouteLds route[kDecodeMaxT];  // wave t routes token t
+    struct {
+      float part[kDecMaxPairs * 2 * kRingMaxUnits];  // [sorted pair][gate units | up units]
+      int32_t key[kDecMaxPairs];
+      int32_t se[kDecMaxPairs];
+      int32_t wsum[kDecMaxPairs / 64];
+    };
+  };
+};
+
+// The codes and block scales of an item: gate row u and up row I + u of
+// expert e, the lane's 16 bytes (chunk lane) of each.
+struct RingSet {
+  u32x4 cw[2];
+  float sc[2];
+};
+
+__device__ __forceinline__ void ring_load(const DecStack &W, int I, int e, int u, int lane, RingSet &o) {
+  const uint8_t *wp = W.packed + int64_t(e) * W.e_bytes + int64_t(lane) * 16;
+  const float *ap = W.absmax + int64_t(e) * W.e_blocks + (lane >> 1);
+  o.cw[0] = *reinterpret_cast<const u32x4 *>(wp + int64_t(u) * (kRingH / 2));
+  o.cw[1] = *reinterpret_cast<const u32x4 *>(wp + int64_t(I + u) * (kRingH / 2));
+  o.sc[0] = ap[int64_t(u) * (kRingH / kBlock)];
+  o.sc[1] = ap[int64_t(I + u) * (kRingH / kBlock)];
+}
+
+__global__ __launch_bounds__(kRingThreads) void decode_gate_up_ring_kernel(
+    const float *__restrict__ logits, int E, int k, int T, int32_t *__restrict__ idx_io, float *__restrict__ w_io,
+    DecStack W, int I, int units, const uint16_t *__restrict__ x, DecCodebook cb, DecodePlan *__restrict__ plan,
+    uint16_t *__restrict__ a) {
+  static_assert(kRingH / 32 == 64 && kBlock == 64, "one chunk per lane, two chunks per block");
+  static_assert(kDecMaxPairs * kRingMaxUnits <= 1024 && kRingMaxUnits <= 4, "item / ub by multiply and shift");
+  static_assert(kRingThreads % kDecThreads == 0, "the code table is filled by the first 256 threads");
+  __shared__ DecodeRingLds L;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid < kDecThreads) fill_code_table(L.tbl, cb);
+  {
+    const u32x4 *xg = reinterpret_cast<const u32x4 *>(x);
+    for (int j = tid; j < T * kRingX4; j += kRingThreads) {
+      const int t = j / kRingX4, g = j % kRingX4;
+      L.xs[t * kRingX4 + (g & 3) * 64 + (g >> 2)] = xg[int64_t(t) * kRingX4 + g];
+    }
+  }
+  decode_group<kRingThreads, kRingMaxE>(logits, E, k, T, logits ? nullptr : idx_io, w_io, L);
+  const int P = T * k, n = L.groups.n;
+  if (blockIdx.x == 0) decode_write_plan(L, P, n, logits != nullptr, idx_io, w_io, plan);
+  const uint32_t *tl = L.tbl + (lane & (kTblCopies - 1));
+  const u32x4 *xl = L.xs + lane;
+  const int nblk = (I + units - 1) / units;
+  for (int b = int(blockIdx.x); b < nblk; b += int(gridDim.x)) {
+    const int u0 = b * units, ub = min(units, I - u0);
+    const int items = n * ub;
+    // this wave's items wv, wv + 16, ...: q-th at i = wv + 16 q
+    const int nq = wv < items ? (items - wv + kRingWaves - 1) / kRingWaves : 0;
+    // i / ub as (i * m) >> 16, m = ceil(2^16 / ub): exact for ub <= 4 and
+    // i < 1024 (the error stays below 1024 * 2 / (3 * 2^16) of a unit)
+    const uint32_t m = (65536u + uint32_t(ub) - 1) / uint32_t(ub);
+    auto item_d = [&](int q) { return int((uint32_t(wv + q * kRingWaves) * m) >> 16); };
+    auto item_u = [&](int q, int d) { return u0 + (wv + q * kRingWaves) - d * ub; };
+    RingSet ring[kRingDepth];
+    dec_static_for<kRingDepth>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      if (r < nq) {
+        const int d = item_d(r);
+        ring_load(W, I, L.groups.expert[d], item_u(r, d), lane, ring[r]);
+      }
+    });
+    for (int q0 = 0; q0 < nq; q0 += kRingDepth) {
+      dec_static_for<kRingDepth>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const int q = q0 + r;
+        if (q < nq) {
+          const int d = item_d(q), u = item_u(q, d);
+          const int s0 = L.groups.first[d], cnt = L.groups.first[d + 1] - s0;
+          uint32_t v[2][16];
+          lookup_chunk(tl, ring[r].cw[0], v[0]);
+          lookup_chunk(tl, ring[r].cw[1], v[1]);
+          const float sg = ring[r].sc[0], su = ring[r].sc[1];
+          __builtin_amdgcn_sched_barrier(0);
+          // this set's next item, loaded under the products
+          if (q + kRingDepth < nq) {
+            const int d2 = item_d(q + kRingDepth);
+            ring_load(W, I, L.groups.expert[d2], item_u(q + kRingDepth, d2), lane, ring[r]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          for (int pp = 0; pp < cnt; ++pp) {
+            const int sp = s0 + pp;
+            const u32x4 *xr = xl + L.vrow[sp] * kRingX4;
+            u32x4 xq[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xq[i] = xr[i * 64];
+            float ag = 0.0f, au = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              ag = dot2_bf16(v[0][i], xq[i >> 2][i & 3], ag);
+              au = dot2_bf16(v[1][i], xq[i >> 2][i & 3], au);
+            }
+            float pg = 0.0f, pu = 0.0f;
+            pg += ag * sg;
+            pu += au * su;
+            pg = group_sum<64>(pg);
+            pu = group_sum<64>(pu);
+            if (lane == 0) {
+              L.part[sp * (2 * kRingMaxUnits) + (u - u0)] = pg;
+              L.part[sp * (2 * kRingMaxUnits) + kRingMaxUnits + (u - u0)] = pu;
+            }
+          }
+        }
+      });
+    }
+    __syncthreads();
+    for (int j = tid; j < P * ub; j += kRingThreads) {
+      const int sp = j / ub, i = j % ub;
+      const float g = L.part[sp * (2 * kRingMaxUnits) + i], uu = L.part[sp * (2 * kRingMaxUnits) + kRingMaxUnits + i];
+      a[int64_t(sp) * I + u0 + i] = f32_to_bf16(g / (1.0f + __expf(-g)) * uu);
     }
     __syncthreads();
   }
@@ -583,13 +772,22 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
       default: return f(std::integral_constant<int, 64>());
     }
   };
-  err = with_lpr(H, [&](auto lpr) {
+  if (!mx && H == kRingH && E <= kRingMaxE) {
+    // one 1024-thread workgroup per CU, blocks of up to kRingMaxUnits units
+    const int units = int(std::min<int64_t>(kRingMaxUnits, std::max<int64_t>(1, (I + cus - 1) / std::max(cus, 1))));
+    const int64_t nblk = (I + units - 1) / units;
+    const dim3 grid(uint32_t(std::min<int64_t>(nblk, std::max(cus, 1))));
+    err = launch_k(ev, E4B_K_DECODE_GATE_UP, decode_gate_up_ring_kernel, grid, dim3(kRingThreads), s, logits, E, k,
+                   T, idx, wts, Wgu, I, units, x, cbk, plan, a);
+  } else {
+    err = with_lpr(H, [&](auto lpr) {
     constexpr int LPR = decltype(lpr)::value;
     return mx ? launch_k(ev, E4B_K_DECODE_GATE_UP, decode_gate_up_kernel<LPR, true>, grid_gu, block, s, logits, E, k,
                          T, idx, wts, Wgu, H, I, x, cbk, plan, a)
               : launch_k(ev, E4B_K_DECODE_GATE_UP, decode_gate_up_kernel<LPR, false>, grid_gu, block, s, logits, E,
                          k, T, idx, wts, Wgu, H, I, x, cbk, plan, a);
-  });
+    });
+  }
   if (err != hipSuccess) return err;
   return with_lpr(I, [&](auto lpr) {
     constexpr int LPR = decltype(lpr)::value;

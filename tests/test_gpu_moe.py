@@ -327,6 +327,40 @@ def test_expert_repeated_within_tokens(path):
     _decode_case(cfg, idx, path=path)
 
 
+def _ids_with_repeats(E, T, k, rng):
+    """Routing ids drawn from a few experts (shared by several tokens, repeated
+    within tokens) plus the last expert id."""
+    idx = rng.integers(0, min(E, 5), size=(T, k)).astype(np.int32)
+    idx[0, 0] = E - 1
+    return idx
+
+
+@pytest.mark.parametrize("E,I,T,k,kind", [(8, 1088, 8, 4, "nf4"), (256, 64, 8, 8, "fp4"), (6, 640, 3, 2, "nf4")])
+def test_decode_rows_of_2048(E, I, T, k, kind):
+    """H = 2048 (one 32-element chunk per lane of a wave) and E <= 256 take the
+    one-workgroup-per-CU gate_up launch: blocks of ceil(I / CUs) units, at most
+    4 (on 256 CUs: I = 1088 gives 272 blocks of 4, so some workgroups take two;
+    I = 640 blocks of 3 with a last block of one unit), experts with up to T
+    tokens and repeated within a token, and 256 experts."""
+    cfg = MoEConfig("rows2048", E=E, H=2048, I=I, k=k, T=T, routing="normal")
+    announce(f"decode rows of 2048 {kind} E{E} I{I} k{k} T{T}")
+    _decode_case(cfg, _ids_with_repeats(E, T, k, np.random.default_rng(E + I + T)), kind=kind)
+
+
+@pytest.mark.parametrize("E,T", [(128, 1), (64, 5), (257, 2)])
+def test_decode_rows_of_2048_routed(E, T):
+    """The same launch routing from logits (one wave per token): ids exact, weights
+    within 1e-6, y against the oracle. E = 257 takes the 256-thread launch."""
+    cfg = MoEConfig("rows2048r", E=E, H=2048, I=64, k=8, T=T, routing="normal")
+    announce(f"decode rows of 2048 routed E{E} I64 k8 T{T}")
+    pb = Problem(cfg, seed=3, with_grad=False)
+    y, idx, w, _ = e4b.moe_forward(pb.layer, pb.x_d, cfg.k, logits=pb.logits_d, path="decode")
+    idx_ref, w_ref = oracle.route(pb.logits, cfg.k)
+    assert np.array_equal(idx.cpu().numpy(), idx_ref)
+    assert np.max(np.abs(w.cpu().numpy() - w_ref)) <= 1e-6
+    tol_check(to_np(y), _oracle_fwd(pb, idx_ref, w_ref), f"y rows2048 routed E{E}")
+
+
 def test_grouped_topk_equals_E():
     """Every token routed to every expert (top_k = E)."""
     cfg = MoEConfig("allE", E=4, H=256, I=128, k=4, T=96, routing="normal")
