@@ -735,6 +735,154 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(kDe
   }
 }
 
+// ---- down for rows of I <= 1024 whose routed inputs fit in LDS ----
+// The same workgroup shape as the gate_up launch above: 1024 threads per
+// CU, one code table, the P rows of a staged in LDS once, and a static ring
+// of weight register sets per wave. A workgroup block is kDnRingRows rows of
+// H; item (expert d, quarter q) is rows 4 q .. 4 q + 3 of the block, and the
+// two 32-lane halves of a wave take two rows each (lane c < I / 32 holds
+// chunk c). Per pair the arithmetic is the 256-thread kernel's with 32 lanes
+// per row, and the combine follows in the same workgroup in slot order, so
+// both give the same bits.
+constexpr int kDnRingRows = 8;                // rows of H per workgroup block
+constexpr int kDnRingA = 48 * 1024;           // a elements (P * I) staged in LDS at most
+constexpr int kDnRingMaxI = 1024;             // one chunk per lane of a 32-lane half
+
+struct DecodeDnRingLds {
+  uint32_t tbl[256 * kTblCopies];
+  // a of sorted pair s: unit g (elements 8 g .. 8 g + 7, g < 4 C with C = I / 32
+  // chunks) at s * 4 C + (g % 4) * C + g / 4, so lane c reads its chunk's units
+  // at c, c + C, c + 2 C, c + 3 C (consecutive lanes, no conflicts)
+  u32x4 as[kDnRingA / 8];
+  float part[kDecMaxPairs * kDnRingRows];
+  DecodeGroups groups;
+  float weight[kDecMaxPairs];
+  int32_t pos[kDecMaxPairs];
+};
+
+__global__ __launch_bounds__(kRingThreads) void decode_down_ring_kernel(DecStack W, int H, int I, int T, int k,
+                                                                        DecCodebook cb,
+                                                                        const DecodePlan *__restrict__ plan,
+                                                                        const uint16_t *__restrict__ a,
+                                                                        uint16_t *__restrict__ y) {
+  __shared__ DecodeDnRingLds L;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int P = T * k, C = I >> 5, U4 = I >> 3;  // chunks per row, 16-byte units per row
+  // the grouping's loads are issued before the table fill's stores
+  const int n = plan->n;
+  const bool pt = tid < P;
+  const float wt = pt ? plan->weight[tid] : 0.0f;
+  const int ps = pt ? plan->pos[tid] : 0;
+  const int ex = tid < n ? plan->expert[tid] : 0, fs = tid < n ? plan->first[tid] : 0;
+  if (tid < kDecThreads) fill_code_table(L.tbl, cb);
+  {
+    const u32x4 *ag = reinterpret_cast<const u32x4 *>(a);
+    for (int j = tid; j < P * U4; j += kRingThreads) {
+      const int sp = j / U4, g = j - sp * U4;
+      L.as[sp * U4 + (g & 3) * C + (g >> 2)] = ag[j];
+    }
+  }
+  if (tid < n) {
+    L.groups.expert[tid] = ex;
+    L.groups.first[tid] = fs;
+  }
+  if (tid == 0) {
+    L.groups.n = n;
+    L.groups.first[n] = P;
+  }
+  if (pt) {
+    L.weight[tid] = wt;
+    L.pos[tid] = ps;
+  }
+  __syncthreads();
+  const uint32_t *tl = L.tbl + (lane & (kTblCopies - 1));
+  const int half = lane >> 5, c = lane & 31;
+  const bool act = c < C;
+  const int cc = act ? c : 0;  // idle lanes load chunk 0 and contribute nothing
+  const u32x4 *al = L.as + cc;
+  const int nblk = (H + kDnRingRows - 1) / kDnRingRows;
+  constexpr int kQ = kDnRingRows / 4;  // items per expert and block
+  for (int b = int(blockIdx.x); b < nblk; b += int(gridDim.x)) {
+    const int r0 = b * kDnRingRows;
+    const int items = n * kQ;
+    const int nq = wv < items ? (items - wv + kRingWaves - 1) / kRingWaves : 0;
+    // item i = wv + 16 q: expert d = i / kQ, rows r0 + 4 (i % kQ) + 2 half + {0, 1}
+    auto item_row = [&](int q) { return r0 + 4 * ((wv + q * kRingWaves) % kQ) + 2 * half; };
+    auto load = [&](int q, RingSet &o) {
+      const int d = (wv + q * kRingWaves) / kQ, row = item_row(q);
+      const int e = L.groups.expert[d];
+      const uint8_t *wp = W.packed + int64_t(e) * W.e_bytes + int64_t(cc) * 16;
+      const float *ap = W.absmax + int64_t(e) * W.e_blocks + (cc >> 1);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rr = min(row + j, H - 1);
+        o.cw[j] = *reinterpret_cast<const u32x4 *>(wp + int64_t(rr) * (I >> 1));
+        o.sc[j] = ap[int64_t(rr) * (I / kBlock)];
+      }
+    };
+    RingSet ring[kRingDepth];
+    dec_static_for<kRingDepth>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      if (r < nq) load(r, ring[r]);
+    });
+    for (int q0 = 0; q0 < nq; q0 += kRingDepth) {
+      dec_static_for<kRingDepth>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        const int q = q0 + r;
+        if (q < nq) {
+          const int d = (wv + q * kRingWaves) / kQ, row = item_row(q);
+          const int s0 = L.groups.first[d], cnt = L.groups.first[d + 1] - s0;
+          uint32_t v[2][16];
+          lookup_chunk(tl, ring[r].cw[0], v[0]);
+          lookup_chunk(tl, ring[r].cw[1], v[1]);
+          const float s_0 = ring[r].sc[0], s_1 = ring[r].sc[1];
+          __builtin_amdgcn_sched_barrier(0);
+          if (q + kRingDepth < nq) load(q + kRingDepth, ring[r]);
+          __builtin_amdgcn_sched_barrier(0);
+          for (int pp = 0; pp < cnt; ++pp) {
+            const int sp = s0 + pp;
+            const u32x4 *ar = al + sp * U4;
+            u32x4 xq[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xq[i] = ar[i * C];
+            float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              a0 = dot2_bf16(v[0][i], xq[i >> 2][i & 3], a0);
+              a1 = dot2_bf16(v[1][i], xq[i >> 2][i & 3], a1);
+            }
+            float p0 = 0.0f, p1 = 0.0f;
+            if (act) {
+              p0 += a0 * s_0;
+              p1 += a1 * s_1;
+            }
+            p0 = group_sum<32>(p0);
+            p1 = group_sum<32>(p1);
+            if (c == 0) {
+              L.part[sp * kDnRingRows + (row - r0)] = p0;
+              L.part[sp * kDnRingRows + (row - r0) + 1] = p1;
+            }
+          }
+        }
+      });
+    }
+    __syncthreads();
+    // y rows of this block: each token's pairs in slot order
+    for (int j = tid; j < T * kDnRingRows; j += kRingThreads) {
+      const int t = j / kDnRingRows, rr = j % kDnRingRows;
+      if (r0 + rr < H) {
+        float acc = 0.0f;
+        for (int jj = 0; jj < k; ++jj) {
+          const int sp = L.pos[t * k + jj];
+          acc += L.weight[sp] * L.part[sp * kDnRingRows + rr];
+        }
+        y[int64_t(t) * H + r0 + rr] = f32_to_bf16(acc);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const uint16_t *x,
                                  const float *logits, int32_t *idx, float *wts, uint16_t *y,
                                  char *ws, hipStream_t s, const e4b_kernel_events *ev) {
@@ -789,6 +937,11 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
     });
   }
   if (err != hipSuccess) return err;
+  if (!mx && I <= kDnRingMaxI && int64_t(T) * k * I <= kDnRingA) {
+    const dim3 grid(uint32_t(std::min<int64_t>((H + kDnRingRows - 1) / kDnRingRows, std::max(cus, 1))));
+    return launch_k(ev, E4B_K_DECODE_DOWN, decode_down_ring_kernel, grid, dim3(kRingThreads), s, Wdn, H, I, T, k, cbk,
+                    plan, a, y);
+  }
   return with_lpr(I, [&](auto lpr) {
     constexpr int LPR = decltype(lpr)::value;
     return mx ? launch_k(ev, E4B_K_DECODE_DOWN, decode_down_kernel<LPR, true>, grid_dn, block, s, Wdn, H, I, T, k,
