@@ -146,6 +146,47 @@ __device__ __forceinline__ void lookup_chunk(const uint32_t *tl, const u32x4 &cw
     for (int y = 0; y < 4; ++y) v[4 * w + y] = tl[((cw[w] >> (8 * y)) & 255u) * kTblCopies];
 }
 
+// Codebook value i (0..15) in bf16, by a select tree on the bits of i (no
+// register array indexed at run time).
+__device__ __forceinline__ uint32_t code_bf16(const DecCodebook &cb, uint32_t i) {
+  const uint32_t h = i >> 1;
+  const uint32_t a0 = (h & 1) ? cb.pair[1] : cb.pair[0], a1 = (h & 1) ? cb.pair[3] : cb.pair[2];
+  const uint32_t a2 = (h & 1) ? cb.pair[5] : cb.pair[4], a3 = (h & 1) ? cb.pair[7] : cb.pair[6];
+  const uint32_t b0 = (h & 2) ? a1 : a0, b1 = (h & 2) ? a3 : a2;
+  const uint32_t c = (h & 4) ? b1 : b0;
+  return (i & 1) ? (c >> 16) : (c & 0xFFFFu);
+}
+
+// The byte table with one copy per lane of a wave: entry (byte b, lane l) at
+// u32 index 64 b + l, so the byte address of lane l's entry for byte b is
+// 256 b + 4 l, which one byte permute builds from the code word (byte b into
+// bits 8..15) and the lane's 4 l (bits 0..7). Filled by NT threads.
+template <int NT>
+__device__ __forceinline__ void fill_code_table64(uint32_t *tbl, const DecCodebook &cb) {
+  static_assert((256 * 64 / 4) % NT == 0, "whole 16-byte units per thread");
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 256 * 64 / 4 / NT; ++i) {
+    const int u = tid + NT * i;  // 16-byte unit: byte u / 16, lanes 4 (u % 16) ..
+    const uint32_t b = uint32_t(u) >> 4;
+    const uint32_t v = code_bf16(cb, b >> 4) | (code_bf16(cb, b & 15) << 16);
+    reinterpret_cast<u32x4 *>(tbl)[u] = u32x4{v, v, v, v};
+  }
+}
+
+// lookup_chunk for the 64-copy table: lane4 = 4 * lane (byte 0 of the permute
+// source), one v_perm per code byte for the address.
+__device__ __forceinline__ void lookup_chunk64(const uint32_t *tbl, uint32_t lane4, const u32x4 &cw,
+                                               uint32_t (&v)[16]) {
+  const char *tb = reinterpret_cast<const char *>(tbl);
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+      v[4 * w + y] =
+          *reinterpret_cast<const uint32_t *>(tb + __builtin_amdgcn_perm(lane4, cw[w], 0x0C0C0004u | (uint32_t(y) << 8)));
+}
+
 // Lanes per weight row for a reduction length of K: one 32-element chunk per
 // lane and pass, the chunks of a row spread over up to 64 lanes.
 __host__ __device__ inline int lanes_per_row(int K) {
@@ -529,8 +570,9 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(kDe
 
 // ---- gate_up for rows of H = 2048: one 32-element chunk per lane of a wave ----
 // One workgroup of 1024 threads per CU instead of three of 256: one code
-// table, and the tokens' x rows staged in LDS once, so a step loads only the
-// two weight rows' codes and scales (into one of kRingDepth register sets,
+// table (a copy per lane, so one byte permute per code byte builds its
+// address), and the tokens' x rows staged in LDS once, so a step loads only
+// the two weight rows' codes and scales (into one of kRingDepth register sets,
 // statically indexed: the sets are reloaded in place, not copied). A
 // workgroup block is `units` gate/up units; item (expert d, unit u) of a
 // block goes to wave i % 16. Per pair the arithmetic is the 256-thread
@@ -545,7 +587,7 @@ constexpr int kRingDepth = 4;      // weight register sets per wave
 constexpr int kRingMaxE = 256;     // expert counts this kernel routes
 
 struct DecodeRingLds {
-  uint32_t tbl[256 * kTblCopies];
+  uint32_t tbl[256 * 64];  // one copy per lane (fill_code_table64)
   // x of token t: unit g (elements 8 g .. 8 g + 7) of the row at
   // t * kRingX4 + (g % 4) * 64 + g / 4, so lane l reads its chunk's four
   // units at l, l + 64, l + 128, l + 192 (consecutive lanes, no conflicts)
@@ -592,7 +634,7 @@ __global__ __launch_bounds__(kRingThreads) void decode_gate_up_ring_kernel(
   static_assert(kRingThreads % kDecThreads == 0, "the code table is filled by the first 256 threads");
   __shared__ DecodeRingLds L;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  if (tid < kDecThreads) fill_code_table(L.tbl, cb);
+  fill_code_table64<kRingThreads>(L.tbl, cb);
   {
     const u32x4 *xg = reinterpret_cast<const u32x4 *>(x);
     for (int j = tid; j < T * kRingX4; j += kRingThreads) {
@@ -603,7 +645,7 @@ __global__ __launch_bounds__(kRingThreads) void decode_gate_up_ring_kernel(
   decode_group<kRingThreads, kRingMaxE>(logits, E, k, T, logits ? nullptr : idx_io, w_io, L);
   const int P = T * k, n = L.groups.n;
   if (blockIdx.x == 0) decode_write_plan(L, P, n, logits != nullptr, idx_io, w_io, plan);
-  const uint32_t *tl = L.tbl + (lane & (kTblCopies - 1));
+  const uint32_t lane4 = uint32_t(lane) * 4;
   const u32x4 *xl = L.xs + lane;
   const int nblk = (I + units - 1) / units;
   for (int b = int(blockIdx.x); b < nblk; b += int(gridDim.x)) {
@@ -632,8 +674,8 @@ __global__ __launch_bounds__(kRingThreads) void decode_gate_up_ring_kernel(
           const int d = item_d(q), u = item_u(q, d);
           const int s0 = L.groups.first[d], cnt = L.groups.first[d + 1] - s0;
           uint32_t v[2][16];
-          lookup_chunk(tl, ring[r].cw[0], v[0]);
-          lookup_chunk(tl, ring[r].cw[1], v[1]);
+          lookup_chunk64(L.tbl, lane4, ring[r].cw[0], v[0]);
+          lookup_chunk64(L.tbl, lane4, ring[r].cw[1], v[1]);
           const float sg = ring[r].sc[0], su = ring[r].sc[1];
           __builtin_amdgcn_sched_barrier(0);
           // this set's next item, loaded under the products
