@@ -616,13 +616,17 @@ struct RingSet {
   float sc[2];
 };
 
+// Offsets are 32-bit: the launch takes these kernels only for stacks below
+// 2^31 bytes, so each address is the stack's base plus one unsigned offset.
 __device__ __forceinline__ void ring_load(const DecStack &W, int I, int e, int u, int lane, RingSet &o) {
-  const uint8_t *wp = W.packed + int64_t(e) * W.e_bytes + int64_t(lane) * 16;
-  const float *ap = W.absmax + int64_t(e) * W.e_blocks + (lane >> 1);
-  o.cw[0] = *reinterpret_cast<const u32x4 *>(wp + int64_t(u) * (kRingH / 2));
-  o.cw[1] = *reinterpret_cast<const u32x4 *>(wp + int64_t(I + u) * (kRingH / 2));
-  o.sc[0] = ap[int64_t(u) * (kRingH / kBlock)];
-  o.sc[1] = ap[int64_t(I + u) * (kRingH / kBlock)];
+  const uint32_t eb = uint32_t(W.e_bytes), ea = uint32_t(W.e_blocks);
+  const uint32_t w0 = uint32_t(e) * eb + uint32_t(u) * (kRingH / 2) + uint32_t(lane) * 16;
+  const uint32_t a0 = uint32_t(e) * ea + uint32_t(u) * (kRingH / kBlock) + (uint32_t(lane) >> 1);
+  const uint32_t wd = uint32_t(I) * (kRingH / 2), ad = uint32_t(I) * (kRingH / kBlock);  // gate -> up row
+  o.cw[0] = *reinterpret_cast<const u32x4 *>(W.packed + w0);
+  o.cw[1] = *reinterpret_cast<const u32x4 *>(W.packed + (w0 + wd));
+  o.sc[0] = W.absmax[a0];
+  o.sc[1] = W.absmax[a0 + ad];
 }
 
 __global__ __launch_bounds__(kRingThreads) void decode_gate_up_ring_kernel(
@@ -852,14 +856,13 @@ __global__ __launch_bounds__(kRingThreads) void decode_down_ring_kernel(DecStack
     auto item_row = [&](int q) { return r0 + 4 * ((wv + q * kRingWaves) % kQ) + 2 * half; };
     auto load = [&](int q, RingSet &o) {
       const int d = (wv + q * kRingWaves) / kQ, row = item_row(q);
-      const int e = L.groups.expert[d];
-      const uint8_t *wp = W.packed + int64_t(e) * W.e_bytes + int64_t(cc) * 16;
-      const float *ap = W.absmax + int64_t(e) * W.e_blocks + (cc >> 1);
+      const uint32_t e = uint32_t(L.groups.expert[d]);
+      const uint32_t wb = e * uint32_t(W.e_bytes) + uint32_t(cc) * 16, ab = e * uint32_t(W.e_blocks) + (cc >> 1);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int rr = min(row + j, H - 1);
-        o.cw[j] = *reinterpret_cast<const u32x4 *>(wp + int64_t(rr) * (I >> 1));
-        o.sc[j] = ap[int64_t(rr) * (I / kBlock)];
+        const uint32_t rr = uint32_t(min(row + j, H - 1));
+        o.cw[j] = *reinterpret_cast<const u32x4 *>(W.packed + (wb + rr * uint32_t(I >> 1)));
+        o.sc[j] = W.absmax[ab + rr * uint32_t(I / kBlock)];
       }
     };
     RingSet ring[kRingDepth];
@@ -962,7 +965,9 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
       default: return f(std::integral_constant<int, 64>());
     }
   };
-  if (!mx && H == kRingH && E <= kRingMaxE) {
+  // the 1024-thread launches address a stack with 32-bit offsets
+  auto small = [](const e4b_stack &st) { return st.E * st.out * st.in / 2 < (int64_t(1) << 31); };
+  if (!mx && H == kRingH && E <= kRingMaxE && small(gu)) {
     // one 1024-thread workgroup per CU, blocks of up to kRingMaxUnits units
     const int units = int(std::min<int64_t>(kRingMaxUnits, std::max<int64_t>(1, (I + cus - 1) / std::max(cus, 1))));
     const int64_t nblk = (I + units - 1) / units;
@@ -979,7 +984,7 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
     });
   }
   if (err != hipSuccess) return err;
-  if (!mx && I <= kDnRingMaxI && int64_t(T) * k * I <= kDnRingA) {
+  if (!mx && I <= kDnRingMaxI && int64_t(T) * k * I <= kDnRingA && small(dn)) {
     const dim3 grid(uint32_t(std::min<int64_t>((H + kDnRingRows - 1) / kDnRingRows, std::max(cus, 1))));
     return launch_k(ev, E4B_K_DECODE_DOWN, decode_down_ring_kernel, grid, dim3(kRingThreads), s, Wdn, H, I, T, k, cbk,
                     plan, a, y);
