@@ -361,6 +361,28 @@ def test_decode_rows_of_2048_routed(E, T):
     tol_check(to_np(y), _oracle_fwd(pb, idx_ref, w_ref), f"y rows2048 routed E{E}")
 
 
+def test_decode_gate_up_launches_agree_bitwise():
+    """The 1024-thread gate_up launch (E <= 256) and the 256-thread one (E = 257)
+    compute each pair with the same products, chunk scaling and lane sums: the
+    same 256 experts routed the same way give the same y bits, whether or not
+    the layer holds a 257th (never routed) expert."""
+    cfg = MoEConfig("agree", E=257, H=2048, I=64, k=8, T=8, routing="normal")
+    announce("decode gate_up launches agree bitwise E256 vs E257 H2048 I64 k8 T8")
+    pb = Problem(cfg, seed=5, with_grad=False)
+    st = [pb.layer.gate_up, pb.layer.down]
+    sub = e4b.MoELayer(*(e4b.QuantStack(q.packed[:256].contiguous(), q.absmax[:256].contiguous(), 256, q.out, q.inn,
+                                        q.codebook) for q in st))
+    idx = _ids_with_repeats(256, cfg.T, cfg.k, np.random.default_rng(5))
+    idx[1] = np.arange(8) * 31  # experts spread over the stack
+    w = (np.random.default_rng(6).random((cfg.T, cfg.k)) + 0.1).astype(np.float32)
+    idx_d, w_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV)
+    y256, _, _, _ = e4b.moe_forward(sub, pb.x_d, cfg.k, topk_idx=idx_d, topk_w=w_d, path="decode")
+    y257, _, _, _ = e4b.moe_forward(pb.layer, pb.x_d, cfg.k, topk_idx=idx_d, topk_w=w_d, path="decode")
+    torch.cuda.synchronize()
+    assert torch.equal(y256.view(torch.int16), y257.view(torch.int16))
+    tol_check(to_np(y256), _oracle_fwd(pb, idx, w.astype(np.float64)), "y agree")
+
+
 def test_grouped_topk_equals_E():
     """Every token routed to every expert (top_k = E)."""
     cfg = MoEConfig("allE", E=4, H=256, I=128, k=4, T=96, routing="normal")
