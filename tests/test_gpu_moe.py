@@ -383,6 +383,27 @@ def test_decode_gate_up_launches_agree_bitwise():
     tol_check(to_np(y256), _oracle_fwd(pb, idx, w.astype(np.float64)), "y agree")
 
 
+def test_decode_down_launches_agree_bitwise():
+    """The 1024-thread down launch (P * I <= 48K: P = 64 here) and the 256-thread
+    one (P = 72: a ninth slot per token, routed with weight 0) compute each pair
+    and each combine the same way: the same y bits."""
+    cfg = MoEConfig("agree_dn", E=16, H=2048, I=768, k=8, T=8, routing="normal")
+    announce("decode down launches agree bitwise P64 vs P72 E16 H2048 I768 T8")
+    pb = Problem(cfg, seed=7, with_grad=False)
+    rng = np.random.default_rng(7)
+    idx8 = np.stack([rng.permutation(16)[:8] for _ in range(cfg.T)]).astype(np.int32)
+    w8 = (rng.random((cfg.T, 8)) + 0.1).astype(np.float32)
+    idx9 = np.concatenate([idx8, idx8[:, :1]], axis=1)
+    w9 = np.concatenate([w8, np.zeros((cfg.T, 1), np.float32)], axis=1)
+    ys = []
+    for idx, w in ((idx8, w8), (idx9, w9)):
+        y, _, _, _ = e4b.moe_forward(pb.layer, pb.x_d, idx.shape[1], topk_idx=torch.from_numpy(idx).to(DEV),
+                                     topk_w=torch.from_numpy(w).to(DEV), path="decode")
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
+
+
 def test_grouped_topk_equals_E():
     """Every token routed to every expert (top_k = E)."""
     cfg = MoEConfig("allE", E=4, H=256, I=128, k=4, T=96, routing="normal")
