@@ -635,7 +635,6 @@ __global__ __launch_bounds__(kRingThreads) void decode_gate_up_ring_kernel(
     uint16_t *__restrict__ a) {
   static_assert(kRingH / 32 == 64 && kBlock == 64, "one chunk per lane, two chunks per block");
   static_assert(kDecMaxPairs * kRingMaxUnits <= 1024 && kRingMaxUnits <= 4, "item / ub by multiply and shift");
-  static_assert(kRingThreads % kDecThreads == 0, "the code table is filled by the first 256 threads");
   __shared__ DecodeRingLds L;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   fill_code_table64<kRingThreads>(L.tbl, cb);
