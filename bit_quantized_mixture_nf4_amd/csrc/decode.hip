@@ -618,17 +618,29 @@ struct RingSet {
 
 // Offsets are 32-bit: the launch takes these kernels only for stacks below
 // 2^31 bytes, so each address is the stack's base plus one unsigned offset.
+// MX: the chunk's E8M0 scale byte (one per 32 elements) instead of the fp32
+// absmax of its 64-element block.
+template <bool MX>
 __device__ __forceinline__ void ring_load(const DecStack &W, int I, int e, int u, int lane, RingSet &o) {
   const uint32_t eb = uint32_t(W.e_bytes), ea = uint32_t(W.e_blocks);
   const uint32_t w0 = uint32_t(e) * eb + uint32_t(u) * (kRingH / 2) + uint32_t(lane) * 16;
-  const uint32_t a0 = uint32_t(e) * ea + uint32_t(u) * (kRingH / kBlock) + (uint32_t(lane) >> 1);
-  const uint32_t wd = uint32_t(I) * (kRingH / 2), ad = uint32_t(I) * (kRingH / kBlock);  // gate -> up row
+  const uint32_t wd = uint32_t(I) * (kRingH / 2);  // gate -> up row
   o.cw[0] = *reinterpret_cast<const u32x4 *>(W.packed + w0);
   o.cw[1] = *reinterpret_cast<const u32x4 *>(W.packed + (w0 + wd));
-  o.sc[0] = W.absmax[a0];
-  o.sc[1] = W.absmax[a0 + ad];
+  if constexpr (MX) {
+    const uint32_t s0 = uint32_t(e) * ea + uint32_t(u) * (kRingH / kMxBlock) + uint32_t(lane);
+    const uint32_t sd = uint32_t(I) * (kRingH / kMxBlock);
+    o.sc[0] = e8m0_value(W.scales[s0]);
+    o.sc[1] = e8m0_value(W.scales[s0 + sd]);
+  } else {
+    const uint32_t a0 = uint32_t(e) * ea + uint32_t(u) * (kRingH / kBlock) + (uint32_t(lane) >> 1);
+    const uint32_t ad = uint32_t(I) * (kRingH / kBlock);
+    o.sc[0] = W.absmax[a0];
+    o.sc[1] = W.absmax[a0 + ad];
+  }
 }
 
+template <bool MX>
 __global__ __launch_bounds__(kRingThreads) void decode_gate_up_ring_kernel(
     const float *__restrict__ logits, int E, int k, int T, int32_t *__restrict__ idx_io, float *__restrict__ w_io,
     DecStack W, int I, int units, const uint16_t *__restrict__ x, DecCodebook cb, DecodePlan *__restrict__ plan,
@@ -666,7 +678,7 @@ __global__ __launch_bounds__(kRingThreads) void decode_gate_up_ring_kernel(
       constexpr int r = decltype(rc)::value;
       if (r < nq) {
         const int d = item_d(r);
-        ring_load(W, I, L.groups.expert[d], item_u(r, d), lane, ring[r]);
+        ring_load<MX>(W, I, L.groups.expert[d], item_u(r, d), lane, ring[r]);
       }
     });
     for (int q0 = 0; q0 < nq; q0 += kRingDepth) {
@@ -684,7 +696,7 @@ __global__ __launch_bounds__(kRingThreads) void decode_gate_up_ring_kernel(
           // this set's next item, loaded under the products
           if (q + kRingDepth < nq) {
             const int d2 = item_d(q + kRingDepth);
-            ring_load(W, I, L.groups.expert[d2], item_u(q + kRingDepth, d2), lane, ring[r]);
+            ring_load<MX>(W, I, L.groups.expert[d2], item_u(q + kRingDepth, d2), lane, ring[r]);
           }
           __builtin_amdgcn_sched_barrier(0);
           for (int pp = 0; pp < cnt; ++pp) {
@@ -805,6 +817,7 @@ struct DecodeDnRingLds {
   int32_t pos[kDecMaxPairs];
 };
 
+template <bool MX>
 __global__ __launch_bounds__(kRingThreads) void decode_down_ring_kernel(DecStack W, int H, int I, int T, int k,
                                                                         DecCodebook cb,
                                                                         const DecodePlan *__restrict__ plan,
@@ -856,12 +869,16 @@ __global__ __launch_bounds__(kRingThreads) void decode_down_ring_kernel(DecStack
     auto load = [&](int q, RingSet &o) {
       const int d = (wv + q * kRingWaves) / kQ, row = item_row(q);
       const uint32_t e = uint32_t(L.groups.expert[d]);
-      const uint32_t wb = e * uint32_t(W.e_bytes) + uint32_t(cc) * 16, ab = e * uint32_t(W.e_blocks) + (cc >> 1);
+      const uint32_t wb = e * uint32_t(W.e_bytes) + uint32_t(cc) * 16;
+      const uint32_t ab = e * uint32_t(W.e_blocks) + (MX ? uint32_t(cc) : uint32_t(cc) >> 1);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const uint32_t rr = uint32_t(min(row + j, H - 1));
         o.cw[j] = *reinterpret_cast<const u32x4 *>(W.packed + (wb + rr * uint32_t(I >> 1)));
-        o.sc[j] = W.absmax[ab + rr * uint32_t(I / kBlock)];
+        if constexpr (MX)
+          o.sc[j] = e8m0_value(W.scales[ab + rr * uint32_t(I / kMxBlock)]);
+        else
+          o.sc[j] = W.absmax[ab + rr * uint32_t(I / kBlock)];
       }
     };
     RingSet ring[kRingDepth];
@@ -966,13 +983,15 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
   };
   // the 1024-thread launches address a stack with 32-bit offsets
   auto small = [](const e4b_stack &st) { return st.E * st.out * st.in / 2 < (int64_t(1) << 31); };
-  if (!mx && H == kRingH && E <= kRingMaxE && small(gu)) {
+  if (H == kRingH && E <= kRingMaxE && small(gu)) {
     // one 1024-thread workgroup per CU, blocks of up to kRingMaxUnits units
     const int units = int(std::min<int64_t>(kRingMaxUnits, std::max<int64_t>(1, (I + cus - 1) / std::max(cus, 1))));
     const int64_t nblk = (I + units - 1) / units;
     const dim3 grid(uint32_t(std::min<int64_t>(nblk, std::max(cus, 1))));
-    err = launch_k(ev, E4B_K_DECODE_GATE_UP, decode_gate_up_ring_kernel, grid, dim3(kRingThreads), s, logits, E, k,
-                   T, idx, wts, Wgu, I, units, x, cbk, plan, a);
+    err = mx ? launch_k(ev, E4B_K_DECODE_GATE_UP, decode_gate_up_ring_kernel<true>, grid, dim3(kRingThreads), s, logits,
+                        E, k, T, idx, wts, Wgu, I, units, x, cbk, plan, a)
+             : launch_k(ev, E4B_K_DECODE_GATE_UP, decode_gate_up_ring_kernel<false>, grid, dim3(kRingThreads), s,
+                        logits, E, k, T, idx, wts, Wgu, I, units, x, cbk, plan, a);
   } else {
     err = with_lpr(H, [&](auto lpr) {
     constexpr int LPR = decltype(lpr)::value;
@@ -983,10 +1002,12 @@ hipError_t launch_decode_forward(const MoePlan &p, const e4b_moe_layer *L, const
     });
   }
   if (err != hipSuccess) return err;
-  if (!mx && I <= kDnRingMaxI && int64_t(T) * k * I <= kDnRingA && small(dn)) {
+  if (I <= kDnRingMaxI && int64_t(T) * k * I <= kDnRingA && small(dn)) {
     const dim3 grid(uint32_t(std::min<int64_t>((H + kDnRingRows - 1) / kDnRingRows, std::max(cus, 1))));
-    return launch_k(ev, E4B_K_DECODE_DOWN, decode_down_ring_kernel, grid, dim3(kRingThreads), s, Wdn, H, I, T, k, cbk,
-                    plan, a, y);
+    return mx ? launch_k(ev, E4B_K_DECODE_DOWN, decode_down_ring_kernel<true>, grid, dim3(kRingThreads), s, Wdn, H, I,
+                         T, k, cbk, plan, a, y)
+              : launch_k(ev, E4B_K_DECODE_DOWN, decode_down_ring_kernel<false>, grid, dim3(kRingThreads), s, Wdn, H, I,
+                         T, k, cbk, plan, a, y);
   }
   return with_lpr(I, [&](auto lpr) {
     constexpr int LPR = decltype(lpr)::value;

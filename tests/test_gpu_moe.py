@@ -335,7 +335,8 @@ def _ids_with_repeats(E, T, k, rng):
     return idx
 
 
-@pytest.mark.parametrize("E,I,T,k,kind", [(8, 1088, 8, 4, "nf4"), (256, 64, 8, 8, "fp4"), (6, 640, 3, 2, "nf4")])
+@pytest.mark.parametrize("E,I,T,k,kind", [(8, 1088, 8, 4, "nf4"), (256, 64, 8, 8, "fp4"), (6, 640, 3, 2, "nf4"),
+                                          (16, 640, 8, 8, "mxfp4")])
 def test_decode_rows_of_2048(E, I, T, k, kind):
     """H = 2048 (one 32-element chunk per lane of a wave) and E <= 256 take the
     one-workgroup-per-CU gate_up launch: blocks of ceil(I / CUs) units, at most
@@ -361,17 +362,22 @@ def test_decode_rows_of_2048_routed(E, T):
     tol_check(to_np(y), _oracle_fwd(pb, idx_ref, w_ref), f"y rows2048 routed E{E}")
 
 
-def test_decode_gate_up_launches_agree_bitwise():
+@pytest.mark.parametrize("kind", ["nf4", "mxfp4"])
+def test_decode_gate_up_launches_agree_bitwise(kind):
     """The 1024-thread gate_up launch (E <= 256) and the 256-thread one (E = 257)
     compute each pair with the same products, chunk scaling and lane sums: the
     same 256 experts routed the same way give the same y bits, whether or not
     the layer holds a 257th (never routed) expert."""
     cfg = MoEConfig("agree", E=257, H=2048, I=64, k=8, T=8, routing="normal")
-    announce("decode gate_up launches agree bitwise E256 vs E257 H2048 I64 k8 T8")
-    pb = Problem(cfg, seed=5, with_grad=False)
+    announce(f"decode gate_up launches agree bitwise {kind} E256 vs E257 H2048 I64 k8 T8")
+    pb = Problem(cfg, seed=5, codebook=kind, with_grad=False)
     st = [pb.layer.gate_up, pb.layer.down]
-    sub = e4b.MoELayer(*(e4b.QuantStack(q.packed[:256].contiguous(), q.absmax[:256].contiguous(), 256, q.out, q.inn,
-                                        q.codebook) for q in st))
+
+    def first(t):
+        return None if t is None else t[:256].contiguous()
+
+    sub = e4b.MoELayer(*(e4b.QuantStack(first(q.packed), first(q.absmax), 256, q.out, q.inn, q.codebook,
+                                        first(q.scales)) for q in st))
     idx = _ids_with_repeats(256, cfg.T, cfg.k, np.random.default_rng(5))
     idx[1] = np.arange(8) * 31  # experts spread over the stack
     w = (np.random.default_rng(6).random((cfg.T, cfg.k)) + 0.1).astype(np.float32)
